@@ -1,0 +1,137 @@
+"""The HiF4 oracle: a plain, slow, obviously correct CPU reference.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP library
+never calls it; the two share no code.
+
+The arithmetic lives in ``hif4_oracle.c`` (plain C, IEEE double); this module
+only marshals numpy arrays through ctypes. bf16 tensors are passed as their
+uint16 bit patterns. Every function cites the page passage it follows in the
+C source.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.hif4o_e6m2_value.argtypes = [ctypes.c_int]
+        lib.hif4o_e6m2_value.restype = ctypes.c_double
+        lib.hif4o_quantize.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
+        lib.hif4o_quantize.restype = ctypes.c_int
+        lib.hif4o_dequantize.argtypes = [p, p, i64, i64, p]
+        lib.hif4o_dequantize.restype = ctypes.c_int
+        lib.hif4o_linear.argtypes = [p, p, p, p, i64, i64, i64, p, p]
+        lib.hif4o_linear.restype = ctypes.c_int
+        lib.hif4o_percentile.argtypes = [p, i64, i64, i64, ctypes.c_double, p]
+        lib.hif4o_percentile.restype = ctypes.c_int
+        lib.hif4o_topn_mask.argtypes = [p, i64, i64, p]
+        lib.hif4o_topn_mask.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc == 1:
+        raise OracleError(f"{what}: invalid argument")
+    if rc == 2:
+        raise OracleError(f"{what}: non-finite input (out of contract)")
+    if rc != 0:
+        raise OracleError(f"{what}: status {rc}")
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def e6m2_value(c: int) -> float:
+    """Value of the level-1 E6M2 code c (0..255)."""
+    return _lib().hif4o_e6m2_value(int(c))
+
+
+def quantize(x_bits: np.ndarray, mask: np.ndarray = None):
+    """HiF4-quantize rows of bf16 bits [rows][k] along k.
+
+    Returns (codes u8 [rows][k/2], meta u32 [rows][k/64], kept u16 [rows][n_mask]).
+    ``mask`` (u8 [k], nonzero = protected) zeroes those channels in the HiF4
+    stream and copies their bf16 bits into ``kept`` in ascending channel order.
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, k = x.shape
+    codes = np.zeros((rows, k // 2), dtype=np.uint8)
+    meta = np.zeros((rows, k // 64), dtype=np.uint32)
+    n_mask = 0
+    m = None
+    kept = np.zeros((rows, 0), dtype=np.uint16)
+    if mask is not None:
+        m = np.ascontiguousarray(mask, dtype=np.uint8)
+        n_mask = int(np.count_nonzero(m))
+        kept = np.zeros((rows, n_mask), dtype=np.uint16)
+    rc = _lib().hif4o_quantize(_ptr(x), rows, k, k, _ptr(m), n_mask,
+                               _ptr(kept) if n_mask else None, _ptr(codes), _ptr(meta))
+    _check(rc, "quantize")
+    return codes, meta, kept
+
+
+def dequantize(codes: np.ndarray, meta: np.ndarray) -> np.ndarray:
+    """Decode HiF4 codes [rows][k/2] + meta [rows][k/64] into float64 [rows][k]."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    m = np.ascontiguousarray(meta, dtype=np.uint32)
+    rows, k = c.shape[0], c.shape[1] * 2
+    out = np.zeros((rows, k), dtype=np.float64)
+    _check(_lib().hif4o_dequantize(_ptr(c), _ptr(m), rows, k, _ptr(out)), "dequantize")
+    return out
+
+
+def linear(xc, xm, wc, wm, with_mag: bool = True):
+    """Y = deq(Q(X)) deq(Q(W))^T in float64 from codes, plus S = sum |a||b|."""
+    xc = np.ascontiguousarray(xc, dtype=np.uint8)
+    xm = np.ascontiguousarray(xm, dtype=np.uint32)
+    wc = np.ascontiguousarray(wc, dtype=np.uint8)
+    wm = np.ascontiguousarray(wm, dtype=np.uint32)
+    m, n, k = xc.shape[0], wc.shape[0], xc.shape[1] * 2
+    if wc.shape[1] * 2 != k:
+        raise OracleError("linear: K mismatch")
+    y = np.zeros((m, n), dtype=np.float64)
+    s = np.zeros((m, n), dtype=np.float64) if with_mag else None
+    _check(_lib().hif4o_linear(_ptr(xc), _ptr(xm), _ptr(wc), _ptr(wm), m, n, k, _ptr(y), _ptr(s)),
+           "linear")
+    return (y, s) if with_mag else y
+
+
+def percentile(x_bits: np.ndarray, q: float) -> np.ndarray:
+    """Per-channel type-7 quantile at level q of |x| over the rows -> float32 [c]."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, c = x.shape
+    stats = np.zeros((c,), dtype=np.float32)
+    _check(_lib().hif4o_percentile(_ptr(x), rows, c, c, float(q), _ptr(stats)), "percentile")
+    return stats
+
+
+def topn_mask(stats: np.ndarray, n_protect: int) -> np.ndarray:
+    """u8 mask [c]: 1 for the n_protect largest stats, ties to the lower index."""
+    s = np.ascontiguousarray(stats, dtype=np.float32)
+    mask = np.zeros((s.shape[0],), dtype=np.uint8)
+    _check(_lib().hif4o_topn_mask(_ptr(s), s.shape[0], int(n_protect), _ptr(mask)), "topn_mask")
+    return mask
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bf16 bit patterns (a plain bit move)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)

@@ -1,0 +1,340 @@
+/*
+ * hif4_oracle.c -- plain, slow CPU oracle for the HiF4 W4A4 hot path.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke entry point and the
+ * cpu_baseline leg of the benchmark may load this code. The product path
+ * (the HIP library) never calls it and shares no source with it.
+ *
+ * Sources (cited by page title and section throughout):
+ *  [HiF4-fmt]  HiFloat4 calibration article (hwcomputing.csdn.net),
+ *              section "一：HiFloat4 (HiF4) 格式": the 64-element unit, the
+ *              E6M2 level-1 scale, the E1 level-2 (per 8) and level-3
+ *              (per 4) micro-exponents, the S1P2 element and its value set,
+ *              and the 32-bit metadata budget.
+ *  [HiGPTQ]    same article, section 3.1 "HiGPTQ": exponents named 1-0,
+ *              2-(0..7), 3-(0..15) in column order, each fixed from
+ *              statistics of the data it covers.
+ *  [HiFlat]    same article, section 3.3 "HiFlatQuant": HiF4's range is wide
+ *              enough that no clipping thresholds are needed.
+ *  [TA-method] "Tail-Aware HiFloat4: W4A4 PTQ calibration for Wan2.2"
+ *              (agents-report.net), sections "方法概述" and
+ *              "尾部百分位統計的動機": per-channel tail percentile statistics
+ *              of the activations build a channel-protection mask.
+ *  [TA-abs]    arXiv 2605.26628 record, abstract: W4A4 HiFloat4 fake
+ *              quantization of the main linear layers.
+ *
+ * The element formula of [HiF4-fmt] is an image that did not survive; the
+ * readings this file takes where the pages are silent are marked READING.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (oracle/build.py).
+ * Floating point is IEEE double; every comparison below is between values
+ * that are exact in double, so the encoder decisions are exact on reals.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define HIF4O_OK 0
+#define HIF4O_ERR_ARG 1
+#define HIF4O_ERR_NONFINITE 2
+
+#define UNIT 64 /* [HiF4-fmt]: one HiF4 unit groups 64 elements */
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16 bit pattern -> its exact value as a double. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Level-1 scale, E6M2 ([HiF4-fmt]: 6 exponent bits, 2 mantissa bits).
+ * READING: unsigned code c in 0..255, exponent field c>>2 with bias 31,
+ * every code normal (no zero / Inf / NaN): v(c) = 2^(c>>2 - 31) * (1 + (c&3)/4). */
+double hif4o_e6m2_value(int c)
+{
+    return ldexp(1.0 + (double)(c & 3) / 4.0, (c >> 2) - 31);
+}
+
+/* E1 micro-exponent ([HiF4-fmt]: power-of-two scaling inside the unit).
+ * READING: bit b multiplies by 2^b. */
+static double e1_factor(int b) { return b ? 2.0 : 1.0; }
+
+/* READING (code layout). Unit u of a row owns bytes [32u, 32u+32) of the row's
+ * codes. Element j of the unit lives in byte 4*(j/8) + (j%4); it is the low
+ * nibble when (j%8) < 4 and the high nibble otherwise. So the 32-bit word w of
+ * the unit holds level-2 group w ([HiGPTQ] order along K): its low nibbles are
+ * level-3 group 2w, its high nibbles level-3 group 2w+1.
+ * meta = c | e2bits << 8 | e3bits << 16, bit g of e2bits for elements 8g..8g+7,
+ * bit q of e3bits for elements 4q..4q+3: 8 + 8 + 16 = 32 bits ([HiF4-fmt]). */
+static int code_byte(int j) { return 4 * (j / 8) + (j % 4); }
+static int code_shift(int j) { return (j % 8) < 4 ? 0 : 4; }
+
+/* S1P2 nibble ([HiF4-fmt]): sign bit, one integer bit, two fraction bits.
+ * READING: sign = bit 3, magnitude k/4 with k = nibble & 7 (integer bit k>>2,
+ * fraction bits k&3), so |value| is one of 0, 0.25, ..., 1.75. */
+static double s1p2_value(int nib)
+{
+    double mag = (double)(nib & 7) / 4.0;
+    return (nib & 8) ? -mag : mag;
+}
+
+/* ------------------------------------------------------------ quantize */
+
+/* Encode one 64-element unit. x[] are exact reals (bf16 values read as
+ * doubles; masked entries already replaced by 0).
+ * READING (the encoding rule; [HiGPTQ] fixes each exponent from the data it
+ * covers, [HiFlat] says no clipping is needed): choose every scale as small
+ * as it can be without any element exceeding its grid maximum, then round
+ * each element to the nearest grid point, ties to even. */
+static void quantize_unit(const double x[UNIT], uint8_t codes[32], uint32_t *meta)
+{
+    /* step 1: the maxima of |x| over the unit, each level-2 group (8) and
+     * each level-3 group (4). */
+    double A = 0.0, M8[8], M4[16];
+    for (int g = 0; g < 8; ++g) M8[g] = 0.0;
+    for (int q = 0; q < 16; ++q) M4[q] = 0.0;
+    for (int j = 0; j < UNIT; ++j) {
+        double a = fabs(x[j]);
+        if (a > A) A = a;
+        if (a > M8[j / 8]) M8[j / 8] = a;
+        if (a > M4[j / 4]) M4[j / 4] = a;
+    }
+
+    /* step 2: level-1 code = the smallest c whose largest representable
+     * magnitude, 1.75 * 2 * 2 * v(c) = 7 v(c), is at least A. If no code
+     * reaches A the range saturates at c = 255. */
+    int c = 255;
+    for (int cc = 0; cc < 256; ++cc) {
+        if (7.0 * hif4o_e6m2_value(cc) >= A) {
+            c = cc;
+            break;
+        }
+    }
+    double s = hif4o_e6m2_value(c);
+
+    /* step 3: level-2 bit of group g is set iff the group does not fit
+     * under 1.75 * 2 * s (its largest magnitude with e2 = 0). */
+    int e2[8];
+    for (int g = 0; g < 8; ++g) e2[g] = M8[g] > 1.75 * 2.0 * s;
+
+    /* step 4: level-3 bit of group q is set iff the group does not fit
+     * under 1.75 * 2^e2 * s (its largest magnitude with e3 = 0). */
+    int e3[16];
+    for (int q = 0; q < 16; ++q) e3[q] = M4[q] > 1.75 * e1_factor(e2[q / 2]) * s;
+
+    /* step 5: round |x| onto the grid {k D / 4 : k = 0..7}, D = s 2^e2 2^e3,
+     * to nearest with ties to even k. The grid midpoints are (2m+1) D / 8;
+     * k counts the midpoints strictly below |x|; at a midpoint the even
+     * neighbour wins. Beyond the last midpoint k stays 7 (saturation). */
+    memset(codes, 0, 32);
+    for (int j = 0; j < UNIT; ++j) {
+        double D = s * e1_factor(e2[j / 8]) * e1_factor(e3[j / 4]);
+        double a = fabs(x[j]);
+        int k = 0;
+        for (int m = 0; m < 7; ++m) {
+            double mid = (double)(2 * m + 1) * D / 8.0;
+            if (a > mid) {
+                k = m + 1;
+            } else {
+                if (a == mid) k = (m % 2 == 0) ? m : m + 1;
+                break;
+            }
+        }
+        /* READING: zero is always +0 (no sign on a zero element). */
+        int sign = (x[j] < 0.0) && (k != 0);
+        int nib = k | (sign << 3);
+        codes[code_byte(j)] |= (uint8_t)(nib << code_shift(j));
+    }
+
+    uint32_t m = (uint32_t)c;
+    for (int g = 0; g < 8; ++g) m |= (uint32_t)e2[g] << (8 + g);
+    for (int q = 0; q < 16; ++q) m |= (uint32_t)e3[q] << (16 + q);
+    *meta = m;
+}
+
+/* x: bf16 bits [rows][ld], k % 64 == 0. codes: [rows][k/2], meta: [rows][k/64].
+ * mask: NULL or u8 [k]; nonzero = protected channel. Protected entries are
+ * encoded as 0 and their bf16 bits copied, in ascending channel order, to
+ * kept [rows][n_mask] ([TA-method]: protected channels stay high precision).
+ * Returns HIF4O_ERR_NONFINITE if any (unprotected) input is Inf or NaN. */
+int hif4o_quantize(const uint16_t *x, int64_t rows, int64_t k, int64_t ld,
+                   const uint8_t *mask, int64_t n_mask, uint16_t *kept,
+                   uint8_t *codes, uint32_t *meta)
+{
+    if (rows < 0 || k < 0 || k % UNIT != 0 || ld < k) return HIF4O_ERR_ARG;
+    if (mask) {
+        int64_t cnt = 0;
+        for (int64_t i = 0; i < k; ++i) cnt += mask[i] != 0;
+        if (cnt != n_mask || (n_mask > 0 && !kept)) return HIF4O_ERR_ARG;
+    }
+    int64_t units = k / UNIT;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * ld;
+        int64_t kp = 0;
+        for (int64_t u = 0; u < units; ++u) {
+            double v[UNIT];
+            for (int j = 0; j < UNIT; ++j) {
+                int64_t ch = u * UNIT + j;
+                double val = bf16_value(xr[ch]);
+                if (mask && mask[ch]) {
+                    kept[r * n_mask + kp++] = xr[ch];
+                    val = 0.0;
+                } else if (!isfinite(val)) {
+                    bad = 1;
+                    val = 0.0;
+                }
+                v[j] = val;
+            }
+            quantize_unit(v, codes + r * (k / 2) + u * 32, meta + r * units + u);
+        }
+    }
+    return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* ---------------------------------------------------------- dequantize */
+
+/* The value of element j of a unit (READING of the lost element formula):
+ * x = S1P2(nibble) * 2^e2[j/8] * 2^e3[j/4] * v(c). */
+static double unit_element(const uint8_t *ucodes, uint32_t m, int j)
+{
+    int nib = (ucodes[code_byte(j)] >> code_shift(j)) & 15;
+    int c = (int)(m & 255u);
+    int e2 = (int)((m >> (8 + j / 8)) & 1u);
+    int e3 = (int)((m >> (16 + j / 4)) & 1u);
+    return s1p2_value(nib) * e1_factor(e2) * e1_factor(e3) * hif4o_e6m2_value(c);
+}
+
+/* codes [rows][k/2], meta [rows][k/64] -> out [rows][k] as doubles. */
+int hif4o_dequantize(const uint8_t *codes, const uint32_t *meta, int64_t rows, int64_t k,
+                     double *out)
+{
+    if (rows < 0 || k < 0 || k % UNIT != 0) return HIF4O_ERR_ARG;
+    int64_t units = k / UNIT;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t u = 0; u < units; ++u)
+            for (int j = 0; j < UNIT; ++j)
+                out[r * k + u * UNIT + j] =
+                    unit_element(codes + r * (k / 2) + u * 32, meta[r * units + u], j);
+    return HIF4O_OK;
+}
+
+/* -------------------------------------------------------------- linear */
+
+/* Fake-quantized linear ([TA-abs]; the form Y = X W^T of the same article's
+ * FlatQuant section): Y[i][j] = sum_t a[i][t] b[j][t] with a = deq(Q(X)),
+ * b = deq(Q(W)), summed in double in t order. S[i][j] = sum_t |a||b| sizes
+ * the error bound of a float32 accumulation. Operands are given as codes. */
+int hif4o_linear(const uint8_t *xc, const uint32_t *xm, const uint8_t *wc, const uint32_t *wm,
+                 int64_t m, int64_t n, int64_t k, double *y, double *s)
+{
+    if (m < 0 || n < 0 || k < 0 || k % UNIT != 0) return HIF4O_ERR_ARG;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(m * k + 1));
+    double *b = (double *)malloc(sizeof(double) * (size_t)(n * k + 1));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return HIF4O_ERR_ARG;
+    }
+    hif4o_dequantize(xc, xm, m, k, a);
+    hif4o_dequantize(wc, wm, n, k, b);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                double p = a[i * k + t] * b[j * k + t];
+                acc += p;
+                mag += fabs(p);
+            }
+            y[i * n + j] = acc;
+            if (s) s[i * n + j] = mag;
+        }
+    }
+    free(a);
+    free(b);
+    return HIF4O_OK;
+}
+
+/* ---------------------------------------------------------- percentile */
+
+static int cmp_double(const void *pa, const void *pb)
+{
+    double a = *(const double *)pa, b = *(const double *)pb;
+    return (a > b) - (a < b);
+}
+
+/* Per-channel tail statistic ([TA-method]: a percentile of the activation
+ * magnitudes per channel, used in place of the maximum).
+ * READING: the type-7 (linear interpolation) quantile at level q of |x[:, ch]|
+ * over all rows: sort ascending into v, h = q (n-1), lo = floor(h),
+ * hi = min(lo+1, n-1), stat = v[lo] + (h - lo) (v[hi] - v[lo]), each double
+ * operation rounded on its own, then rounded to float. */
+int hif4o_percentile(const uint16_t *x, int64_t rows, int64_t c, int64_t ld, double q,
+                     float *stats)
+{
+    if (rows < 1 || c < 0 || ld < c || !(q >= 0.0 && q <= 1.0)) return HIF4O_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int64_t ch = 0; ch < c; ++ch) {
+        double *v = (double *)malloc(sizeof(double) * (size_t)rows);
+        if (!v) {
+            bad = 1;
+            continue;
+        }
+        for (int64_t r = 0; r < rows; ++r) {
+            v[r] = fabs(bf16_value(x[r * ld + ch]));
+            if (!isfinite(v[r])) bad = 1;
+        }
+        qsort(v, (size_t)rows, sizeof(double), cmp_double);
+        double h = q * (double)(rows - 1);
+        double lo_f = floor(h);
+        int64_t lo = (int64_t)lo_f;
+        int64_t hi = lo + 1 < rows ? lo + 1 : rows - 1;
+        double f = h - lo_f;
+        double d = v[hi] - v[lo];
+        double t = f * d;
+        double r = v[lo] + t;
+        stats[ch] = (float)r;
+        free(v);
+    }
+    return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* ----------------------------------------------------------------- mask */
+
+static const float *g_sort_stats; /* used only inside hif4o_topn_mask */
+
+static int cmp_rank(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    float sa = g_sort_stats[a], sb = g_sort_stats[b];
+    if (sa > sb) return -1;
+    if (sa < sb) return 1;
+    return (a > b) - (a < b);
+}
+
+/* Channel-protection mask ([TA-method]: the channels with the largest tail
+ * statistics are protected). READING: order channels by (stat descending,
+ * index ascending); the first n_protect get mask 1. Not thread-safe (qsort
+ * comparator state); the tests call it from one thread. */
+int hif4o_topn_mask(const float *stats, int64_t c, int64_t n_protect, uint8_t *mask)
+{
+    if (c < 0 || n_protect < 0 || n_protect > c) return HIF4O_ERR_ARG;
+    int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)(c + 1));
+    if (!idx) return HIF4O_ERR_ARG;
+    for (int64_t i = 0; i < c; ++i) idx[i] = i;
+    g_sort_stats = stats;
+    qsort(idx, (size_t)c, sizeof(int64_t), cmp_rank);
+    for (int64_t i = 0; i < c; ++i) mask[i] = 0;
+    for (int64_t i = 0; i < n_protect; ++i) mask[idx[i]] = 1;
+    free(idx);
+    return HIF4O_OK;
+}

@@ -1,0 +1,531 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-runs the oracle's own formula: each compares it with a
+fixed fact of the pages (golden fixtures under tests/golden/, cited there), a
+hand-worked example, a closed form, an invariant, brute force on tiny inputs,
+or a library routine (numpy) where the method reduces to one.
+
+Pages: HiFloat4 calibration article (hwcomputing.csdn.net), section
+"一：HiFloat4 (HiF4) 格式" and section 3.1 "HiGPTQ"; Tail-Aware HiFloat4 summary
+(agents-report.net), sections "方法概述" and "尾部百分位統計的動機".
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import golden_io
+import oracle
+
+UNIT = 64
+
+
+# ----------------------------------------------------------------- helpers
+
+def to_bits(vals):
+    """bf16 bit patterns of values that are exactly representable in bf16."""
+    f = np.asarray(vals, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def bits_to_f64(bits):
+    return oracle.bf16_bits_to_float(bits).astype(np.float64)
+
+
+def nibble(codes_row, j):
+    """Element j's nibble under the documented code layout (reading): byte
+    4*(j//8) + j%4 of its unit, low nibble when j%8 < 4."""
+    u, jj = divmod(j, UNIT)
+    b = codes_row[u * 32 + 4 * (jj // 8) + jj % 4]
+    return int(b >> 4) if jj % 8 >= 4 else int(b & 15)
+
+
+def unit_fields(meta_word):
+    c = meta_word & 255
+    e2 = [(meta_word >> (8 + g)) & 1 for g in range(8)]
+    e3 = [(meta_word >> (16 + q)) & 1 for q in range(16)]
+    return int(c), e2, e3
+
+
+# ------------------------------------------------- fixed facts of the pages
+
+def test_s1p2_value_set_decodes_exactly():
+    """All 16 nibbles decode to the S1P2 set of the format section (golden)."""
+    mags = golden_io.s1p2_magnitudes()
+    assert mags == [k / 4 for k in range(8)]
+    codes = np.zeros((1, 32), np.uint8)
+    for j in range(16):  # element j carries nibble j; e2 = e3 = 0
+        b = 4 * (j // 8) + j % 4
+        codes[0, b] |= (j << 4) if j % 8 >= 4 else j
+    meta = np.array([[124]], np.uint32)  # level-1 scale 1.0 under the E6M2 reading
+    x = oracle.dequantize(codes, meta)[0]
+    for j in range(16):
+        k, neg = j & 7, j >> 3
+        assert abs(x[j]) == mags[k]
+        if k:
+            assert (x[j] < 0) == bool(neg)
+    assert sorted(set(abs(v) for v in x[:16])) == mags
+
+
+def test_metadata_budget():
+    """4-bit elements + 32 metadata bits per 64 elements (golden budget)."""
+    b = golden_io.unit_budget()
+    assert b["level1_bits"] + b["level2_count"] * b["level2_bits_each"] + \
+        b["level3_count"] * b["level3_bits_each"] == b["metadata_bits"]
+    assert b["level1_exponent_bits"] + b["level1_mantissa_bits"] == b["level1_bits"]
+    rows, k = 3, 256
+    x = _random_bits(rows * k // UNIT, seed=3).reshape(rows, k)
+    codes, meta, _ = oracle.quantize(x)
+    assert codes.nbytes * 8 == rows * k * b["element_bits"]
+    assert meta.nbytes * 8 == rows * (k // b["unit_elements"]) * b["metadata_bits"]
+    assert (codes.nbytes + meta.nbytes) * 8 / (rows * k) == 4.5
+
+
+def test_e6m2_scale_has_two_mantissa_bits_and_power_of_two_steps():
+    """E6M2 (format section): 4 mantissa steps per binade, 64 binades.
+    The bias (31) and "no specials" are readings: parity unpinned."""
+    v = [oracle.e6m2_value(c) for c in range(256)]
+    assert all(a < b for a, b in zip(v, v[1:]))
+    for c in range(252):
+        assert v[c + 4] == 2 * v[c]
+    for c in range(256):
+        m = v[c] / 2.0 ** math.floor(math.log2(v[c]))
+        assert m in (1.0, 1.25, 1.5, 1.75)
+    assert v[255] / v[0] == 1.75 * 2.0 ** 63
+
+
+# --------------------------------------------------- hand-worked examples
+
+@pytest.mark.parametrize("u", golden_io.hand_units(), ids=lambda u: u["name"])
+def test_hand_units(u):
+    x = golden_io.expand(u["x"], UNIT, 0.0)
+    codes, meta, _ = oracle.quantize(to_bits(x).reshape(1, UNIT))
+    assert int(meta[0, 0]) == u["meta"], hex(int(meta[0, 0]))
+    nib = golden_io.expand(u["nib"], UNIT, 0)
+    assert [nibble(codes[0], j) for j in range(UNIT)] == nib
+    by = golden_io.expand(u["bytes"], 32, 0)
+    assert list(codes[0]) == by
+    deq = golden_io.expand(u["deq"], UNIT, 0.0)
+    assert list(oracle.dequantize(codes, meta)[0]) == deq
+
+
+# ------------------------------------------------ the level-1 rule, exact
+
+def test_level1_code_is_minimal_for_every_bf16_magnitude():
+    """For every positive finite bf16 A (alone in a unit): c is the smallest
+    code with 7 v(c) >= A, or 255 when none reaches A (exact rationals)."""
+    a_bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    x = np.zeros((a_bits.size, UNIT), np.uint16)
+    x[:, 17] = a_bits
+    _, meta, _ = oracle.quantize(x)
+    v = [Fraction(oracle.e6m2_value(c)) for c in range(256)]
+    top = 7 * v[255]
+    for A_bits, m in zip(a_bits, meta[:, 0]):
+        A = Fraction(float(bits_to_f64(np.array([A_bits]))[0]))
+        c = int(m) & 255
+        if A > top:
+            assert c == 255
+            continue
+        assert 7 * v[c] >= A
+        assert c == 0 or 7 * v[c - 1] < A
+
+
+# ------------------------------------------ element rounding, exact rationals
+
+def _check_unit_exact(xrow_bits, codes_row, meta_word, deq_row):
+    """RNE onto S1P2 on exact rationals: |x - xhat| <= D/8, ties to even k,
+    no element beyond 7D/4 unless the level-1 range saturated."""
+    c, e2, e3 = unit_fields(int(meta_word))
+    s = Fraction(oracle.e6m2_value(c))
+    xs = bits_to_f64(xrow_bits)
+    for j in range(UNIT):
+        x = Fraction(float(xs[j]))
+        D = s * 2 ** (e2[j // 8] + e3[j // 4])
+        nib = nibble(codes_row, j)
+        k = nib & 7
+        xhat = Fraction(float(deq_row[j]))
+        assert abs(xhat) == k * D / 4
+        if k == 0:
+            assert nib == 0  # canonical +0
+        else:
+            assert (xhat < 0) == (x < 0)
+        err = abs(abs(x) - k * D / 4)
+        if c == 255 and abs(x) > 7 * D / 4:
+            assert k == 7
+            continue
+        assert abs(x) <= 7 * D / 4  # no clipping
+        assert err <= D / 8
+        if err == D / 8:
+            assert k % 2 == 0, "tie must go to even k"
+
+
+def _random_bits(n, seed, spread=3.0, zero_p=0.2):
+    r = np.random.default_rng(seed)
+    x = r.standard_t(3, size=(n, UNIT)) * np.exp(r.normal(0, spread, size=(n, 1)))
+    x[r.random(size=x.shape) < zero_p] = 0.0
+    u = np.float32(x).view(np.uint32) & np.uint32(0xFFFF0000)
+    return (u >> 16).astype(np.uint16)
+
+
+def _midpoint_bits(n, seed):
+    """Units whose elements sit exactly on grid midpoints of their own unit."""
+    r = np.random.default_rng(seed)
+    rows = []
+    while len(rows) < n:
+        c = int(r.integers(20, 230))
+        s = Fraction(oracle.e6m2_value(c))
+        vals = [0.0] * UNIT
+        vals[0] = float(7 * s)  # fixes c; group 0 gets e2 = e3 = 1
+        for j in range(8, UNIT):
+            D = s  # groups 1..7 stay at e2 = e3 = 0 if all |x| <= 1.75 s
+            m = int(r.integers(0, 7))
+            v = (2 * m + 1) * D / 8
+            if v > Fraction(7, 4) * s:
+                v = Fraction(7, 4) * s
+            vals[j] = float(v) * (1 if r.random() < 0.5 else -1)
+        f = np.float32(vals)
+        if np.all((f.view(np.uint32) & 0xFFFF) == 0):
+            rows.append((f.view(np.uint32) >> 16).astype(np.uint16))
+    return np.stack(rows)
+
+
+def test_element_rounding_is_exact_rne_random():
+    x = _random_bits(1500, seed=11)
+    codes, meta, _ = oracle.quantize(x)
+    deq = oracle.dequantize(codes, meta)
+    for i in range(x.shape[0]):
+        _check_unit_exact(x[i], codes[i], meta[i, 0], deq[i])
+
+
+def test_element_rounding_ties_go_to_even():
+    x = _midpoint_bits(300, seed=12)
+    codes, meta, _ = oracle.quantize(x)
+    deq = oracle.dequantize(codes, meta)
+    n_ties = 0
+    for i in range(x.shape[0]):
+        _check_unit_exact(x[i], codes[i], meta[i, 0], deq[i])
+        c, e2, e3 = unit_fields(int(meta[i, 0]))
+        assert e2[1:] == [0] * 7 and e3[2:] == [0] * 14
+        n_ties += UNIT - 8
+    assert n_ties > 10000
+
+
+def test_element_rounding_every_bf16_against_each_grid():
+    """Every positive finite bf16 magnitude, placed in a unit whose group has
+    D = s (e2 = e3 = 0), for several level-1 codes with each mantissa."""
+    allbits = np.arange(1, 0x7F80, dtype=np.uint16)
+    vals = bits_to_f64(allbits)
+    for c in (100, 101, 102, 103, 130, 131):
+        s = oracle.e6m2_value(c)
+        keep = allbits[(vals <= 1.75 * s)]
+        n = keep.size
+        x = np.zeros((n, UNIT), np.uint16)
+        x[:, 0] = to_bits([7 * s])[0]
+        x[:, 40] = keep
+        codes, meta, _ = oracle.quantize(x)
+        assert np.all(meta[:, 0] & 255 == c)
+        deq = oracle.dequantize(codes, meta)[:, 40]
+        S = Fraction(s)
+        for b, xhat in zip(keep, deq):
+            xv = Fraction(float(bits_to_f64(np.array([b]))[0]))
+            k = Fraction(xhat) / (S / 4)
+            assert k.denominator == 1 and 0 <= k <= 7
+            err = abs(xv - k * S / 4)
+            assert err <= S / 8
+            if err == S / 8:
+                assert k % 2 == 0
+
+
+# -------------------------------------------- brute force over scale choices
+
+def _rne_grid(x, D):
+    """Nearest of {k D/4, k=0..7} to |x| (ties to even), exact rationals."""
+    a = abs(x)
+    best = None
+    for k in range(8):
+        e = abs(a - k * D / 4)
+        if best is None or e < best[0] or (e == best[0] and k % 2 == 0):
+            best = (e, k)
+    return best[1] * D / 4 * (1 if x >= 0 else -1)
+
+
+def _group_options(xs, s):
+    """All 8 (e2, e3a, e3b) choices for a level-2 group of 8 exact values:
+    returns list of (no_clip, [xhat]) ."""
+    out = []
+    for e2, ea, eb in itertools.product((0, 1), repeat=3):
+        xh, ok = [], True
+        for t, x in enumerate(xs):
+            D = s * 2 ** (e2 + (ea if t < 4 else eb))
+            if abs(x) > 7 * D / 4:
+                ok = False
+            xh.append(_rne_grid(x, D))
+        out.append((ok, xh))
+    return out
+
+
+def test_micro_exponents_are_elementwise_optimal_among_no_clip_choices():
+    """With the level-1 code fixed, the rule's level-2/3 bits give, element by
+    element, the smallest error of all no-clip choices (brute force)."""
+    x = _random_bits(120, seed=21, spread=1.0, zero_p=0.3)
+    codes, meta, _ = oracle.quantize(x)
+    deq = oracle.dequantize(codes, meta)
+    xs = bits_to_f64(x)
+    for i in range(x.shape[0]):
+        c, e2, e3 = unit_fields(int(meta[i, 0]))
+        if c == 255:
+            continue
+        s = Fraction(oracle.e6m2_value(c))
+        for g in range(8):
+            vals = [Fraction(float(v)) for v in xs[i, 8 * g:8 * g + 8]]
+            mine = [Fraction(float(v)) for v in deq[i, 8 * g:8 * g + 8]]
+            opts = [xh for ok, xh in _group_options(vals, s) if ok]
+            assert opts, "some choice must avoid clipping"
+            for t in range(8):
+                best = min(abs(vals[t] - o[t]) for o in opts)
+                assert abs(vals[t] - mine[t]) == best
+
+
+def test_global_search_reports_rule_error_bound():
+    """Brute force over level-1 codes (a window of 4 binades either side of
+    the rule's code) x all micro choices on tiny units: the rule's per-element
+    error obeys |x - xhat| <= 2^(E-3) s, and its max-abs error is compared
+    (reported) with the searched optimum."""
+    x = _random_bits(6, seed=31, spread=0.5, zero_p=0.5)
+    codes, meta, _ = oracle.quantize(x)
+    deq = oracle.dequantize(codes, meta)
+    xs = bits_to_f64(x)
+    worse = 0
+    for i in range(x.shape[0]):
+        c, e2, e3 = unit_fields(int(meta[i, 0]))
+        s = Fraction(oracle.e6m2_value(c))
+        vals = [Fraction(float(v)) for v in xs[i]]
+        mine = [Fraction(float(v)) for v in deq[i]]
+        for j in range(UNIT):
+            E = e2[j // 8] + e3[j // 4]
+            assert abs(vals[j] - mine[j]) <= s * 2 ** E / 8
+        rule_max = max(abs(a - b) for a, b in zip(vals, mine))
+        best_max = None
+        for cc in range(max(0, c - 16), min(256, c + 17)):
+            sc = Fraction(oracle.e6m2_value(cc))
+            tot = Fraction(0)
+            for g in range(8):
+                grp = vals[8 * g:8 * g + 8]
+                errs = [max(abs(a - b) for a, b in zip(grp, xh))
+                        for _, xh in _group_options(grp, sc)]
+                tot = max(tot, min(errs))
+            best_max = tot if best_max is None else min(best_max, tot)
+        assert best_max <= rule_max
+        worse += best_max < rule_max
+    print(f"units where a searched choice beats the no-clip rule on max error: {worse}/6")
+
+
+# ----------------------------------------------------------- invariants
+
+def _canonical_unit(r):
+    """A random code unit that the rule reproduces: minimal bits, canonical
+    zeros, and its decoded maximum equal to 7 v(c)."""
+    c = int(r.integers(8, 248))
+    e2 = [int(r.integers(0, 2)) for _ in range(8)]
+    e3 = [int(r.integers(0, 2)) for _ in range(16)]
+    k = [int(r.integers(0, 8)) for _ in range(UNIT)]
+    e2[0], e3[0] = 1, 1
+    k[int(r.integers(0, 4))] = 7  # decoded max 7 v(c) fixes c
+    for g in range(8):
+        if e2[g] and not (e3[2 * g] or e3[2 * g + 1]):
+            e3[2 * g + int(r.integers(0, 2))] = 1
+        if e2[g]:
+            qs = [q for q in (2 * g, 2 * g + 1) if e3[q]]
+            q = qs[int(r.integers(0, len(qs)))]
+            j = 4 * q + int(r.integers(0, 4))
+            k[j] = max(k[j], 4)
+    for q in range(16):
+        if e3[q] and max(k[4 * q:4 * q + 4]) < 4:
+            k[4 * q + int(r.integers(0, 4))] = int(r.integers(4, 8))
+    sign = [int(r.integers(0, 2)) if k[j] else 0 for j in range(UNIT)]
+    codes = np.zeros(32, np.uint8)
+    for j in range(UNIT):
+        nib = k[j] | (sign[j] << 3)
+        codes[4 * (j // 8) + j % 4] |= (nib << 4) if j % 8 >= 4 else nib
+    meta = c | sum(e2[g] << (8 + g) for g in range(8)) | sum(e3[q] << (16 + q) for q in range(16))
+    return codes, np.uint32(meta)
+
+
+def test_round_trip_of_canonical_units():
+    r = np.random.default_rng(41)
+    units = [_canonical_unit(r) for _ in range(400)]
+    codes = np.stack([u[0] for u in units])
+    meta = np.array([[u[1]] for u in units], np.uint32)
+    deq = oracle.dequantize(codes, meta)
+    x = to_bits(deq.astype(np.float32)).reshape(deq.shape)  # exact in bf16
+    assert np.array_equal(bits_to_f64(x), deq)
+    c2, m2, _ = oracle.quantize(x)
+    assert np.array_equal(m2, meta)
+    assert np.array_equal(c2, codes)
+
+
+def test_requantization_is_not_always_idempotent_but_settles():
+    """Documented counterexample: s = 1, A = 6.25 -> 6 -> 6.125 -> 6.125."""
+    x = np.zeros((1, UNIT), np.uint16)
+    x[0, 0] = to_bits([6.25])[0]
+    a = oracle.dequantize(*oracle.quantize(x)[:2])[0, 0]
+    assert a == 6.0
+    b = oracle.dequantize(*oracle.quantize(to_bits([[a] + [0.0] * 63]).reshape(1, UNIT))[:2])[0, 0]
+    assert b == 6.125
+    c = oracle.dequantize(*oracle.quantize(to_bits([[b] + [0.0] * 63]).reshape(1, UNIT))[:2])[0, 0]
+    assert c == 6.125
+
+
+def test_scale_equivariance():
+    """Q(2^p x): same nibbles and E1 bits, level-1 code shifted by 4p."""
+    x = _random_bits(200, seed=51, spread=0.5)
+    c0, m0, _ = oracle.quantize(x)
+    lv = m0[:, 0] & 255
+    ok = (lv > 40) & (lv < 200)
+    for p in (-5, -1, 1, 3, 7):
+        xs = bits_to_f64(x) * 2.0 ** p
+        xb = to_bits(xs.astype(np.float32)).reshape(x.shape)
+        c1, m1, _ = oracle.quantize(xb)
+        assert np.array_equal(c1[ok], c0[ok])
+        assert np.array_equal(m1[ok] >> 8, m0[ok] >> 8)
+        assert np.array_equal((m1[ok] & 255).astype(int), (m0[ok] & 255).astype(int) + 4 * p)
+
+
+def test_sign_symmetry():
+    x = _random_bits(300, seed=61)
+    c0, m0, _ = oracle.quantize(x)
+    c1, m1, _ = oracle.quantize(x ^ np.uint16(0x8000))
+    assert np.array_equal(m0, m1)
+    for i in range(x.shape[0]):
+        for j in range(UNIT):
+            a, b = nibble(c0[i], j), nibble(c1[i], j)
+            if a & 7:
+                assert b == a ^ 8
+            else:
+                assert a == b == 0
+
+
+def test_grouping_locality_along_k():
+    """Raising one element to the unit maximum changes only its own level-2
+    group: its e2 bit, its two e3 bits and its own code word (format section:
+    per-8 and per-4 sharing; HiGPTQ section: exponent order along K)."""
+    r = np.random.default_rng(71)
+    x = _random_bits(60, seed=72, spread=0.3)
+    c0, m0, _ = oracle.quantize(x)
+    xs = bits_to_f64(x)
+    for i in range(x.shape[0]):
+        j = int(r.integers(0, UNIT))
+        amax = np.abs(xs[i]).max()
+        y = x[i].copy()
+        y[j] = to_bits([amax])[0]
+        c1, m1, _ = oracle.quantize(y.reshape(1, UNIT))
+        g = j // 8
+        allowed = (1 << (8 + g)) | (1 << (16 + 2 * g)) | (1 << (17 + 2 * g))
+        assert (int(m0[i, 0]) ^ int(m1[0, 0])) & ~allowed == 0
+        diff = np.nonzero(c0[i] != c1[0])[0]
+        assert all(4 * g <= b < 4 * g + 4 for b in diff)
+
+
+def test_masked_channels_become_zero_and_are_kept():
+    x = _random_bits(16, seed=81).reshape(4, 256)
+    mask = np.zeros(256, np.uint8)
+    mask[[3, 64, 65, 200, 255]] = 1
+    c, m, kept = oracle.quantize(x, mask)
+    y = x.copy()
+    y[:, mask != 0] = 0
+    c2, m2, _ = oracle.quantize(y)
+    assert np.array_equal(c, c2) and np.array_equal(m, m2)
+    assert np.array_equal(kept, x[:, [3, 64, 65, 200, 255]])
+
+
+def test_nonfinite_input_is_out_of_contract():
+    x = np.zeros((1, UNIT), np.uint16)
+    x[0, 3] = 0x7FC0  # NaN
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize(x)
+
+
+# ------------------------------------------------------------------ linear
+
+def test_linear_matches_numpy_fp64_matmul():
+    import workloads
+    t = workloads.workload("tiny")
+    xb, wb = workloads.bits(t["x"]), workloads.bits(t["w"])
+    xc, xm, _ = oracle.quantize(xb)
+    wc, wm, _ = oracle.quantize(wb)
+    a, b = oracle.dequantize(xc, xm), oracle.dequantize(wc, wm)
+    y, s = oracle.linear(xc, xm, wc, wm)
+    ref = a @ b.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * s)
+    assert np.allclose(s, np.abs(a) @ np.abs(b).T, rtol=1e-14, atol=0)
+    assert y.shape == (64, 128)
+
+
+def test_linear_one_hot_weight_column_is_exact():
+    """A W row with a single element 7 (decodes to exactly 7) gives column j
+    of Y = 7 * deq(Q(X))[:, t], bit for bit."""
+    import workloads
+    xb = workloads.bits(workloads.tiny_x(16, 192, seed=5))
+    xc, xm, _ = oracle.quantize(xb)
+    a = oracle.dequantize(xc, xm)
+    w = np.zeros((3, 192), np.uint16)
+    cols = [5, 77, 190]
+    for j, t in enumerate(cols):
+        w[j, t] = to_bits([7.0])[0]
+    wc, wm, _ = oracle.quantize(w)
+    assert np.array_equal(oracle.dequantize(wc, wm)[np.arange(3), cols], [7.0] * 3)
+    y = oracle.linear(xc, xm, wc, wm, with_mag=False)
+    for j, t in enumerate(cols):
+        assert np.array_equal(y[:, j], 7.0 * a[:, t])
+
+
+# -------------------------------------------------------------- percentile
+
+@pytest.mark.parametrize("case", golden_io.percentile_cases())
+def test_percentile_golden(case):
+    q, vals, exp = case
+    x = to_bits(vals).reshape(-1, 1)
+    assert oracle.percentile(x, q)[0] == np.float32(exp)
+
+
+def test_percentile_matches_numpy_linear():
+    r = np.random.default_rng(91)
+    x = r.standard_t(3, size=(257, 40)) * np.exp(r.normal(0, 1, size=(1, 40)))
+    x[:, 7] = 2.5  # constant channel
+    xb = to_bits((np.float32(x).view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32))
+    xb = xb.reshape(x.shape)
+    vals = np.abs(bits_to_f64(xb))
+    for q in (0.0, 0.5, 0.75, 0.9, 0.99, 0.999, 1.0):
+        mine = oracle.percentile(xb, q)
+        ref = np.percentile(vals, q * 100.0, axis=0, method="linear").astype(np.float32)
+        ulp = np.spacing(np.maximum(np.abs(ref), np.float32(1e-30)))
+        assert np.all(np.abs(mine - ref) <= ulp), q
+        assert mine[7] == np.float32(2.5)
+        h = q * 256
+        if h == int(h):  # an exact order statistic
+            assert np.array_equal(mine, np.sort(vals, axis=0)[int(h)].astype(np.float32))
+
+
+# -------------------------------------------------------------------- mask
+
+def test_topn_mask_matches_stable_argsort():
+    r = np.random.default_rng(101)
+    for c, n in ((256, 13), (5120, 52), (7, 0), (7, 7)):
+        s = np.float32(r.exponential(size=c))
+        s[r.integers(0, c, size=c // 5)] = s[0]  # ties
+        mine = oracle.topn_mask(s, n)
+        order = np.argsort(-s.astype(np.float64), kind="stable")
+        ref = np.zeros(c, np.uint8)
+        ref[order[:n]] = 1
+        assert np.array_equal(mine, ref)
+        assert int(mine.sum()) == n
+
+
+def test_topn_mask_ties_prefer_lower_index():
+    s = np.float32([1, 3, 3, 2, 3, 0])
+    assert list(oracle.topn_mask(s, 2)) == [0, 1, 1, 0, 0, 0]
+    assert list(oracle.topn_mask(s, 3)) == [0, 1, 1, 0, 1, 0]
