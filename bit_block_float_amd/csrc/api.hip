@@ -1,0 +1,158 @@
+// api.hip -- the C ABI of libhif4.so (declared and documented in
+// include/hif4.h). Every argument check runs before any HIP call, so invalid
+// calls return a status without touching the device or the outputs.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/hif4.h"
+#include "hif4_dev.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other. Benign race: every writer stores the
+// same value for a device.
+int g_dev_kind[64];
+
+hif4_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return HIF4_ERR_DEVICE;
+  if (dev < 64 && g_dev_kind[dev] != 0) return g_dev_kind[dev] == 1 ? HIF4_OK : HIF4_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return HIF4_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_kind[dev] = ok ? 1 : 2;
+  return ok ? HIF4_OK : HIF4_ERR_DEVICE;
+}
+
+hif4_status launched(hipError_t e) { return e == hipSuccess ? HIF4_OK : HIF4_ERR_LAUNCH; }
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hif4_status_string(int status) {
+  switch (status) {
+    case HIF4_OK: return "ok";
+    case HIF4_ERR_NULL: return "a required pointer is NULL";
+    case HIF4_ERR_SHAPE: return "invalid shape (negative size, k % 64 != 0, ld < k, ...)";
+    case HIF4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case HIF4_ERR_WORKSPACE: return "workspace missing or too small";
+    case HIF4_ERR_DTYPE: return "unknown dtype";
+    case HIF4_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case HIF4_ERR_LAUNCH: return "kernel launch failed";
+    case HIF4_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int hif4_version(void) { return HIF4_API_VERSION; }
+
+hif4_status hif4_quantize(const void* x, int64_t rows, int64_t k, int64_t ld, const uint8_t* mask,
+                          int64_t n_mask, void* kept, uint8_t* codes, uint32_t* meta,
+                          hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 64 != 0 || ld < k || n_mask < 0) return HIF4_ERR_SHAPE;
+  if (mask && (k > 65536 || n_mask > k)) return HIF4_ERR_SHAPE;
+  if (rows == 0 || k == 0) return HIF4_OK;
+  if (!x || !codes || !meta) return HIF4_ERR_NULL;
+  if (mask && n_mask > 0 && !kept) return HIF4_ERR_NULL;
+  if (!aligned(x, 16) || ld % 8 != 0 || !aligned(codes, 16) || !aligned(meta, 4))
+    return HIF4_ERR_ALIGN;
+  if (mask && !aligned(mask, 8)) return HIF4_ERR_ALIGN;
+  if (mask && n_mask > 0 && !aligned(kept, 2)) return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  const uint16_t* xb = (const uint16_t*)x;
+  st = launched(hif4_launch_quantize(xb, rows, k, ld, mask, codes, meta, nullptr, stream));
+  if (st != HIF4_OK || !mask || n_mask == 0) return st;
+  return launched(hif4_launch_gather_kept(xb, rows, k, ld, mask, n_mask, (uint16_t*)kept, stream));
+}
+
+hif4_status hif4_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t rows, int64_t k,
+                            void* out, int out_dtype, hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
+  if (out_dtype != HIF4_F32 && out_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+  if (rows == 0 || k == 0) return HIF4_OK;
+  if (!codes || !meta || !out) return HIF4_ERR_NULL;
+  if (!aligned(codes, 16) || !aligned(meta, 4) || !aligned(out, 16)) return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_dequantize(codes, meta, rows, k, out, out_dtype == HIF4_BF16, stream));
+}
+
+// Workspace: the bf16 decoded activation [m][k] then the decoded weight [n][k].
+size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return 0;
+  return align256((size_t)m * (size_t)k * 2) + align256((size_t)n * (size_t)k * 2);
+}
+
+hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32_t* x_meta,
+                             const uint8_t* w_codes, const uint32_t* w_meta, int64_t m, int64_t n,
+                             int64_t k, void* y, int y_dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
+  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31)) return HIF4_ERR_SHAPE;
+  if (y_dtype != HIF4_F32 && y_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+  if (m == 0 || n == 0) return HIF4_OK;
+  if (!y) return HIF4_ERR_NULL;
+  if (k > 0) {
+    if (!w_codes || !w_meta) return HIF4_ERR_NULL;
+    if (!x && (!x_codes || !x_meta)) return HIF4_ERR_NULL;
+  }
+  if (!aligned(y, 16)) return HIF4_ERR_ALIGN;
+  if (k > 0) {
+    if (x && !aligned(x, 16)) return HIF4_ERR_ALIGN;
+    if (!x && (!aligned(x_codes, 16) || !aligned(x_meta, 4))) return HIF4_ERR_ALIGN;
+    if (!aligned(w_codes, 16) || !aligned(w_meta, 4)) return HIF4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < hif4_linear_workspace_bytes(m, n, k))
+      return HIF4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
+  }
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  if (k == 0) {
+    // Empty contraction: Y = 0.
+    const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
+    return launched(hif4_launch_zero(y, bytes, stream));
+  }
+  uint16_t* xa = (uint16_t*)workspace;
+  uint16_t* wb = (uint16_t*)((char*)workspace + align256((size_t)m * (size_t)k * 2));
+  if (x) {
+    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, nullptr, nullptr, nullptr, xa,
+                                       stream));
+  } else {
+    st = launched(hif4_launch_dequantize(x_codes, x_meta, m, k, xa, 1, stream));
+  }
+  if (st != HIF4_OK) return st;
+  st = launched(hif4_launch_dequantize(w_codes, w_meta, n, k, wb, 1, stream));
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_gemm_bf16_nt(xa, wb, m, n, k, y, y_dtype == HIF4_BF16, stream));
+}
+
+size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {
+  (void)rows;
+  if (c < 0) return 0;
+  return hif4_percentile_ws_bytes(c);
+}
+
+hif4_status hif4_percentile_mask(const void* x, int64_t rows, int64_t c, int64_t ld, double q,
+                                 int64_t n_protect, float* stats, uint8_t* mask, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 1 || c < 1 || c > 65536 || ld < c) return HIF4_ERR_SHAPE;
+  if (n_protect < 0 || n_protect > c) return HIF4_ERR_SHAPE;
+  if (!(q >= 0.0 && q <= 1.0)) return HIF4_ERR_ARG;
+  if (!x || !stats || !mask) return HIF4_ERR_NULL;
+  if (!aligned(x, 16) || ld % 8 != 0 || !aligned(stats, 4)) return HIF4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hif4_percentile_workspace_bytes(rows, c))
+    return HIF4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_percentile((const uint16_t*)x, rows, c, ld, q, n_protect, stats, mask,
+                                         workspace, stream));
+}
+
+}  // extern "C"

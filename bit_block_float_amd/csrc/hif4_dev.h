@@ -1,0 +1,101 @@
+// hif4_dev.h -- device helpers and internal launcher declarations of libhif4.
+// gfx950 (CDNA4) only: 64-lane wavefronts, DPP cross-lane moves.
+//
+// Format: HiFloat4 calibration article (hwcomputing.csdn.net), section
+// "一：HiFloat4 (HiF4) 格式" -- 64-element units, one E6M2 level-1 scale, E1
+// level-2 (per 8) and level-3 (per 4) exponents, S1P2 elements. The readings
+// of what the article leaves open (E6M2 bias, E1 direction, nibble layout,
+// scale rule, rounding) are stated in include/hif4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hif4 {
+
+constexpr int kUnit = 64;  // elements per HiF4 unit
+
+// E6M2 level-1 value v(c) = 2^((c>>2) - 31) * (1 + (c&3)/4), built as fp32
+// bits: biased exponent (c>>2) - 31 + 127, two mantissa bits on top.
+__device__ __forceinline__ float e6m2_f32(uint32_t c) {
+  return __uint_as_float((((c >> 2) + 96u) << 23) | ((c & 3u) << 21));
+}
+
+// Smallest level-1 code c with 7 v(c) >= a (a >= 0, exact bf16 value), 255 if
+// none. An estimate from a/7 is off by at most one code; the two exact
+// comparisons settle it (7 v(c) has at most 6 significant bits: exact in fp32).
+__device__ __forceinline__ uint32_t level1_code(float a) {
+  const float r = a * (1.0f / 7.0f);
+  const uint32_t b = __float_as_uint(r);
+  const int e = (int)(b >> 23) - 96;
+  const uint32_t m = b & 0x7FFFFFu;
+  int c = 4 * e + (int)(m >> 21) + ((m & 0x1FFFFFu) != 0u);
+  c = c < 0 ? 0 : (c > 255 ? 255 : c);
+  if (c > 0 && 7.0f * e6m2_f32((uint32_t)c - 1u) >= a) {
+    c -= 1;
+  } else if (c < 255 && 7.0f * e6m2_f32((uint32_t)c) < a) {
+    c += 1;
+  }
+  return (uint32_t)c;
+}
+
+// 16 / (4 + m), m = 0..3, correctly rounded to double: 4 / v(c) without the
+// power of two. Each has relative error 2^-54 or less, small enough that
+// |x| * (4 / D) rounds to an exact half-integer whenever the real quotient is
+// one (the tie cases), so rint() below is round-to-nearest-even on the reals.
+__device__ __forceinline__ double inv_mant16(uint32_t m) {
+  return m == 0u ? 4.0 : (m == 1u ? 3.2 : (m == 2u ? 2.6666666666666665 : 2.2857142857142856));
+}
+
+// DPP lane moves within a row of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i in 8
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, Ctrl, 0xF, 0xF, false);
+}
+
+// Max / OR over the 8 lanes of an aligned group of 8.
+__device__ __forceinline__ uint32_t max8_u32(uint32_t v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t or8_u32(uint32_t v) {
+  v |= dpp<kDppQuadXor1>(v);
+  v |= dpp<kDppQuadXor2>(v);
+  v |= dpp<kDppHalfMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace hif4
+
+// ---------------------------------------------------------------- launchers
+// Internal (hidden) host launchers; argument checks happen in api.hip.
+hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                                const uint8_t* mask, uint8_t* codes, uint32_t* meta,
+                                uint16_t* deq_bf16, hipStream_t stream);
+hipError_t hif4_launch_gather_kept(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                                   const uint8_t* mask, int64_t n_mask, uint16_t* kept,
+                                   hipStream_t stream);
+hipError_t hif4_launch_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t rows,
+                                  int64_t k, void* out, int out_bf16, hipStream_t stream);
+hipError_t hif4_launch_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
+                                    int64_t k, void* y, int y_bf16, hipStream_t stream);
+hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
+                                  double q, int64_t n_protect, float* stats, uint8_t* mask,
+                                  void* workspace, hipStream_t stream);
+size_t hif4_percentile_ws_bytes(int64_t c);
+hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream);

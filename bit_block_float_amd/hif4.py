@@ -1,0 +1,159 @@
+"""Python binding of libhif4.so (the C ABI in include/hif4.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current HIP stream. There is no CPU
+fallback: if the library or a gfx950 device is missing, calls raise.
+
+Tensors: bf16 inputs are torch.bfloat16 on the GPU; codes are uint8
+[rows][k/2]; meta is int32 [rows][k/64] holding the u32 metadata words bit
+for bit; masks are uint8.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhif4.so")
+
+HIF4_F32, HIF4_BF16 = 0, 1
+_lib = None
+
+
+class Hif4Error(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {lib().hif4_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library (ctypes). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_block_float_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.hif4_status_string.argtypes = [ctypes.c_int]
+        L.hif4_status_string.restype = ctypes.c_char_p
+        L.hif4_version.argtypes = []
+        L.hif4_version.restype = ctypes.c_int
+        L.hif4_quantize.argtypes = [p, i64, i64, i64, p, i64, p, p, p, p]
+        L.hif4_quantize.restype = ctypes.c_int
+        L.hif4_dequantize.argtypes = [p, p, i64, i64, p, ctypes.c_int, p]
+        L.hif4_dequantize.restype = ctypes.c_int
+        L.hif4_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.hif4_linear_workspace_bytes.restype = sz
+        L.hif4_linear_w4a4.argtypes = [p, p, p, p, p, i64, i64, i64, p, ctypes.c_int, p, sz, p]
+        L.hif4_linear_w4a4.restype = ctypes.c_int
+        L.hif4_percentile_workspace_bytes.argtypes = [i64, i64]
+        L.hif4_percentile_workspace_bytes.restype = sz
+        L.hif4_percentile_mask.argtypes = [p, i64, i64, i64, ctypes.c_double, i64, p, p, p, sz, p]
+        L.hif4_percentile_mask.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def require_gpu():
+    """Raise unless a gfx950 GPU is visible and the library loads."""
+    lib()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: libhif4 runs only on gfx950 (MI355X)")
+    arch = torch.cuda.get_device_properties(torch.cuda.current_device()).gcnArchName
+    if not arch.startswith("gfx950"):
+        raise RuntimeError(f"libhif4 needs gfx950, found {arch}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ok(status, what):
+    if status != 0:
+        raise Hif4Error(status, what)
+
+
+def _check_bf16_rows(x, name):
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D bf16 CUDA tensor with unit column stride")
+
+
+def quantize(x, mask=None, codes=None, meta=None, kept=None, stream=None):
+    """HiF4-quantize bf16 x [rows][k] along k -> (codes u8, meta int32, kept bf16)."""
+    _check_bf16_rows(x, "x")
+    rows, k = x.shape
+    dev = x.device
+    codes = codes if codes is not None else torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    meta = meta if meta is not None else torch.empty((rows, k // 64), dtype=torch.int32, device=dev)
+    n_mask = 0
+    if mask is not None:
+        n_mask = int(torch.count_nonzero(mask).item())
+        if kept is None:
+            kept = torch.empty((rows, n_mask), dtype=torch.bfloat16, device=dev)
+    st = lib().hif4_quantize(_ptr(x), rows, k, x.stride(0), _ptr(mask), n_mask,
+                             _ptr(kept) if n_mask else None, _ptr(codes), _ptr(meta), _stream(stream))
+    _ok(st, "hif4_quantize")
+    return codes, meta, kept
+
+
+def dequantize(codes, meta, out_dtype=torch.float32, out=None, stream=None):
+    """Decode codes [rows][k/2] + meta [rows][k/64] -> [rows][k] fp32 or bf16."""
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    dt = HIF4_F32 if out_dtype == torch.float32 else HIF4_BF16
+    out = out if out is not None else torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    st = lib().hif4_dequantize(_ptr(codes), _ptr(meta), rows, k, _ptr(out), dt, _stream(stream))
+    _ok(st, "hif4_dequantize")
+    return out
+
+
+def linear_workspace_bytes(m, n, k):
+    return int(lib().hif4_linear_workspace_bytes(m, n, k))
+
+
+def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, y_dtype=torch.float32,
+                y=None, workspace=None, stream=None):
+    """Y = deq(Q(X)) deq(Q(W))^T. X as bf16 x [m][k] or as (x_codes, x_meta)."""
+    n, k = w_codes.shape[0], w_codes.shape[1] * 2
+    if x is not None:
+        _check_bf16_rows(x, "x")
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous (row stride k)")
+        m = x.shape[0]
+    else:
+        m = x_codes.shape[0]
+    dev = w_codes.device
+    dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
+    y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=dev)
+    need = linear_workspace_bytes(m, n, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    st = lib().hif4_linear_w4a4(_ptr(x), _ptr(x_codes), _ptr(x_meta), _ptr(w_codes), _ptr(w_meta),
+                                m, n, k, _ptr(y), dt, _ptr(workspace), workspace.numel(),
+                                _stream(stream))
+    _ok(st, "hif4_linear_w4a4")
+    return y
+
+
+def percentile_workspace_bytes(rows, c):
+    return int(lib().hif4_percentile_workspace_bytes(rows, c))
+
+
+def percentile_mask(x, q, n_protect, stats=None, mask=None, workspace=None, stream=None):
+    """Per-channel type-7 quantile of |x| over rows -> (stats fp32 [c], mask u8 [c])."""
+    _check_bf16_rows(x, "x")
+    rows, c = x.shape
+    dev = x.device
+    stats = stats if stats is not None else torch.empty((c,), dtype=torch.float32, device=dev)
+    mask = mask if mask is not None else torch.empty((c,), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty((percentile_workspace_bytes(rows, c),), dtype=torch.uint8, device=dev)
+    st = lib().hif4_percentile_mask(_ptr(x), rows, c, x.stride(0), float(q), int(n_protect),
+                                    _ptr(stats), _ptr(mask), _ptr(workspace), workspace.numel(),
+                                    _stream(stream))
+    _ok(st, "hif4_percentile_mask")
+    return stats, mask

@@ -1,0 +1,178 @@
+/*
+ * hif4.h -- C ABI of libhif4.so: HiFloat4 (HiF4) W4A4 fake-quantized linear
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * Sources:
+ *  [HiF4-fmt]  HiFloat4 calibration article (hwcomputing.csdn.net), section
+ *              "一：HiFloat4 (HiF4) 格式": 64-element units, one E6M2 level-1
+ *              scale, 8 E1 level-2 exponents (one per 8 elements), 16 E1
+ *              level-3 exponents (one per 4), S1P2 4-bit elements with
+ *              magnitudes 0 and 0.25..1.75, 32 metadata bits per unit.
+ *  [HiGPTQ]    same article, section 3.1: exponent order along K (1-0,
+ *              2-(0..7), 3-(0..15)), each fixed from the data it covers.
+ *  [HiFlat]    same article, section 3.3: HiF4 needs no clipping thresholds.
+ *  [TA-method] "Tail-Aware HiFloat4: W4A4 PTQ calibration for Wan2.2"
+ *              (agents-report.net), sections "方法概述", "校準與緊湊 PTQ 狀態"
+ *              and "尾部百分位統計的動機": W4A4 fake quantization of the target
+ *              linear layers; per-channel tail-percentile statistics of the
+ *              calibration activations build a channel-protection mask;
+ *              protected channels stay in high precision.
+ *  [TA-abs]    arXiv 2605.26628 record, abstract (same method, English).
+ *
+ * ENCODING (where the pages are silent this library takes, and its oracle
+ * pins, the following readings):
+ *  - level-1 code c (u8): v(c) = 2^((c>>2) - 31) * (1 + (c&3)/4), all codes
+ *    normal; an E1 bit b scales by 2^b; a nibble is sign<<3 | k, |value| = k/4.
+ *  - element j of a unit: x = S1P2(nibble_j) * 2^e2[j/8] * 2^e3[j/4] * v(c).
+ *  - quantize: c = smallest code with 7 v(c) >= max|x| (255 if none);
+ *    e2[g] = [max over 8 > 3.5 v(c)]; e3[q] = [max over 4 > 1.75 2^e2 v(c)];
+ *    k = round-to-nearest-even(4|x| / (v(c) 2^(e2+e3))), at most 7; zero is +0.
+ *  - layout: a row of k elements has k/64 units. codes [rows][k/2] bytes: unit
+ *    u owns bytes 32u..32u+31; element j of the unit sits in byte
+ *    4*(j/8) + j%4, low nibble if j%8 < 4, else high nibble. meta
+ *    [rows][k/64] u32: c | e2bits << 8 | e3bits << 16 (bit g of e2bits for
+ *    elements 8g..8g+7, bit q of e3bits for elements 4q..4q+3).
+ *
+ * CONVENTIONS (all entry points):
+ *  - Every pointer argument is DEVICE memory owned by the caller; the library
+ *    allocates nothing and keeps no state between calls (a per-device
+ *    "is this gfx950" flag is cached). Calls are reentrant.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the null stream); the
+ *    library never synchronizes. Faults inside a kernel surface at the
+ *    caller's next synchronization.
+ *  - Argument checks happen before any HIP call; on an error nothing is
+ *    enqueued and outputs are untouched. No C++ exception crosses the ABI.
+ *  - Results are deterministic and identical from run to run (integer
+ *    histograms, no floating-point atomics, fixed reduction order).
+ *  - Inputs must be finite; Inf/NaN inputs give unspecified (but in-bounds)
+ *    results.
+ */
+#ifndef HIF4_H
+#define HIF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HIF4_API_VERSION 1
+
+#ifndef HIF4_EXPORT
+#define HIF4_EXPORT __attribute__((visibility("default")))
+#endif
+
+typedef enum hif4_status {
+    HIF4_OK = 0,
+    HIF4_ERR_NULL = 1,      /* a required pointer is NULL */
+    HIF4_ERR_SHAPE = 2,     /* a size is negative, k % 64 != 0, ld < k, n_protect > c, ... */
+    HIF4_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks the stated alignment */
+    HIF4_ERR_WORKSPACE = 4, /* workspace NULL or smaller than the *_workspace_bytes query */
+    HIF4_ERR_DTYPE = 5,     /* unknown hif4_dtype */
+    HIF4_ERR_DEVICE = 6,    /* current device is not gfx950, or no device */
+    HIF4_ERR_LAUNCH = 7,    /* a kernel failed to enqueue */
+    HIF4_ERR_ARG = 8        /* another argument is out of range (q outside [0,1], ...) */
+} hif4_status;
+
+typedef enum hif4_dtype { HIF4_F32 = 0, HIF4_BF16 = 1 } hif4_dtype;
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+HIF4_EXPORT const char *hif4_status_string(int status);
+
+/* HIF4_API_VERSION of the built library. */
+HIF4_EXPORT int hif4_version(void);
+
+/*
+ * hif4_quantize -- HiF4-quantize the rows of a bf16 matrix along k
+ * ([HiF4-fmt] unit structure; [HiGPTQ] order and per-group statistics;
+ * [HiFlat] no clipping; rule as stated above).
+ *
+ *  x      bf16 [rows][ld], row-major; 16-byte aligned, ld % 8 == 0, ld >= k.
+ *  rows   >= 0 (0 enqueues nothing).   k   >= 0, k % 64 == 0.
+ *  mask   NULL, or u8 [k], 8-byte aligned: nonzero = protected input channel
+ *         ([TA-method]).
+ *         Protected entries are encoded as +0 and do not influence the scales.
+ *  n_mask number of nonzero mask bytes (must equal it; kept entries beyond
+ *         the true count are left unwritten, none is written out of bounds).
+ *  kept   NULL when mask is NULL or n_mask == 0; else bf16 [rows][n_mask]:
+ *         row r receives x[r][ch] for every protected ch, ascending ch.
+ *  codes  u8 [rows][k/2], 16-byte aligned.    meta  u32 [rows][k/64], 4-byte aligned.
+ *  With a mask, k must be <= 65536.
+ */
+HIF4_EXPORT hif4_status hif4_quantize(const void *x, int64_t rows, int64_t k, int64_t ld,
+                          const uint8_t *mask, int64_t n_mask, void *kept,
+                          uint8_t *codes, uint32_t *meta, hipStream_t stream);
+
+/*
+ * hif4_dequantize -- decode HiF4 codes to real values ([HiF4-fmt]; the
+ * quantize-then-dequantize form of fake quantization, [TA-abs]). Every decoded
+ * value is exact in both fp32 and bf16.
+ *
+ *  codes u8 [rows][k/2] (16-byte aligned), meta u32 [rows][k/64].
+ *  out   [rows][k] of out_dtype (HIF4_F32 or HIF4_BF16), 16-byte aligned.
+ */
+HIF4_EXPORT hif4_status hif4_dequantize(const uint8_t *codes, const uint32_t *meta, int64_t rows, int64_t k,
+                            void *out, int out_dtype, hipStream_t stream);
+
+/*
+ * hif4_linear_workspace_bytes -- bytes of device workspace hif4_linear_w4a4
+ * needs for an (m x k) activation and an (n x k) weight.
+ */
+HIF4_EXPORT size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/*
+ * hif4_linear_w4a4 -- W4A4 fake-quantized linear layer ([TA-abs]; the layer
+ * form Y = X W^T of the calibration article's FlatQuant section):
+ *     Y[i][j] = sum_t deq(Q(X))[i][t] * deq(Q(W))[j][t],
+ * accumulated in fp32 (|error| <= 1e-5 * sum_t |a||b| per output).
+ *
+ *  X is given EITHER as bf16 x [m][k] (row stride k; it is quantized along k
+ *  into the workspace first) OR pre-quantized (x == NULL; x_codes [m][k/2],
+ *  x_meta [m][k/64]). W is always pre-quantized: w_codes [n][k/2],
+ *  w_meta [n][k/64] (the nn.Linear [out][in] layout, quantized along in).
+ *  y        [m][n] of y_dtype (HIF4_F32, or HIF4_BF16 rounded to nearest even).
+ *  workspace device memory of at least hif4_linear_workspace_bytes(m, n, k)
+ *            bytes, 256-byte aligned; its contents are scratch.
+ *  Pointers 16-byte aligned except meta (4-byte). m, n >= 0; k % 64 == 0.
+ */
+HIF4_EXPORT hif4_status hif4_linear_w4a4(const void *x, const uint8_t *x_codes, const uint32_t *x_meta,
+                             const uint8_t *w_codes, const uint32_t *w_meta,
+                             int64_t m, int64_t n, int64_t k, void *y, int y_dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask
+ * over c channels.
+ */
+HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
+
+/*
+ * hif4_percentile_mask -- tail-aware channel statistics and protection mask
+ * ([TA-method]: a per-channel percentile of the activation magnitudes stands
+ * in for the maximum; the channels with the largest statistics are protected).
+ *
+ *  stats[ch] = type-7 quantile at level q of |x[0..rows-1][ch]|: with the
+ *    magnitudes sorted ascending into v, h = q (rows-1), lo = floor(h),
+ *    hi = min(lo+1, rows-1), stats = fp32(v[lo] + (h-lo) (v[hi]-v[lo])),
+ *    each double operation rounded separately.
+ *  mask[ch] = 1 for the n_protect largest stats (ties: lower ch first), else 0.
+ *
+ *  x         bf16 [rows][ld], 16-byte aligned, ld % 8 == 0, ld >= c, rows >= 1.
+ *  c         number of channels, 1 <= c <= 65536.   q in [0, 1].
+ *  n_protect 0 <= n_protect <= c (e.g. ceil(p * c) for a top-p mask).
+ *  stats     fp32 [c];  mask  u8 [c].
+ *  workspace >= hif4_percentile_workspace_bytes(rows, c) bytes, 256-byte
+ *            aligned; scratch.
+ */
+HIF4_EXPORT hif4_status hif4_percentile_mask(const void *x, int64_t rows, int64_t c, int64_t ld, double q,
+                                 int64_t n_protect, float *stats, uint8_t *mask,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIF4_H */

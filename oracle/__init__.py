@@ -55,6 +55,11 @@ def _check(rc, what):
         raise OracleError(f"{what}: status {rc}")
 
 
+def _shape(a, shape, what):
+    if tuple(a.shape) != tuple(shape):
+        raise OracleError(f"{what}: shape {tuple(a.shape)}, expected {tuple(shape)}")
+
+
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
@@ -73,6 +78,8 @@ def quantize(x_bits: np.ndarray, mask: np.ndarray = None):
     """
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     rows, k = x.shape
+    if mask is not None:
+        _shape(np.asarray(mask), (k,), "mask")
     codes = np.zeros((rows, k // 2), dtype=np.uint8)
     meta = np.zeros((rows, k // 64), dtype=np.uint32)
     n_mask = 0
@@ -93,6 +100,7 @@ def dequantize(codes: np.ndarray, meta: np.ndarray) -> np.ndarray:
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     m = np.ascontiguousarray(meta, dtype=np.uint32)
     rows, k = c.shape[0], c.shape[1] * 2
+    _shape(m, (rows, k // 64), "meta")
     out = np.zeros((rows, k), dtype=np.float64)
     _check(_lib().hif4o_dequantize(_ptr(c), _ptr(m), rows, k, _ptr(out)), "dequantize")
     return out
@@ -107,6 +115,8 @@ def linear(xc, xm, wc, wm, with_mag: bool = True):
     m, n, k = xc.shape[0], wc.shape[0], xc.shape[1] * 2
     if wc.shape[1] * 2 != k:
         raise OracleError("linear: K mismatch")
+    _shape(xm, (m, k // 64), "x meta")
+    _shape(wm, (n, k // 64), "w meta")
     y = np.zeros((m, n), dtype=np.float64)
     s = np.zeros((m, n), dtype=np.float64) if with_mag else None
     _check(_lib().hif4o_linear(_ptr(xc), _ptr(xm), _ptr(wc), _ptr(wm), m, n, k, _ptr(y), _ptr(s)),

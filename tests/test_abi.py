@@ -1,0 +1,136 @@
+"""C-ABI contract of libhif4.so, checked without a GPU.
+
+Loads the built library, checks that it exports exactly the entry points
+declared in include/hif4.h, and that invalid arguments return the documented
+status codes before any device work (no compute call reaches a kernel here).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hif4.h")
+LIB = os.path.join(ROOT, "bit_block_float_amd", "libhif4.so")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DTYPE, DEVICE, LAUNCH, ARG = range(9)
+A = 0x100000  # a 256-byte-aligned stand-in address; never dereferenced here
+
+
+def declared():
+    text = open(HEADER, encoding="utf-8").read()
+    return set(re.findall(r"HIF4_EXPORT\s+[\w\s\*]+?\b(hif4_\w+)\s*\(", text))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        from bit_block_float_amd import build
+        build.build()
+    from bit_block_float_amd import hif4
+    return hif4.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared()
+    for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
+               "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
+               "hif4_status_string", "hif4_version"):
+        assert fn in names
+
+
+def test_library_exports_exactly_the_declared_symbols(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    hif4_syms = {s for s in exported if s.startswith("hif4_")}
+    assert hif4_syms == declared()
+    for s in declared():
+        assert hasattr(L, s)
+
+
+def test_version_and_status_strings(L):
+    assert L.hif4_version() == 1
+    for s in range(9):
+        assert L.hif4_status_string(s)
+    assert L.hif4_status_string(12345) == b"unknown status"
+
+
+def test_quantize_argument_checks(L):
+    q = L.hif4_quantize
+    assert q(A, -1, 64, 64, None, 0, None, A, A, None) == SHAPE
+    assert q(A, 4, 65, 72, None, 0, None, A, A, None) == SHAPE
+    assert q(A, 4, 128, 64, None, 0, None, A, A, None) == SHAPE   # ld < k
+    assert q(A, 0, 64, 64, None, 0, None, None, None, None) == OK  # empty: no work
+    assert q(A, 4, 0, 0, None, 0, None, None, None, None) == OK
+    assert q(None, 4, 64, 64, None, 0, None, A, A, None) == NULL
+    assert q(A, 4, 64, 64, None, 0, None, None, A, None) == NULL
+    assert q(A, 4, 64, 64, A, 3, None, A, A, None) == NULL         # kept missing
+    assert q(A + 2, 4, 64, 64, None, 0, None, A, A, None) == ALIGN
+    assert q(A, 4, 64, 68, None, 0, None, A, A, None) == ALIGN     # ld % 8
+    assert q(A, 4, 64, 64, None, 0, None, A + 4, A, None) == ALIGN
+    assert q(A, 4, 64, 64, None, 0, None, A, A + 2, None) == ALIGN
+    assert q(A, 4, 64, 64, A + 1, 1, A, A, A, None) == ALIGN
+    assert q(A, 4, 65536 + 64, 65536 + 64, A, 1, A, A, A, None) == SHAPE  # masked k limit
+    assert q(A, 4, 64, 64, A, 65, A, A, A, None) == SHAPE          # n_mask > k
+
+
+def test_dequantize_argument_checks(L):
+    d = L.hif4_dequantize
+    assert d(A, A, 4, 100, A, 0, None) == SHAPE
+    assert d(A, A, 4, 64, A, 7, None) == DTYPE
+    assert d(None, A, 4, 64, A, 0, None) == NULL
+    assert d(A, A, 4, 64, A + 8, 0, None) == ALIGN
+    assert d(A, A, 0, 64, None, 1, None) == OK
+
+
+def test_linear_argument_checks(L):
+    f = L.hif4_linear_w4a4
+    ws = L.hif4_linear_workspace_bytes(8, 8, 64)
+    assert ws == 2 * 1024
+    assert L.hif4_linear_workspace_bytes(-1, 8, 64) == 0
+    assert f(A, None, None, A, A, 8, 8, 60, A, 0, A, ws, None) == SHAPE
+    assert f(A, None, None, A, A, 8, 8, 64, A, 3, A, ws, None) == DTYPE
+    assert f(None, None, None, A, A, 8, 8, 64, A, 0, A, ws, None) == NULL
+    assert f(A, None, None, None, A, 8, 8, 64, A, 0, A, ws, None) == NULL
+    assert f(A, None, None, A, A, 8, 8, 64, None, 0, A, ws, None) == NULL
+    assert f(A, None, None, A, A, 8, 8, 64, A, 0, A, ws - 1, None) == WORKSPACE
+    assert f(A, None, None, A, A, 8, 8, 64, A, 0, None, ws, None) == WORKSPACE
+    assert f(A, None, None, A, A, 8, 8, 64, A, 0, A + 16, ws, None) == ALIGN
+    assert f(A + 2, None, None, A, A, 8, 8, 64, A, 0, A, ws, None) == ALIGN
+    assert f(A, None, None, A, A, 0, 8, 64, A, 0, None, 0, None) == OK
+
+
+def test_percentile_argument_checks(L):
+    f = L.hif4_percentile_mask
+    ws = L.hif4_percentile_workspace_bytes(100, 256)
+    assert ws >= 256 * (256 + 128 + 1) * 4
+    assert f(A, 0, 256, 256, 0.5, 1, A, A, A, ws, None) == SHAPE
+    assert f(A, 100, 256, 256, 0.5, 257, A, A, A, ws, None) == SHAPE
+    assert f(A, 100, 256, 200, 0.5, 1, A, A, A, ws, None) == SHAPE
+    assert f(A, 100, 256, 256, 1.5, 1, A, A, A, ws, None) == ARG
+    assert f(A, 100, 256, 256, float("nan"), 1, A, A, A, ws, None) == ARG
+    assert f(A, 100, 256, 256, 0.5, 1, None, A, A, ws, None) == NULL
+    assert f(A, 100, 256, 260, 0.5, 1, A, A, A, ws, None) == ALIGN
+    assert f(A, 100, 256, 256, 0.5, 1, A, A, A, ws - 1, None) == WORKSPACE
+
+
+def test_valid_call_without_gfx950_reports_device_error():
+    """With no GPU visible a well-formed call must stop at the device check."""
+    code = (
+        "import ctypes, sys; sys.path.insert(0, %r)\n"
+        "from bit_block_float_amd import hif4\n"
+        "L = hif4.lib(); A = 0x100000\n"
+        "print(L.hif4_dequantize(A, A, 4, 64, A, 0, None))\n" % ROOT)
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is visible in this process environment")
+    except ImportError:
+        pass
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert int(out.stdout.strip().splitlines()[-1]) == DEVICE

@@ -1,0 +1,126 @@
+"""GPU parity at the full workload sizes (the shapes bench.py runs).
+
+Quantize outputs and masks are compared in full, bit for bit. The linear
+layer is compared on sampled rows (64 evenly spaced rows plus the rows that
+hold the largest |x| of the outlier channels) over all N columns, since the
+fp64 oracle cannot afford all M rows. The calibration percentile is compared
+on sampled channels (all protected ones plus a spread of others) and checked
+at every channel through properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def host_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def sample_rows(x, n=64):
+    m = x.shape[0]
+    rows = set(np.linspace(0, m - 1, n).astype(np.int64).tolist())
+    amax = x.float().abs().amax(dim=1)
+    rows.update(torch.topk(amax, 8).indices.cpu().tolist())  # outlier rows
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["attn", "ffn_up", "ffn_down"])
+def test_quantize_full_activation(hip, name):
+    w = workloads.WORKLOADS[name]
+    print(f"[case] quantize X {name} {w['M']}x{w['K']}", flush=True)
+    x = (workloads.heavy_tailed_x(w["M"], w["K"], device="cuda", seed=w["index"])
+         if name != "ffn_down" else workloads.gelu_x(w["M"], w["K"], device="cuda", seed=w["index"]))
+    codes, meta, _ = hip.quantize(x)
+    xb = workloads.bits(x)
+    del x
+    c_o, m_o, _ = oracle.quantize(xb)
+    assert np.array_equal(host_u32(meta), m_o)
+    assert np.array_equal(codes.cpu().numpy(), c_o)
+
+
+@pytest.mark.parametrize("name,y_dtype,via_codes", [("attn", torch.float32, False),
+                                                    ("attn", torch.bfloat16, False),
+                                                    ("ffn_up", torch.float32, True),
+                                                    ("ffn_down", torch.float32, False)])
+def test_linear_full_shape_sampled_rows(hip, name, y_dtype, via_codes):
+    w = workloads.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    print(f"[case] linear {name} {M}x{N}x{K} {y_dtype} codes={via_codes}", flush=True)
+    x = (workloads.heavy_tailed_x(M, K, device="cuda", seed=w["index"])
+         if name != "ffn_down" else workloads.gelu_x(M, K, device="cuda", seed=w["index"]))
+    wt = workloads.normal_bf16(N, K, 0.015 if name == "ffn_down" else 0.02, device="cuda",
+                               seed=w["index"] + 1000)
+    wcodes, wmeta, _ = hip.quantize(wt)
+    if via_codes:
+        xcodes, xmeta, _ = hip.quantize(x)
+        y = hip.linear_w4a4(wcodes, wmeta, x_codes=xcodes, x_meta=xmeta, y_dtype=y_dtype)
+    else:
+        y = hip.linear_w4a4(wcodes, wmeta, x=x, y_dtype=y_dtype)
+    rows = sample_rows(x)
+    xs = workloads.bits(x[torch.from_numpy(rows).cuda()])
+    wb = workloads.bits(wt)
+    y_rows = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    del x, y
+    xc, xm, _ = oracle.quantize(xs)
+    wc, wm, _ = oracle.quantize(wb)
+    assert np.array_equal(wcodes.cpu().numpy(), wc)
+    y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+    tol = 1e-5 * s_ref + (2.0 ** -8 * np.abs(y_ref) if y_dtype == torch.bfloat16 else 0.0)
+    err = np.abs(y_rows - y_ref)
+    assert np.all(err <= tol), f"max excess {np.max(err - tol)}"
+
+
+def _check_mask_properties(stats, mask, n_protect):
+    assert int(mask.sum()) == n_protect
+    on, off = stats[mask == 1], stats[mask == 0]
+    if on.size and off.size:
+        lo_on = on.min()
+        assert lo_on >= off.max()
+        # ties at the boundary go to the lower channel index
+        tied_off = np.nonzero((mask == 0) & (stats == lo_on))[0]
+        tied_on = np.nonzero((mask == 1) & (stats == lo_on))[0]
+        if tied_off.size:
+            assert tied_on.max() < tied_off.min()
+
+
+def test_percentile_bench_batch(hip):
+    """The bench's percentile call: one FFN-up batch (57600 x 5120), q=0.999."""
+    w = workloads.WORKLOADS["ffn_up"]
+    x = workloads.heavy_tailed_x(w["M"], w["K"], device="cuda", seed=w["index"])
+    stats, mask = hip.percentile_mask(x, w["q"], w["n_protect"])
+    s, mk = stats.cpu().numpy(), mask.cpu().numpy()
+    _check_mask_properties(s, mk, w["n_protect"])
+    chans = np.unique(np.concatenate([np.nonzero(mk)[0], np.linspace(0, w["K"] - 1, 200).astype(int)]))
+    cols = workloads.bits(x[:, torch.from_numpy(chans).cuda()])
+    ref = oracle.percentile(cols, w["q"])
+    assert np.array_equal(s[chans].view(np.uint32), ref.view(np.uint32))
+
+
+def test_percentile_calibration_pass_and_masked_weight(hip):
+    """Calibration at full size: 16 x 57600 tokens x 5120 channels (9.4 GB),
+    q = 0.999, top-1% mask; then the FFN-up weight quantized with that mask."""
+    w = workloads.WORKLOADS["calib"]
+    rows = w["batches"] * w["rows_per_batch"]
+    print(f"[case] calibration {rows}x{w['C']}", flush=True)
+    x = workloads.calib_x(w["batches"], w["rows_per_batch"], w["C"], device="cuda", seed=w["index"])
+    stats, mask = hip.percentile_mask(x, w["q"], w["n_protect"])
+    s, mk = stats.cpu().numpy(), mask.cpu().numpy()
+    _check_mask_properties(s, mk, w["n_protect"])
+    r = np.random.default_rng(0)
+    chans = np.unique(np.concatenate([np.nonzero(mk)[0][:12], r.choice(w["C"], 12, replace=False)]))
+    cols = workloads.bits(x[:, torch.from_numpy(chans).cuda()])
+    del x
+    ref = oracle.percentile(cols, w["q"])
+    assert np.array_equal(s[chans].view(np.uint32), ref.view(np.uint32))
+
+    wt = workloads.normal_bf16(w["N"], w["C"], 0.02, device="cuda", seed=w["index"] + 1000)
+    codes, meta, kept = hip.quantize(wt, mask)
+    c_o, m_o, k_o = oracle.quantize(workloads.bits(wt), mk)
+    assert np.array_equal(host_u32(meta), m_o)
+    assert np.array_equal(codes.cpu().numpy(), c_o)
+    assert np.array_equal(kept.cpu().view(torch.int16).numpy().view(np.uint16), k_o)

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes here are small enough for the oracle to finish in seconds while still
+spanning several tiles and ragged tails. Codes, meta, masks and percentile
+statistics must be bit-exact; the linear layer must satisfy
+|Y - Y_ref| <= 1e-5 * sum_t |a||b| per output (fp32 output), plus 2^-8 |Y_ref|
+for bf16 output (its own rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unit_cases as uc
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_bf16(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def host_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def host_bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_quantize(hip, bits, mask=None):
+    x = dev_bf16(bits)
+    m = torch.from_numpy(mask).cuda() if mask is not None else None
+    codes, meta, kept = hip.quantize(x, m)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), host_u32(meta), (host_bits(kept) if kept is not None else None)
+
+
+def assert_same_quant(hip, bits, mask=None):
+    c_g, m_g, k_g = gpu_quantize(hip, bits, mask)
+    c_o, m_o, k_o = oracle.quantize(bits, mask)
+    bad = np.nonzero(m_g != m_o)
+    assert np.array_equal(m_g, m_o), f"meta differs at {bad[0][:5]}, {bad[1][:5]}"
+    assert np.array_equal(c_g, c_o), f"codes differ at {np.nonzero(c_g != c_o)[0][:5]}"
+    if mask is not None and k_o.shape[1]:
+        assert np.array_equal(k_g, k_o)
+
+
+# ---------------------------------------------------------------- quantize
+
+def test_quantize_tiny_workload(hip):
+    t = workloads.workload("tiny")
+    assert_same_quant(hip, workloads.bits(t["x"]))
+    assert_same_quant(hip, workloads.bits(t["w"]))
+
+
+def test_quantize_every_bf16_magnitude_as_unit_max(hip):
+    assert_same_quant(hip, uc.all_magnitudes_as_unit_max())
+    assert_same_quant(hip, uc.all_magnitudes_as_unit_max(position=63, negative=True))
+
+
+@pytest.mark.parametrize("c", [0, 1, 2, 3, 60, 101, 102, 103, 124, 126, 127, 200, 251, 254, 255])
+def test_quantize_every_bf16_rounded_under_each_mantissa(hip, c):
+    assert_same_quant(hip, uc.all_magnitudes_under_code(c, oracle.e6m2_value))
+
+
+def test_quantize_random_and_tie_units(hip):
+    assert_same_quant(hip, uc.random_bits(4096, seed=1))
+    assert_same_quant(hip, uc.random_bits(4096, seed=2, spread=12.0))
+    assert_same_quant(hip, uc.midpoint_bits(512, seed=3, e6m2_value=oracle.e6m2_value))
+    assert_same_quant(hip, uc.special_values_bits())
+
+
+@pytest.mark.parametrize("rows,k", [(1, 64), (3, 320), (257, 192), (1000, 5120), (7, 13824)])
+def test_quantize_ragged_shapes(hip, rows, k):
+    bits = uc.random_bits(rows * k // 64, seed=rows + k).reshape(rows, k)
+    assert_same_quant(hip, bits)
+
+
+def test_quantize_strided_rows(hip):
+    bits = uc.random_bits(50 * 12, seed=9).reshape(50, 768)
+    x = dev_bf16(bits)[:, :512]  # row stride 768, k = 512
+    codes, meta, _ = hip.quantize(x)
+    c_o, m_o, _ = oracle.quantize(np.ascontiguousarray(bits[:, :512]))
+    assert np.array_equal(host_u32(meta), m_o)
+    assert np.array_equal(codes.cpu().numpy(), c_o)
+
+
+def test_quantize_empty_is_a_no_op(hip):
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    codes, meta, _ = hip.quantize(x)
+    assert codes.shape == (0, 64) and meta.shape == (0, 2)
+
+
+def test_quantize_with_mask_and_kept(hip):
+    bits = uc.random_bits(64 * 8, seed=11).reshape(64, 512)
+    r = np.random.default_rng(12)
+    for n in (0, 1, 7, 26):
+        mask = np.zeros(512, np.uint8)
+        mask[r.choice(512, size=n, replace=False)] = 1 + r.integers(0, 200, size=n)
+        assert_same_quant(hip, bits, mask)
+
+
+def test_quantize_deterministic(hip):
+    bits = uc.random_bits(2048, seed=13).reshape(256, 512)
+    a = gpu_quantize(hip, bits)
+    b = gpu_quantize(hip, bits)
+    assert all(np.array_equal(u, v) for u, v in zip(a[:2], b[:2]))
+
+
+# -------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_matches_oracle_exactly(hip, dtype):
+    bits = uc.random_bits(1024, seed=21, spread=8.0).reshape(128, 512)
+    c_o, m_o, _ = oracle.quantize(bits)
+    # plus arbitrary (non-canonical) codes: every nibble, every meta word
+    r = np.random.default_rng(22)
+    c_r = r.integers(0, 256, size=(64, 256), dtype=np.uint8)
+    m_r = r.integers(0, 2**32, size=(64, 8), dtype=np.uint64).astype(np.uint32)
+    for codes, meta in ((c_o, m_o), (c_r, m_r)):
+        ref = oracle.dequantize(codes, meta)
+        out = hip.dequantize(torch.from_numpy(codes).cuda(),
+                             torch.from_numpy(meta.view(np.int32)).cuda(), out_dtype=dtype)
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref)
+        assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+# ------------------------------------------------------------------ linear
+
+def check_linear(y_gpu, y_ref, s_ref, bf16_out=False):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    tol = 1e-5 * s_ref + (2.0 ** -8 * np.abs(y_ref) if bf16_out else 0.0)
+    worst = np.max(err - tol)
+    assert np.all(err <= tol), f"max excess {worst}"
+
+
+def run_linear_case(hip, xb, wb, y_dtype=torch.float32, via_codes=False):
+    xc, xm, _ = oracle.quantize(xb)
+    wc, wm, _ = oracle.quantize(wb)
+    y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+    w_codes = torch.from_numpy(wc).cuda()
+    w_meta = torch.from_numpy(wm.view(np.int32)).cuda()
+    if via_codes:
+        y = hip.linear_w4a4(w_codes, w_meta, x_codes=torch.from_numpy(xc).cuda(),
+                            x_meta=torch.from_numpy(xm.view(np.int32)).cuda(), y_dtype=y_dtype)
+    else:
+        y = hip.linear_w4a4(w_codes, w_meta, x=dev_bf16(xb), y_dtype=y_dtype)
+    check_linear(y.float().cpu().numpy(), y_ref, s_ref, bf16_out=(y_dtype == torch.bfloat16))
+
+
+def test_linear_tiny_workload(hip):
+    t = workloads.workload("tiny")
+    xb, wb = workloads.bits(t["x"]), workloads.bits(t["w"])
+    run_linear_case(hip, xb, wb)
+    run_linear_case(hip, xb, wb, via_codes=True)
+    run_linear_case(hip, xb, wb, y_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 200, 320), (1, 1, 64), (257, 513, 128), (512, 256, 1024),
+                                   (33, 700, 192)])
+def test_linear_ragged_shapes(hip, m, n, k):
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + n, outlier_channels=1))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=k))
+    run_linear_case(hip, xb, wb)
+
+
+def test_linear_one_hot_weight_is_exact(hip):
+    """W row j = a single 7 at column t: Y[:, j] = 7 * deq(Q(X))[:, t] exactly
+    (one exact product per output, no rounding)."""
+    xb = workloads.bits(workloads.heavy_tailed_x(300, 256, seed=3))
+    xc, xm, _ = oracle.quantize(xb)
+    a = oracle.dequantize(xc, xm)
+    cols = [0, 5, 77, 128, 255, 31]
+    w = np.zeros((len(cols), 256), np.uint16)
+    for j, t in enumerate(cols):
+        w[j, t] = uc.to_bits([7.0])[0]
+    wc, wm, _ = oracle.quantize(w)
+    y = hip.linear_w4a4(torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda(),
+                        x=dev_bf16(xb)).cpu().numpy()
+    for j, t in enumerate(cols):
+        assert np.array_equal(y[:, j].astype(np.float64), 7.0 * a[:, t])
+
+
+def test_linear_empty_k_gives_zero(hip):
+    w_codes = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    w_meta = torch.zeros((5, 0), dtype=torch.int32, device="cuda")
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((3, 5), 7.0, device="cuda")
+    hip.linear_w4a4(w_codes, w_meta, x=x, y=y)
+    assert torch.count_nonzero(y).item() == 0
+
+
+# -------------------------------------------------------------- percentile
+
+def run_pct_case(hip, bits, q, n_protect, ld=None):
+    x = dev_bf16(bits)
+    if ld is not None:
+        full = torch.zeros((bits.shape[0], ld), dtype=torch.bfloat16, device="cuda")
+        full[:, :bits.shape[1]] = x
+        x = full[:, :bits.shape[1]]
+    stats, mask = hip.percentile_mask(x, q, n_protect)
+    s_ref = oracle.percentile(bits, q)
+    m_ref = oracle.topn_mask(s_ref, n_protect)
+    s_gpu = stats.cpu().numpy()
+    assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(mask.cpu().numpy(), m_ref)
+
+
+def test_percentile_tiny_workload(hip):
+    t = workloads.workload("tiny")
+    run_pct_case(hip, workloads.bits(t["x"]), t["q"], t["n_protect"])
+
+
+@pytest.mark.parametrize("rows,c,q,n", [(1, 64, 0.99, 3), (2, 128, 0.5, 0), (1000, 200, 0.999, 2),
+                                        (777, 77, 0.0, 77), (4096, 384, 1.0, 10),
+                                        (5000, 256, 0.75, 13)])
+def test_percentile_ragged(hip, rows, c, q, n):
+    bits = workloads.bits(workloads.heavy_tailed_x(rows, c, seed=rows + c, outlier_channels=2))
+    ld = ((c + 7) // 8) * 8 if c % 8 else None
+    run_pct_case(hip, bits, q, n, ld=ld)
+
+
+def test_percentile_constant_and_tied_channels(hip):
+    r = np.random.default_rng(31)
+    x = uc.truncate_to_bits(r.standard_t(3, size=(3000, 256)))
+    x[:, 10] = uc.to_bits([2.5])[0]          # constant channel
+    x[:, 20] = x[:, 30]                       # duplicated channels -> tied stats
+    x[:, 40] = x[:, 30] ^ np.uint16(0x8000)   # sign-flipped duplicate: same |x|
+    run_pct_case(hip, x, 0.99, 40)
+    run_pct_case(hip, x, 0.5, 128)
+
+
+def test_percentile_wide_magnitude_range(hip):
+    """Values spanning subnormals to huge bf16, and rank boundaries that fall
+    exactly at coarse-bin edges."""
+    r = np.random.default_rng(41)
+    a = r.integers(0, 0x7F7F, size=(2001, 136)).astype(np.uint16)
+    a[:, :8] = r.integers(0, 0x0100, size=(2001, 8)).astype(np.uint16)  # subnormal/tiny
+    run_pct_case(hip, a, 0.999, 5)
+    run_pct_case(hip, a, 0.5, 5)
