@@ -67,10 +67,13 @@ def torch_index(idx):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -85,6 +88,15 @@ def main():
     hif4.require_gpu()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones((n,), dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 copies of {args.copy_probe} MiB done")
+        return
     spec = workloads.WORKLOADS["ffn_up"]
     M, N, K = spec["M"], spec["N"], spec["K"]
     q, n_protect = spec["q"], spec["n_protect"]
@@ -177,8 +189,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_bf16_nt_kernel (inside hif4_linear_w4a4; the linear's two "
-                      "decode kernels add < 0.1% to its time)",
+            "kernel": "hif4_linear_w4a4 call (X/W decode + gemm_bf16_nt_kernel), timed with "
+                      "HIP events on its stream",
             "achieved": gemm_tflops,
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -12,27 +12,55 @@
 // the operands: no per-unit rescale is needed in the K loop.
 //
 // Tiling: 256x256 output tile per workgroup (4 waves, 2x2, each 128x128 =
-// 4x4 blocks of v_mfma_f32_32x32x16_bf16), K step 64 (one HiF4 unit). Tiles
-// go global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4, no VGPR
-// staging), double-buffered: 2 stages x (A + B) x 256 rows x 128 B = 128 KiB.
-// Each LDS row holds 8 16-byte chunks of K; chunk c of row r is stored in
-// slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit
-// 8 different slots (all 32 banks once). The DMA writes a wave's 64 lanes to
-// 1 KiB of consecutive LDS, so the swizzle is applied on the global side:
-// the lane that lands in slot j of row r fetches chunk j ^ (r & 7).
+// 4x4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane in
+// AGPRs). K advances 32 per stage through a 4-stage LDS ring (4 x (A + B) x
+// 256 rows x 64 B = 128 KiB of the 160 KiB), filled by direct-to-LDS buffer
+// DMA (buffer_load_dwordx4 ... lds): no VGPR staging, the K offset rides in
+// an SGPR, rows past M / N read as zero through the buffer range check.
+// Stages are issued three ahead of the one being consumed; one barrier per
+// stage.
+//
+// LDS layout: a row is 4 chunks of 16 B (8 bf16 of K). Chunk c of row r is
+// stored in slot c ^ ((r >> 2) & 3). gfx950's LDS serves a 16-byte read for
+// 16 lanes per cycle across 64 banks; the fragment reads of 16 consecutive
+// rows then land in 16 distinct bank groups (rows r, r+4, r+8, r+12 share a
+// bank base, and the XOR separates them). The DMA writes a wave's 64 lanes to
+// 1 KiB of consecutive LDS, so the swizzle is applied on the global side: the
+// lane that lands in slot j of row r fetches chunk j ^ ((r >> 2) & 3).
 #include "hif4_dev.h"
 
 namespace hif4 {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kRowBytes = kBK * 2;               // 128 B per LDS row
-constexpr int kTileBytes = kBM * kRowBytes;      // one operand, one stage: 32 KiB
-constexpr int kLdsBytes = 2 * 2 * kTileBytes;    // 2 stages x (A, B)
-
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBM = 256, kBN = 256;
+constexpr int kBK = 32;                          // K per stage
+constexpr int kStages = 4;
+constexpr int kRowBytes = kBK * 2;               // 64 B per LDS row
+constexpr int kTileBytes = kBM * kRowBytes;      // one operand, one stage: 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;      // A + B
+constexpr int kLdsBytes = kStages * kStageBytes; // 128 KiB
+constexpr int kRsrcWord3 = 0x00020000;           // raw buffer, 32-bit data format (gfx9)
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every DMA stage in flight, i.e. vmcnt(0)). Each wave first waits
+// for its own DMA of the stage it is about to read (wait_vmcnt); after the
+// barrier every wave's part of that stage is in LDS. The asm statements keep
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int M,
@@ -65,31 +93,34 @@ void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // Global load mapping: 8 lanes cover one 128-byte row chunk (64 bf16),
-  // 32 rows per pass, 8 passes per operand.
-  // DMA mapping: wave w fills rows 64w .. 64w+63 of each operand tile, 8 rows
-  // (1 KiB) per instruction. Lane l lands in row 8i + l/8, slot l%8, and
-  // fetches K chunk (l%8) ^ (l/8) of that row. Rows past M (N) are clamped to
-  // the last valid row: they only feed outputs that are never stored.
-  const int drow = wave * 64 + (lane >> 3);
-  const int dchunk = (lane & 7) ^ (lane >> 3);
-  uint32_t offA[8], offB[8];  // byte offsets of this lane's chunk at kt = 0
+  // DMA mapping: per stage and operand, wave w fills rows 64w .. 64w+63 with
+  // 4 instructions of 1 KiB (16 rows x 64 B). Lane l lands in row 16i + l/4,
+  // slot l%4, and fetches chunk (l%4) ^ ((row >> 2) & 3) = (l%4) ^ ((l>>4)&3).
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * K * 2, kRsrcWord3);
+  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t voffA[4], voffB[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    offA[i] = (uint32_t)(((size_t)min(m0 + drow + 8 * i, M - 1) * K + dchunk * 8) * 2);
-    offB[i] = (uint32_t)(((size_t)min(n0 + drow + 8 * i, N - 1) * K + dchunk * 8) * 2);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 16 * i + (lane >> 2));
+    voffA[i] = ((uint32_t)(m0 + r) * (uint32_t)K + dchunk * 8) * 2;
+    voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + dchunk * 8) * 2;
   }
-  const char* Ab = reinterpret_cast<const char*>(A);
-  const char* Bb = reinterpret_cast<const char*>(B);
-  auto dma = [&](int kt, int stage) {
-    char* As = lds + stage * 2 * kTileBytes + wave * 64 * kRowBytes;
+  // DMA of quarter i of a stage (one A and one B instruction).
+  auto dma_i = [&](int stage, int kt, int i) {
+    char* As = lds + stage * kStageBytes + wave * 64 * kRowBytes;
     char* Bs = As + kTileBytes;
-    const size_t kofs = (size_t)kt * kRowBytes;
+    const int soff = kt * kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_t*)(As + i * 1024), 16, voffA[i], soff,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)(Bs + i * 1024), 16, voffB[i], soff,
+                                             0, 0);
+  };
+  auto dma = [&](int stage, int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_global_load_lds(Ab + kofs + offA[i], (lds_void_t*)(As + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Bb + kofs + offB[i], (lds_void_t*)(Bs + i * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) dma_i(stage, kt, i);
   };
 
   f32x16_t acc[4][4];
@@ -100,41 +131,57 @@ void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = K / kBK;
-  dma(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
   // Fragment addressing: lane l supplies row (l % 32) and K values
-  // 8*(l/32) .. +7 of each 16-wide K step, i.e. chunk 2s + l/32 (same
+  // 8*(l/32) .. +7 of each 16-wide K step s, i.e. chunk 2s + l/32 (same
   // mapping for A and B, so the contraction pairs matching K indices
   // whatever the hardware's K order inside an instruction).
   const int frow = lane & 31;
-  const int fsw = lane & 7;  // (row & 7) of every row this lane reads
+  const int fsw = (frow >> 2) & 3;
   const int fhalf = lane >> 5;
+  const int slot0 = ((0 + fhalf) ^ fsw) * 16;
+  const int slot1 = ((2 + fhalf) ^ fsw) * 16;
+
+  const int KT = K / kBK;
+  dma(0, 0);
+  if (KT > 1) dma(1, 1);
+  if (KT > 2) dma(2, 2);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) dma(kt + 1, cur ^ 1);
-    const char* As = lds + cur * 2 * kTileBytes + (wm * 128 + frow) * kRowBytes;
-    const char* Bs = lds + cur * 2 * kTileBytes + kTileBytes + (wn * 128 + frow) * kRowBytes;
+    const int rem = KT - 1 - kt;  // stages issued after this one (at most 2)
+    if (rem >= 2) wait_vmcnt<16>();
+    else if (rem == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    // The DMA of stage kt+3 is spread over this stage's MFMAs (a burst of
+    // eight DMA instructions ahead of them stalls the wave's issue).
+    const bool prefetch = kt + 3 < KT;
+    const char* st = lds + (kt & 3) * kStageBytes;
+    const char* As = st + (wm * 128 + frow) * kRowBytes;
+    const char* Bs = st + kTileBytes + (wn * 128 + frow) * kRowBytes;
+    // All 16 fragments of the stage go into distinct registers first, so the
+    // LDS latency is exposed once per stage, not once per 4 MFMAs.
+    bf16x8_t af[2][4], bfr[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int slot = ((2 * s + fhalf) ^ fsw) * 16;
-      bf16x8_t af[4], bfr[4];
+    for (int s = 0; s < 2; ++s) {
+      const int slot = s ? slot1 : slot0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * kRowBytes + slot);
+        af[s][i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * kRowBytes + slot);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * kRowBytes + slot);
+        bfr[s][j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * kRowBytes + slot);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (s == 0 && prefetch) dma_i((kt + 3) & 3, kt + 3, i);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Epilogue. 32x32 block output layout: lane l holds column l % 32 and,
@@ -182,7 +229,7 @@ hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The DMA addresses are 32-bit byte offsets from the operand base, so each
+// The DMA addresses are 32-bit byte offsets inside a buffer resource, so each
 // launch covers at most 2^31 bytes of A rows and of B rows; larger problems
 // are split into row blocks of A and of B (Y sub-blocks with stride n).
 hipError_t hif4_launch_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,

@@ -48,11 +48,20 @@ __global__ void pct_init_kernel(uint32_t* __restrict__ h1, uint32_t* __restrict_
   }
 }
 
-// Load the magnitude keys of this lane's (up to) two channels for one row.
-__device__ __forceinline__ uint32_t load_pair(const uint16_t* __restrict__ xr, int ch, int c) {
-  if (ch + 1 < c) return *reinterpret_cast<const uint32_t*>(xr + ch) & 0x7FFF7FFFu;
-  if (ch < c) return (uint32_t)(xr[ch] & 0x7FFFu) | 0xFFFF0000u;  // high half: no channel
-  return 0xFFFFFFFFu;
+// Per-lane channel setup: the lane reads the 32-bit word of channels ch and
+// ch+1 of every row. Lanes past the last channel read channel 0 instead (a
+// valid address) and mark both halves invalid; when c is odd the last lane's
+// word also covers element c, which exists because ld >= c + 1 then (ld is a
+// multiple of 8), and its high half is marked invalid. Loads stay branch-free.
+struct LaneCh {
+  uint32_t off;     // element offset of the word inside a row
+  uint32_t valid;   // bit 0: low half (ch) valid, bit 1: high half (ch+1) valid
+};
+__device__ __forceinline__ LaneCh lane_channels(int ch, int c) {
+  LaneCh l;
+  l.off = ch < c ? (uint32_t)ch : 0u;
+  l.valid = (ch < c ? 1u : 0u) | (ch + 1 < c ? 2u : 0u);
+  return l;
 }
 
 // Pass 1: coarse histograms. LDS counters are u16 pairs (rows per workgroup
@@ -66,31 +75,42 @@ __global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kPctCh;
-  const int ch = c0 + 2 * lane;
+  const LaneCh lc = lane_channels(c0 + 2 * lane, c);
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(rows, r0 + rows_per_block);
   const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
   constexpr int kWaves = kPctThreads / 64;
+  const uint16_t* xl = x + lc.off;
 
-  for (int64_t rb = r0 + wave; rb < r1; rb += (int64_t)kWaves * kPctUnroll) {
+  auto count = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) {
+      const bool row_ok = !tail || rb + (int64_t)u * kWaves < r1;
+      const uint32_t ka = v[u] & 0x7FFFu, kb = (v[u] >> 16) & 0x7FFFu;
+      const uint32_t ba = ka >> 7, bb = kb >> 7;
+      const uint32_t ia = (row_ok && (lc.valid & 1u)) ? 1u << (16 * (ba & 1u)) : 0u;
+      const uint32_t ib = (row_ok && (lc.valid & 2u)) ? 1u << (16 * (bb & 1u)) : 0u;
+      atomicAdd(&hist[(ba >> 1) * kPctCh + colA], ia);
+      atomicAdd(&hist[(bb >> 1) * kPctCh + colB], ib);
+    }
+  };
+  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
+  int64_t rb = r0 + wave;
+  for (; rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; rb += step) {
+    const uint16_t* p = xl + rb * ld;
+    uint32_t v[kPctUnroll];
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
+    count(v, rb, false);
+  }
+  if (rb < r1) {  // last partial block: rows clamped to r1 - 1, extra rows not counted
     uint32_t v[kPctUnroll];
 #pragma unroll
     for (int u = 0; u < kPctUnroll; ++u) {
-      const int64_t r = rb + (int64_t)u * kWaves;
-      v[u] = r < r1 ? load_pair(x + r * ld, ch, c) : 0xFFFFFFFFu;
+      const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
+      v[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
     }
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      const uint32_t ka = v[u] & 0xFFFFu, kb = v[u] >> 16;
-      if (ka != 0xFFFFu) {
-        const uint32_t bin = ka >> 7;
-        atomicAdd(&hist[(bin >> 1) * kPctCh + colA], 1u << (16 * (bin & 1)));
-      }
-      if (kb != 0xFFFFu) {
-        const uint32_t bin = kb >> 7;
-        atomicAdd(&hist[(bin >> 1) * kPctCh + colB], 1u << (16 * (bin & 1)));
-      }
-    }
+    count(v, rb, true);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
@@ -115,33 +135,67 @@ __device__ __forceinline__ void type7_ranks(int64_t n, double q, int64_t* lo, in
   *f = __dsub_rn(h, fl);
 }
 
-// Between passes: find the coarse bins (and ranks inside them) of lo and hi.
-__global__ void pct_select_kernel(const uint32_t* __restrict__ h1, int64_t rows, int c, double q,
-                                  PctSel* __restrict__ sel) {
-  const int ch = blockIdx.x * blockDim.x + threadIdx.x;
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele with
+// cross-lane reads; used only by the small per-channel kernels).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// First position (bin) whose running count exceeds `rank`, for counts laid
+// out as `per` consecutive bins per lane; returns the bin and the count of
+// all bins before it. Every lane gets the answer.
+template <int kPer>
+__device__ __forceinline__ void wave_find_rank(const uint32_t (&cnt)[kPer], int64_t rank,
+                                               uint32_t* bin, int64_t* before) {
+  const int lane = threadIdx.x & 63;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += cnt[i];
+  const uint32_t incl = wave_incl_scan(mine);
+  const uint32_t excl = incl - mine;
+  // the lane whose [excl, incl) range holds rank
+  const bool here = (int64_t)excl <= rank && rank < (int64_t)incl;
+  const uint64_t who = __ballot(here);
+  const int src = who ? __ffsll((unsigned long long)who) - 1 : 63;
+  uint32_t b = 0, run = excl;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (!found && (int64_t)(run + cnt[i]) > rank) {
+      b = (uint32_t)(lane * kPer + i);
+      found = true;
+    } else if (!found) {
+      run += cnt[i];
+    }
+  }
+  *bin = (uint32_t)__shfl((int)b, src, 64);
+  *before = (int64_t)(uint32_t)__shfl((int)run, src, 64);
+}
+
+// Between passes: one wave per channel finds the coarse bins (and ranks
+// inside them) of lo and hi.
+__global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restrict__ h1,
+                                                         int64_t rows, int c, double q,
+                                                         PctSel* __restrict__ sel) {
+  const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (ch >= c) return;
+  const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
   type7_ranks(rows, q, &lo, &hi, &f);
-  const uint32_t* h = h1 + (int64_t)ch * 256;
-  int64_t cum = 0;
-  uint32_t blo = 255, bhi = 255, rlo = 0, rhi = 0;
-  bool got_lo = false, got_hi = false;
-  for (int b = 0; b < 256; ++b) {
-    const int64_t nxt = cum + h[b];
-    if (!got_lo && nxt > lo) {
-      blo = b;
-      rlo = (uint32_t)(lo - cum);
-      got_lo = true;
-    }
-    if (!got_hi && nxt > hi) {
-      bhi = b;
-      rhi = (uint32_t)(hi - cum);
-      got_hi = true;
-    }
-    cum = nxt;
-  }
-  sel[ch] = PctSel{blo, rlo, bhi, rhi};
+  const uint4 w = reinterpret_cast<const uint4*>(h1 + (int64_t)ch * 256)[lane];
+  const uint32_t cnt[4] = {w.x, w.y, w.z, w.w};
+  uint32_t blo, bhi;
+  int64_t before_lo, before_hi;
+  wave_find_rank<4>(cnt, lo, &blo, &before_lo);
+  wave_find_rank<4>(cnt, hi, &bhi, &before_hi);
+  if (lane == 0) sel[ch] = PctSel{blo, (uint32_t)(lo - before_lo), bhi, (uint32_t)(hi - before_hi)};
 }
 
 // Pass 2: fine histograms inside bin b_lo and the minimum key of bin b_hi.
@@ -157,36 +211,52 @@ __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kPctCh;
   const int ch = c0 + 2 * lane;
+  const LaneCh lc = lane_channels(ch, c);
   const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
-  // Bins to watch; 0xFFFF never matches a key >> 7 (at most 255).
-  uint32_t loA = 0xFFFFu, hiA = 0xFFFFu, loB = 0xFFFFu, hiB = 0xFFFFu;
-  if (ch < c) {
+  // Bins to watch; 0x1FF never matches a bin (at most 255).
+  uint32_t loA = 0x1FFu, hiA = 0x1FFu, loB = 0x1FFu, hiB = 0x1FFu;
+  if (lc.valid & 1u) {
     loA = sel[ch].b_lo;
-    hiA = sel[ch].b_hi != sel[ch].b_lo ? sel[ch].b_hi : 0xFFFFu;
+    hiA = sel[ch].b_hi != sel[ch].b_lo ? sel[ch].b_hi : 0x1FFu;
   }
-  if (ch + 1 < c) {
+  if (lc.valid & 2u) {
     loB = sel[ch + 1].b_lo;
-    hiB = sel[ch + 1].b_hi != sel[ch + 1].b_lo ? sel[ch + 1].b_hi : 0xFFFFu;
+    hiB = sel[ch + 1].b_hi != sel[ch + 1].b_lo ? sel[ch + 1].b_hi : 0x1FFu;
   }
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(rows, r0 + rows_per_block);
   constexpr int kWaves = kPctThreads / 64;
+  const uint16_t* xl = x + lc.off;
 
-  for (int64_t rb = r0 + wave; rb < r1; rb += (int64_t)kWaves * kPctUnroll) {
-    uint32_t v[kPctUnroll];
+  auto scan = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
 #pragma unroll
     for (int u = 0; u < kPctUnroll; ++u) {
-      const int64_t r = rb + (int64_t)u * kWaves;
-      v[u] = r < r1 ? load_pair(x + r * ld, ch, c) : 0xFFFFFFFFu;
-    }
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      const uint32_t ka = v[u] & 0xFFFFu, kb = v[u] >> 16;
+      // a clamped (repeated) row must not count: push its bins out of range
+      const uint32_t kill = (!tail || rb + (int64_t)u * kWaves < r1) ? 0u : 0x1000000u;
+      const uint32_t ka = (v[u] & 0x7FFFu) | kill, kb = ((v[u] >> 16) & 0x7FFFu) | kill;
       if ((ka >> 7) == loA) atomicAdd(&hist[(ka & 127u) * kPctCh + colA], 1u);
       if ((ka >> 7) == hiA) atomicMin(&mins[colA], ka);
       if ((kb >> 7) == loB) atomicAdd(&hist[(kb & 127u) * kPctCh + colB], 1u);
       if ((kb >> 7) == hiB) atomicMin(&mins[colB], kb);
     }
+  };
+  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
+  int64_t rb = r0 + wave;
+  for (; rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; rb += step) {
+    const uint16_t* p = xl + rb * ld;
+    uint32_t v[kPctUnroll];
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
+    scan(v, rb, false);
+  }
+  if (rb < r1) {
+    uint32_t v[kPctUnroll];
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) {
+      const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
+      v[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
+    }
+    scan(v, rb, true);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
@@ -205,60 +275,128 @@ __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
 }
 
 // Exact keys of ranks lo / hi -> type-7 statistic, double then fp32 (RNE).
-__global__ void pct_final_kernel(const uint32_t* __restrict__ h2, const PctSel* __restrict__ sel,
-                                 const uint32_t* __restrict__ minkey, int64_t rows, int c,
-                                 double q, float* __restrict__ stats) {
-  const int ch = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per channel.
+__global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restrict__ h2,
+                                                        const PctSel* __restrict__ sel,
+                                                        const uint32_t* __restrict__ minkey,
+                                                        int64_t rows, int c, double q,
+                                                        float* __restrict__ stats) {
+  const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (ch >= c) return;
+  const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
   type7_ranks(rows, q, &lo, &hi, &f);
   const PctSel s = sel[ch];
-  const uint32_t* h = h2 + (int64_t)ch * 128;
-  uint32_t klo = 0, khi = 0;
-  bool got_lo = false, got_hi = false;
-  int64_t cum = 0;
-  for (int b = 0; b < 128; ++b) {
-    const int64_t nxt = cum + h[b];
-    if (!got_lo && nxt > (int64_t)s.r_lo) {
-      klo = (s.b_lo << 7) | (uint32_t)b;
-      got_lo = true;
-    }
-    if (!got_hi && s.b_hi == s.b_lo && nxt > (int64_t)s.r_hi) {
-      khi = (s.b_lo << 7) | (uint32_t)b;
-      got_hi = true;
-    }
-    cum = nxt;
+  const uint2 w = reinterpret_cast<const uint2*>(h2 + (int64_t)ch * 128)[lane];
+  const uint32_t cnt[2] = {w.x, w.y};
+  uint32_t flo, fhi;
+  int64_t before;
+  wave_find_rank<2>(cnt, (int64_t)s.r_lo, &flo, &before);
+  const uint32_t klo = (s.b_lo << 7) | flo;
+  uint32_t khi;
+  if (s.b_hi == s.b_lo) {
+    wave_find_rank<2>(cnt, (int64_t)s.r_hi, &fhi, &before);
+    khi = (s.b_lo << 7) | fhi;
+  } else {
+    khi = minkey[ch];
   }
-  if (s.b_hi != s.b_lo) khi = minkey[ch];
-  const double vlo = (double)__uint_as_float(klo << 16);
-  const double vhi = (double)__uint_as_float(khi << 16);
-  const double d = __dsub_rn(vhi, vlo);
-  const double t = __dmul_rn(f, d);
-  const double r = __dadd_rn(vlo, t);
-  stats[ch] = __double2float_rn(r);
+  if (lane == 0) {
+    const double vlo = (double)__uint_as_float(klo << 16);
+    const double vhi = (double)__uint_as_float(khi << 16);
+    const double d = __dsub_rn(vhi, vlo);
+    const double t = __dmul_rn(f, d);
+    const double r = __dadd_rn(vlo, t);
+    stats[ch] = __double2float_rn(r);
+  }
 }
 
-// Top-n mask: rank of ch = #{j : s[j] > s[ch] or (s[j] == s[ch] and j < ch)};
-// protected iff rank < n_protect. Stats are staged through LDS in tiles.
-__global__ __launch_bounds__(256) void topn_mask_kernel(const float* __restrict__ stats, int c,
-                                                        int n_protect, uint8_t* __restrict__ mask) {
-  __shared__ float tile[1024];
-  const int ch = blockIdx.x * blockDim.x + threadIdx.x;
-  const float mine = ch < c ? stats[ch] : 0.0f;
-  int rank = 0;
-  for (int t0 = 0; t0 < c; t0 += 1024) {
-    const int n = min(1024, c - t0);
+// Top-n mask by radix select over the stats' bit patterns (stats are >= 0,
+// so unsigned order = numeric order). One workgroup: four 8-bit digit passes
+// (most significant first) find tau, the n-th largest value; channels above
+// tau are protected, and of the channels equal to tau the lowest-indexed
+// (n - count_above) are protected (ties go to the lower index).
+constexpr int kMaskThreads = 1024;
+__global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __restrict__ stats,
+                                                                 int c, int n_protect,
+                                                                 uint8_t* __restrict__ mask) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix, s_need, s_above;
+  __shared__ uint32_t part[kMaskThreads];
+  const int tid = threadIdx.x;
+  if (n_protect <= 0 || n_protect >= c) {
+    const uint8_t v = n_protect <= 0 ? 0 : 1;
+    for (int i = tid; i < c; i += kMaskThreads) mask[i] = v;
+    return;
+  }
+  // rank (0-based, descending) of the element we look for
+  if (tid == 0) {
+    s_prefix = 0u;
+    s_need = (uint32_t)(n_protect - 1);
+  }
+  uint32_t prefix_mask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) tile[i] = stats[t0 + i];
+    const uint32_t pre = s_prefix;
+    for (int i = tid; i < c; i += kMaskThreads) {
+      const uint32_t u = __float_as_uint(stats[i]);
+      if ((u & prefix_mask) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
     __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      const float o = tile[i];
-      const int j = t0 + i;
-      rank += (o > mine) || (o == mine && j < ch);
+    if (tid == 0) {
+      // walk digits from the top: find the digit holding rank s_need (descending)
+      uint32_t need = s_need, d = 255;
+      for (int dd = 255; dd >= 0; --dd) {
+        if (need < hist[dd]) {
+          d = (uint32_t)dd;
+          break;
+        }
+        need -= hist[dd];
+      }
+      s_prefix = pre | (d << shift);
+      s_need = need;
+    }
+    prefix_mask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t tau = s_prefix;
+  // count_above and, per thread chunk, the number of ties (for the index-ordered tie rank)
+  const int chunk = (c + kMaskThreads - 1) / kMaskThreads;
+  const int b0 = min(c, tid * chunk), b1 = min(c, b0 + chunk);
+  uint32_t above = 0, ties = 0;
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t u = __float_as_uint(stats[i]);
+    above += u > tau;
+    ties += u == tau;
+  }
+  part[tid] = ties;
+  if (tid == 0) s_above = 0u;
+  __syncthreads();
+  atomicAdd(&s_above, above);
+  // exclusive scan of the tie counts (thread order = channel order)
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int i = 0; i < kMaskThreads; ++i) {
+      const uint32_t v = part[i];
+      part[i] = run;
+      run += v;
     }
   }
-  if (ch < c) mask[ch] = rank < n_protect ? 1 : 0;
+  __syncthreads();
+  const uint32_t take = (uint32_t)n_protect - s_above;  // ties to protect
+  uint32_t tie_rank = part[tid];
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t u = __float_as_uint(stats[i]);
+    uint8_t m = 0;
+    if (u > tau) {
+      m = 1;
+    } else if (u == tau) {
+      m = tie_rank < take ? 1 : 0;
+      ++tie_rank;
+    }
+    mask[i] = m;
+  }
 }
 
 }  // namespace hif4
@@ -306,8 +444,8 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
                        x + rbase * ld, rows - rbase, ci, ld, (int)rpb, h1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 255) / 256), dim3(256), 0, stream, h1, rows,
-                     ci, q, sel);
+  hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1, rows, ci, q,
+                     sel);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t s0 = 0; s0 < nsplit; s0 += 65535) {
     const int64_t ns = nsplit - s0 < 65535 ? nsplit - s0 : 65535;
@@ -316,10 +454,10 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
                        x + rbase * ld, rows - rbase, ci, ld, (int)rpb, sel, h2, minkey);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 255) / 256), dim3(256), 0, stream, h2, sel,
-                     minkey, rows, ci, q, stats);
+  hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel, minkey,
+                     rows, ci, q, stats);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topn_mask_kernel, dim3((ci + 255) / 256), dim3(256), 0, stream, stats, ci,
+  hipLaunchKernelGGL(topn_mask_kernel, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,
                      (int)n_protect, mask);
   return hipGetLastError();
 }
