@@ -61,7 +61,7 @@ hif4_status hif4_quantize(const void* x, int64_t rows, int64_t k, int64_t ld, co
   if (mask && n_mask > 0 && !kept) return HIF4_ERR_NULL;
   if (!aligned(x, 16) || ld % 8 != 0 || !aligned(codes, 16) || !aligned(meta, 4))
     return HIF4_ERR_ALIGN;
-  if (mask && !aligned(mask, 8)) return HIF4_ERR_ALIGN;
+  if (mask && !aligned(mask, 16)) return HIF4_ERR_ALIGN;
   if (mask && n_mask > 0 && !aligned(kept, 2)) return HIF4_ERR_ALIGN;
   hif4_status st = check_device();
   if (st != HIF4_OK) return st;

@@ -22,8 +22,9 @@ __device__ __forceinline__ float e6m2_f32(uint32_t c) {
 }
 
 // Smallest level-1 code c with 7 v(c) >= a (a >= 0, exact bf16 value), 255 if
-// none. An estimate from a/7 is off by at most one code; the two exact
-// comparisons settle it (7 v(c) has at most 6 significant bits: exact in fp32).
+// none. An estimate from a/7 is off by at most one code; two exact
+// comparisons settle it (7 v(c) has at most 6 significant bits: exact in
+// fp32). Branch-free.
 __device__ __forceinline__ uint32_t level1_code(float a) {
   const float r = a * (1.0f / 7.0f);
   const uint32_t b = __float_as_uint(r);
@@ -31,20 +32,32 @@ __device__ __forceinline__ uint32_t level1_code(float a) {
   const uint32_t m = b & 0x7FFFFFu;
   int c = 4 * e + (int)(m >> 21) + ((m & 0x1FFFFFu) != 0u);
   c = c < 0 ? 0 : (c > 255 ? 255 : c);
-  if (c > 0 && 7.0f * e6m2_f32((uint32_t)c - 1u) >= a) {
-    c -= 1;
-  } else if (c < 255 && 7.0f * e6m2_f32((uint32_t)c) < a) {
-    c += 1;
-  }
-  return (uint32_t)c;
+  // bitwise & (not &&): no short-circuit, no branch; e6m2_f32 of an
+  // out-of-range code is a harmless finite float that the mask discards
+  const uint32_t down = (uint32_t)(c > 0) & (uint32_t)(7.0f * e6m2_f32((uint32_t)(c - 1)) >= a);
+  const uint32_t up = (uint32_t)(c < 255) & (uint32_t)(7.0f * e6m2_f32((uint32_t)c) < a);
+  return (uint32_t)c - down + up;
 }
 
-// 16 / (4 + m), m = 0..3, correctly rounded to double: 4 / v(c) without the
-// power of two. Each has relative error 2^-54 or less, small enough that
-// |x| * (4 / D) rounds to an exact half-integer whenever the real quotient is
-// one (the tie cases), so rint() below is round-to-nearest-even on the reals.
-__device__ __forceinline__ double inv_mant16(uint32_t m) {
-  return m == 0u ? 4.0 : (m == 1u ? 3.2 : (m == 2u ? 2.6666666666666665 : 2.2857142857142856));
+// 16 / (4 + m) as an unevaluated fp32 sum hi + lo (hi = RN(16/(4+m)),
+// lo = RN(16/(4+m) - hi)): the HiF4 element quotient 4|x| / D is
+// t = fma(|x|, hi 2^p, |x| lo 2^p) with D's power of two folded into p. For
+// every bf16 |x| this t is within half an fp32 ulp of the real quotient, so
+// exact half-integers (the ties) come out exact and rintf() rounds to nearest
+// even exactly as on the reals (checked exhaustively for all four mantissas).
+// 4-way select by bit masks (v_bfi_b32), no branches.
+__device__ __forceinline__ uint32_t select4(uint32_t m, uint32_t t0, uint32_t t1, uint32_t t2,
+                                            uint32_t t3) {
+  const uint32_t b0 = 0u - (m & 1u), b1 = 0u - ((m >> 1) & 1u);
+  const uint32_t t01 = (t1 & b0) | (t0 & ~b0);
+  const uint32_t t23 = (t3 & b0) | (t2 & ~b0);
+  return (t23 & b1) | (t01 & ~b1);
+}
+__device__ __forceinline__ float inv_mant_hi(uint32_t m) {
+  return __uint_as_float(select4(m, 0x40800000u, 0x404CCCCDu, 0x402AAAABu, 0x40124925u));
+}
+__device__ __forceinline__ float inv_mant_lo(uint32_t m) {
+  return __uint_as_float(select4(m, 0x00000000u, 0xB34CCCCDu, 0xB3AAAAABu, 0xB3DB6DB7u));
 }
 
 // DPP lane moves within a row of 16 lanes (gfx9 encodings).

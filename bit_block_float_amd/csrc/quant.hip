@@ -8,11 +8,13 @@
 // Protected channels: Tail-Aware HiFloat4 summary (agents-report.net),
 // section "方法概述". The rule and layout readings are stated in hif4.h.
 //
-// Work mapping: one lane owns one level-2 group (8 consecutive elements along
-// k, one 16-byte load); 8 aligned lanes own one unit; the unit maximum and the
-// metadata word are formed with DPP moves inside the 8 lanes. Each lane emits
-// one 32-bit code word (its two level-3 groups as low/high nibbles), so a
-// wave writes 256 contiguous code bytes and 32 contiguous meta bytes.
+// Work mapping (quantize): one lane owns 16 consecutive elements along k (two
+// level-2 groups, two 16-byte loads); 4 aligned lanes own one unit; the unit
+// maximum and the metadata word are formed with DPP moves inside the quad.
+// Each lane emits two 32-bit code words (a level-2 group each, its two
+// level-3 groups as low/high nibbles), so a wave writes 512 contiguous code
+// bytes and 64 contiguous meta bytes. The element rounding runs in fp32 with
+// a two-term reciprocal (inv_mant_hi/lo) that makes it exact.
 #include "hif4_dev.h"
 
 namespace hif4 {
@@ -35,90 +37,146 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
-template <bool kMask, bool kCodes, bool kDeq>
-__global__ __launch_bounds__(256) void quantize_kernel(
-    const uint16_t* __restrict__ x, int64_t ld, uint32_t groups_per_row, FastDiv grp_div,
-    uint32_t total_groups, const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta, uint16_t* __restrict__ deq) {
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t grp = blockIdx.x * blockDim.x + threadIdx.x; grp < total_groups; grp += stride) {
-    const uint32_t row = fdiv(grp, grp_div);
-    const uint32_t gi = grp - row * groups_per_row;  // level-2 group index within the row
-    const uint32_t g = gi & 7u;                     // level-2 group index within the unit
+// Max over the 4 lanes of an aligned quad (DPP quad_perm), and OR.
+__device__ __forceinline__ uint32_t max4_u32(uint32_t v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t or4_u32(uint32_t v) {
+  v |= dpp<kDppQuadXor1>(v);
+  v |= dpp<kDppQuadXor2>(v);
+  return v;
+}
 
-    const uint4 w = *reinterpret_cast<const uint4*>(x + (int64_t)row * ld + (int64_t)gi * 8);
-    uint32_t bits[8] = {w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u,
-                        w.z << 16, w.z & 0xFFFF0000u, w.w << 16, w.w & 0xFFFF0000u};
-    if (kMask) {
-      // Protected channels are quantized as +0 and do not enter the maxima.
-      const uint2 mk = *reinterpret_cast<const uint2*>(mask + (size_t)gi * 8);
+// One level-2 group (8 elements, one code word): steps 3-5 given the unit's
+// level-1 scale. w: the group's 8 bf16 values (element 2i in the low half of
+// word i). Returns the code word; e3 bits and the fake-quant values by ref.
+template <bool kDeq>
+__device__ __forceinline__ uint32_t encode_group(uint4 w, float s, int p, float rh, float rl,
+                                                 uint32_t& e2, uint32_t& e3a, uint32_t& e3b,
+                                                 uint4& deq) {
+  const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y),
+                      bf16hi_to_f32(w.y), bf16lo_to_f32(w.z), bf16hi_to_f32(w.z),
+                      bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
+  const float m4a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  const float m4b = fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
+  // steps 3-4: level-2 / level-3 bits (exact compares)
+  e2 = fmaxf(m4a, m4b) > 3.5f * s;
+  const float t3 = (e2 ? 3.5f : 1.75f) * s;
+  e3a = m4a > t3;
+  e3b = m4b > t3;
+  // step 5: k = RNE(4|x| / D), D = s 2^E, 4/D = (16/(4+m)) 2^(31-e-E) (inv_mant_hi)
+  const int pa = p - (int)(e2 + e3a), pb = p - (int)(e2 + e3b);
+  const float rha = ldexpf(rh, pa), rla = ldexpf(rl, pa);
+  const float rhb = ldexpf(rh, pb), rlb = ldexpf(rl, pb);
+  float kf[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if ((mk.x >> (8 * i)) & 0xFFu) bits[i] = 0u;
-        if ((mk.y >> (8 * i)) & 0xFFu) bits[4 + i] = 0u;
-      }
-    }
-
-    // step 1: maxima of |x| (compared as bit patterns of non-negative floats)
-    uint32_t m4a = 0u, m4b = 0u;
+  for (int i = 0; i < 8; ++i) {
+    const float ax = fabsf(v[i]);
+    const float t = i < 4 ? fmaf(ax, rha, ax * rla) : fmaf(ax, rhb, ax * rlb);
+    kf[i] = fminf(rintf(t), 7.0f);
+  }
+  // magnitudes: element b of the low level-3 group -> low nibble of byte b,
+  // element 4+b -> high nibble of byte b
+  uint32_t lo = 0u, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m4a = max(m4a, bits[i] & 0x7FFFFFFFu);
-      m4b = max(m4b, bits[4 + i] & 0x7FFFFFFFu);
-    }
-    const uint32_t m8 = max(m4a, m4b);
-    const float amax = __uint_as_float(max8_u32(m8));
-
-    // step 2: level-1 code; steps 3-4: level-2 / level-3 bits (exact compares)
-    const uint32_t c = level1_code(amax);
-    const float s = e6m2_f32(c);
-    const uint32_t e2 = __uint_as_float(m8) > 3.5f * s;
-    const float t3 = (e2 ? 3.5f : 1.75f) * s;
-    const uint32_t e3a = __uint_as_float(m4a) > t3;
-    const uint32_t e3b = __uint_as_float(m4b) > t3;
-
-    // step 5: k = RNE(4|x| / D), D = s 2^E, computed as |x| * (4/D) in double
-    const double rbase = inv_mant16(c & 3u);
-    const int p = 31 - (int)(c >> 2);
-    const double ra = ldexp(rbase, p - (int)(e2 + e3a));
-    const double rb = ldexp(rbase, p - (int)(e2 + e3b));
-    uint32_t k[8];
+  for (int b = 0; b < 4; ++b) {
+    lo = __builtin_amdgcn_cvt_pk_u8_f32(kf[b], b, lo);
+    hi = __builtin_amdgcn_cvt_pk_u8_f32(kf[4 + b], b, hi);
+  }
+  const uint32_t mag = lo | (hi << 4);
+  // signs: the high byte of each bf16 carries its sign in bit 7
+  const uint32_t sl = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);  // elements 0..3
+  const uint32_t sh = __builtin_amdgcn_perm(w.w, w.z, 0x07050301u);  // elements 4..7
+  const uint32_t sgn = ((sl >> 4) & 0x08080808u) | (sh & 0x80808080u);
+  // a zero element keeps +0: sign only where the magnitude nibble is nonzero
+  const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
+  if (kDeq) {
+    // Exact: k (3 bits) times D/4 (3 significant bits) fits bf16.
+    const float da = ldexpf(s, (int)(e2 + e3a) - 2);
+    const float db = ldexpf(s, (int)(e2 + e3b) - 2);
+    uint32_t h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const double t = (double)__uint_as_float(bits[i] & 0x7FFFFFFFu) * (i < 4 ? ra : rb);
-      k[i] = (uint32_t)fmin(rint(t), 7.0);
+      const float y = kf[i] * (i < 4 ? da : db);
+      const uint32_t sg = kf[i] != 0.0f ? (__float_as_uint(v[i]) & 0x80000000u) : 0u;
+      h[i] = (__float_as_uint(y) | sg) >> 16;
+    }
+    deq = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16));
+  }
+  return mag | (sgn & nz);
+}
+
+// Work mapping: one lane owns two level-2 groups (16 consecutive elements,
+// two 16-byte loads), 4 aligned lanes own a unit; unit maximum and metadata
+// word via DPP inside the quad. A wave covers 16 units.
+template <bool kMask, bool kCodes, bool kDeq>
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t ld, uint32_t items_per_row, FastDiv item_div,
+    uint32_t total_items, const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
+    uint32_t* __restrict__ meta, uint16_t* __restrict__ deq) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t it = blockIdx.x * blockDim.x + threadIdx.x; it < total_items; it += stride) {
+    const uint32_t row = fdiv(it, item_div);
+    const uint32_t j = it - row * items_per_row;  // 16-element item within the row
+    const uint32_t q = j & 3u;                    // item within the unit (groups 2q, 2q+1)
+
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)row * ld + (int64_t)j * 16);
+    uint4 w0 = src[0], w1 = src[1];
+    if (kMask) {
+      // Protected channels are quantized as +0 and do not enter the maxima.
+      const uint4 mk = *reinterpret_cast<const uint4*>(mask + (size_t)j * 16);
+      const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
+      uint32_t* ww0 = &w0.x;
+      uint32_t* ww1 = &w1.x;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t mb = (mw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        uint32_t* ww = i < 8 ? ww0 : ww1;
+        const int e = i & 7;
+        if (mb) ww[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      }
     }
 
-    if (kCodes) {
-      uint32_t word = 0u;
+    // step 1: unit maximum of |x|, compared as bit patterns of non-negative
+    // floats (sign bits dropped), over the lane's 16 values, then the quad
+    uint32_t am = 0u;
+    {
+      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t sgn = (bits[i] >> 31) & (k[i] != 0u);
-        const uint32_t nib = k[i] | (sgn << 3);
-        word |= nib << (i < 4 ? 8 * i : 8 * (i - 4) + 4);
+        am = max(am, (ww[i] << 16) & 0x7FFFFFFFu);
+        am = max(am, ww[i] & 0x7FFF0000u);
       }
-      codes32[grp] = word;
-      const uint32_t mb = (e2 << (8 + g)) | (e3a << (16 + 2 * g)) | (e3b << (17 + 2 * g));
-      const uint32_t mw = or8_u32(mb) | c;
-      if (g == 0u) meta[grp >> 3] = mw;
+    }
+    const float amax = __uint_as_float(max4_u32(am));
+
+    // step 2: level-1 code (shared by the quad)
+    const uint32_t c = level1_code(amax);
+    const float s = e6m2_f32(c);
+    const int p = 31 - (int)(c >> 2);
+    const float rh = inv_mant_hi(c & 3u), rl = inv_mant_lo(c & 3u);
+
+    uint32_t e2a, e3a0, e3b0, e2b, e3a1, e3b1;
+    uint4 d0, d1;
+    const uint32_t cw0 = encode_group<kDeq>(w0, s, p, rh, rl, e2a, e3a0, e3b0, d0);
+    const uint32_t cw1 = encode_group<kDeq>(w1, s, p, rh, rl, e2b, e3a1, e3b1, d1);
+
+    if (kCodes) {
+      reinterpret_cast<uint2*>(codes32)[it] = make_uint2(cw0, cw1);
+      const uint32_t g0 = 2 * q, g1 = 2 * q + 1;
+      const uint32_t mb = (e2a << (8 + g0)) | (e2b << (8 + g1)) | (e3a0 << (16 + 2 * g0)) |
+                          (e3b0 << (17 + 2 * g0)) | (e3a1 << (16 + 2 * g1)) |
+                          (e3b1 << (17 + 2 * g1));
+      const uint32_t mw = or4_u32(mb) | c;
+      if (q == 0u) meta[it >> 2] = mw;
     }
     if (kDeq) {
-      // Exact: k (3 bits) times D/4 (3 significant bits) fits bf16.
-      const float da = ldexpf(s, (int)(e2 + e3a) - 2);
-      const float db = ldexpf(s, (int)(e2 + e3b) - 2);
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = (float)k[i] * (i < 4 ? da : db);
-        const uint32_t sgn = (bits[i] & 0x80000000u) & (k[i] != 0u ? 0xFFFFFFFFu : 0u);
-        h[i] = (__float_as_uint(v) | sgn) >> 16;
-      }
-      uint4 o;
-      o.x = h[0] | (h[1] << 16);
-      o.y = h[2] | (h[3] << 16);
-      o.z = h[4] | (h[5] << 16);
-      o.w = h[6] | (h[7] << 16);
-      *reinterpret_cast<uint4*>(deq + (int64_t)grp * 8) = o;
+      uint4* dst = reinterpret_cast<uint4*>(deq + (int64_t)it * 16);
+      dst[0] = d0;
+      dst[1] = d1;
     }
   }
 }
@@ -222,7 +280,7 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
                                 const uint8_t* mask, uint8_t* codes, uint32_t* meta,
                                 uint16_t* deq_bf16, hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
-  const uint32_t gpr = (uint32_t)(k / 8);
+  const uint32_t gpr = (uint32_t)(k / 16);  // 16-element items per row
   const FastDiv fd = make_fastdiv(gpr);
   const int64_t max_rows = ((int64_t)1 << 30) / gpr;
   for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {

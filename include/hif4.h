@@ -92,7 +92,7 @@ HIF4_EXPORT int hif4_version(void);
  *
  *  x      bf16 [rows][ld], row-major; 16-byte aligned, ld % 8 == 0, ld >= k.
  *  rows   >= 0 (0 enqueues nothing).   k   >= 0, k % 64 == 0.
- *  mask   NULL, or u8 [k], 8-byte aligned: nonzero = protected input channel
+ *  mask   NULL, or u8 [k], 16-byte aligned: nonzero = protected input channel
  *         ([TA-method]).
  *         Protected entries are encoded as +0 and do not influence the scales.
  *  n_mask number of nonzero mask bytes (must equal it; kept entries beyond

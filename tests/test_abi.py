@@ -72,7 +72,7 @@ def test_quantize_argument_checks(L):
     assert q(A, 4, 64, 68, None, 0, None, A, A, None) == ALIGN     # ld % 8
     assert q(A, 4, 64, 64, None, 0, None, A + 4, A, None) == ALIGN
     assert q(A, 4, 64, 64, None, 0, None, A, A + 2, None) == ALIGN
-    assert q(A, 4, 64, 64, A + 1, 1, A, A, A, None) == ALIGN
+    assert q(A, 4, 64, 64, A + 8, 1, A, A, A, None) == ALIGN
     assert q(A, 4, 65536 + 64, 65536 + 64, A, 1, A, A, A, None) == SHAPE  # masked k limit
     assert q(A, 4, 64, 64, A, 65, A, A, A, None) == SHAPE          # n_mask > k
 
