@@ -70,7 +70,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -189,7 +189,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "hif4_linear_w4a4 call (X/W decode + gemm_bf16_nt_kernel), timed with "
+            "kernel": "hif4_linear_w4a4 call (W decode + gemm_w4a4_kernel, X decoded per tile), "
+                      "timed with "
                       "HIP events on its stream",
             "achieved": gemm_tflops,
             "peak": BF16_MFMA_PEAK_TFLOPS,

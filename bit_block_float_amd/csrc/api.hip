@@ -66,7 +66,7 @@ hif4_status hif4_quantize(const void* x, int64_t rows, int64_t k, int64_t ld, co
   hif4_status st = check_device();
   if (st != HIF4_OK) return st;
   const uint16_t* xb = (const uint16_t*)x;
-  st = launched(hif4_launch_quantize(xb, rows, k, ld, mask, codes, meta, nullptr, stream));
+  st = launched(hif4_launch_quantize(xb, rows, k, ld, mask, codes, meta, stream));
   if (st != HIF4_OK || !mask || n_mask == 0) return st;
   return launched(hif4_launch_gather_kept(xb, rows, k, ld, mask, n_mask, (uint16_t*)kept, stream));
 }
@@ -83,10 +83,13 @@ hif4_status hif4_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t 
   return launched(hif4_launch_dequantize(codes, meta, rows, k, out, out_dtype == HIF4_BF16, stream));
 }
 
-// Workspace: the bf16 decoded activation [m][k] then the decoded weight [n][k].
+// Workspace: the activation's HiF4 codes [m][k/2] and meta [m][k/64] (used
+// when X comes in as bf16), then the decoded weight, bf16 [n][k].
+static size_t ws_x_codes(int64_t m, int64_t k) { return align256((size_t)m * (size_t)(k / 2)); }
+static size_t ws_x_meta(int64_t m, int64_t k) { return align256((size_t)m * (size_t)(k / 64) * 4); }
 size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || n < 0 || k < 0) return 0;
-  return align256((size_t)m * (size_t)k * 2) + align256((size_t)n * (size_t)k * 2);
+  return ws_x_codes(m, k) + ws_x_meta(m, k) + align256((size_t)n * (size_t)k * 2);
 }
 
 hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32_t* x_meta,
@@ -118,18 +121,21 @@ hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32
     const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
     return launched(hif4_launch_zero(y, bytes, stream));
   }
-  uint16_t* xa = (uint16_t*)workspace;
-  uint16_t* wb = (uint16_t*)((char*)workspace + align256((size_t)m * (size_t)k * 2));
+  uint8_t* xc = (uint8_t*)workspace;
+  uint32_t* xm = (uint32_t*)((char*)workspace + ws_x_codes(m, k));
+  uint16_t* wb = (uint16_t*)((char*)workspace + ws_x_codes(m, k) + ws_x_meta(m, k));
   if (x) {
-    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, nullptr, nullptr, nullptr, xa,
-                                       stream));
-  } else {
-    st = launched(hif4_launch_dequantize(x_codes, x_meta, m, k, xa, 1, stream));
+    // X in bf16: quantize it to HiF4 first (the same codes hif4_quantize gives).
+    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, nullptr, xc, xm, stream));
+    if (st != HIF4_OK) return st;
+    x_codes = xc;
+    x_meta = xm;
   }
-  if (st != HIF4_OK) return st;
+  // W decoded to bf16 once; X codes are decoded tile by tile inside the GEMM.
   st = launched(hif4_launch_dequantize(w_codes, w_meta, n, k, wb, 1, stream));
   if (st != HIF4_OK) return st;
-  return launched(hif4_launch_gemm_bf16_nt(xa, wb, m, n, k, y, y_dtype == HIF4_BF16, stream));
+  return launched(hif4_launch_gemm_w4a4(x_codes, x_meta, wb, m, n, k, y, y_dtype == HIF4_BF16,
+                                        stream));
 }
 
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {

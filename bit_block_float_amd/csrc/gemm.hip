@@ -1,32 +1,33 @@
-// gemm.hip -- the W4A4 contraction Y = A B^T on gfx950 matrix cores.
+// gemm.hip -- the W4A4 contraction Y = deq(Q(X)) deq(Q(W))^T on gfx950
+// matrix cores.
 //
 // Layer form Y = X W^T: HiFloat4 calibration article (hwcomputing.csdn.net),
 // section 2.3 "FlatQuant"; W4A4 fake quantization of the main linear layers:
 // Tail-Aware HiFloat4 (arXiv 2605.26628 record, abstract).
 //
-// Operands are the HiF4-decoded values of X and W in bf16. Every decoded HiF4
-// value k/4 * 2^(e2+e3) * v(c) has at most 6 significant bits (3 from k, 3 from
-// the E6M2 mantissa) and an exponent in [-33, 35], so it is EXACT in bf16, every
+// Operands are HiF4-decoded values in bf16. Every decoded HiF4 value
+// k/4 * 2^(e2+e3) * v(c) has at most 6 significant bits (3 from k, 3 from the
+// E6M2 mantissa) and an exponent in [-33, 35], so it is EXACT in bf16, every
 // product is exact in fp32, and the only rounding is the fp32 accumulation
 // inside the MFMA. The per-unit level-1 scales are therefore already inside
 // the operands: no per-unit rescale is needed in the K loop.
 //
 // Tiling: 256x256 output tile per workgroup (4 waves, 2x2, each 128x128 =
 // 4x4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane in
-// AGPRs). K advances 32 per stage through a 4-stage LDS ring (4 x (A + B) x
-// 256 rows x 64 B = 128 KiB of the 160 KiB), filled by direct-to-LDS buffer
-// DMA (buffer_load_dwordx4 ... lds): no VGPR staging, the K offset rides in
-// an SGPR, rows past M / N read as zero through the buffer range check.
-// Stages are issued three ahead of the one being consumed; one barrier per
-// stage.
+// AGPRs), one workgroup per CU. Operands reach LDS by direct-to-LDS buffer
+// DMA (buffer_load ... lds): no VGPR staging, the K offset rides in an SGPR,
+// rows past M / N read as zero through the buffer range check.
 //
-// LDS layout: a row is 4 chunks of 16 B (8 bf16 of K). Chunk c of row r is
-// stored in slot c ^ ((r >> 2) & 3). gfx950's LDS serves a 16-byte read for
-// 16 lanes per cycle across 64 banks; the fragment reads of 16 consecutive
-// rows then land in 16 distinct bank groups (rows r, r+4, r+8, r+12 share a
-// bank base, and the XOR separates them). The DMA writes a wave's 64 lanes to
-// 1 KiB of consecutive LDS, so the swizzle is applied on the global side: the
-// lane that lands in slot j of row r fetches chunk j ^ ((r >> 2) & 3).
+// LDS rows of bf16 operands are 64 B (32 K values) = 4 chunks of 16 B; chunk
+// c of row r sits in slot c ^ ((r >> 2) & 3). gfx950's LDS serves a 16-byte
+// read for 16 lanes per cycle across 64 banks; the fragment reads of 16
+// consecutive rows then land in 16 distinct bank groups (rows r, r+4, r+8,
+// r+12 share a bank base, and the XOR separates them). The DMA writes a
+// wave's 64 lanes to 1 KiB of consecutive LDS, so the swizzle is applied on
+// the global side: the lane that lands in slot j of row r fetches chunk
+// j ^ ((r >> 2) & 3).
+#include <type_traits>
+
 #include "hif4_dev.h"
 
 namespace hif4 {
@@ -37,46 +38,101 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kBK = 32;                          // K per stage
-constexpr int kStages = 4;
 constexpr int kRowBytes = kBK * 2;               // 64 B per LDS row
 constexpr int kTileBytes = kBM * kRowBytes;      // one operand, one stage: 16 KiB
-constexpr int kStageBytes = 2 * kTileBytes;      // A + B
-constexpr int kLdsBytes = kStages * kStageBytes; // 128 KiB
 constexpr int kRsrcWord3 = 0x00020000;           // raw buffer, 32-bit data format (gfx9)
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every DMA stage in flight, i.e. vmcnt(0)). Each wave first waits
-// for its own DMA of the stage it is about to read (wait_vmcnt); after the
-// barrier every wave's part of that stage is in LDS. The asm statements keep
-// the compiler from moving LDS accesses across the barrier.
+// for its own DMA of the stage it is about to read (s_waitcnt vmcnt); after
+// the barrier every wave's part of that stage is in LDS. The asm statements
+// keep the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 GEMM with the activation operand in HiF4: Y = deq(A_codes) B^T.
+//
+// A arrives as HiF4 codes + meta (0.5625 B per element) through the DMA ring
+// and is decoded ONCE per workgroup into a bf16 LDS tile; B (the weight,
+// decoded to bf16 once per call) arrives as bf16. Fetching 4.5 KiB of A
+// codes instead of 16 KiB of bf16 per 32-wide K step cuts the global->LDS
+// traffic, which bounds a kernel fed with bf16 on both sides.
+//
+// Decode (HiF4 element = S1P2 nibble k/4 x 2^E x v(c), E = e2 + e3 in
+// {0, 1, 2}, v(c) = 2^(e-31) (1 + m/4) with e = c >> 2, m = c & 3): write
+// e = 2a + p. Then |x| = [k (1 + m/4) 2^(E + p - 33)] 2^(2a), and the bracket
+// takes one of 24 x 8 values, all exact in bf16 (k (4 + m) <= 49). A 24-entry
+// LDS table holds, per (m, E, p), the low and high bytes of the bracket's
+// bf16 for k = 0..7 as two byte planes. Multiplying by 2^(2a) adds a to the
+// high byte of every non-zero value (the exponent's low bit stays put), so a
+// level-3 quad decodes as: add a to the high plane (sparing k = 0), two
+// v_perm_b32 plane lookups by the 4 magnitudes, OR the 4 signs into the high
+// bytes, two v_perm_b32 to interleave into 4 bf16. The table is 384 B: the
+// lanes of a read either share an entry (broadcast) or hit distinct banks.
+//
+// Thread t decodes row t of the tile, whose codes its own wave fetched.
+// LDS map (bytes):
+//   [0, 64K)          B ring: 4 stages x 256 rows x 64 B (16-row swizzle)
+//   [64K, 96K)        decoded A: 2 buffers x 256 rows x 64 B (same swizzle)
+//   [96K, 123K)       A code ring: 3 units x (256 x 32 B codes + 256 x 4 B meta)
+//   [123K, +384)      decode table
+//
+// Step h covers K = 32h .. 32h+31 (half h&1 of unit h>>1) as two 16-wide
+// MFMA K-chunks with one barrier between them, so that the fragments of the
+// next chunk always load under the MFMAs of the current one (one wave per
+// SIMD: nothing else would hide the LDS latency). Loads past the end of K
+// are clamped to the last stage / unit and land in ring slots no one reads
+// again, which keeps the loop free of branches; the vmcnt accounting is
+// spelled out at the loop.
+constexpr int kLdsB = 0;
+constexpr int kLdsADec = 4 * kTileBytes;                    // 65536
+constexpr int kLdsACodes = kLdsADec + 2 * kTileBytes;       // 98304
+constexpr int kCodeSlotBytes = 256 * 32 + 256 * 4;          // 9216
+constexpr int kLdsTable = kLdsACodes + 3 * kCodeSlotBytes;  // 125952
+constexpr int kLdsW4A4Bytes = kLdsTable + 24 * 16;          // 126336
+
+// 16-byte LDS access through a native vector type. (Through the uint4
+// struct it is split into four i32 accesses and re-merged, and the compiler
+// then makes it wait for every LDS-DMA in flight, draining the ring.)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_u32x4(const char* p) {
+  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
+
+// One level-3 quad: `nib` holds 4 nibbles in its bytes' low halves
+// (magnitude bits 0-2, sign bit 3); t = table entry (lo plane k0-3, k4-7,
+// hi plane k0-3, k4-7) with the exponent offset already in the hi plane.
+__device__ __forceinline__ uint2 decode_quad(uint32_t nib, uint4 t) {
+  const uint32_t sel = nib & 0x07070707u;
+  const uint32_t lob = __builtin_amdgcn_perm(t.y, t.x, sel);  // low bytes of the 4 bf16
+  uint32_t hib = __builtin_amdgcn_perm(t.w, t.z, sel);        // high bytes
+  hib |= (nib << 4) & 0x80808080u;                             // signs
+  return make_uint2(__builtin_amdgcn_perm(hib, lob, 0x05010400u),
+                    __builtin_amdgcn_perm(hib, lob, 0x07030602u));
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int M,
-                         int N, int K, void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m,
-                         int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
+                      const uint16_t* __restrict__ B, int M, int N, int K, void* __restrict__ Y,
+                      int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsW4A4Bytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware tile order: consecutive workgroup ids land on different XCDs
-  // (round-robin over 8), so give each XCD a contiguous run of tiles, and
-  // walk that run column-major in groups of 8 tile-rows so that tiles in
-  // flight on one XCD share A and B panels in its L2.
+  // Tile order: consecutive workgroup ids go to different XCDs (round
+  // robin), so give each XCD a contiguous run of tiles; within the order,
+  // groups of 8 tile-rows are walked column by column so that the B tiles
+  // in flight are shared by 8 neighbouring workgroups through L2.
   const int ntiles = tiles_m * tiles_n;
   int t = blockIdx.x;
   {
@@ -93,34 +149,117 @@ void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // DMA mapping: per stage and operand, wave w fills rows 64w .. 64w+63 with
-  // 4 instructions of 1 KiB (16 rows x 64 B). Lane l lands in row 16i + l/4,
-  // slot l%4, and fetches chunk (l%4) ^ ((row >> 2) & 3) = (l%4) ^ ((l>>4)&3).
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * K * 2, kRsrcWord3);
+  // ---- decode table: entry (m, E, p) at 16 ((3m + E) 2 + p), built by threads 0..23
+  if (tid < 24) {
+    const int m = tid / 6, E = (tid >> 1) % 3, p = tid & 1;
+    const float d = ldexpf(1.0f + 0.25f * (float)m, E + p - 33);  // value of k = 1
+    uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const uint32_t bits = __float_as_uint((float)k * d) >> 16;  // exact bf16
+      const uint32_t lb = bits & 0xFFu, hb = bits >> 8;
+      if (k < 4) {
+        lo0 |= lb << (8 * k);
+        hi0 |= hb << (8 * k);
+      } else {
+        lo1 |= lb << (8 * (k - 4));
+        hi1 |= hb << (8 * (k - 4));
+      }
+    }
+    const u32x4_t v = {lo0, lo1, hi0, hi1};
+    *reinterpret_cast<u32x4_t*>(lds + kLdsTable + 16 * tid) = v;
+  }
+
+  // ---- DMA setup
+  const __amdgpu_buffer_rsrc_t rsAc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Ac, (short)0, M * (K / 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsAm =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Am, (short)0, M * (K / 64) * 4, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * K * 2, kRsrcWord3);
+  // B: wave w rows 64w.., 4 x 1 KiB per stage, chunk swizzle on the global side
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t voffA[4], voffB[4];
+  uint32_t voffB[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t r = (uint32_t)(wave * 64 + 16 * i + (lane >> 2));
-    voffA[i] = ((uint32_t)(m0 + r) * (uint32_t)K + dchunk * 8) * 2;
     voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + dchunk * 8) * 2;
   }
-  // DMA of quarter i of a stage (one A and one B instruction).
-  auto dma_i = [&](int stage, int kt, int i) {
-    char* As = lds + stage * kStageBytes + wave * 64 * kRowBytes;
-    char* Bs = As + kTileBytes;
-    const int soff = kt * kRowBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_t*)(As + i * 1024), 16, voffA[i], soff,
-                                             0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)(Bs + i * 1024), 16, voffB[i], soff,
-                                             0, 0);
-  };
-  auto dma = [&](int stage, int kt) {
+  // A codes: wave w fetches (and later decodes) rows 64w..64w+63, so its
+  // code reads need no barrier, only its own vmcnt. Part i = rows
+  // 64w+32i..+31 (1 KiB): lane l -> row 64w+32i+(l&31), 16-byte half l>>5,
+  // stored half-major (512 B per half) so the decode reads of 32 consecutive
+  // rows are contiguous. Meta: rows 64w.. (256 B, lane l -> row 64w+l).
+  uint32_t voffAc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_i(stage, kt, i);
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 32 * i + (lane & 31));
+    voffAc[i] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (lane >> 5) * 16;
+  }
+  const uint32_t voffAm = ((uint32_t)(m0 + wave * 64 + lane) * (uint32_t)(K / 64)) * 4;
+
+  const int KH = K / kBK;  // half-unit steps (even)
+  const int KU = K / 64;   // units
+  auto dma_b_part = [&](int h, int i) {  // rows 16i.. of stage min(h, KH-1) into slot h & 3
+    char* Bs = lds + kLdsB + (h & 3) * kTileBytes + wave * 64 * kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)(Bs + i * 1024), 16, voffB[i],
+                                             min(h, KH - 1) * kRowBytes, 0, 0);
+  };
+  auto dma_b = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b_part(h, i);
+  };
+  auto dma_codes = [&](int u, int i) {  // part i of unit min(u, KU-1) into slot u % 3
+    char* slot = lds + kLdsACodes + (u % 3) * kCodeSlotBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)(slot + wave * 2048 + i * 1024),
+                                             16, voffAc[i], min(u, KU - 1) * 32, 0, 0);
+  };
+  auto dma_meta = [&](int u) {
+    char* slot = lds + kLdsACodes + (u % 3) * kCodeSlotBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)(slot + 8192 + wave * 256), 4,
+                                             voffAm, min(u, KU - 1) * 4, 0, 0);
+  };
+
+  // ---- decode state: thread tid decodes row tid of a half hn
+  const int dsw = (tid >> 2) & 3;
+  uint32_t dmw = 0;              // meta word of the row's unit
+  uint4 dcw = make_uint4(0, 0, 0, 0);  // the row's 16 code bytes of half hn
+  uint4 t8[8];                   // table entries of the 8 quads
+  const char* dbase = lds;       // table entry (m, 0, p) of the unit
+  uint32_t dd = 0, dd0 = 0;      // a in every byte; the same but not for k = 0
+  uint2 dq0 = make_uint2(0, 0);  // decoded low quad of the current group
+  auto dec_in = [&](int hn) {    // meta + codes of half hn
+    const char* slot = lds + kLdsACodes + ((hn >> 1) % 3) * kCodeSlotBytes;
+    dmw = *reinterpret_cast<const uint32_t*>(slot + 8192 + tid * 4);
+    dcw = lds_u32x4(slot + (tid >> 5) * 1024 + (hn & 1) * 512 + (tid & 31) * 16);
+  };
+  auto dec_unit = [&]() {
+    const uint32_t c = dmw & 255u;
+    const uint32_t a = c >> 3, p = (c >> 2) & 1u, m = c & 3u;
+    dbase = lds + kLdsTable + (m * 6u + p) * 16u;
+    dd = __builtin_amdgcn_perm(a, a, 0u);
+    dd0 = dd & 0xFFFFFF00u;
+  };
+  // table read of quad q (group g = 4 (hn & 1) + q / 2, half q & 1)
+  auto dec_tab = [&](int hn_odd, int q) {
+    const int g = hn_odd * 4 + (q >> 1);
+    const uint32_t E = ((dmw >> (8 + g)) & 1u) + ((dmw >> (16 + 2 * g + (q & 1))) & 1u);
+    t8[q] = lds_u32x4(dbase + 32 * E);
+  };
+  // decode quad q of half hn; the second quad of a group writes the group
+  auto dec_quad = [&](int hn, int q) {
+    const uint32_t words[4] = {dcw.x, dcw.y, dcw.z, dcw.w};
+    uint4 tq = t8[q];
+    tq.z += dd0;
+    tq.w += dd;
+    const uint2 v = decode_quad(words[q >> 1] >> (4 * (q & 1)), tq);
+    if ((q & 1) == 0) {
+      dq0 = v;
+    } else {
+      char* dst = lds + kLdsADec + (hn & 1) * kTileBytes + tid * kRowBytes;
+      const u32x4_t w = {dq0.x, dq0.y, v.x, v.y};
+      *reinterpret_cast<u32x4_t*>(dst + (((q >> 1) ^ dsw) * 16)) = w;
+    }
   };
 
   f32x16_t acc[4][4];
@@ -131,61 +270,111 @@ void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Fragment addressing: lane l supplies row (l % 32) and K values
-  // 8*(l/32) .. +7 of each 16-wide K step s, i.e. chunk 2s + l/32 (same
-  // mapping for A and B, so the contraction pairs matching K indices
-  // whatever the hardware's K order inside an instruction).
   const int frow = lane & 31;
   const int fsw = (frow >> 2) & 3;
   const int fhalf = lane >> 5;
-  const int slot0 = ((0 + fhalf) ^ fsw) * 16;
-  const int slot1 = ((2 + fhalf) ^ fsw) * 16;
+  const int fslot[2] = {((0 + fhalf) ^ fsw) * 16, ((2 + fhalf) ^ fsw) * 16};
+  // fragment f of K-chunk s of step h: f < 4 -> A rows wm*128 + 32f, else B rows wn*128 + 32(f-4)
+  auto frag = [&](int h, int s, int f) {
+    const char* p = f < 4
+        ? lds + kLdsADec + (h & 1) * kTileBytes + (wm * 128 + f * 32 + frow) * kRowBytes
+        : lds + kLdsB + (h & 3) * kTileBytes + (wn * 128 + (f - 4) * 32 + frow) * kRowBytes;
+    return *reinterpret_cast<const bf16x8_t*>(p + fslot[s]);
+  };
+  bf16x8_t f0[8], f1[8];  // fragments of K-chunks 0 and 1 of the current step
 
-  const int KT = K / kBK;
-  dma(0, 0);
-  if (KT > 1) dma(1, 1);
-  if (KT > 2) dma(2, 2);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int rem = KT - 1 - kt;  // stages issued after this one (at most 2)
-    if (rem >= 2) wait_vmcnt<16>();
-    else if (rem == 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    // The DMA of stage kt+3 is spread over this stage's MFMAs (a burst of
-    // eight DMA instructions ahead of them stalls the wave's issue).
-    const bool prefetch = kt + 3 < KT;
-    const char* st = lds + (kt & 3) * kStageBytes;
-    const char* As = st + (wm * 128 + frow) * kRowBytes;
-    const char* Bs = st + kTileBytes + (wn * 128 + frow) * kRowBytes;
-    // All 16 fragments of the stage go into distinct registers first, so the
-    // LDS latency is exposed once per stage, not once per 4 MFMAs.
-    bf16x8_t af[2][4], bfr[2][4];
+  // ---- prologue: units 0..2, B stages 0..3, all landed; half 0 decoded,
+  // half 1 read and its first group decoded; chunk-0 fragments of step 0.
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int slot = s ? slot1 : slot0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[s][i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * kRowBytes + slot);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[s][j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * kRowBytes + slot);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (s == 0 && prefetch) dma_i((kt + 3) & 3, kt + 3, i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
-      }
-    __builtin_amdgcn_sched_barrier(0);
+  for (int u = 0; u < 3; ++u) {
+    dma_codes(u, 0);
+    dma_codes(u, 1);
+    dma_meta(u);
   }
+#pragma unroll
+  for (int st = 0; st < 4; ++st) dma_b(st);
+  wait_vmcnt0();
+  __syncthreads();  // table + every wave's stage loads visible
+  dec_in(0);
+  dec_unit();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dec_tab(0, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dec_quad(0, q);
+  dec_in(1);
+  dec_unit();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dec_tab(1, q);
+  dec_quad(1, 0);
+  dec_quad(1, 1);
+  __syncthreads();  // half 0 decoded by every wave
+#pragma unroll
+  for (int f = 0; f < 8; ++f) f0[f] = frag(0, 0, f);
 
-  // Epilogue. 32x32 block output layout: lane l holds column l % 32 and,
-  // in register r, row 8*(r/4) + 4*(l/32) + r%4.
+  // ---- main loop. Step h: phase 1 = 16 MFMAs on K-chunk 0 (f0) while the
+  // chunk-1 fragments load and quads 2..7 of half h+1 are decoded; then
+  // vmcnt <= 11 (every load of steps <= h-3 landed: B stage h+1 and the
+  // unit of half h+2), lgkmcnt(0), barrier; issue B stage h+4 and a third of
+  // a code unit; phase 2 = 16 MFMAs on K-chunk 1 (f1) while the chunk-0
+  // fragments of step h+1 load and half h+2 is read and its first group
+  // decoded. Loads per wave: h even 4 + 2 (unit h/2+3 codes rows 0..31 and
+  // meta), h odd 4 + 1 (unit (h+5)/2 codes rows 32..63): 11 per two steps.
+  auto step = [&](int h, auto odd) {
+    constexpr int kOdd = decltype(odd)::value ? 1 : 0;  // parity of h
+    // phase 1
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < 4) {
+        f1[2 * c] = frag(h, 1, 2 * c);
+        f1[2 * c + 1] = frag(h, 1, 2 * c + 1);
+      }
+      if (c < 6) dec_quad(h + 1, 2 + c);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = c >> 1, j = (c & 1) * 2 + r;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    dec_in(h + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 2 (the step's loads go out one per MFMA pair)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < 4) dma_b_part(h + 4, c);
+      if constexpr (kOdd) {
+        if (c == 4) dma_codes((h + 5) >> 1, 1);
+      } else {
+        if (c == 4) dma_codes((h + 6) >> 1, 0);
+        if (c == 5) dma_meta((h + 6) >> 1);
+      }
+      if (c < 4) {
+        f0[2 * c] = frag(h + 1, 0, 2 * c);
+        f0[2 * c + 1] = frag(h + 1, 0, 2 * c + 1);
+      }
+      if (c == 2) dec_unit();
+      if (c >= 2 && c < 6) {
+        dec_tab(kOdd, 2 * (c - 2));
+        dec_tab(kOdd, 2 * (c - 2) + 1);
+      }
+      if (c >= 6) dec_quad(h + 2, c - 6);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = c >> 1, j = (c & 1) * 2 + r;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int h = 0; h < KH; h += 2) {
+    step(h, std::false_type{});
+    step(h + 1, std::true_type{});
+  }
+  wait_vmcnt0();  // no LDS-DMA may outlive the workgroup
+
   const int col_in = lane & 31, row_in = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -232,10 +421,13 @@ hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream) {
 // The DMA addresses are 32-bit byte offsets inside a buffer resource, so each
 // launch covers at most 2^31 bytes of A rows and of B rows; larger problems
 // are split into row blocks of A and of B (Y sub-blocks with stride n).
-hipError_t hif4_launch_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
-                                    int64_t k, void* y, int y_bf16, hipStream_t stream) {
+// A in HiF4 codes (+ meta), B bf16. Same row-block split as the bf16 kernel;
+// the code/meta offsets stay far inside 32 bits whenever the bf16 B offsets do.
+hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
+                                 const uint16_t* b, int64_t m, int64_t n, int64_t k, void* y,
+                                 int y_bf16, hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (k == 0) return hipErrorInvalidValue;  // handled by the caller (zero fill)
+  if (k == 0) return hipErrorInvalidValue;
   const int64_t max_rows = (((int64_t)1 << 31) / (2 * k)) / kBM * kBM;
   if (max_rows < kBM) return hipErrorInvalidValue;
   const size_t ysz = y_bf16 ? 2 : 4;
@@ -245,9 +437,9 @@ hipError_t hif4_launch_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_
       const int64_t nc = n - n0 < max_rows ? n - n0 : max_rows;
       const int tiles_m = (int)((mc + kBM - 1) / kBM), tiles_n = (int)((nc + kBN - 1) / kBN);
       void* ys = (char*)y + ((size_t)m0 * n + n0) * ysz;
-      hipLaunchKernelGGL(gemm_bf16_nt_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
-                         stream, a + m0 * k, b + n0 * k, (int)mc, (int)nc, (int)k, ys, n, y_bf16,
-                         tiles_m, tiles_n);
+      hipLaunchKernelGGL(gemm_w4a4_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                         stream, a_codes + m0 * (k / 2), a_meta + m0 * (k / 64), b + n0 * k,
+                         (int)mc, (int)nc, (int)k, ys, n, y_bf16, tiles_m, tiles_n);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

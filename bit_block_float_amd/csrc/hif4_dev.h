@@ -99,14 +99,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // Internal (hidden) host launchers; argument checks happen in api.hip.
 hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
                                 const uint8_t* mask, uint8_t* codes, uint32_t* meta,
-                                uint16_t* deq_bf16, hipStream_t stream);
+                                hipStream_t stream);
 hipError_t hif4_launch_gather_kept(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
                                    const uint8_t* mask, int64_t n_mask, uint16_t* kept,
                                    hipStream_t stream);
 hipError_t hif4_launch_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t rows,
                                   int64_t k, void* out, int out_bf16, hipStream_t stream);
-hipError_t hif4_launch_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n,
-                                    int64_t k, void* y, int y_bf16, hipStream_t stream);
+hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
+                                 const uint16_t* b, int64_t m, int64_t n, int64_t k, void* y,
+                                 int y_bf16, hipStream_t stream);
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
                                   double q, int64_t n_protect, float* stats, uint8_t* mask,
                                   void* workspace, hipStream_t stream);

@@ -51,11 +51,9 @@ __device__ __forceinline__ uint32_t or4_u32(uint32_t v) {
 
 // One level-2 group (8 elements, one code word): steps 3-5 given the unit's
 // level-1 scale. w: the group's 8 bf16 values (element 2i in the low half of
-// word i). Returns the code word; e3 bits and the fake-quant values by ref.
-template <bool kDeq>
+// word i). Returns the code word; e2 and e3 bits by reference.
 __device__ __forceinline__ uint32_t encode_group(uint4 w, float s, int p, float rh, float rl,
-                                                 uint32_t& e2, uint32_t& e3a, uint32_t& e3b,
-                                                 uint4& deq) {
+                                                 uint32_t& e2, uint32_t& e3a, uint32_t& e3b) {
   const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y),
                       bf16hi_to_f32(w.y), bf16lo_to_f32(w.z), bf16hi_to_f32(w.z),
                       bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
@@ -92,31 +90,17 @@ __device__ __forceinline__ uint32_t encode_group(uint4 w, float s, int p, float 
   const uint32_t sgn = ((sl >> 4) & 0x08080808u) | (sh & 0x80808080u);
   // a zero element keeps +0: sign only where the magnitude nibble is nonzero
   const uint32_t nz = (mag + 0x77777777u) & 0x88888888u;
-  if (kDeq) {
-    // Exact: k (3 bits) times D/4 (3 significant bits) fits bf16.
-    const float da = ldexpf(s, (int)(e2 + e3a) - 2);
-    const float db = ldexpf(s, (int)(e2 + e3b) - 2);
-    uint32_t h[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y = kf[i] * (i < 4 ? da : db);
-      const uint32_t sg = kf[i] != 0.0f ? (__float_as_uint(v[i]) & 0x80000000u) : 0u;
-      h[i] = (__float_as_uint(y) | sg) >> 16;
-    }
-    deq = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                     h[6] | (h[7] << 16));
-  }
   return mag | (sgn & nz);
 }
 
 // Work mapping: one lane owns two level-2 groups (16 consecutive elements,
 // two 16-byte loads), 4 aligned lanes own a unit; unit maximum and metadata
 // word via DPP inside the quad. A wave covers 16 units.
-template <bool kMask, bool kCodes, bool kDeq>
+template <bool kMask>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t ld, uint32_t items_per_row, FastDiv item_div,
     uint32_t total_items, const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta, uint16_t* __restrict__ deq) {
+    uint32_t* __restrict__ meta) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t it = blockIdx.x * blockDim.x + threadIdx.x; it < total_items; it += stride) {
     const uint32_t row = fdiv(it, item_div);
@@ -160,24 +144,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const float rh = inv_mant_hi(c & 3u), rl = inv_mant_lo(c & 3u);
 
     uint32_t e2a, e3a0, e3b0, e2b, e3a1, e3b1;
-    uint4 d0, d1;
-    const uint32_t cw0 = encode_group<kDeq>(w0, s, p, rh, rl, e2a, e3a0, e3b0, d0);
-    const uint32_t cw1 = encode_group<kDeq>(w1, s, p, rh, rl, e2b, e3a1, e3b1, d1);
+    const uint32_t cw0 = encode_group(w0, s, p, rh, rl, e2a, e3a0, e3b0);
+    const uint32_t cw1 = encode_group(w1, s, p, rh, rl, e2b, e3a1, e3b1);
 
-    if (kCodes) {
-      reinterpret_cast<uint2*>(codes32)[it] = make_uint2(cw0, cw1);
-      const uint32_t g0 = 2 * q, g1 = 2 * q + 1;
-      const uint32_t mb = (e2a << (8 + g0)) | (e2b << (8 + g1)) | (e3a0 << (16 + 2 * g0)) |
-                          (e3b0 << (17 + 2 * g0)) | (e3a1 << (16 + 2 * g1)) |
-                          (e3b1 << (17 + 2 * g1));
-      const uint32_t mw = or4_u32(mb) | c;
-      if (q == 0u) meta[it >> 2] = mw;
-    }
-    if (kDeq) {
-      uint4* dst = reinterpret_cast<uint4*>(deq + (int64_t)it * 16);
-      dst[0] = d0;
-      dst[1] = d1;
-    }
+    reinterpret_cast<uint2*>(codes32)[it] = make_uint2(cw0, cw1);
+    const uint32_t g0 = 2 * q, g1 = 2 * q + 1;
+    const uint32_t mb = (e2a << (8 + g0)) | (e2b << (8 + g1)) | (e3a0 << (16 + 2 * g0)) |
+                        (e3b0 << (17 + 2 * g0)) | (e3a1 << (16 + 2 * g1)) |
+                        (e3b1 << (17 + 2 * g1));
+    const uint32_t mw = or4_u32(mb) | c;
+    if (q == 0u) meta[it >> 2] = mw;
   }
 }
 
@@ -278,7 +254,7 @@ using namespace hif4;
 // Rows are processed in chunks so that group indices stay below 2^31.
 hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
                                 const uint8_t* mask, uint8_t* codes, uint32_t* meta,
-                                uint16_t* deq_bf16, hipStream_t stream) {
+                                hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
   const uint32_t gpr = (uint32_t)(k / 16);  // 16-element items per row
   const FastDiv fd = make_fastdiv(gpr);
@@ -287,24 +263,15 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
     const int64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
     const uint32_t total = (uint32_t)(nr * gpr);
     const uint16_t* xs = x + r0 * ld;
-    uint32_t* cs = codes ? reinterpret_cast<uint32_t*>(codes + r0 * (k / 2)) : nullptr;
-    uint32_t* ms = meta ? meta + r0 * (k / 64) : nullptr;
-    uint16_t* ds = deq_bf16 ? deq_bf16 + r0 * k : nullptr;
+    uint32_t* cs = reinterpret_cast<uint32_t*>(codes + r0 * (k / 2));
+    uint32_t* ms = meta + r0 * (k / 64);
     const dim3 grid(grid_for(total)), block(256);
-    if (mask) {
-      if (ds) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((quantize_kernel<true, true, false>), grid, block, 0, stream, xs, ld, gpr,
-                         fd, total, mask, cs, ms, ds);
-    } else if (ds && cs) {
-      hipLaunchKernelGGL((quantize_kernel<false, true, true>), grid, block, 0, stream, xs, ld, gpr,
-                         fd, total, mask, cs, ms, ds);
-    } else if (ds) {
-      hipLaunchKernelGGL((quantize_kernel<false, false, true>), grid, block, 0, stream, xs, ld,
-                         gpr, fd, total, mask, cs, ms, ds);
-    } else {
-      hipLaunchKernelGGL((quantize_kernel<false, true, false>), grid, block, 0, stream, xs, ld,
-                         gpr, fd, total, mask, cs, ms, ds);
-    }
+    if (mask)
+      hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, stream, xs, ld, gpr, fd, total,
+                         mask, cs, ms);
+    else
+      hipLaunchKernelGGL(quantize_kernel<false>, grid, block, 0, stream, xs, ld, gpr, fd, total,
+                         mask, cs, ms);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -162,10 +162,36 @@ def test_linear_tiny_workload(hip):
 
 @pytest.mark.parametrize("m,n,k", [(300, 200, 320), (1, 1, 64), (257, 513, 128), (512, 256, 1024),
                                    (33, 700, 192)])
-def test_linear_ragged_shapes(hip, m, n, k):
+@pytest.mark.parametrize("via_codes", [False, True])
+def test_linear_ragged_shapes(hip, m, n, k, via_codes):
     xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + n, outlier_channels=1))
     wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=k))
-    run_linear_case(hip, xb, wb)
+    run_linear_case(hip, xb, wb, via_codes=via_codes)
+
+
+def random_units(rows, k, seed):
+    """Arbitrary well-formed HiF4 units: every level-1 code, every micro-exponent
+    pattern, every nibble (both signs, both zeros)."""
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    c = r.integers(0, 256, size=(rows, k // 64), dtype=np.uint32)
+    c.flat[:256] = np.arange(min(256, c.size), dtype=np.uint32)[: c.size]
+    e2 = r.integers(0, 256, size=c.shape, dtype=np.uint32)
+    e3 = r.integers(0, 1 << 16, size=c.shape, dtype=np.uint32)
+    return codes, c | (e2 << 8) | (e3 << 16)
+
+
+@pytest.mark.parametrize("m,n,k,y_dtype", [(300, 200, 320, torch.float32), (513, 257, 640, torch.float32),
+                                           (260, 300, 128, torch.bfloat16)])
+def test_linear_random_codes(hip, m, n, k, y_dtype):
+    """Decode inside the GEMM over every level-1 code and exponent pattern."""
+    xc, xm = random_units(m, k, 5)
+    wc, wm = random_units(n, k, 6)
+    y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+    y = hip.linear_w4a4(torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda(),
+                        x_codes=torch.from_numpy(xc).cuda(),
+                        x_meta=torch.from_numpy(xm.view(np.int32)).cuda(), y_dtype=y_dtype)
+    check_linear(y.float().cpu().numpy(), y_ref, s_ref, bf16_out=(y_dtype == torch.bfloat16))
 
 
 def test_linear_one_hot_weight_is_exact(hip):
