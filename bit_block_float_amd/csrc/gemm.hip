@@ -80,22 +80,30 @@ __device__ __forceinline__ void stage_barrier() {
 // LDS map (bytes):
 //   [0, 64K)          B ring: 4 stages x 256 rows x 64 B (16-row swizzle)
 //   [64K, 96K)        decoded A: 2 buffers x 256 rows x 64 B (same swizzle)
-//   [96K, 123K)       A code ring: 3 units x (256 x 32 B codes + 256 x 4 B meta)
-//   [123K, +384)      decode table
+//   [96K, 144K)       A code ring: 3 slots x 2 units x 256 rows x 32 B
+//   [144K, 152K)      A meta ring: 2 slots x 4 units x 256 rows x 4 B
+//   [152K, +384)      decode table
+// Code bytes are fetched two units (64 B) per row and meta four units (16 B)
+// per row, so that one DMA instruction touches 16 (codes) or 64 (meta) rows
+// instead of 32-64 rows for 32 or 4 bytes each: the vector L1 looks up far
+// fewer lines per instruction.
 //
 // Step h covers K = 32h .. 32h+31 (half h&1 of unit h>>1) as two 16-wide
 // MFMA K-chunks with one barrier between them, so that the fragments of the
 // next chunk always load under the MFMAs of the current one (one wave per
-// SIMD: nothing else would hide the LDS latency). Loads past the end of K
-// are clamped to the last stage / unit and land in ring slots no one reads
+// SIMD: nothing else would hide the LDS latency). The loop runs a multiple
+// of 8 steps; halves past the end of K decode as zeros, and loads past the
+// end read clamped or range-checked (zero) data into ring slots no one reads
 // again, which keeps the loop free of branches; the vmcnt accounting is
 // spelled out at the loop.
 constexpr int kLdsB = 0;
-constexpr int kLdsADec = 4 * kTileBytes;                    // 65536
-constexpr int kLdsACodes = kLdsADec + 2 * kTileBytes;       // 98304
-constexpr int kCodeSlotBytes = 256 * 32 + 256 * 4;          // 9216
-constexpr int kLdsTable = kLdsACodes + 3 * kCodeSlotBytes;  // 125952
-constexpr int kLdsW4A4Bytes = kLdsTable + 24 * 16;          // 126336
+constexpr int kLdsADec = 4 * kTileBytes;                     // 65536
+constexpr int kLdsACodes = kLdsADec + 2 * kTileBytes;        // 98304
+constexpr int kCodeSlotBytes = 256 * 64;                     // 16384: 2 units
+constexpr int kLdsAMeta = kLdsACodes + 3 * kCodeSlotBytes;   // 147456
+constexpr int kMetaSlotBytes = 256 * 16;                     // 4096: 4 units
+constexpr int kLdsTable = kLdsAMeta + 2 * kMetaSlotBytes;    // 155648
+constexpr int kLdsW4A4Bytes = kLdsTable + 24 * 16;           // 156032
 
 // 16-byte LDS access through a native vector type. (Through the uint4
 // struct it is split into four i32 accesses and re-merged, and the compiler
@@ -118,6 +126,10 @@ __device__ __forceinline__ uint2 decode_quad(uint32_t nib, uint4 t) {
                     __builtin_amdgcn_perm(hib, lob, 0x07030602u));
 }
 
+// kMeta16: meta rows are 16-byte aligned (K a multiple of 256 and an aligned
+// base), so a unit quad is one 16-byte load per row; otherwise four 4-byte
+// loads, one per unit.
+template <bool kMeta16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
                       const uint16_t* __restrict__ B, int M, int N, int K, void* __restrict__ Y,
@@ -185,21 +197,24 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
     const uint32_t r = (uint32_t)(wave * 64 + 16 * i + (lane >> 2));
     voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + dchunk * 8) * 2;
   }
-  // A codes: wave w fetches (and later decodes) rows 64w..64w+63, so its
-  // code reads need no barrier, only its own vmcnt. Part i = rows
-  // 64w+32i..+31 (1 KiB): lane l -> row 64w+32i+(l&31), 16-byte half l>>5,
-  // stored half-major (512 B per half) so the decode reads of 32 consecutive
-  // rows are contiguous. Meta: rows 64w.. (256 B, lane l -> row 64w+l).
-  uint32_t voffAc[2];
+  // A: wave w fetches (and later decodes) rows 64w..64w+63, so its code
+  // reads need no barrier, only its own vmcnt. Codes, unit pair P (64 B per
+  // row), block i = rows 64w+16i..+15 (1 KiB): lane l -> row 64w+16i+(l>>2),
+  // LDS chunk l&3 holding global chunk (l&3) ^ ((row>>2)&3), so that the
+  // decode reads of 16 consecutive rows hit 16 distinct bank groups. Meta,
+  // unit quad Q (16 B per row): lane l -> row 64w+l. The K offsets ride in
+  // the range-checked vector offset: past the end of a row they read the
+  // next row (never decoded), past the end of the matrix they read zeros.
+  const uint32_t KU = (uint32_t)(K / 64);  // units per row
+  uint32_t voffAc[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t r = (uint32_t)(wave * 64 + 32 * i + (lane & 31));
-    voffAc[i] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (lane >> 5) * 16;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 16 * i + (lane >> 2));
+    voffAc[i] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
   }
-  const uint32_t voffAm = ((uint32_t)(m0 + wave * 64 + lane) * (uint32_t)(K / 64)) * 4;
+  const uint32_t voffAm = (uint32_t)(m0 + wave * 64 + lane) * KU * 4;
 
   const int KH = K / kBK;  // half-unit steps (even)
-  const int KU = K / 64;   // units
   auto dma_b_part = [&](int h, int i) {  // rows 16i.. of stage min(h, KH-1) into slot h & 3
     char* Bs = lds + kLdsB + (h & 3) * kTileBytes + wave * 64 * kRowBytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)(Bs + i * 1024), 16, voffB[i],
@@ -209,16 +224,25 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b_part(h, i);
   };
-  auto dma_codes = [&](int u, int i) {  // part i of unit min(u, KU-1) into slot u % 3
-    char* slot = lds + kLdsACodes + (u % 3) * kCodeSlotBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)(slot + wave * 2048 + i * 1024),
-                                             16, voffAc[i], min(u, KU - 1) * 32, 0, 0);
+  auto dma_codes = [&](int P, int i) {  // block i of unit pair P into slot P % 3
+    char* slot = lds + kLdsACodes + (P % 3) * kCodeSlotBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)(slot + wave * 4096 + i * 1024),
+                                             16, voffAc[i] + (uint32_t)P * 64u, 0, 0, 0);
   };
-  auto dma_meta = [&](int u) {
-    char* slot = lds + kLdsACodes + (u % 3) * kCodeSlotBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)(slot + 8192 + wave * 256), 4,
-                                             voffAm, min(u, KU - 1) * 4, 0, 0);
+  // meta slot layout: kMeta16 -> [row][4 units]; else [wave][unit][64 rows]
+  auto dma_meta = [&](int Q) {  // unit quad Q into slot Q % 2
+    char* slot = lds + kLdsAMeta + (Q & 1) * kMetaSlotBytes + wave * 1024;
+    if constexpr (kMeta16) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)slot, 16,
+                                               voffAm + (uint32_t)Q * 16u, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)(slot + j * 256), 4,
+                                                 voffAm + (uint32_t)(4 * Q + j) * 4u, 0, 0, 0);
+    }
   };
+  constexpr int kMetaLoads = kMeta16 ? 1 : 4;
 
   // ---- decode state: thread tid decodes row tid of a half hn
   const int dsw = (tid >> 2) & 3;
@@ -228,10 +252,15 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
   const char* dbase = lds;       // table entry (m, 0, p) of the unit
   uint32_t dd = 0, dd0 = 0;      // a in every byte; the same but not for k = 0
   uint2 dq0 = make_uint2(0, 0);  // decoded low quad of the current group
-  auto dec_in = [&](int hn) {    // meta + codes of half hn
-    const char* slot = lds + kLdsACodes + ((hn >> 1) % 3) * kCodeSlotBytes;
-    dmw = *reinterpret_cast<const uint32_t*>(slot + 8192 + tid * 4);
-    dcw = lds_u32x4(slot + (tid >> 5) * 1024 + (hn & 1) * 512 + (tid & 31) * 16);
+  auto dec_in = [&](int hn) {    // meta + codes of half hn (all zero past the end of K)
+    const char* ms = lds + kLdsAMeta + ((hn >> 3) & 1) * kMetaSlotBytes;
+    const char* cs = lds + kLdsACodes + ((hn >> 2) % 3) * kCodeSlotBytes;
+    dmw = kMeta16 ? *reinterpret_cast<const uint32_t*>(ms + tid * 16 + ((hn >> 1) & 3) * 4)
+                  : *reinterpret_cast<const uint32_t*>(ms + (tid >> 6) * 1024 +
+                                                       ((hn >> 1) & 3) * 256 + (tid & 63) * 4);
+    const uint4 w = lds_u32x4(cs + tid * 64 + (((hn & 3) ^ dsw) * 16));
+    const bool live = hn < KH;
+    dcw = make_uint4(live ? w.x : 0u, live ? w.y : 0u, live ? w.z : 0u, live ? w.w : 0u);
   };
   auto dec_unit = [&]() {
     const uint32_t c = dmw & 255u;
@@ -262,6 +291,32 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
     }
   };
 
+  // the same in two halves, to spread a quad over two MFMAs: (a) plane
+  // lookups, (b) signs, interleave, write
+  uint32_t qlo = 0, qhi = 0, qnib = 0;
+  auto dec_quad_a = [&](int q) {
+    const uint32_t words[4] = {dcw.x, dcw.y, dcw.z, dcw.w};
+    qnib = words[q >> 1] >> (4 * (q & 1));
+    uint4 tq = t8[q];
+    tq.z += dd0;
+    tq.w += dd;
+    const uint32_t sel = qnib & 0x07070707u;
+    qlo = __builtin_amdgcn_perm(tq.y, tq.x, sel);
+    qhi = __builtin_amdgcn_perm(tq.w, tq.z, sel);
+  };
+  auto dec_quad_b = [&](int hn, int q) {
+    const uint32_t hib = qhi | ((qnib << 4) & 0x80808080u);
+    const uint2 v = make_uint2(__builtin_amdgcn_perm(hib, qlo, 0x05010400u),
+                               __builtin_amdgcn_perm(hib, qlo, 0x07030602u));
+    if ((q & 1) == 0) {
+      dq0 = v;
+    } else {
+      char* dst = lds + kLdsADec + (hn & 1) * kTileBytes + tid * kRowBytes;
+      const u32x4_t w = {dq0.x, dq0.y, v.x, v.y};
+      *reinterpret_cast<u32x4_t*>(dst + (((q >> 1) ^ dsw) * 16)) = w;
+    }
+  };
+
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -283,14 +338,15 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
   };
   bf16x8_t f0[8], f1[8];  // fragments of K-chunks 0 and 1 of the current step
 
-  // ---- prologue: units 0..2, B stages 0..3, all landed; half 0 decoded,
-  // half 1 read and its first group decoded; chunk-0 fragments of step 0.
+  // ---- prologue: unit pairs 0..2, unit quads 0..1, B stages 0..3, all
+  // landed; half 0 decoded, half 1 read and its first group decoded; chunk-0
+  // fragments of step 0.
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    dma_codes(u, 0);
-    dma_codes(u, 1);
-    dma_meta(u);
-  }
+  for (int P = 0; P < 3; ++P)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_codes(P, i);
+  dma_meta(0);
+  dma_meta(1);
 #pragma unroll
   for (int st = 0; st < 4; ++st) dma_b(st);
   wait_vmcnt0();
@@ -313,65 +369,75 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
 
   // ---- main loop. Step h: phase 1 = 16 MFMAs on K-chunk 0 (f0) while the
   // chunk-1 fragments load and quads 2..7 of half h+1 are decoded; then
-  // vmcnt <= 11 (every load of steps <= h-3 landed: B stage h+1 and the
-  // unit of half h+2), lgkmcnt(0), barrier; issue B stage h+4 and a third of
-  // a code unit; phase 2 = 16 MFMAs on K-chunk 1 (f1) while the chunk-0
-  // fragments of step h+1 load and half h+2 is read and its first group
-  // decoded. Loads per wave: h even 4 + 2 (unit h/2+3 codes rows 0..31 and
-  // meta), h odd 4 + 1 (unit (h+5)/2 codes rows 32..63): 11 per two steps.
-  auto step = [&](int h, auto odd) {
-    constexpr int kOdd = decltype(odd)::value ? 1 : 0;  // parity of h
-    // phase 1
+  // vmcnt wait, lgkmcnt(0), barrier; phase 2 = 16 MFMAs on K-chunk 1 (f1)
+  // while the chunk-0 fragments of step h+1 load, half h+2 is read and its
+  // first group decoded, and the step's loads go out one per MFMA pair:
+  // B stage h+4 (4 loads), block (h+2)&3 of unit pair (h+10)/4 (1 load) and,
+  // when h = 6 mod 8, unit quad (h+10)/8 (1 load). Every load is needed at
+  // least 3 barriers later (B stage h+1 at B_h; the pair holding half h+2 was
+  // issued by step h-5, its quad by step h-8), so "vmcnt <= loads of steps
+  // h-1 and h-2" at B_h is enough; that count depends on h mod 8 only.
+  // Ring reuse: B stage h+4 overwrites stage h (last read before B_h); pair
+  // P+3 overwrites pair P (last read at step 4P+1, first overwritten at step
+  // 4P+2); quad Q+2 overwrites quad Q (last read at step 8Q+5, overwritten
+  // at step 8Q+6).
+  auto step = [&](int h, auto phase) {
+    constexpr int kPh = decltype(phase)::value;  // h mod 8
+    constexpr int kOdd = kPh & 1;
+    constexpr int kLoads1 = 5 + (((kPh + 7) & 7) == 6 ? kMetaLoads : 0);  // loads of step h-1
+    constexpr int kLoads2 = 5 + (((kPh + 6) & 7) == 6 ? kMetaLoads : 0);  // ... of step h-2
+    // phase 1: one MFMA per slot, at most a few VALU ops between two MFMAs
+    // (a longer run would leave the matrix pipe idle)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (c < 4) {
-        f1[2 * c] = frag(h, 1, 2 * c);
-        f1[2 * c + 1] = frag(h, 1, 2 * c + 1);
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8) f1[c] = frag(h, 1, c);
+      if (c >= 2 && c < 14) {
+        if (((c - 2) & 1) == 0) dec_quad_a(2 + ((c - 2) >> 1));
+        else dec_quad_b(h + 1, 2 + ((c - 2) >> 1));
       }
-      if (c < 6) dec_quad(h + 1, 2 + c);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int i = c >> 1, j = (c & 1) * 2 + r;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
-      }
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+    static_assert(kLoads1 + kLoads2 == 10 || kLoads1 + kLoads2 == 11 ||
+                  kLoads1 + kLoads2 == 14, "vmcnt");
+    if constexpr (kLoads1 + kLoads2 == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else if constexpr (kLoads1 + kLoads2 == 11) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();
     dec_in(h + 2);
     __builtin_amdgcn_sched_barrier(0);
-    // phase 2 (the step's loads go out one per MFMA pair)
+    // phase 2
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (c < 4) dma_b_part(h + 4, c);
-      if constexpr (kOdd) {
-        if (c == 4) dma_codes((h + 5) >> 1, 1);
-      } else {
-        if (c == 4) dma_codes((h + 6) >> 1, 0);
-        if (c == 5) dma_meta((h + 6) >> 1);
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8 && (c & 1) == 0) dma_b_part(h + 4, c >> 1);
+      if (c == 8) dma_codes((h + 10) >> 2, (kPh + 2) & 3);
+      if constexpr (kPh == 6) {
+        if (c == 10) dma_meta((h + 10) >> 3);
       }
-      if (c < 4) {
-        f0[2 * c] = frag(h + 1, 0, 2 * c);
-        f0[2 * c + 1] = frag(h + 1, 0, 2 * c + 1);
+      if (c < 8) f0[c] = frag(h + 1, 0, c);
+      if (c == 4) dec_unit();
+      if (c >= 5 && c < 13) dec_tab(kOdd, c - 5);
+      if (c >= 12) {
+        if ((c & 1) == 0) dec_quad_a((c - 12) >> 1);
+        else dec_quad_b(h + 2, (c - 12) >> 1);
       }
-      if (c == 2) dec_unit();
-      if (c >= 2 && c < 6) {
-        dec_tab(kOdd, 2 * (c - 2));
-        dec_tab(kOdd, 2 * (c - 2) + 1);
-      }
-      if (c >= 6) dec_quad(h + 2, c - 6);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int i = c >> 1, j = (c & 1) * 2 + r;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
-      }
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int h = 0; h < KH; h += 2) {
-    step(h, std::false_type{});
-    step(h + 1, std::true_type{});
+  const int KHp = (KH + 7) & ~7;
+  for (int h = 0; h < KHp; h += 8) {
+    step(h + 0, std::integral_constant<int, 0>{});
+    step(h + 1, std::integral_constant<int, 1>{});
+    step(h + 2, std::integral_constant<int, 2>{});
+    step(h + 3, std::integral_constant<int, 3>{});
+    step(h + 4, std::integral_constant<int, 4>{});
+    step(h + 5, std::integral_constant<int, 5>{});
+    step(h + 6, std::integral_constant<int, 6>{});
+    step(h + 7, std::integral_constant<int, 7>{});
   }
   wait_vmcnt0();  // no LDS-DMA may outlive the workgroup
 
@@ -437,9 +503,15 @@ hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
       const int64_t nc = n - n0 < max_rows ? n - n0 : max_rows;
       const int tiles_m = (int)((mc + kBM - 1) / kBM), tiles_n = (int)((nc + kBN - 1) / kBN);
       void* ys = (char*)y + ((size_t)m0 * n + n0) * ysz;
-      hipLaunchKernelGGL(gemm_w4a4_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
-                         stream, a_codes + m0 * (k / 2), a_meta + m0 * (k / 64), b + n0 * k,
-                         (int)mc, (int)nc, (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+      const uint32_t* am = a_meta + m0 * (k / 64);
+      if ((k / 64) % 4 == 0 && ((uintptr_t)am & 15) == 0)
+        hipLaunchKernelGGL(gemm_w4a4_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                           0, stream, a_codes + m0 * (k / 2), am, b + n0 * k, (int)mc, (int)nc,
+                           (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+      else
+        hipLaunchKernelGGL(gemm_w4a4_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                           0, stream, a_codes + m0 * (k / 2), am, b + n0 * k, (int)mc, (int)nc,
+                           (int)k, ys, n, y_bf16, tiles_m, tiles_n);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
