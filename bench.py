@@ -2,19 +2,26 @@
 
 One step = one pass of the whole hot path over one batch of synthetic
 Wan2.2 FFN-up activations (57,600 video tokens x 5120 channels) and the
-FFN-up weight (13,824 x 5120):
+FFN-up weight (13,824 x 5120), each stage one C-ABI call:
   1. hif4_percentile_mask: per-channel type-7 99.9th percentile of |X| and
      the top-1% (52-channel) protection mask;
   2. hif4_quantize(W, mask): weight codes + meta, protected channels kept bf16;
   3. hif4_quantize(X): the 4-bit activation stream;
-  4. hif4_linear_w4a4(X codes, W codes): decode + GEMM, Y fp32 [57600][13824].
+  4. hif4_dequantize(W codes -> bf16): the weight operand, decoded once;
+  5. hif4_linear_xcodes_wbf16(X codes, W): the W4A4 contraction, Y fp32
+     [57600][13824] (one gemm_w4a4_kernel launch, which decodes X per tile).
 Inputs are resident in HBM before the timed region. `value` is whole-step
 throughput counted as the linear layer's 2*M*N*K flops per step time.
+`roofline` is the contraction kernel's, timed with HIP events on its stream;
+its `traffic` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
+profiles/ and is reported only while the kernel source still hashes to the
+value recorded there.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -57,6 +64,27 @@ def cpu_baseline(x, w, mask_np, rows_sample):
         "sample": f"{rows_sample} of {x.shape[0]} rows of X quantized + full W quantized "
                   f"(masked) + fp64 linear on those rows; {dt:.1f} s",
     }
+
+
+GEMM_SRC = os.path.join(ROOT, "bit_block_float_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_kernel_ffn_up_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of gemm_w4a4_kernel from the committed counter
+    summary, or None if it is missing or the kernel source has changed."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE, encoding="utf-8"):
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+        if fields.get("gemm.hip sha256") != src:
+            return None
+        return float(fields["traffic bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def torch_index(idx):
@@ -114,8 +142,8 @@ def main():
     kept = torch.empty((N, n_protect), dtype=torch.bfloat16, device=dev)
     xcodes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     xmeta = torch.empty((M, K // 64), dtype=torch.int32, device=dev)
+    wdeq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    lws = torch.empty((hif4.linear_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -130,16 +158,17 @@ def main():
         if ev: ev[2].record(stream)
         hif4.quantize(x, codes=xcodes, meta=xmeta, stream=stream)
         if ev: ev[3].record(stream)
-        hif4.linear_w4a4(wcodes, wmeta, x_codes=xcodes, x_meta=xmeta, y=y, workspace=lws,
-                         stream=stream)
+        hif4.dequantize(wcodes, wmeta, out_dtype=torch.bfloat16, out=wdeq, stream=stream)
         if ev: ev[4].record(stream)
+        hif4.linear_xcodes_wbf16(xcodes, xmeta, wdeq, y=y, stream=stream)
+        if ev: ev[5].record(stream)
 
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -151,11 +180,13 @@ def main():
     def avg_ms(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
 
-    t_pct, t_wq, t_xq, t_lin = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
+    t_pct, t_wq, t_xq, t_wd, t_lin = (avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4),
+                                      avg_ms(4, 5))
     ms_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     q_bytes = M * K * (2 + 0.5 + 4 / 64)            # read bf16, write codes + meta
     wq_bytes = N * K * (2 + 0.5 + 4 / 64) + N * n_protect * 2 + K
+    wd_bytes = N * K * (0.5 + 4 / 64 + 2)           # read codes + meta, write bf16
     pct_bytes = M * K * 2                           # one read of X (algorithmic minimum)
     gemm_tflops = flops / (t_lin * 1e-3) / 1e12
     parts = {
@@ -165,8 +196,9 @@ def main():
                               "note": "W (141.6 MB bf16) fits the 256 MB MALL"},
         "quantize_x": {"ms": t_xq, "GB/s": q_bytes / t_xq / 1e6,
                        "frac_hbm": q_bytes / t_xq / 1e6 / HBM_PEAK_GBS},
-        "linear_w4a4": {"ms": t_lin, "TFLOP/s": gemm_tflops,
-                        "frac_bf16_mfma": gemm_tflops / BF16_MFMA_PEAK_TFLOPS},
+        "dequantize_w": {"ms": t_wd, "GB/s": wd_bytes / t_wd / 1e6},
+        "gemm_w4a4": {"ms": t_lin, "TFLOP/s": gemm_tflops,
+                      "frac_bf16_mfma": gemm_tflops / BF16_MFMA_PEAK_TFLOPS},
     }
     out = {
         "metric": METRIC,
@@ -189,14 +221,13 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "hif4_linear_w4a4 call (W decode + gemm_w4a4_kernel, X decoded per tile), "
-                      "timed with "
-                      "HIP events on its stream",
+            "kernel": "gemm_w4a4_kernel (hif4_linear_xcodes_wbf16, one launch per step), "
+                      "2*M*N*K flops per launch over its HIP-event time",
             "achieved": gemm_tflops,
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gemm_tflops / BF16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "quantize": parts["quantize_x"],
         "parts": parts,

@@ -138,6 +138,28 @@ hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32
                                         stream));
 }
 
+hif4_status hif4_linear_xcodes_wbf16(const uint8_t* x_codes, const uint32_t* x_meta,
+                                     const void* w, int64_t m, int64_t n, int64_t k, void* y,
+                                     int y_dtype, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
+  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31)) return HIF4_ERR_SHAPE;
+  if (y_dtype != HIF4_F32 && y_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+  if (m == 0 || n == 0) return HIF4_OK;
+  if (!y) return HIF4_ERR_NULL;
+  if (k > 0 && (!x_codes || !x_meta || !w)) return HIF4_ERR_NULL;
+  if (!aligned(y, 16)) return HIF4_ERR_ALIGN;
+  if (k > 0 && (!aligned(x_codes, 16) || !aligned(x_meta, 4) || !aligned(w, 16)))
+    return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  if (k == 0) {
+    const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
+    return launched(hif4_launch_zero(y, bytes, stream));
+  }
+  return launched(hif4_launch_gemm_w4a4(x_codes, x_meta, (const uint16_t*)w, m, n, k, y,
+                                        y_dtype == HIF4_BF16, stream));
+}
+
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {
   (void)rows;
   if (c < 0) return 0;

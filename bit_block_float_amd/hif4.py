@@ -46,6 +46,8 @@ def lib():
         L.hif4_linear_workspace_bytes.restype = sz
         L.hif4_linear_w4a4.argtypes = [p, p, p, p, p, i64, i64, i64, p, ctypes.c_int, p, sz, p]
         L.hif4_linear_w4a4.restype = ctypes.c_int
+        L.hif4_linear_xcodes_wbf16.argtypes = [p, p, p, i64, i64, i64, p, ctypes.c_int, p]
+        L.hif4_linear_xcodes_wbf16.restype = ctypes.c_int
         L.hif4_percentile_workspace_bytes.argtypes = [i64, i64]
         L.hif4_percentile_workspace_bytes.restype = sz
         L.hif4_percentile_mask.argtypes = [p, i64, i64, i64, ctypes.c_double, i64, p, p, p, sz, p]
@@ -136,6 +138,20 @@ def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, y_dtype=torc
                                 m, n, k, _ptr(y), dt, _ptr(workspace), workspace.numel(),
                                 _stream(stream))
     _ok(st, "hif4_linear_w4a4")
+    return y
+
+
+def linear_xcodes_wbf16(x_codes, x_meta, w, y_dtype=torch.float32, y=None, stream=None):
+    """Y = deq(X codes) w^T with w bf16 [n][k] (e.g. a weight decoded once)."""
+    _check_bf16_rows(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous (row stride k)")
+    m, n, k = x_codes.shape[0], w.shape[0], w.shape[1]
+    dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
+    y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=w.device)
+    st = lib().hif4_linear_xcodes_wbf16(_ptr(x_codes), _ptr(x_meta), _ptr(w), m, n, k, _ptr(y), dt,
+                                        _stream(stream))
+    _ok(st, "hif4_linear_xcodes_wbf16")
     return y
 
 

@@ -144,6 +144,24 @@ HIF4_EXPORT hif4_status hif4_linear_w4a4(const void *x, const uint8_t *x_codes, 
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * hif4_linear_xcodes_wbf16 -- the contraction step of hif4_linear_w4a4 with
+ * the weight already decoded (the serving case: a static weight is decoded
+ * once with hif4_dequantize(..., HIF4_BF16) and reused for every batch):
+ *     Y[i][j] = sum_t deq(X codes)[i][t] * w[j][t],  accumulated in fp32.
+ *
+ *  x_codes [m][k/2], x_meta [m][k/64]: HiF4 activation (hif4_quantize layout).
+ *  w       bf16 [n][k], row stride k. With w = deq(Q(W)) (every value exact
+ *          in bf16) the result equals hif4_linear_w4a4's bit for bit; any
+ *          other bf16 w gives Y = deq(X) w^T with the same accumulation.
+ *  y       [m][n] of y_dtype (HIF4_F32, or HIF4_BF16 rounded to nearest even).
+ *  No workspace. Pointers 16-byte aligned except x_meta (4-byte); m, n >= 0;
+ *  k % 64 == 0. k == 0 writes Y = 0.
+ */
+HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16(const uint8_t *x_codes, const uint32_t *x_meta,
+                                     const void *w, int64_t m, int64_t n, int64_t k,
+                                     void *y, int y_dtype, hipStream_t stream);
+
+/*
  * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask
  * over c channels.
  */

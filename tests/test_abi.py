@@ -36,6 +36,7 @@ def L():
 def test_header_declares_the_four_entry_points():
     names = declared()
     for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
+               "hif4_linear_xcodes_wbf16",
                "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
                "hif4_status_string", "hif4_version"):
         assert fn in names
@@ -101,6 +102,21 @@ def test_linear_argument_checks(L):
     assert f(A, None, None, A, A, 8, 8, 64, A, 0, A + 16, ws, None) == ALIGN
     assert f(A + 2, None, None, A, A, 8, 8, 64, A, 0, A, ws, None) == ALIGN
     assert f(A, None, None, A, A, 0, 8, 64, A, 0, None, 0, None) == OK
+
+
+def test_linear_xcodes_wbf16_argument_checks(L):
+    f = L.hif4_linear_xcodes_wbf16
+    assert f(A, A, A, 8, 8, 60, A, 0, None) == SHAPE
+    assert f(A, A, A, -1, 8, 64, A, 0, None) == SHAPE
+    assert f(A, A, A, 8, 8, 64, A, 2, None) == DTYPE
+    assert f(None, A, A, 8, 8, 64, A, 0, None) == NULL
+    assert f(A, None, A, 8, 8, 64, A, 0, None) == NULL
+    assert f(A, A, None, 8, 8, 64, A, 0, None) == NULL
+    assert f(A, A, A, 8, 8, 64, None, 0, None) == NULL
+    assert f(A, A, A + 8, 8, 8, 64, A, 0, None) == ALIGN
+    assert f(A + 8, A, A, 8, 8, 64, A, 0, None) == ALIGN
+    assert f(A, A + 2, A, 8, 8, 64, A, 0, None) == ALIGN
+    assert f(A, A, A, 0, 8, 64, None, 0, None) == OK
 
 
 def test_percentile_argument_checks(L):

@@ -194,6 +194,26 @@ def test_linear_random_codes(hip, m, n, k, y_dtype):
     check_linear(y.float().cpu().numpy(), y_ref, s_ref, bf16_out=(y_dtype == torch.bfloat16))
 
 
+@pytest.mark.parametrize("m,n,k,y_dtype", [(300, 200, 320, torch.float32), (257, 513, 1024, torch.float32),
+                                           (64, 96, 192, torch.bfloat16)])
+def test_linear_with_decoded_weight_matches(hip, m, n, k, y_dtype):
+    """hif4_linear_xcodes_wbf16 on W decoded by hif4_dequantize: the same
+    bits as hif4_linear_w4a4, and the oracle's values."""
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + 7, outlier_channels=1))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=n + 7))
+    xc, xm, _ = oracle.quantize(xb)
+    wc, wm, _ = oracle.quantize(wb)
+    y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+    xcd, xmd = torch.from_numpy(xc).cuda(), torch.from_numpy(xm.view(np.int32)).cuda()
+    wcd, wmd = torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda()
+    w_deq = hip.dequantize(wcd, wmd, out_dtype=torch.bfloat16)
+    y1 = hip.linear_xcodes_wbf16(xcd, xmd, w_deq, y_dtype=y_dtype)
+    y2 = hip.linear_w4a4(wcd, wmd, x_codes=xcd, x_meta=xmd, y_dtype=y_dtype)
+    assert torch.equal(y1.view(torch.int16 if y_dtype == torch.bfloat16 else torch.int32),
+                       y2.view(torch.int16 if y_dtype == torch.bfloat16 else torch.int32))
+    check_linear(y1.float().cpu().numpy(), y_ref, s_ref, bf16_out=(y_dtype == torch.bfloat16))
+
+
 def test_linear_one_hot_weight_is_exact(hip):
     """W row j = a single 7 at column t: Y[:, j] = 7 * deq(Q(X))[:, t] exactly
     (one exact product per output, no rounding)."""
