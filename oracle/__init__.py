@@ -33,6 +33,7 @@ def _lib():
         lib.hif4o_dequantize.argtypes = [p, p, i64, i64, p]
         lib.hif4o_dequantize.restype = ctypes.c_int
         lib.hif4o_linear.argtypes = [p, p, p, p, i64, i64, i64, p, p]
+        lib.hif4o_linear_protected.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p, p]
         lib.hif4o_linear.restype = ctypes.c_int
         lib.hif4o_percentile.argtypes = [p, i64, i64, i64, ctypes.c_double, p]
         lib.hif4o_percentile.restype = ctypes.c_int
@@ -121,6 +122,30 @@ def linear(xc, xm, wc, wm, with_mag: bool = True):
     s = np.zeros((m, n), dtype=np.float64) if with_mag else None
     _check(_lib().hif4o_linear(_ptr(xc), _ptr(xm), _ptr(wc), _ptr(wm), m, n, k, _ptr(y), _ptr(s)),
            "linear")
+    return (y, s) if with_mag else y
+
+
+def linear_protected(xc, xm, xk, wc, wm, wk, with_mag: bool = True):
+    """Y = deq(Q(X)) deq(Q(W))^T + xk wk^T in float64 (protected channels kept
+    in bf16: xk [m][nk], wk [n][nk] as uint16 bit patterns), plus S."""
+    xc = np.ascontiguousarray(xc, dtype=np.uint8)
+    xm = np.ascontiguousarray(xm, dtype=np.uint32)
+    wc = np.ascontiguousarray(wc, dtype=np.uint8)
+    wm = np.ascontiguousarray(wm, dtype=np.uint32)
+    m, n, k = xc.shape[0], wc.shape[0], xc.shape[1] * 2
+    if wc.shape[1] * 2 != k:
+        raise OracleError("linear_protected: K mismatch")
+    _shape(xm, (m, k // 64), "x meta")
+    _shape(wm, (n, k // 64), "w meta")
+    nk = 0 if xk is None else xk.shape[1]
+    xk = np.ascontiguousarray(xk if xk is not None else np.zeros((m, 0)), dtype=np.uint16)
+    wk = np.ascontiguousarray(wk if wk is not None else np.zeros((n, 0)), dtype=np.uint16)
+    _shape(xk, (m, nk), "x kept")
+    _shape(wk, (n, nk), "w kept")
+    y = np.zeros((m, n), dtype=np.float64)
+    s = np.zeros((m, n), dtype=np.float64) if with_mag else None
+    _check(_lib().hif4o_linear_protected(_ptr(xc), _ptr(xm), _ptr(xk), _ptr(wc), _ptr(wm), _ptr(wk),
+                                         m, n, k, nk, _ptr(y), _ptr(s)), "linear_protected")
     return (y, s) if with_mag else y
 
 

@@ -271,6 +271,38 @@ static int cmp_double(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
+/* W4A4 linear with protected channels ([TA-method], section "方法概述":
+ * the channels the mask protects stay in high precision; layer form
+ * Y = X W^T from the article's FlatQuant section). The HiF4 streams hold +0
+ * at the protected channels (the mask removes them before quantization,
+ * see hif4o_quantize), and their original bf16 values come separately as
+ * xk [m][nk] and wk [n][nk], channels in the same (ascending) order on both
+ * sides. In double:
+ *   Y = deq(Q(X)) deq(Q(W))^T + xk wk^T,
+ * and S = the sum of |product| over both parts. */
+int hif4o_linear_protected(const uint8_t *xc, const uint32_t *xm, const uint16_t *xk,
+                           const uint8_t *wc, const uint32_t *wm, const uint16_t *wk,
+                           int64_t m, int64_t n, int64_t k, int64_t nk, double *y, double *s)
+{
+    if (nk < 0 || nk > k) return HIF4O_ERR_ARG;
+    int rc = hif4o_linear(xc, xm, wc, wm, m, n, k, y, s);
+    if (rc != HIF4O_OK) return rc;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < nk; ++t) {
+                double p = bf16_value(xk[i * nk + t]) * bf16_value(wk[j * nk + t]);
+                acc += p;
+                mag += fabs(p);
+            }
+            y[i * n + j] += acc;
+            if (s) s[i * n + j] += mag;
+        }
+    }
+    return HIF4O_OK;
+}
+
 /* Per-channel tail statistic ([TA-method]: a percentile of the activation
  * magnitudes per channel, used in place of the maximum).
  * READING: the type-7 (linear interpolation) quantile at level q of |x[:, ch]|

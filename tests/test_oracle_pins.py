@@ -483,6 +483,65 @@ def test_linear_one_hot_weight_column_is_exact():
         assert np.array_equal(y[:, j], 7.0 * a[:, t])
 
 
+def _dense_with_kept(codes, meta, kept, mask):
+    """deq(codes) with the kept bf16 values written back at the masked
+    channels (ascending channel order): the matrix the protected linear
+    multiplies, built with numpy instead of the oracle's residual loop."""
+    a = oracle.dequantize(codes, meta)
+    chans = np.nonzero(mask)[0]
+    if chans.size:
+        a[:, chans] = (kept.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a
+
+
+@pytest.mark.parametrize("n_mask", [0, 1, 13, 64])
+def test_linear_protected_equals_dense_product(n_mask):
+    """[TA-method]: protected channels stay in high precision. The oracle's
+    HiF4 product plus its bf16 residual equals numpy's fp64 product of the
+    dense matrices in which the masked channels hold their original values;
+    with no mask it is the plain linear."""
+    import workloads
+    k = 256
+    r = np.random.default_rng(n_mask + 3)
+    xb = workloads.bits(workloads.heavy_tailed_x(40, k, seed=n_mask + 1, outlier_channels=3))
+    wb = workloads.bits(workloads.normal_bf16(24, k, 0.02, seed=n_mask + 2))
+    mask = np.zeros(k, np.uint8)
+    mask[r.choice(k, n_mask, replace=False)] = 1
+    xc, xm, xk = oracle.quantize(xb, mask if n_mask else None)
+    wc, wm, wk = oracle.quantize(wb, mask if n_mask else None)
+    y, s = oracle.linear_protected(xc, xm, xk, wc, wm, wk)
+    a = _dense_with_kept(xc, xm, xk, mask)
+    b = _dense_with_kept(wc, wm, wk, mask)
+    ref = a @ b.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * s)
+    assert np.allclose(s, np.abs(a) @ np.abs(b).T, rtol=1e-13, atol=0)
+    if n_mask == 0:
+        y0, s0 = oracle.linear(xc, xm, wc, wm)
+        assert np.array_equal(y, y0) and np.array_equal(s, s0)
+    else:
+        # the masked channels really are exact: their columns of a hold the inputs
+        chans = np.nonzero(mask)[0]
+        assert np.array_equal(a[:, chans], xb[:, chans].astype(np.uint32).__lshift__(16)
+                              .view(np.float32).astype(np.float64))
+
+
+def test_linear_protected_all_channels_masked_is_bf16_matmul():
+    """Everything protected: the HiF4 part is all zeros and Y is the plain
+    fp64 product of the bf16 inputs."""
+    import workloads
+    k = 64
+    xb = workloads.bits(workloads.tiny_x(8, k, seed=11))
+    wb = workloads.bits(workloads.normal_bf16(5, k, 0.02, seed=12))
+    mask = np.ones(k, np.uint8)
+    xc, xm, xk = oracle.quantize(xb, mask)
+    wc, wm, wk = oracle.quantize(wb, mask)
+    assert not xc.any() and not wc.any()
+    y = oracle.linear_protected(xc, xm, xk, wc, wm, wk, with_mag=False)
+    fx = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    fw = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.allclose(y, fx @ fw.T, rtol=1e-13, atol=1e-300)
+
+
 # -------------------------------------------------------------- percentile
 
 @pytest.mark.parametrize("case", golden_io.percentile_cases())
