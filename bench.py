@@ -6,10 +6,13 @@ FFN-up weight (13,824 x 5120), each stage one C-ABI call:
   1. hif4_percentile_mask: per-channel type-7 99.9th percentile of |X| and
      the top-1% (52-channel) protection mask;
   2. hif4_quantize(W, mask): weight codes + meta, protected channels kept bf16;
-  3. hif4_quantize(X): the 4-bit activation stream;
+  3. hif4_quantize(X, mask): the 4-bit activation stream, protected channels
+     kept bf16;
   4. hif4_dequantize(W codes -> bf16): the weight operand, decoded once;
-  5. hif4_linear_xcodes_wbf16(X codes, W): the W4A4 contraction, Y fp32
-     [57600][13824] (one gemm_w4a4_kernel launch, which decodes X per tile).
+  5. hif4_linear_xcodes_wbf16(X codes, W, kept): the W4A4 contraction plus the
+     bf16 residual over the 52 protected channels, Y fp32 [57600][13824]
+     (two small packing kernels and one gemm_w4a4_kernel launch, which
+     decodes X per tile and adds the residual before its epilogue).
 Inputs are resident in HBM before the timed region. `value` is whole-step
 throughput counted as the linear layer's 2*M*N*K flops per step time.
 `roofline` is the contraction kernel's, timed with HIP events on its stream;
@@ -51,9 +54,9 @@ def cpu_baseline(x, w, mask_np, rows_sample):
     wb = workloads.bits(w)
     threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    wc, wm, _ = oracle.quantize(wb, mask_np)
-    xc, xm, _ = oracle.quantize(xs)
-    oracle.linear(xc, xm, wc, wm, with_mag=False)
+    wc, wm, wk = oracle.quantize(wb, mask_np)
+    xc, xm, xk = oracle.quantize(xs, mask_np)
+    oracle.linear_protected(xc, xm, xk, wc, wm, wk, with_mag=False)
     dt = time.perf_counter() - t0
     n, k = w.shape
     flops = 2.0 * rows_sample * n * k
@@ -61,8 +64,9 @@ def cpu_baseline(x, w, mask_np, rows_sample):
     cores = min(threads, int(omp)) if omp and omp.isdigit() else threads
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-        "sample": f"{rows_sample} of {x.shape[0]} rows of X quantized + full W quantized "
-                  f"(masked) + fp64 linear on those rows; {dt:.1f} s",
+        "sample": f"{rows_sample} of {x.shape[0]} rows of X quantized (masked) + full W quantized "
+                  f"(masked) + fp64 linear with the protected-channel residual on those rows; "
+                  f"{dt:.1f} s",
     }
 
 
@@ -142,7 +146,10 @@ def main():
     kept = torch.empty((N, n_protect), dtype=torch.bfloat16, device=dev)
     xcodes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     xmeta = torch.empty((M, K // 64), dtype=torch.int32, device=dev)
+    xkept = torch.empty((M, n_protect), dtype=torch.bfloat16, device=dev)
     wdeq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    lws = torch.empty((hif4.linear_workspace_bytes(M, N, 0, n_protect),), dtype=torch.uint8,
+                      device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -156,11 +163,15 @@ def main():
                                       hif4._stream(stream))
         hif4._ok(st, "hif4_quantize(W)")
         if ev: ev[2].record(stream)
-        hif4.quantize(x, codes=xcodes, meta=xmeta, stream=stream)
+        st = hif4.lib().hif4_quantize(hif4._ptr(x), M, K, K, hif4._ptr(mask), n_protect,
+                                      hif4._ptr(xkept), hif4._ptr(xcodes), hif4._ptr(xmeta),
+                                      hif4._stream(stream))
+        hif4._ok(st, "hif4_quantize(X)")
         if ev: ev[3].record(stream)
         hif4.dequantize(wcodes, wmeta, out_dtype=torch.bfloat16, out=wdeq, stream=stream)
         if ev: ev[4].record(stream)
-        hif4.linear_xcodes_wbf16(xcodes, xmeta, wdeq, y=y, stream=stream)
+        hif4.linear_xcodes_wbf16(xcodes, xmeta, wdeq, x_kept=xkept, w_kept=kept, y=y,
+                                 workspace=lws, stream=stream)
         if ev: ev[5].record(stream)
 
     for i in range(args.warmup):
@@ -184,7 +195,7 @@ def main():
                                       avg_ms(4, 5))
     ms_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
-    q_bytes = M * K * (2 + 0.5 + 4 / 64)            # read bf16, write codes + meta
+    q_bytes = M * K * (2 + 0.5 + 4 / 64) + M * n_protect * 2 + K  # + kept values, mask
     wq_bytes = N * K * (2 + 0.5 + 4 / 64) + N * n_protect * 2 + K
     wd_bytes = N * K * (0.5 + 4 / 64 + 2)           # read codes + meta, write bf16
     pct_bytes = M * K * 2                           # one read of X (algorithmic minimum)
@@ -194,7 +205,7 @@ def main():
                             "frac_hbm": pct_bytes / t_pct / 1e6 / HBM_PEAK_GBS},
         "quantize_w_masked": {"ms": t_wq, "GB/s": wq_bytes / t_wq / 1e6,
                               "note": "W (141.6 MB bf16) fits the 256 MB MALL"},
-        "quantize_x": {"ms": t_xq, "GB/s": q_bytes / t_xq / 1e6,
+        "quantize_x_masked": {"ms": t_xq, "GB/s": q_bytes / t_xq / 1e6,
                        "frac_hbm": q_bytes / t_xq / 1e6 / HBM_PEAK_GBS},
         "dequantize_w": {"ms": t_wd, "GB/s": wd_bytes / t_wd / 1e6},
         "gemm_w4a4": {"ms": t_lin, "TFLOP/s": gemm_tflops,
@@ -229,7 +240,7 @@ def main():
             "frac": gemm_tflops / BF16_MFMA_PEAK_TFLOPS,
             "traffic": measured_traffic(),
         },
-        "quantize": parts["quantize_x"],
+        "quantize": parts["quantize_x_masked"],
         "parts": parts,
     }
     if not args.no_cpu_baseline:

@@ -83,81 +83,148 @@ hif4_status hif4_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t 
   return launched(hif4_launch_dequantize(codes, meta, rows, k, out, out_dtype == HIF4_BF16, stream));
 }
 
-// Workspace: the activation's HiF4 codes [m][k/2] and meta [m][k/64] (used
-// when X comes in as bf16), then the decoded weight, bf16 [n][k].
+// Workspace of the linear entry points, in order (each part 256-byte aligned):
+//   X codes [m][k/2], X meta [m][k/64]   (X given in bf16)
+//   W~ bf16 [n][k]                        (hif4_linear_w4a4: W decoded once)
+//   X kept bf16 [m][n_kept]               (X given in bf16 with a mask)
+//   Xr bf16 [m][kr], Wr bf16 [n][kr]      (protected channels zero-padded to
+//                                          kr = n_kept rounded up to 64)
+// With k = 0 the same formula gives what hif4_linear_xcodes_wbf16 needs.
+static int64_t resid_cols(int64_t n_kept) { return (n_kept + 63) / 64 * 64; }
 static size_t ws_x_codes(int64_t m, int64_t k) { return align256((size_t)m * (size_t)(k / 2)); }
 static size_t ws_x_meta(int64_t m, int64_t k) { return align256((size_t)m * (size_t)(k / 64) * 4); }
-size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m < 0 || n < 0 || k < 0) return 0;
-  return ws_x_codes(m, k) + ws_x_meta(m, k) + align256((size_t)n * (size_t)k * 2);
+static size_t ws_w_deq(int64_t n, int64_t k) { return align256((size_t)n * (size_t)k * 2); }
+static size_t ws_x_kept(int64_t m, int64_t nk) { return align256((size_t)m * (size_t)nk * 2); }
+static size_t ws_resid(int64_t rows, int64_t nk) {
+  return align256((size_t)rows * (size_t)resid_cols(nk) * 2);
+}
+size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t n_kept) {
+  if (m < 0 || n < 0 || k < 0 || n_kept < 0) return 0;
+  return ws_x_codes(m, k) + ws_x_meta(m, k) + ws_w_deq(n, k) + ws_x_kept(m, n_kept) +
+         ws_resid(m, n_kept) + ws_resid(n, n_kept);
+}
+
+// Shared tail of both linear entry points: pack the protected channels (if
+// any) into the zero-padded residual operands, then the W4A4 kernel.
+static hif4_status linear_tail(const uint8_t* x_codes, const uint32_t* x_meta, const uint16_t* w,
+                               const uint16_t* x_kept, const uint16_t* w_kept, int64_t n_kept,
+                               int64_t m, int64_t n, int64_t k, void* y, int y_dtype,
+                               char* resid_ws, hipStream_t stream) {
+  uint16_t* xr = nullptr;
+  uint16_t* wr = nullptr;
+  const int64_t kr = n_kept ? resid_cols(n_kept) : 0;
+  if (n_kept) {
+    xr = (uint16_t*)resid_ws;
+    wr = (uint16_t*)(resid_ws + ws_resid(m, n_kept));
+    hif4_status st = launched(hif4_launch_pack_kept(x_kept, m, n_kept, kr, xr, stream));
+    if (st != HIF4_OK) return st;
+    st = launched(hif4_launch_pack_kept(w_kept, n, n_kept, kr, wr, stream));
+    if (st != HIF4_OK) return st;
+  }
+  return launched(hif4_launch_gemm_w4a4(x_codes, x_meta, w, m, n, k, y, y_dtype == HIF4_BF16, xr,
+                                        wr, kr, stream));
+}
+
+static hif4_status check_linear_common(int64_t m, int64_t n, int64_t k, int64_t n_kept,
+                                       int y_dtype) {
+  if (m < 0 || n < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
+  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31)) return HIF4_ERR_SHAPE;
+  if (n_kept < 0 || n_kept > k || n_kept > 65536) return HIF4_ERR_SHAPE;
+  if (y_dtype != HIF4_F32 && y_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+  return HIF4_OK;
 }
 
 hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32_t* x_meta,
-                             const uint8_t* w_codes, const uint32_t* w_meta, int64_t m, int64_t n,
-                             int64_t k, void* y, int y_dtype, void* workspace,
+                             const uint8_t* w_codes, const uint32_t* w_meta, const uint8_t* mask,
+                             const void* x_kept, const void* w_kept, int64_t n_kept, int64_t m,
+                             int64_t n, int64_t k, void* y, int y_dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
-  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31)) return HIF4_ERR_SHAPE;
-  if (y_dtype != HIF4_F32 && y_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+  hif4_status st = check_linear_common(m, n, k, n_kept, y_dtype);
+  if (st != HIF4_OK) return st;
   if (m == 0 || n == 0) return HIF4_OK;
   if (!y) return HIF4_ERR_NULL;
   if (k > 0) {
     if (!w_codes || !w_meta) return HIF4_ERR_NULL;
     if (!x && (!x_codes || !x_meta)) return HIF4_ERR_NULL;
+    if (n_kept > 0 && (!w_kept || (x ? !mask : !x_kept))) return HIF4_ERR_NULL;
+    if (x && n_kept > 0 && k > 65536) return HIF4_ERR_SHAPE;  // channel list of the gather
   }
   if (!aligned(y, 16)) return HIF4_ERR_ALIGN;
   if (k > 0) {
     if (x && !aligned(x, 16)) return HIF4_ERR_ALIGN;
     if (!x && (!aligned(x_codes, 16) || !aligned(x_meta, 4))) return HIF4_ERR_ALIGN;
     if (!aligned(w_codes, 16) || !aligned(w_meta, 4)) return HIF4_ERR_ALIGN;
-    if (!workspace || workspace_bytes < hif4_linear_workspace_bytes(m, n, k))
+    if (n_kept > 0) {
+      if (!aligned(w_kept, 2) || (!x && !aligned(x_kept, 2))) return HIF4_ERR_ALIGN;
+      if (x && !aligned(mask, 16)) return HIF4_ERR_ALIGN;
+    }
+    if (!workspace || workspace_bytes < hif4_linear_workspace_bytes(m, n, k, n_kept))
       return HIF4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
   }
-  hif4_status st = check_device();
+  st = check_device();
   if (st != HIF4_OK) return st;
   if (k == 0) {
     // Empty contraction: Y = 0.
     const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
     return launched(hif4_launch_zero(y, bytes, stream));
   }
-  uint8_t* xc = (uint8_t*)workspace;
-  uint32_t* xm = (uint32_t*)((char*)workspace + ws_x_codes(m, k));
-  uint16_t* wb = (uint16_t*)((char*)workspace + ws_x_codes(m, k) + ws_x_meta(m, k));
+  char* ws = (char*)workspace;
+  uint8_t* xc = (uint8_t*)ws;
+  uint32_t* xm = (uint32_t*)(ws + ws_x_codes(m, k));
+  uint16_t* wb = (uint16_t*)(ws + ws_x_codes(m, k) + ws_x_meta(m, k));
+  uint16_t* xk = (uint16_t*)(ws + ws_x_codes(m, k) + ws_x_meta(m, k) + ws_w_deq(n, k));
+  char* rws = ws + ws_x_codes(m, k) + ws_x_meta(m, k) + ws_w_deq(n, k) + ws_x_kept(m, n_kept);
   if (x) {
-    // X in bf16: quantize it to HiF4 first (the same codes hif4_quantize gives).
-    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, nullptr, xc, xm, stream));
+    // X in bf16: quantize it to HiF4 first (the same codes hif4_quantize
+    // gives), with the protected channels masked out and gathered.
+    const uint8_t* xmask = n_kept ? mask : nullptr;
+    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, xmask, xc, xm, stream));
     if (st != HIF4_OK) return st;
+    if (n_kept) {
+      st = launched(hif4_launch_gather_kept((const uint16_t*)x, m, k, k, mask, n_kept, xk, stream));
+      if (st != HIF4_OK) return st;
+      x_kept = xk;
+    }
     x_codes = xc;
     x_meta = xm;
   }
   // W decoded to bf16 once; X codes are decoded tile by tile inside the GEMM.
   st = launched(hif4_launch_dequantize(w_codes, w_meta, n, k, wb, 1, stream));
   if (st != HIF4_OK) return st;
-  return launched(hif4_launch_gemm_w4a4(x_codes, x_meta, wb, m, n, k, y, y_dtype == HIF4_BF16,
-                                        stream));
+  return linear_tail(x_codes, x_meta, wb, (const uint16_t*)x_kept, (const uint16_t*)w_kept, n_kept,
+                     m, n, k, y, y_dtype, rws, stream);
 }
 
 hif4_status hif4_linear_xcodes_wbf16(const uint8_t* x_codes, const uint32_t* x_meta,
-                                     const void* w, int64_t m, int64_t n, int64_t k, void* y,
-                                     int y_dtype, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k % 64 != 0) return HIF4_ERR_SHAPE;
-  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31)) return HIF4_ERR_SHAPE;
-  if (y_dtype != HIF4_F32 && y_dtype != HIF4_BF16) return HIF4_ERR_DTYPE;
+                                     const void* w, const void* x_kept, const void* w_kept,
+                                     int64_t n_kept, int64_t m, int64_t n, int64_t k, void* y,
+                                     int y_dtype, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  hif4_status st = check_linear_common(m, n, k, n_kept, y_dtype);
+  if (st != HIF4_OK) return st;
   if (m == 0 || n == 0) return HIF4_OK;
   if (!y) return HIF4_ERR_NULL;
   if (k > 0 && (!x_codes || !x_meta || !w)) return HIF4_ERR_NULL;
+  if (n_kept > 0 && (!x_kept || !w_kept)) return HIF4_ERR_NULL;
   if (!aligned(y, 16)) return HIF4_ERR_ALIGN;
   if (k > 0 && (!aligned(x_codes, 16) || !aligned(x_meta, 4) || !aligned(w, 16)))
     return HIF4_ERR_ALIGN;
-  hif4_status st = check_device();
+  if (n_kept > 0) {
+    if (!aligned(x_kept, 2) || !aligned(w_kept, 2)) return HIF4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < hif4_linear_workspace_bytes(m, n, 0, n_kept))
+      return HIF4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
+  }
+  st = check_device();
   if (st != HIF4_OK) return st;
   if (k == 0) {
     const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
     return launched(hif4_launch_zero(y, bytes, stream));
   }
-  return launched(hif4_launch_gemm_w4a4(x_codes, x_meta, (const uint16_t*)w, m, n, k, y,
-                                        y_dtype == HIF4_BF16, stream));
+  return linear_tail(x_codes, x_meta, (const uint16_t*)w, (const uint16_t*)x_kept,
+                     (const uint16_t*)w_kept, n_kept, m, n, k, y, y_dtype,
+                     (char*)workspace + ws_x_kept(m, 0), stream);
 }
 
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {

@@ -129,9 +129,16 @@ __device__ __forceinline__ uint2 decode_quad(uint32_t nib, uint4 t) {
 // kMeta16: meta rows are 16-byte aligned (K a multiple of 256 and an aligned
 // base), so a unit quad is one 16-byte load per row; otherwise four 4-byte
 // loads, one per unit.
-template <bool kMeta16>
+//
+// kResid: protected channels ([TA-method]: kept in high precision). Xr [M][KR]
+// and Wr [N][KR] hold their bf16 values, zero-padded to KR (a multiple of
+// 64); Y += Xr Wr^T is computed after the main loop, 64 columns at a time,
+// in the B ring: the first 64 columns are fetched by the last four steps of
+// the loop (whose B stages would lie past K), the rest after it.
+template <bool kMeta16, bool kResid>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
+void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
+                      const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
                       const uint16_t* __restrict__ B, int M, int N, int K, void* __restrict__ Y,
                       int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsW4A4Bytes];
@@ -243,6 +250,21 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
     }
   };
   constexpr int kMetaLoads = kMeta16 ? 1 : 4;
+
+  // Residual tiles, laid out like B stages (16-row swizzle) in B-ring slot
+  // `slot`: part = 0/1 -> Wr columns 64c + 32part.., 2/3 -> Xr columns
+  // 64c + 32(part-2).. . Rows past M / N read zeros (range check).
+  auto dma_resid = [&](int c, int part, int i) {
+    const bool is_x = part >= 2;
+    const uint32_t row = (uint32_t)((is_x ? m0 : n0) + wave * 64 + 16 * i + (lane >> 2));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(is_x ? (const void*)Xr : (const void*)Wr), (short)0, (is_x ? M : N) * KR * 2,
+        kRsrcWord3);
+    char* dst = lds + kLdsB + (part & 3) * kTileBytes + wave * 64 * kRowBytes + i * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_t*)dst, 16, row * (uint32_t)(KR * 2) + (uint32_t)(dchunk * 16),
+        (64 * c + 32 * (part & 1)) * 2, 0, 0);
+  };
 
   // ---- decode state: thread tid decodes row tid of a half hn
   const int dsw = (tid >> 2) & 3;
@@ -381,8 +403,9 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
   // P+3 overwrites pair P (last read at step 4P+1, first overwritten at step
   // 4P+2); quad Q+2 overwrites quad Q (last read at step 8Q+5, overwritten
   // at step 8Q+6).
-  auto step = [&](int h, auto phase) {
+  auto step = [&](int h, auto phase, auto last) {
     constexpr int kPh = decltype(phase)::value;  // h mod 8
+    constexpr bool kPrefetchResid = kResid && decltype(last)::value && kPh >= 4;
     constexpr int kOdd = kPh & 1;
     constexpr int kLoads1 = 5 + (((kPh + 7) & 7) == 6 ? kMetaLoads : 0);  // loads of step h-1
     constexpr int kLoads2 = 5 + (((kPh + 6) & 7) == 6 ? kMetaLoads : 0);  // ... of step h-2
@@ -411,7 +434,11 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
     // phase 2
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8 && (c & 1) == 0) dma_b_part(h + 4, c >> 1);
+      if (c < 8 && (c & 1) == 0) {
+        // past the loop's end: the first residual chunk instead of stage h + 4
+        if constexpr (kPrefetchResid) dma_resid(0, kPh - 4, c >> 1);
+        else dma_b_part(h + 4, c >> 1);
+      }
       if (c == 8) dma_codes((h + 10) >> 2, (kPh + 2) & 3);
       if constexpr (kPh == 6) {
         if (c == 10) dma_meta((h + 10) >> 3);
@@ -429,17 +456,63 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
     }
   };
   const int KHp = (KH + 7) & ~7;
-  for (int h = 0; h < KHp; h += 8) {
-    step(h + 0, std::integral_constant<int, 0>{});
-    step(h + 1, std::integral_constant<int, 1>{});
-    step(h + 2, std::integral_constant<int, 2>{});
-    step(h + 3, std::integral_constant<int, 3>{});
-    step(h + 4, std::integral_constant<int, 4>{});
-    step(h + 5, std::integral_constant<int, 5>{});
-    step(h + 6, std::integral_constant<int, 6>{});
-    step(h + 7, std::integral_constant<int, 7>{});
+  using F = std::false_type;
+  using T = std::true_type;
+  auto eight = [&](int h, auto last) {
+    step(h + 0, std::integral_constant<int, 0>{}, last);
+    step(h + 1, std::integral_constant<int, 1>{}, last);
+    step(h + 2, std::integral_constant<int, 2>{}, last);
+    step(h + 3, std::integral_constant<int, 3>{}, last);
+    step(h + 4, std::integral_constant<int, 4>{}, last);
+    step(h + 5, std::integral_constant<int, 5>{}, last);
+    step(h + 6, std::integral_constant<int, 6>{}, last);
+    step(h + 7, std::integral_constant<int, 7>{}, last);
+  };
+  if constexpr (kResid) {
+    for (int h = 0; h < KHp - 8; h += 8) eight(h, F{});
+    eight(KHp - 8, T{});
+  } else {
+    for (int h = 0; h < KHp; h += 8) eight(h, F{});
   }
   wait_vmcnt0();  // no LDS-DMA may outlive the workgroup
+
+  if constexpr (kResid) {
+    // Y += Xr Wr^T, 64 columns per chunk: B-ring slots 0/1 = Wr halves,
+    // 2/3 = Xr halves (chunk 0 already fetched by the last loop steps).
+    const int chunks = KR / 64;
+    for (int c = 0; c < chunks; ++c) {
+      if (c > 0) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();  // every wave is done with chunk c-1
+#pragma unroll
+        for (int part = 0; part < 4; ++part)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dma_resid(c, part, i);
+        wait_vmcnt0();
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      stage_barrier();
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk) {
+          bf16x8_t fa[4], fb[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            fa[f] = *reinterpret_cast<const bf16x8_t*>(
+                lds + kLdsB + (2 + r) * kTileBytes + (wm * 128 + f * 32 + frow) * kRowBytes + fslot[sk]);
+            fb[f] = *reinterpret_cast<const bf16x8_t*>(
+                lds + kLdsB + r * kTileBytes + (wn * 128 + f * 32 + frow) * kRowBytes + fslot[sk]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
 
   const int col_in = lane & 31, row_in = (lane >> 5) * 4;
 #pragma unroll
@@ -460,6 +533,29 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ Ac, const uint32_t* __restrict
         }
       }
     }
+  }
+}
+
+// Protected-channel values for the residual: kept [rows][nk] (dense, any
+// nk) -> out [rows][kr] zero-padded, kr a multiple of 64, so that the
+// residual tiles load like B stages (16-byte rows chunks, 16-byte aligned).
+__global__ __launch_bounds__(256) void pack_kept_kernel(const uint16_t* __restrict__ kept,
+                                                        int64_t rows, int nk, int kr,
+                                                        uint16_t* __restrict__ out) {
+  const int64_t groups = rows * (kr / 8);  // 8 outputs (16 bytes) per item
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const int64_t r = g / (kr / 8);
+    const int c0 = (int)(g - r * (kr / 8)) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ca = c0 + 2 * e, cb = ca + 1;
+      const uint32_t lo = ca < nk ? kept[r * nk + ca] : 0u;
+      const uint32_t hi = cb < nk ? kept[r * nk + cb] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(out + r * kr + c0) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -489,12 +585,34 @@ hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream) {
 // are split into row blocks of A and of B (Y sub-blocks with stride n).
 // A in HiF4 codes (+ meta), B bf16. Same row-block split as the bf16 kernel;
 // the code/meta offsets stay far inside 32 bits whenever the bf16 B offsets do.
+hipError_t hif4_launch_pack_kept(const uint16_t* kept, int64_t rows, int64_t nk, int64_t kr,
+                                 uint16_t* out, hipStream_t stream) {
+  if (rows == 0 || kr == 0) return hipSuccess;
+  const int64_t items = rows * (kr / 8);
+  const int64_t blocks = (items + 255) / 256;
+  hipLaunchKernelGGL(pack_kept_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, stream, kept, rows, (int)nk, (int)kr, out);
+  return hipGetLastError();
+}
+
+// A in HiF4 codes (+ meta), B bf16, optional residual xr/wr [.][kr] (kr = 0:
+// none). Same row-block split as before: all 32-bit offsets stay in range.
+template <bool kMeta16, bool kResid>
+static void launch_w4a4(dim3 grid, hipStream_t stream, const uint16_t* xr, const uint16_t* wr,
+                        int kr, const uint8_t* ac, const uint32_t* am, const uint16_t* b, int mc,
+                        int nc, int k, void* ys, int64_t ldy, int y_bf16, int tiles_m,
+                        int tiles_n) {
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kMeta16, kResid>), grid, dim3(256), 0, stream, xr, wr, kr,
+                     ac, am, b, mc, nc, k, ys, ldy, y_bf16, tiles_m, tiles_n);
+}
+
 hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
                                  const uint16_t* b, int64_t m, int64_t n, int64_t k, void* y,
-                                 int y_bf16, hipStream_t stream) {
+                                 int y_bf16, const uint16_t* xr, const uint16_t* wr, int64_t kr,
+                                 hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
   if (k == 0) return hipErrorInvalidValue;
-  const int64_t max_rows = (((int64_t)1 << 31) / (2 * k)) / kBM * kBM;
+  const int64_t max_rows = (((int64_t)1 << 31) / (2 * (k + kr))) / kBM * kBM;
   if (max_rows < kBM) return hipErrorInvalidValue;
   const size_t ysz = y_bf16 ? 2 : 4;
   for (int64_t m0 = 0; m0 < m; m0 += max_rows) {
@@ -502,16 +620,26 @@ hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
     for (int64_t n0 = 0; n0 < n; n0 += max_rows) {
       const int64_t nc = n - n0 < max_rows ? n - n0 : max_rows;
       const int tiles_m = (int)((mc + kBM - 1) / kBM), tiles_n = (int)((nc + kBN - 1) / kBN);
+      const dim3 grid((unsigned)(tiles_m * tiles_n));
       void* ys = (char*)y + ((size_t)m0 * n + n0) * ysz;
       const uint32_t* am = a_meta + m0 * (k / 64);
-      if ((k / 64) % 4 == 0 && ((uintptr_t)am & 15) == 0)
-        hipLaunchKernelGGL(gemm_w4a4_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
-                           0, stream, a_codes + m0 * (k / 2), am, b + n0 * k, (int)mc, (int)nc,
-                           (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+      const uint8_t* ac = a_codes + m0 * (k / 2);
+      const uint16_t* bs = b + n0 * k;
+      const uint16_t* xs = kr ? xr + m0 * kr : nullptr;
+      const uint16_t* ws = kr ? wr + n0 * kr : nullptr;
+      const bool meta16 = (k / 64) % 4 == 0 && ((uintptr_t)am & 15) == 0;
+      if (meta16 && kr)
+        launch_w4a4<true, true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
+                                (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+      else if (meta16)
+        launch_w4a4<true, false>(grid, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k, ys,
+                                 n, y_bf16, tiles_m, tiles_n);
+      else if (kr)
+        launch_w4a4<false, true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
+                                 (int)k, ys, n, y_bf16, tiles_m, tiles_n);
       else
-        hipLaunchKernelGGL(gemm_w4a4_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
-                           0, stream, a_codes + m0 * (k / 2), am, b + n0 * k, (int)mc, (int)nc,
-                           (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+        launch_w4a4<false, false>(grid, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k,
+                                  ys, n, y_bf16, tiles_m, tiles_n);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

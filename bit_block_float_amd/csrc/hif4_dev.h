@@ -107,7 +107,10 @@ hipError_t hif4_launch_dequantize(const uint8_t* codes, const uint32_t* meta, in
                                   int64_t k, void* out, int out_bf16, hipStream_t stream);
 hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
                                  const uint16_t* b, int64_t m, int64_t n, int64_t k, void* y,
-                                 int y_bf16, hipStream_t stream);
+                                 int y_bf16, const uint16_t* xr, const uint16_t* wr, int64_t kr,
+                                 hipStream_t stream);
+hipError_t hif4_launch_pack_kept(const uint16_t* kept, int64_t rows, int64_t nk, int64_t kr,
+                                 uint16_t* out, hipStream_t stream);
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
                                   double q, int64_t n_protect, float* stats, uint8_t* mask,
                                   void* workspace, hipStream_t stream);

@@ -42,11 +42,13 @@ def lib():
         L.hif4_quantize.restype = ctypes.c_int
         L.hif4_dequantize.argtypes = [p, p, i64, i64, p, ctypes.c_int, p]
         L.hif4_dequantize.restype = ctypes.c_int
-        L.hif4_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.hif4_linear_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.hif4_linear_workspace_bytes.restype = sz
-        L.hif4_linear_w4a4.argtypes = [p, p, p, p, p, i64, i64, i64, p, ctypes.c_int, p, sz, p]
+        L.hif4_linear_w4a4.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, p, ctypes.c_int,
+                                       p, sz, p]
         L.hif4_linear_w4a4.restype = ctypes.c_int
-        L.hif4_linear_xcodes_wbf16.argtypes = [p, p, p, i64, i64, i64, p, ctypes.c_int, p]
+        L.hif4_linear_xcodes_wbf16.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, ctypes.c_int, p,
+                                               sz, p]
         L.hif4_linear_xcodes_wbf16.restype = ctypes.c_int
         L.hif4_percentile_workspace_bytes.argtypes = [i64, i64]
         L.hif4_percentile_workspace_bytes.restype = sz
@@ -113,13 +115,26 @@ def dequantize(codes, meta, out_dtype=torch.float32, out=None, stream=None):
     return out
 
 
-def linear_workspace_bytes(m, n, k):
-    return int(lib().hif4_linear_workspace_bytes(m, n, k))
+def linear_workspace_bytes(m, n, k, n_kept=0):
+    return int(lib().hif4_linear_workspace_bytes(m, n, k, n_kept))
 
 
-def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, y_dtype=torch.float32,
-                y=None, workspace=None, stream=None):
-    """Y = deq(Q(X)) deq(Q(W))^T. X as bf16 x [m][k] or as (x_codes, x_meta)."""
+def _kept_count(x_kept, w_kept):
+    if w_kept is None:
+        return 0
+    if w_kept.dtype != torch.bfloat16 or not w_kept.is_contiguous():
+        raise ValueError("w_kept must be a contiguous bf16 tensor [n][n_kept]")
+    if x_kept is not None and (x_kept.dtype != torch.bfloat16 or not x_kept.is_contiguous()
+                               or x_kept.shape[1] != w_kept.shape[1]):
+        raise ValueError("x_kept must be a contiguous bf16 tensor [m][n_kept]")
+    return w_kept.shape[1]
+
+
+def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, mask=None, x_kept=None,
+                w_kept=None, y_dtype=torch.float32, y=None, workspace=None, stream=None):
+    """Y = deq(Q(X)) deq(Q(W))^T (+ x_kept w_kept^T over protected channels).
+    X as bf16 x [m][k] (with `mask` when there are protected channels) or as
+    (x_codes, x_meta[, x_kept])."""
     n, k = w_codes.shape[0], w_codes.shape[1] * 2
     if x is not None:
         _check_bf16_rows(x, "x")
@@ -128,29 +143,38 @@ def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, y_dtype=torc
         m = x.shape[0]
     else:
         m = x_codes.shape[0]
+    n_kept = _kept_count(x_kept, w_kept)
     dev = w_codes.device
     dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
     y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=dev)
-    need = linear_workspace_bytes(m, n, k)
+    need = linear_workspace_bytes(m, n, k, n_kept)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     st = lib().hif4_linear_w4a4(_ptr(x), _ptr(x_codes), _ptr(x_meta), _ptr(w_codes), _ptr(w_meta),
-                                m, n, k, _ptr(y), dt, _ptr(workspace), workspace.numel(),
-                                _stream(stream))
+                                _ptr(mask), _ptr(x_kept), _ptr(w_kept), n_kept, m, n, k, _ptr(y),
+                                dt, _ptr(workspace), workspace.numel(), _stream(stream))
     _ok(st, "hif4_linear_w4a4")
     return y
 
 
-def linear_xcodes_wbf16(x_codes, x_meta, w, y_dtype=torch.float32, y=None, stream=None):
-    """Y = deq(X codes) w^T with w bf16 [n][k] (e.g. a weight decoded once)."""
+def linear_xcodes_wbf16(x_codes, x_meta, w, x_kept=None, w_kept=None, y_dtype=torch.float32,
+                        y=None, workspace=None, stream=None):
+    """Y = deq(X codes) w^T (+ x_kept w_kept^T) with w bf16 [n][k] (e.g. a
+    weight decoded once)."""
     _check_bf16_rows(w, "w")
     if not w.is_contiguous():
         raise ValueError("w must be contiguous (row stride k)")
     m, n, k = x_codes.shape[0], w.shape[0], w.shape[1]
+    n_kept = _kept_count(x_kept, w_kept)
     dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
     y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=w.device)
-    st = lib().hif4_linear_xcodes_wbf16(_ptr(x_codes), _ptr(x_meta), _ptr(w), m, n, k, _ptr(y), dt,
-                                        _stream(stream))
+    if workspace is None and n_kept:
+        workspace = torch.empty((linear_workspace_bytes(m, n, 0, n_kept),), dtype=torch.uint8,
+                                device=w.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib().hif4_linear_xcodes_wbf16(_ptr(x_codes), _ptr(x_meta), _ptr(w), _ptr(x_kept),
+                                        _ptr(w_kept), n_kept, m, n, k, _ptr(y), dt,
+                                        _ptr(workspace), ws_bytes, _stream(stream))
     _ok(st, "hif4_linear_xcodes_wbf16")
     return y
 

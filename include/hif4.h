@@ -118,48 +118,70 @@ HIF4_EXPORT hif4_status hif4_dequantize(const uint8_t *codes, const uint32_t *me
                             void *out, int out_dtype, hipStream_t stream);
 
 /*
- * hif4_linear_workspace_bytes -- bytes of device workspace hif4_linear_w4a4
- * needs for an (m x k) activation and an (n x k) weight.
+ * hif4_linear_workspace_bytes -- bytes of device workspace the linear entry
+ * points need for an (m x k) activation, an (n x k) weight and n_kept
+ * protected channels: hif4_linear_w4a4 needs (m, n, k, n_kept),
+ * hif4_linear_xcodes_wbf16 needs (m, n, 0, n_kept) (0 when n_kept == 0).
+ * Returns 0 for negative sizes.
  */
-HIF4_EXPORT size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+HIF4_EXPORT size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t n_kept);
 
 /*
  * hif4_linear_w4a4 -- W4A4 fake-quantized linear layer ([TA-abs]; the layer
- * form Y = X W^T of the calibration article's FlatQuant section):
- *     Y[i][j] = sum_t deq(Q(X))[i][t] * deq(Q(W))[j][t],
- * accumulated in fp32 (|error| <= 1e-5 * sum_t |a||b| per output).
+ * form Y = X W^T of the calibration article's FlatQuant section), with
+ * optional protected channels ([TA-method], "方法概述": the channels the
+ * mask protects stay in high precision):
+ *     Y[i][j] = sum_t deq(Q(X))[i][t] * deq(Q(W))[j][t]
+ *             + sum_{p < n_kept} x_kept[i][p] * w_kept[j][p],
+ * accumulated in fp32 (|error| <= 1e-5 * sum |a||b| over both parts per output).
  *
  *  X is given EITHER as bf16 x [m][k] (row stride k; it is quantized along k
- *  into the workspace first) OR pre-quantized (x == NULL; x_codes [m][k/2],
- *  x_meta [m][k/64]). W is always pre-quantized: w_codes [n][k/2],
- *  w_meta [n][k/64] (the nn.Linear [out][in] layout, quantized along in).
+ *  into the workspace first, with `mask` applied when n_kept > 0) OR
+ *  pre-quantized (x == NULL; x_codes [m][k/2], x_meta [m][k/64], and
+ *  x_kept bf16 [m][n_kept] when n_kept > 0 -- hif4_quantize's outputs).
+ *  W is always pre-quantized: w_codes [n][k/2], w_meta [n][k/64] (the
+ *  nn.Linear [out][in] layout, quantized along in) and, when n_kept > 0,
+ *  w_kept bf16 [n][n_kept] (hif4_quantize with the same mask).
+ *  mask     u8 [k], 16-byte aligned, exactly n_kept nonzero entries (used
+ *           only when x is given and n_kept > 0; then k <= 65536).
+ *  n_kept   0 <= n_kept <= k; 0 = no protected channels (mask, x_kept and
+ *           w_kept are then ignored and may be NULL).
  *  y        [m][n] of y_dtype (HIF4_F32, or HIF4_BF16 rounded to nearest even).
- *  workspace device memory of at least hif4_linear_workspace_bytes(m, n, k)
- *            bytes, 256-byte aligned; its contents are scratch.
- *  Pointers 16-byte aligned except meta (4-byte). m, n >= 0; k % 64 == 0.
+ *  workspace device memory of at least hif4_linear_workspace_bytes(m, n, k,
+ *            n_kept) bytes, 256-byte aligned; its contents are scratch.
+ *  Pointers 16-byte aligned except meta (4-byte) and kept (2-byte).
+ *  m, n >= 0; k % 64 == 0.
  */
 HIF4_EXPORT hif4_status hif4_linear_w4a4(const void *x, const uint8_t *x_codes, const uint32_t *x_meta,
                              const uint8_t *w_codes, const uint32_t *w_meta,
-                             int64_t m, int64_t n, int64_t k, void *y, int y_dtype,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+                             const uint8_t *mask, const void *x_kept, const void *w_kept,
+                             int64_t n_kept, int64_t m, int64_t n, int64_t k, void *y,
+                             int y_dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * hif4_linear_xcodes_wbf16 -- the contraction step of hif4_linear_w4a4 with
  * the weight already decoded (the serving case: a static weight is decoded
  * once with hif4_dequantize(..., HIF4_BF16) and reused for every batch):
- *     Y[i][j] = sum_t deq(X codes)[i][t] * w[j][t],  accumulated in fp32.
+ *     Y[i][j] = sum_t deq(X codes)[i][t] * w[j][t]
+ *             + sum_{p < n_kept} x_kept[i][p] * w_kept[j][p],  accumulated in fp32.
  *
  *  x_codes [m][k/2], x_meta [m][k/64]: HiF4 activation (hif4_quantize layout).
  *  w       bf16 [n][k], row stride k. With w = deq(Q(W)) (every value exact
  *          in bf16) the result equals hif4_linear_w4a4's bit for bit; any
  *          other bf16 w gives Y = deq(X) w^T with the same accumulation.
+ *  x_kept, w_kept, n_kept: protected channels as in hif4_linear_w4a4.
  *  y       [m][n] of y_dtype (HIF4_F32, or HIF4_BF16 rounded to nearest even).
- *  No workspace. Pointers 16-byte aligned except x_meta (4-byte); m, n >= 0;
- *  k % 64 == 0. k == 0 writes Y = 0.
+ *  workspace: needed only when n_kept > 0: at least
+ *          hif4_linear_workspace_bytes(m, n, 0, n_kept) bytes, 256-byte aligned.
+ *  Pointers 16-byte aligned except x_meta (4-byte) and kept (2-byte);
+ *  m, n >= 0; k % 64 == 0. k == 0 writes Y = 0.
  */
 HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16(const uint8_t *x_codes, const uint32_t *x_meta,
-                                     const void *w, int64_t m, int64_t n, int64_t k,
-                                     void *y, int y_dtype, hipStream_t stream);
+                                     const void *w, const void *x_kept, const void *w_kept,
+                                     int64_t n_kept, int64_t m, int64_t n, int64_t k, void *y,
+                                     int y_dtype, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /*
  * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask

@@ -89,34 +89,65 @@ def test_dequantize_argument_checks(L):
 
 def test_linear_argument_checks(L):
     f = L.hif4_linear_w4a4
-    ws = L.hif4_linear_workspace_bytes(8, 8, 64)
+    ws = L.hif4_linear_workspace_bytes(8, 8, 64, 0)
     assert ws == 256 + 256 + 1024  # X codes, X meta, W bf16 (each 256-B aligned)
-    assert L.hif4_linear_workspace_bytes(-1, 8, 64) == 0
-    assert f(A, None, None, A, A, 8, 8, 60, A, 0, A, ws, None) == SHAPE
-    assert f(A, None, None, A, A, 8, 8, 64, A, 3, A, ws, None) == DTYPE
-    assert f(None, None, None, A, A, 8, 8, 64, A, 0, A, ws, None) == NULL
-    assert f(A, None, None, None, A, 8, 8, 64, A, 0, A, ws, None) == NULL
-    assert f(A, None, None, A, A, 8, 8, 64, None, 0, A, ws, None) == NULL
-    assert f(A, None, None, A, A, 8, 8, 64, A, 0, A, ws - 1, None) == WORKSPACE
-    assert f(A, None, None, A, A, 8, 8, 64, A, 0, None, ws, None) == WORKSPACE
-    assert f(A, None, None, A, A, 8, 8, 64, A, 0, A + 16, ws, None) == ALIGN
-    assert f(A + 2, None, None, A, A, 8, 8, 64, A, 0, A, ws, None) == ALIGN
-    assert f(A, None, None, A, A, 0, 8, 64, A, 0, None, 0, None) == OK
+    assert L.hif4_linear_workspace_bytes(-1, 8, 64, 0) == 0
+    assert L.hif4_linear_workspace_bytes(8, 8, 64, -1) == 0
+    # protected channels add X kept, and Xr / Wr padded to 64 columns
+    assert L.hif4_linear_workspace_bytes(8, 8, 64, 3) == ws + 256 + 1024 + 1024
+    assert L.hif4_linear_workspace_bytes(8, 8, 0, 3) == 256 + 1024 + 1024
+
+    def call(x=A, xc=None, xm=None, wc=A, wm=A, mask=None, xk=None, wk=None, nk=0, m=8, n=8, k=64,
+             y=A, dt=0, w=A, wb=None):
+        return f(x, xc, xm, wc, wm, mask, xk, wk, nk, m, n, k, y, dt, w,
+                 ws if wb is None else wb, None)
+
+    assert call(k=60) == SHAPE
+    assert call(dt=3) == DTYPE
+    assert call(x=None) == NULL
+    assert call(wc=None) == NULL
+    assert call(y=None) == NULL
+    assert call(wb=ws - 1) == WORKSPACE
+    assert call(w=None) == WORKSPACE
+    assert call(w=A + 16) == ALIGN
+    assert call(x=A + 2) == ALIGN
+    assert call(m=0, w=None, wb=0) == OK
+    # protected channels
+    assert call(nk=65) == SHAPE                          # n_kept > k
+    assert call(nk=-1) == SHAPE
+    wsk = L.hif4_linear_workspace_bytes(8, 8, 64, 3)
+    assert call(nk=3, mask=A, wk=None, wb=wsk) == NULL   # w_kept missing
+    assert call(nk=3, mask=None, wk=A, wb=wsk) == NULL   # bf16 X needs the mask
+    assert call(x=None, xc=A, xm=A, nk=3, wk=A, wb=wsk) == NULL  # codes X needs x_kept
+    assert call(nk=3, mask=A + 8, wk=A, wb=wsk) == ALIGN
+    assert call(nk=3, mask=A, wk=A + 1, wb=wsk) == ALIGN
+    assert call(nk=3, mask=A, wk=A, wb=wsk - 1) == WORKSPACE
+    assert call(nk=3, mask=A, wk=A, k=65536 + 64, wb=1 << 40) == SHAPE  # gather limit
 
 
 def test_linear_xcodes_wbf16_argument_checks(L):
     f = L.hif4_linear_xcodes_wbf16
-    assert f(A, A, A, 8, 8, 60, A, 0, None) == SHAPE
-    assert f(A, A, A, -1, 8, 64, A, 0, None) == SHAPE
-    assert f(A, A, A, 8, 8, 64, A, 2, None) == DTYPE
-    assert f(None, A, A, 8, 8, 64, A, 0, None) == NULL
-    assert f(A, None, A, 8, 8, 64, A, 0, None) == NULL
-    assert f(A, A, None, 8, 8, 64, A, 0, None) == NULL
-    assert f(A, A, A, 8, 8, 64, None, 0, None) == NULL
-    assert f(A, A, A + 8, 8, 8, 64, A, 0, None) == ALIGN
-    assert f(A + 8, A, A, 8, 8, 64, A, 0, None) == ALIGN
-    assert f(A, A + 2, A, 8, 8, 64, A, 0, None) == ALIGN
-    assert f(A, A, A, 0, 8, 64, None, 0, None) == OK
+
+    def call(xc=A, xm=A, w=A, xk=None, wk=None, nk=0, m=8, n=8, k=64, y=A, dt=0, ws=None, wb=0):
+        return f(xc, xm, w, xk, wk, nk, m, n, k, y, dt, ws, wb, None)
+
+    assert call(k=60) == SHAPE
+    assert call(m=-1) == SHAPE
+    assert call(dt=2) == DTYPE
+    assert call(xc=None) == NULL
+    assert call(xm=None) == NULL
+    assert call(w=None) == NULL
+    assert call(y=None) == NULL
+    assert call(w=A + 8) == ALIGN
+    assert call(xc=A + 8) == ALIGN
+    assert call(xm=A + 2) == ALIGN
+    assert call(m=0, y=None) == OK
+    wsk = L.hif4_linear_workspace_bytes(8, 8, 0, 5)
+    assert call(nk=5, xk=A) == NULL                      # w_kept missing
+    assert call(nk=5, xk=A, wk=A) == WORKSPACE           # workspace missing
+    assert call(nk=5, xk=A, wk=A, ws=A, wb=wsk - 1) == WORKSPACE
+    assert call(nk=5, xk=A, wk=A, ws=A + 16, wb=wsk) == ALIGN
+    assert call(nk=65, xk=A, wk=A, ws=A, wb=wsk) == SHAPE
 
 
 def test_percentile_argument_checks(L):

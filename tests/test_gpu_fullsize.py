@@ -75,6 +75,33 @@ def test_linear_full_shape_sampled_rows(hip, name, y_dtype, via_codes):
     assert np.all(err <= tol), f"max excess {np.max(err - tol)}"
 
 
+def test_linear_ffn_up_protected_channels(hip):
+    """The whole method at the FFN-up shape: the percentile mask of X (52
+    channels), W and X quantized with it, the linear with the bf16 residual;
+    sampled rows against the oracle."""
+    w = workloads.WORKLOADS["ffn_up"]
+    M, N, K = w["M"], w["N"], w["K"]
+    x = workloads.heavy_tailed_x(M, K, device="cuda", seed=w["index"])
+    wt = workloads.normal_bf16(N, K, 0.02, device="cuda", seed=w["index"] + 1000)
+    _, mask = hip.percentile_mask(x, w["q"], w["n_protect"])
+    wcodes, wmeta, wkept = hip.quantize(wt, mask)
+    xcodes, xmeta, xkept = hip.quantize(x, mask)
+    w_deq = hip.dequantize(wcodes, wmeta, out_dtype=torch.bfloat16)
+    y = hip.linear_xcodes_wbf16(xcodes, xmeta, w_deq, x_kept=xkept, w_kept=wkept)
+    rows = sample_rows(x)
+    mk = mask.cpu().numpy()
+    xs = workloads.bits(x[torch.from_numpy(rows).cuda()])
+    y_rows = y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    wb = workloads.bits(wt)
+    del x, y
+    xc, xm, xk = oracle.quantize(xs, mk)
+    wc, wm, wk = oracle.quantize(wb, mk)
+    assert np.array_equal(wkept.cpu().view(torch.int16).numpy().view(np.uint16), wk)
+    y_ref, s_ref = oracle.linear_protected(xc, xm, xk, wc, wm, wk)
+    err = np.abs(y_rows - y_ref)
+    assert np.all(err <= 1e-5 * s_ref), f"max excess {np.max(err - 1e-5 * s_ref)}"
+
+
 def _check_mask_properties(stats, mask, n_protect):
     assert int(mask.sum()) == n_protect
     on, off = stats[mask == 1], stats[mask == 0]

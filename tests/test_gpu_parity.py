@@ -214,6 +214,39 @@ def test_linear_with_decoded_weight_matches(hip, m, n, k, y_dtype):
     check_linear(y1.float().cpu().numpy(), y_ref, s_ref, bf16_out=(y_dtype == torch.bfloat16))
 
 
+def _bf16_dev(bits_2d):
+    return torch.from_numpy(np.ascontiguousarray(bits_2d).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("m,n,k,n_kept", [(300, 200, 320, 1), (257, 513, 640, 13), (64, 96, 256, 64),
+                                          (33, 700, 192, 65), (260, 300, 1024, 139), (1, 1, 64, 64)])
+@pytest.mark.parametrize("path", ["bf16_x", "codes", "decoded_w"])
+def test_linear_protected_channels(hip, m, n, k, n_kept, path):
+    """[TA-method]: protected channels stay in high precision. The HiF4
+    product plus the bf16 residual over the masked channels, against the
+    oracle, through each entry point (1 to 3 residual chunks of 64)."""
+    print(f"[case] protected {path} {m}x{n}x{k} n_kept={n_kept}", flush=True)
+    r = np.random.default_rng(m + n + k + n_kept)
+    mask = np.zeros(k, np.uint8)
+    mask[r.choice(k, n_kept, replace=False)] = 1
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + 3, outlier_channels=2))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=n + 5))
+    xc, xm, xk = oracle.quantize(xb, mask)
+    wc, wm, wk = oracle.quantize(wb, mask)
+    y_ref, s_ref = oracle.linear_protected(xc, xm, xk, wc, wm, wk)
+    wcd, wmd = torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda()
+    xcd, xmd = torch.from_numpy(xc).cuda(), torch.from_numpy(xm.view(np.int32)).cuda()
+    xkd, wkd = _bf16_dev(xk), _bf16_dev(wk)
+    if path == "bf16_x":
+        y = hip.linear_w4a4(wcd, wmd, x=dev_bf16(xb), mask=torch.from_numpy(mask).cuda(), w_kept=wkd)
+    elif path == "codes":
+        y = hip.linear_w4a4(wcd, wmd, x_codes=xcd, x_meta=xmd, x_kept=xkd, w_kept=wkd)
+    else:
+        w_deq = hip.dequantize(wcd, wmd, out_dtype=torch.bfloat16)
+        y = hip.linear_xcodes_wbf16(xcd, xmd, w_deq, x_kept=xkd, w_kept=wkd)
+    check_linear(y.cpu().numpy(), y_ref, s_ref)
+
+
 def test_linear_one_hot_weight_is_exact(hip):
     """W row j = a single 7 at column t: Y[:, j] = 7 * deq(Q(X))[:, t] exactly
     (one exact product per output, no rounding)."""
