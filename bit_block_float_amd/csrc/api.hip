@@ -66,9 +66,8 @@ hif4_status hif4_quantize(const void* x, int64_t rows, int64_t k, int64_t ld, co
   hif4_status st = check_device();
   if (st != HIF4_OK) return st;
   const uint16_t* xb = (const uint16_t*)x;
-  st = launched(hif4_launch_quantize(xb, rows, k, ld, mask, codes, meta, stream));
-  if (st != HIF4_OK || !mask || n_mask == 0) return st;
-  return launched(hif4_launch_gather_kept(xb, rows, k, ld, mask, n_mask, (uint16_t*)kept, stream));
+  return launched(hif4_launch_quantize(xb, rows, k, ld, mask, mask ? n_mask : 0,
+                                       (uint16_t*)kept, codes, meta, stream));
 }
 
 hif4_status hif4_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t rows, int64_t k,
@@ -179,13 +178,10 @@ hif4_status hif4_linear_w4a4(const void* x, const uint8_t* x_codes, const uint32
     // X in bf16: quantize it to HiF4 first (the same codes hif4_quantize
     // gives), with the protected channels masked out and gathered.
     const uint8_t* xmask = n_kept ? mask : nullptr;
-    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, xmask, xc, xm, stream));
+    st = launched(hif4_launch_quantize((const uint16_t*)x, m, k, k, xmask, n_kept, xk, xc, xm,
+                                       stream));
     if (st != HIF4_OK) return st;
-    if (n_kept) {
-      st = launched(hif4_launch_gather_kept((const uint16_t*)x, m, k, k, mask, n_kept, xk, stream));
-      if (st != HIF4_OK) return st;
-      x_kept = xk;
-    }
+    if (n_kept) x_kept = xk;
     x_codes = xc;
     x_meta = xm;
   }

@@ -98,11 +98,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // ---------------------------------------------------------------- launchers
 // Internal (hidden) host launchers; argument checks happen in api.hip.
 hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
-                                const uint8_t* mask, uint8_t* codes, uint32_t* meta,
-                                hipStream_t stream);
-hipError_t hif4_launch_gather_kept(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
-                                   const uint8_t* mask, int64_t n_mask, uint16_t* kept,
-                                   hipStream_t stream);
+                                const uint8_t* mask, int64_t n_mask, uint16_t* kept,
+                                uint8_t* codes, uint32_t* meta, hipStream_t stream);
 hipError_t hif4_launch_dequantize(const uint8_t* codes, const uint32_t* meta, int64_t rows,
                                   int64_t k, void* out, int out_bf16, hipStream_t stream);
 hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,

@@ -93,14 +93,64 @@ __device__ __forceinline__ uint32_t encode_group(uint4 w, float s, int p, float 
   return mag | (sgn & nz);
 }
 
+// Nonzero bytes of a 32-bit word -> bits 0..3.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+  const uint32_t hi = (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+  return ((hi >> 7) | (hi >> 14) | (hi >> 21) | (hi >> 28)) & 0xFu;
+}
+
+constexpr int kMaxMaskChunks = 65536 / 16;  // masked rows are at most 65536 wide
+
 // Work mapping: one lane owns two level-2 groups (16 consecutive elements,
 // two 16-byte loads), 4 aligned lanes own a unit; unit maximum and metadata
 // word via DPP inside the quad. A wave covers 16 units.
+//
+// kMask: protected channels become +0 in the HiF4 stream and their bf16
+// values go to kept[row][rank], rank = the channel's position among the
+// masked channels. Each workgroup first builds the rank of every 16-channel
+// chunk of the mask in LDS (a prefix count), so the lanes that meet masked
+// channels store their values directly: no second pass over X.
 template <bool kMask>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t ld, uint32_t items_per_row, FastDiv item_div,
     uint32_t total_items, const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta) {
+    uint32_t* __restrict__ meta, uint16_t* __restrict__ kept, int n_mask) {
+  // per 16-channel chunk: rank of its first masked channel (low 16 bits) and
+  // its 16 mask bits (high 16 bits)
+  __shared__ uint32_t chunk_info[kMask ? kMaxMaskChunks : 1];
+  __shared__ uint32_t part[kMask ? 256 : 1];
+  if (kMask) {
+    // chunks t*per .. t*per+per-1 belong to thread t
+    const int chunks = (int)items_per_row, tid = threadIdx.x;
+    const int per = (chunks + 255) / 256;
+    const int c0 = min(chunks, tid * per), c1 = min(chunks, c0 + per);
+    uint32_t run = 0;
+    for (int c = c0; c < c1; ++c) {
+      const uint4 mk = *reinterpret_cast<const uint4*>(mask + (size_t)c * 16);
+      const uint32_t m16 = nonzero_bytes(mk.x) | (nonzero_bytes(mk.y) << 4) |
+                           (nonzero_bytes(mk.z) << 8) | (nonzero_bytes(mk.w) << 12);
+      chunk_info[c] = m16 << 16;
+      run += __popc(m16);
+    }
+    part[tid] = run;
+    __syncthreads();
+    if (tid == 0) {  // exclusive prefix over the 256 thread totals
+      uint32_t acc = 0;
+      for (int i = 0; i < 256; ++i) {
+        const uint32_t v = part[i];
+        part[i] = acc;
+        acc += v;
+      }
+    }
+    __syncthreads();
+    run = part[tid];
+    for (int c = c0; c < c1; ++c) {
+      const uint32_t m16 = chunk_info[c] >> 16;
+      chunk_info[c] |= run & 0xFFFFu;
+      run += __popc(m16);
+    }
+    __syncthreads();
+  }
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t it = blockIdx.x * blockDim.x + threadIdx.x; it < total_items; it += stride) {
     const uint32_t row = fdiv(it, item_div);
@@ -110,17 +160,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)row * ld + (int64_t)j * 16);
     uint4 w0 = src[0], w1 = src[1];
     if (kMask) {
-      // Protected channels are quantized as +0 and do not enter the maxima.
-      const uint4 mk = *reinterpret_cast<const uint4*>(mask + (size_t)j * 16);
-      const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
-      uint32_t* ww0 = &w0.x;
-      uint32_t* ww1 = &w1.x;
+      // Protected channels are quantized as +0 and do not enter the maxima;
+      // their values go to kept (rare: only lanes whose chunk has any).
+      const uint32_t info = chunk_info[j];
+      const uint32_t m16 = info >> 16;
+      if (m16) {
+        uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t mm = m16;
+        while (mm) {
+          const uint32_t e = __ffs(mm) - 1;
+          const uint32_t rank = (info & 0xFFFFu) + __popc(m16 & ((1u << e) - 1u));
+          if (rank < (uint32_t)n_mask)
+            kept[(int64_t)row * n_mask + rank] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+          mm &= mm - 1;
+        }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t mb = (mw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        uint32_t* ww = i < 8 ? ww0 : ww1;
-        const int e = i & 7;
-        if (mb) ww[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = (m16 >> (2 * i)) & 1u, hi = (m16 >> (2 * i + 1)) & 1u;
+          ww[i] &= ~((lo * 0x0000FFFFu) | (hi * 0xFFFF0000u));
+        }
+        w0 = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+        w1 = make_uint4(ww[4], ww[5], ww[6], ww[7]);
       }
     }
 
@@ -154,50 +214,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                         (e3b1 << (17 + 2 * g1));
     const uint32_t mw = or4_u32(mb) | c;
     if (q == 0u) meta[it >> 2] = mw;
-  }
-}
-
-// Gather protected-channel entries into kept [rows][n_mask], ascending
-// channel order. Each block first compacts the mask into a channel list in
-// LDS (k <= 65536), then copies its rows.
-__global__ __launch_bounds__(256) void gather_kept_kernel(const uint16_t* __restrict__ x,
-                                                          int64_t rows, int k, int64_t ld,
-                                                          const uint8_t* __restrict__ mask,
-                                                          int n_mask, uint16_t* __restrict__ kept,
-                                                          int rows_per_block) {
-  extern __shared__ uint16_t chan[];  // n_mask entries
-  __shared__ int counts[256];
-  const int tid = threadIdx.x;
-  const int chunk = (k + 255) / 256;
-  const int c0 = min(k, tid * chunk), c1 = min(k, c0 + chunk);
-  int cnt = 0;
-  for (int ch = c0; ch < c1; ++ch) cnt += mask[ch] != 0;
-  counts[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = counts[i];
-      counts[i] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  int pos = counts[tid];
-  for (int ch = c0; ch < c1; ++ch) {
-    if (mask[ch] != 0) {
-      if (pos < n_mask) chan[pos] = (uint16_t)ch;
-      ++pos;
-    }
-  }
-  __shared__ int total;
-  if (tid == 255) total = pos;  // exclusive prefix of the last thread + its own count
-  __syncthreads();
-  const int nf = min(total, n_mask);
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
-  for (int64_t r = r0; r < r1; ++r) {
-    for (int i = tid; i < nf; i += 256) kept[r * n_mask + i] = x[r * ld + chan[i]];
   }
 }
 
@@ -253,8 +269,8 @@ using namespace hif4;
 
 // Rows are processed in chunks so that group indices stay below 2^31.
 hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
-                                const uint8_t* mask, uint8_t* codes, uint32_t* meta,
-                                hipStream_t stream) {
+                                const uint8_t* mask, int64_t n_mask, uint16_t* kept,
+                                uint8_t* codes, uint32_t* meta, hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
   const uint32_t gpr = (uint32_t)(k / 16);  // 16-element items per row
   const FastDiv fd = make_fastdiv(gpr);
@@ -265,37 +281,17 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
     const uint16_t* xs = x + r0 * ld;
     uint32_t* cs = reinterpret_cast<uint32_t*>(codes + r0 * (k / 2));
     uint32_t* ms = meta + r0 * (k / 64);
-    const dim3 grid(grid_for(total)), block(256);
-    if (mask)
+    const dim3 block(256);
+    if (mask) {
+      // fewer, longer-lived workgroups: each builds the mask's rank table once
+      const unsigned g = grid_for(total);
+      const dim3 grid(g < 256u * 8u ? g : 256u * 8u);
       hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, stream, xs, ld, gpr, fd, total,
-                         mask, cs, ms);
-    else
-      hipLaunchKernelGGL(quantize_kernel<false>, grid, block, 0, stream, xs, ld, gpr, fd, total,
-                         mask, cs, ms);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-hipError_t hif4_launch_gather_kept(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
-                                   const uint8_t* mask, int64_t n_mask, uint16_t* kept,
-                                   hipStream_t stream) {
-  if (rows == 0 || n_mask == 0) return hipSuccess;
-  const int rows_per_block = 16;
-  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  const size_t lds = (size_t)n_mask * sizeof(uint16_t);
-  if (lds > 48 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gather_kept_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  for (int64_t b0 = 0; b0 < blocks; b0 += (1 << 30)) {
-    const int64_t nb = blocks - b0 < (1 << 30) ? blocks - b0 : (1 << 30);
-    const int64_t r0 = b0 * rows_per_block;
-    hipLaunchKernelGGL(gather_kept_kernel, dim3((unsigned)nb), dim3(256),
-                       (size_t)n_mask * sizeof(uint16_t), stream, x + r0 * ld, rows - r0, (int)k,
-                       ld, mask, (int)n_mask, kept + r0 * n_mask, rows_per_block);
+                         mask, cs, ms, kept ? kept + r0 * n_mask : nullptr, (int)n_mask);
+    } else {
+      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(total)), block, 0, stream, xs, ld,
+                         gpr, fd, total, mask, cs, ms, nullptr, 0);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
