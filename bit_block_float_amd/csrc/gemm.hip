@@ -352,6 +352,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   const int fhalf = lane >> 5;
   const int fslot[2] = {((0 + fhalf) ^ fsw) * 16, ((2 + fhalf) ^ fsw) * 16};
   // fragment f of K-chunk s of step h: f < 4 -> A rows wm*128 + 32f, else B rows wn*128 + 32(f-4)
+  // (h only enters through h & 3: callers pass the step's phase, a constant)
   auto frag = [&](int h, int s, int f) {
     const char* p = f < 4
         ? lds + kLdsADec + (h & 1) * kTileBytes + (wm * 128 + f * 32 + frow) * kRowBytes
@@ -413,7 +414,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
     // (a longer run would leave the matrix pipe idle)
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8) f1[c] = frag(h, 1, c);
+      if (c < 8) f1[c] = frag(kPh, 1, c);
       if (c >= 2 && c < 14) {
         if (((c - 2) & 1) == 0) dec_quad_a(2 + ((c - 2) >> 1));
         else dec_quad_b(h + 1, 2 + ((c - 2) >> 1));
@@ -443,7 +444,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
       if constexpr (kPh == 6) {
         if (c == 10) dma_meta((h + 10) >> 3);
       }
-      if (c < 8) f0[c] = frag(h + 1, 0, c);
+      if (c < 8) f0[c] = frag(kPh + 1, 0, c);
       if (c == 4) dec_unit();
       if (c >= 5 && c < 13) dec_tab(kOdd, c - 5);
       if (c >= 12) {
