@@ -64,6 +64,50 @@ __device__ __forceinline__ LaneCh lane_channels(int ch, int c) {
   return l;
 }
 
+// Row streaming shared by the two passes: wave w of the workgroup reads rows
+// r0 + w, r0 + w + 8, ... in blocks of kPctUnroll rows, the next block's
+// loads issued before the current block is processed (two register buffers),
+// so loads stay in flight while the histogram work runs. body(v, rb, tail)
+// gets the block's words; the last partial block has its rows clamped to
+// r1 - 1 and tail = true (the body must not count rows >= r1).
+template <typename Body>
+__device__ __forceinline__ void stream_rows(const uint16_t* xl, int64_t ld, int64_t r0,
+                                            int64_t r1, int wave, Body&& body) {
+  constexpr int kWaves = kPctThreads / 64;
+  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
+  auto full = [&](int64_t rb) { return rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; };
+  auto load = [&](uint32_t (&v)[kPctUnroll], int64_t rb) {
+    const uint16_t* p = xl + rb * ld;
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
+  };
+  int64_t rb = r0 + wave;
+  uint32_t va[kPctUnroll], vb[kPctUnroll];
+  if (full(rb)) {
+    load(va, rb);
+    for (;;) {
+      const bool nb = full(rb + step);
+      if (nb) load(vb, rb + step);
+      body(va, rb, false);
+      rb += step;
+      if (!nb) break;
+      const bool na = full(rb + step);
+      if (na) load(va, rb + step);
+      body(vb, rb, false);
+      rb += step;
+      if (!na) break;
+    }
+  }
+  if (rb < r1) {  // last partial block
+#pragma unroll
+    for (int u = 0; u < kPctUnroll; ++u) {
+      const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
+      va[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
+    }
+    body(va, rb, true);
+  }
+}
+
 // Pass 1: coarse histograms. LDS counters are u16 pairs (rows per workgroup
 // never exceed 65535), 256 bins x 128 channels = 64 KiB.
 __global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
@@ -94,24 +138,7 @@ __global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
       atomicAdd(&hist[(bb >> 1) * kPctCh + colB], ib);
     }
   };
-  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
-  int64_t rb = r0 + wave;
-  for (; rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; rb += step) {
-    const uint16_t* p = xl + rb * ld;
-    uint32_t v[kPctUnroll];
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
-    count(v, rb, false);
-  }
-  if (rb < r1) {  // last partial block: rows clamped to r1 - 1, extra rows not counted
-    uint32_t v[kPctUnroll];
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
-      v[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
-    }
-    count(v, rb, true);
-  }
+  stream_rows(xl, ld, r0, r1, wave, count);
   __syncthreads();
   for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
     const uint32_t w = hist[i];
@@ -240,24 +267,7 @@ __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
       if ((kb >> 7) == hiB) atomicMin(&mins[colB], kb);
     }
   };
-  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
-  int64_t rb = r0 + wave;
-  for (; rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; rb += step) {
-    const uint16_t* p = xl + rb * ld;
-    uint32_t v[kPctUnroll];
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
-    scan(v, rb, false);
-  }
-  if (rb < r1) {
-    uint32_t v[kPctUnroll];
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
-      v[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
-    }
-    scan(v, rb, true);
-  }
+  stream_rows(xl, ld, r0, r1, wave, scan);
   __syncthreads();
   for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
     const uint32_t w = hist[i];
