@@ -232,7 +232,7 @@ size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {
 hif4_status hif4_percentile_mask(const void* x, int64_t rows, int64_t c, int64_t ld, double q,
                                  int64_t n_protect, float* stats, uint8_t* mask, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  if (rows < 1 || c < 1 || c > 65536 || ld < c) return HIF4_ERR_SHAPE;
+  if (rows < 1 || c < 1 || c > 65536 || ld < c || ld > (1 << 22)) return HIF4_ERR_SHAPE;
   if (n_protect < 0 || n_protect > c) return HIF4_ERR_SHAPE;
   if (!(q >= 0.0 && q <= 1.0)) return HIF4_ERR_ARG;
   if (!x || !stats || !mask) return HIF4_ERR_NULL;

@@ -17,24 +17,40 @@
 // Histograms are integers (LDS atomics per workgroup, then global atomics):
 // results do not depend on scheduling.
 //
-// Mapping: a workgroup of 8 waves owns 128 channels and a slice of rows; each
-// lane reads one 32-bit word (2 channels) per row, so every LDS atomic of an
-// instruction targets a distinct channel. Channel p of the block is stored at
-// LDS column (p & 1) * 64 + (p >> 1): the 64 lanes of a wave then hit 64
-// distinct columns, i.e. the 32 banks exactly twice.
+// Mapping: the work of a pass is the sequence of (channel block, row) pairs,
+// a channel block being 128 channels. The grid is a whole number of waves of
+// resident workgroups (one 16-wave workgroup per CU, the LDS bound of pass 1),
+// and workgroup g takes the g-th equal contiguous slice of that sequence:
+// every workgroup reads the same number of rows, so no partial last wave of
+// workgroups idles the chip. A slice is one or a few segments (rows r0..r1 of
+// one channel block); the LDS histogram is flushed to global memory at the end
+// of each segment. In a segment each lane reads one 32-bit word (2 channels)
+// per row, so every LDS atomic of an instruction targets a distinct channel.
+// Channel p of the block is stored at LDS column (p & 1) * 64 + (p >> 1): the
+// 64 lanes of a wave then hit 64 distinct columns, i.e. the 32 banks exactly
+// twice. Lanes whose channels lie past the last channel read a valid word and
+// count into their own columns, which are never flushed: the counting itself
+// needs no per-lane validity test.
 #include "hif4_dev.h"
 
 namespace hif4 {
 
-constexpr int kPctThreads = 512;
+constexpr int kPctThreads = 1024;
+constexpr int kPctWaves = kPctThreads / 64;
 constexpr int kPctCh = 128;    // channels per workgroup
-constexpr int kPctUnroll = 16; // rows in flight per lane
+constexpr int kPctUnroll = 16; // rows per block of loads
+constexpr int kRsrcWord3Pct = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 
 struct PctSel {
   uint32_t b_lo, r_lo, b_hi, r_hi;
 };
 
 __device__ __forceinline__ int col_of(int p) { return (p & 1) * 64 + (p >> 1); }
+
+// LDS column -> channel offset inside the block (inverse of col_of).
+__device__ __forceinline__ int chan_of_col(int col) {
+  return (col < 64) ? 2 * col : 2 * (col - 64) + 1;
+}
 
 // Zero the histograms, reset the per-channel minimum keys.
 __global__ void pct_init_kernel(uint32_t* __restrict__ h1, uint32_t* __restrict__ h2,
@@ -48,38 +64,42 @@ __global__ void pct_init_kernel(uint32_t* __restrict__ h1, uint32_t* __restrict_
   }
 }
 
-// Per-lane channel setup: the lane reads the 32-bit word of channels ch and
-// ch+1 of every row. Lanes past the last channel read channel 0 instead (a
-// valid address) and mark both halves invalid; when c is odd the last lane's
-// word also covers element c, which exists because ld >= c + 1 then (ld is a
-// multiple of 8), and its high half is marked invalid. Loads stay branch-free.
-struct LaneCh {
-  uint32_t off;     // element offset of the word inside a row
-  uint32_t valid;   // bit 0: low half (ch) valid, bit 1: high half (ch+1) valid
-};
-__device__ __forceinline__ LaneCh lane_channels(int ch, int c) {
-  LaneCh l;
-  l.off = ch < c ? (uint32_t)ch : 0u;
-  l.valid = (ch < c ? 1u : 0u) | (ch + 1 < c ? 2u : 0u);
-  return l;
+// Element offset of the 32-bit word (channels ch, ch + 1) a lane reads in
+// each row. Lanes past the last channel read channel 0 instead (a valid
+// address); when c is odd the last lane's word also covers element c, which
+// exists because ld >= c + 1 then (ld is a multiple of 8).
+__device__ __forceinline__ uint32_t lane_offset(int ch, int c) {
+  return ch < c ? (uint32_t)ch : 0u;
 }
 
-// Row streaming shared by the two passes: wave w of the workgroup reads rows
-// r0 + w, r0 + w + 8, ... in blocks of kPctUnroll rows, the next block's
+// Row streaming shared by the two passes (lane element offset loff inside a
+// row): wave w of the workgroup reads rows
+// r0 + w, r0 + w + 16, ... in blocks of kPctUnroll rows, the next block's
 // loads issued before the current block is processed (two register buffers),
 // so loads stay in flight while the histogram work runs. body(v, rb, tail)
 // gets the block's words; the last partial block has its rows clamped to
 // r1 - 1 and tail = true (the body must not count rows >= r1).
 template <typename Body>
-__device__ __forceinline__ void stream_rows(const uint16_t* xl, int64_t ld, int64_t r0,
-                                            int64_t r1, int wave, Body&& body) {
-  constexpr int kWaves = kPctThreads / 64;
-  const int64_t step = (int64_t)kWaves * kPctUnroll, rstride = (int64_t)kWaves * ld;
+__device__ __forceinline__ void stream_rows(const uint16_t* x, uint32_t loff, int64_t ld,
+                                            int64_t r0, int64_t r1, int wave, Body&& body) {
+  constexpr int kWaves = kPctWaves;
+  const int64_t step = (int64_t)kWaves * kPctUnroll;
   auto full = [&](int64_t rb) { return rb + (int64_t)(kPctUnroll - 1) * kWaves < r1; };
+  // Buffer loads: the row base of a block is scalar, the lane offset and the
+  // row step are 32-bit (ld <= 2^22 keeps every offset below 2^31).
+  const uint32_t vbytes = loff * 2u;
+  const int sstep = (int)(kWaves * ld * 2);
+  auto word = [&](int64_t r) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + r * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, vbytes, 0, 0);
+  };
   auto load = [&](uint32_t (&v)[kPctUnroll], int64_t rb) {
-    const uint16_t* p = xl + rb * ld;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
 #pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) v[u] = *reinterpret_cast<const uint32_t*>(p + u * rstride);
+    for (int u = 0; u < kPctUnroll; ++u)
+      v[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, vbytes, u * sstep, 0);
   };
   int64_t rb = r0 + wave;
   uint32_t va[kPctUnroll], vb[kPctUnroll];
@@ -102,54 +122,79 @@ __device__ __forceinline__ void stream_rows(const uint16_t* xl, int64_t ld, int6
 #pragma unroll
     for (int u = 0; u < kPctUnroll; ++u) {
       const int64_t r = min(rb + (int64_t)u * kWaves, r1 - 1);
-      va[u] = *reinterpret_cast<const uint32_t*>(xl + r * ld);
+      va[u] = word(r);
     }
     body(va, rb, true);
   }
 }
 
-// Pass 1: coarse histograms. LDS counters are u16 pairs (rows per workgroup
-// never exceed 65535), 256 bins x 128 channels = 64 KiB.
-__global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int rows_per_block,
-    uint32_t* __restrict__ h1) {
-  __shared__ uint32_t hist[128 * kPctCh];  // [bin/2][column]
-  for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) hist[i] = 0u;
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * kPctCh;
-  const LaneCh lc = lane_channels(c0 + 2 * lane, c);
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
-  const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
-  constexpr int kWaves = kPctThreads / 64;
-  const uint16_t* xl = x + lc.off;
-
-  auto count = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      const bool row_ok = !tail || rb + (int64_t)u * kWaves < r1;
-      const uint32_t ka = v[u] & 0x7FFFu, kb = (v[u] >> 16) & 0x7FFFu;
-      const uint32_t ba = ka >> 7, bb = kb >> 7;
-      const uint32_t ia = (row_ok && (lc.valid & 1u)) ? 1u << (16 * (ba & 1u)) : 0u;
-      const uint32_t ib = (row_ok && (lc.valid & 2u)) ? 1u << (16 * (bb & 1u)) : 0u;
-      atomicAdd(&hist[(ba >> 1) * kPctCh + colA], ia);
-      atomicAdd(&hist[(bb >> 1) * kPctCh + colB], ib);
+// Segments of workgroup g's slice [g * per_wg, (g + 1) * per_wg) of the
+// (channel block, row) sequence; body(c0, r0, r1) runs once per segment, with
+// values uniform over the workgroup. The sequence is ordered in slabs of
+// per_wg rows (slab, then channel block, then row; the last slab may be
+// shorter), so that workgroups g .. g + cblocks - 1 stream the same rows at
+// the same time and the chip reads whole rows of X together.
+template <typename Body>
+__device__ __forceinline__ void for_segments(int64_t rows, int cblocks, int64_t per_wg,
+                                             Body&& body) {
+  const int64_t total = (int64_t)cblocks * rows;
+  const int64_t slab_items = (int64_t)cblocks * per_wg;
+  const int64_t full_slabs = rows / per_wg;
+  int64_t pos = (int64_t)blockIdx.x * per_wg;
+  const int64_t end = min(total, pos + per_wg);
+  while (pos < end) {
+    int64_t slab = pos / slab_items, rn = per_wg;
+    if (slab >= full_slabs) {
+      slab = full_slabs;
+      rn = rows - full_slabs * per_wg;
     }
-  };
-  stream_rows(xl, ld, r0, r1, wave, count);
-  __syncthreads();
-  for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
-    const uint32_t w = hist[i];
-    if (!w) continue;
-    const int col = i % kPctCh, bin2 = i / kPctCh;
-    const int p = (col < 64) ? 2 * col : 2 * (col - 64) + 1;
-    const int chan = c0 + p;
-    if (chan >= c) continue;
-    if (w & 0xFFFFu) atomicAdd(&h1[(int64_t)chan * 256 + 2 * bin2], w & 0xFFFFu);
-    if (w >> 16) atomicAdd(&h1[(int64_t)chan * 256 + 2 * bin2 + 1], w >> 16);
+    const int64_t rs = slab * per_wg;
+    const int64_t rem = pos - slab * slab_items;
+    const int64_t cb = rem / rn;
+    const int64_t off = rem - cb * rn;
+    const int64_t r0 = rs + off;
+    const int64_t r1 = rs + min(rn, off + (end - pos));
+    body((int)cb * kPctCh, r0, r1);
+    pos += r1 - r0;
   }
+}
+
+// Pass 1: coarse histograms, u32 counters, 256 bins x 128 channels = 128 KiB.
+// The bin of the low channel of word v is bits 7..14, of the high channel
+// bits 23..30: one bit-field extract and one shift-or per channel.
+__global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
+    uint32_t* __restrict__ h1) {
+  __shared__ uint32_t hist[256 * kPctCh];  // [bin][column]
+  for (int i = threadIdx.x; i < 256 * kPctCh; i += kPctThreads) hist[i] = 0u;
+  __syncthreads();
+
+  // the wave index is uniform: row addresses then live in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
+  const int cblocks = (c + kPctCh - 1) / kPctCh;
+
+  for_segments(rows, cblocks, per_wg, [&](int c0, int64_t r0, int64_t r1) {
+    auto count = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
+#pragma unroll
+      for (int u = 0; u < kPctUnroll; ++u) {
+        if (tail && rb + (int64_t)u * kPctWaves >= r1) continue;  // clamped row
+        atomicAdd(&hist[((v[u] >> 7) & 255u) * kPctCh + colA], 1u);
+        atomicAdd(&hist[((v[u] >> 23) & 255u) * kPctCh + colB], 1u);
+      }
+    };
+    stream_rows(x, lane_offset(c0 + 2 * lane, c), ld, r0, r1, wave, count);
+    __syncthreads();
+    // flush the segment's counts and clear the histogram for the next one
+    for (int i = threadIdx.x; i < 256 * kPctCh; i += kPctThreads) {
+      const uint32_t w = hist[i];
+      if (!w) continue;
+      hist[i] = 0u;
+      const int chan = c0 + chan_of_col(i % kPctCh);
+      if (chan < c) atomicAdd(&h1[(int64_t)chan * 256 + i / kPctCh], w);
+    }
+    __syncthreads();
+  });
 }
 
 // Ranks lo and hi of the type-7 quantile: h = q (n-1), lo = floor(h).
@@ -226,62 +271,76 @@ __global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restr
 }
 
 // Pass 2: fine histograms inside bin b_lo and the minimum key of bin b_hi.
+// With lo7 = b_lo << 7, a key k lies in bin b_lo exactly when t = k ^ lo7 is
+// below 128, and t is then its fine index: min(t, 128) is the fine index, or
+// the spare row 128 of the histogram (never flushed) for keys of other bins,
+// so the count needs no branch. Likewise the smallest k ^ (b_hi << 7) below
+// 128 gives the smallest key of bin b_hi; each lane keeps that minimum in a
+// register (a lane owns its channels within its wave) and the workgroup
+// merges it once per segment.
 __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int rows_per_block,
+    const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
     const PctSel* __restrict__ sel, uint32_t* __restrict__ h2, uint32_t* __restrict__ minkey) {
-  __shared__ uint32_t hist[128 * kPctCh];  // [fine bin][column]
+  __shared__ uint32_t hist[129 * kPctCh];  // [fine bin, spare][column]
   __shared__ uint32_t mins[kPctCh];
-  for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) hist[i] = 0u;
+  for (int i = threadIdx.x; i < 129 * kPctCh; i += kPctThreads) hist[i] = 0u;
   for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) mins[i] = 0xFFFFFFFFu;
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * kPctCh;
-  const int ch = c0 + 2 * lane;
-  const LaneCh lc = lane_channels(ch, c);
+  // the wave index is uniform: row addresses then live in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
-  // Bins to watch; 0x1FF never matches a bin (at most 255).
-  uint32_t loA = 0x1FFu, hiA = 0x1FFu, loB = 0x1FFu, hiB = 0x1FFu;
-  if (lc.valid & 1u) {
-    loA = sel[ch].b_lo;
-    hiA = sel[ch].b_hi != sel[ch].b_lo ? sel[ch].b_hi : 0x1FFu;
-  }
-  if (lc.valid & 2u) {
-    loB = sel[ch + 1].b_lo;
-    hiB = sel[ch + 1].b_hi != sel[ch + 1].b_lo ? sel[ch + 1].b_hi : 0x1FFu;
-  }
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
-  constexpr int kWaves = kPctThreads / 64;
-  const uint16_t* xl = x + lc.off;
+  const int cblocks = (c + kPctCh - 1) / kPctCh;
 
-  auto scan = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
-#pragma unroll
-    for (int u = 0; u < kPctUnroll; ++u) {
-      // a clamped (repeated) row must not count: push its bins out of range
-      const uint32_t kill = (!tail || rb + (int64_t)u * kWaves < r1) ? 0u : 0x1000000u;
-      const uint32_t ka = (v[u] & 0x7FFFu) | kill, kb = ((v[u] >> 16) & 0x7FFFu) | kill;
-      if ((ka >> 7) == loA) atomicAdd(&hist[(ka & 127u) * kPctCh + colA], 1u);
-      if ((ka >> 7) == hiA) atomicMin(&mins[colA], ka);
-      if ((kb >> 7) == loB) atomicAdd(&hist[(kb & 127u) * kPctCh + colB], 1u);
-      if ((kb >> 7) == hiB) atomicMin(&mins[colB], kb);
+  for_segments(rows, cblocks, per_wg, [&](int c0, int64_t r0, int64_t r1) {
+    const int ch = c0 + 2 * lane;
+    // Bins to watch, shifted into key position; 0x1FF << 7 never matches a key
+    // (keys are below 0x8000).
+    uint32_t loA = 0x1FFu << 7, hiA = 0x1FFu << 7, loB = 0x1FFu << 7, hiB = 0x1FFu << 7;
+    if (ch < c) {
+      const PctSel s = sel[ch];
+      loA = s.b_lo << 7;
+      if (s.b_hi != s.b_lo) hiA = s.b_hi << 7;
     }
-  };
-  stream_rows(xl, ld, r0, r1, wave, scan);
-  __syncthreads();
-  for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
-    const uint32_t w = hist[i];
-    if (!w) continue;
-    const int col = i % kPctCh, fb = i / kPctCh;
-    const int p = (col < 64) ? 2 * col : 2 * (col - 64) + 1;
-    const int chan = c0 + p;
-    if (chan < c) atomicAdd(&h2[(int64_t)chan * 128 + fb], w);
-  }
-  for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) {
-    const int p = (i < 64) ? 2 * i : 2 * (i - 64) + 1;
-    const int chan = c0 + p;
-    if (chan < c && mins[i] != 0xFFFFFFFFu) atomicMin(&minkey[chan], mins[i]);
-  }
+    if (ch + 1 < c) {
+      const PctSel s = sel[ch + 1];
+      loB = s.b_lo << 7;
+      if (s.b_hi != s.b_lo) hiB = s.b_hi << 7;
+    }
+    uint32_t mnA = 0xFFFFFFFFu, mnB = 0xFFFFFFFFu;
+    auto scan = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
+#pragma unroll
+      for (int u = 0; u < kPctUnroll; ++u) {
+        // a clamped (repeated) row must not count: push it out of every bin
+        const uint32_t kill = (!tail || rb + (int64_t)u * kPctWaves < r1) ? 0u : 0x1000000u;
+        const uint32_t ka = (v[u] & 0x7FFFu) | kill, kb = ((v[u] >> 16) & 0x7FFFu) | kill;
+        atomicAdd(&hist[min(ka ^ loA, 128u) * kPctCh + colA], 1u);
+        atomicAdd(&hist[min(kb ^ loB, 128u) * kPctCh + colB], 1u);
+        mnA = min(mnA, ka ^ hiA);
+        mnB = min(mnB, kb ^ hiB);
+      }
+    };
+    stream_rows(x, lane_offset(ch, c), ld, r0, r1, wave, scan);
+    if (mnA < 128u) atomicMin(&mins[colA], mnA ^ hiA);
+    if (mnB < 128u) atomicMin(&mins[colB], mnB ^ hiB);
+    __syncthreads();
+    // flush and clear for the next segment (the spare row is never read)
+    for (int i = threadIdx.x; i < 128 * kPctCh; i += kPctThreads) {
+      const uint32_t w = hist[i];
+      if (!w) continue;
+      hist[i] = 0u;
+      const int chan = c0 + chan_of_col(i % kPctCh);
+      if (chan < c) atomicAdd(&h2[(int64_t)chan * 128 + i / kPctCh], w);
+    }
+    for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) {
+      const uint32_t w = mins[i];
+      if (w == 0xFFFFFFFFu) continue;
+      mins[i] = 0xFFFFFFFFu;
+      const int chan = c0 + chan_of_col(i);
+      if (chan < c) atomicMin(&minkey[chan], w);
+    }
+    __syncthreads();
+  });
 }
 
 // Exact keys of ranks lo / hi -> type-7 statistic, double then fp32 (RNE).
@@ -332,7 +391,7 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
                                                                  uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_prefix, s_need, s_above;
-  __shared__ uint32_t part[kMaskThreads];
+  __shared__ uint32_t part[kMaskThreads / 64];
   const int tid = threadIdx.x;
   if (n_protect <= 0 || n_protect >= c) {
     const uint8_t v = n_protect <= 0 ? 0 : 1;
@@ -354,18 +413,20 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
       if ((u & prefix_mask) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      // walk digits from the top: find the digit holding rank s_need (descending)
-      uint32_t need = s_need, d = 255;
-      for (int dd = 255; dd >= 0; --dd) {
-        if (need < hist[dd]) {
-          d = (uint32_t)dd;
-          break;
-        }
-        need -= hist[dd];
+    if (tid < 64) {
+      // the digit holding rank s_need, counting from the top digit down:
+      // lane l holds digits 255 - 4l .. 252 - 4l
+      const uint32_t need = s_need;
+      uint32_t cnt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - (tid * 4 + i)];
+      uint32_t pos;
+      int64_t before;
+      wave_find_rank<4>(cnt, (int64_t)need, &pos, &before);
+      if (tid == 0) {
+        s_prefix = pre | ((255u - pos) << shift);
+        s_need = need - (uint32_t)before;
       }
-      s_prefix = pre | (d << shift);
-      s_need = need;
     }
     prefix_mask |= 255u << shift;
     __syncthreads();
@@ -380,22 +441,18 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
     above += u > tau;
     ties += u == tau;
   }
-  part[tid] = ties;
   if (tid == 0) s_above = 0u;
+  // exclusive scan of the tie counts in thread order (= channel order):
+  // within each wave, then over the wave totals
+  const uint32_t incl = wave_incl_scan(ties);
+  if ((tid & 63) == 63) part[tid >> 6] = incl;
   __syncthreads();
   atomicAdd(&s_above, above);
-  // exclusive scan of the tie counts (thread order = channel order)
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < kMaskThreads; ++i) {
-      const uint32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
-  }
+  uint32_t wave_base = 0;
+  for (int w = 0; w < (tid >> 6); ++w) wave_base += part[w];
   __syncthreads();
   const uint32_t take = (uint32_t)n_protect - s_above;  // ties to protect
-  uint32_t tie_rank = part[tid];
+  uint32_t tie_rank = wave_base + incl - ties;
   for (int i = b0; i < b1; ++i) {
     const uint32_t u = __float_as_uint(stats[i]);
     uint8_t m = 0;
@@ -412,6 +469,21 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
 }  // namespace hif4
 
 using namespace hif4;
+
+namespace {
+// Compute units of the current device (cached per device; 256 on MI355X).
+int g_cus[64];
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && g_cus[dev] > 0) return g_cus[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) g_cus[dev] = n;
+  return n;
+}
+}  // namespace
 
 size_t hif4_percentile_ws_bytes(int64_t c) {
   // h1 [c][256] + h2 [c][128] + minkey [c] (u32) + sel [c] (16 B), 256-B aligned parts
@@ -438,32 +510,25 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // Rows per workgroup: enough workgroups to fill the chip (>= ~1024), at
-  // most 65535 rows each (u16 LDS counters in pass 1).
+  // Grid: a whole number of waves of resident workgroups (one per CU), each
+  // taking an equal slice of the (channel block, row) sequence of at most
+  // 65535 rows.
   const int cblocks = (ci + kPctCh - 1) / kPctCh;
-  int64_t splits = (1024 + cblocks - 1) / cblocks;
-  if (splits > rows) splits = rows;
-  int64_t rpb = (rows + splits - 1) / splits;
-  if (rpb > 65535) rpb = 65535;
-  if (rpb < 1) rpb = 1;
-  const int64_t nsplit = (rows + rpb - 1) / rpb;
-  for (int64_t s0 = 0; s0 < nsplit; s0 += 65535) {
-    const int64_t ns = nsplit - s0 < 65535 ? nsplit - s0 : 65535;
-    const int64_t rbase = s0 * rpb;
-    hipLaunchKernelGGL(pct_pass1_kernel, dim3(cblocks, (unsigned)ns), dim3(kPctThreads), 0, stream,
-                       x + rbase * ld, rows - rbase, ci, ld, (int)rpb, h1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  const int64_t total = (int64_t)cblocks * rows;
+  const int64_t resident = (int64_t)cu_count();
+  const int64_t waves = (total + resident * 65535 - 1) / (resident * 65535);
+  const int64_t per_wg = (total + resident * waves - 1) / (resident * waves);
+  const int64_t grid = (total + per_wg - 1) / per_wg;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
+                     rows, ci, ld, per_wg, h1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1, rows, ci, q,
                      sel);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int64_t s0 = 0; s0 < nsplit; s0 += 65535) {
-    const int64_t ns = nsplit - s0 < 65535 ? nsplit - s0 : 65535;
-    const int64_t rbase = s0 * rpb;
-    hipLaunchKernelGGL(pct_pass2_kernel, dim3(cblocks, (unsigned)ns), dim3(kPctThreads), 0, stream,
-                       x + rbase * ld, rows - rbase, ci, ld, (int)rpb, sel, h2, minkey);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(pct_pass2_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
+                     rows, ci, ld, per_wg, sel, h2, minkey);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel, minkey,
                      rows, ci, q, stats);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -200,7 +200,8 @@ HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
  *    each double operation rounded separately.
  *  mask[ch] = 1 for the n_protect largest stats (ties: lower ch first), else 0.
  *
- *  x         bf16 [rows][ld], 16-byte aligned, ld % 8 == 0, ld >= c, rows >= 1.
+ *  x         bf16 [rows][ld], 16-byte aligned, ld % 8 == 0, c <= ld <= 2^22,
+ *            rows >= 1.
  *  c         number of channels, 1 <= c <= 65536.   q in [0, 1].
  *  n_protect 0 <= n_protect <= c (e.g. ceil(p * c) for a top-p mask).
  *  stats     fp32 [c];  mask  u8 [c].

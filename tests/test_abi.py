@@ -157,6 +157,7 @@ def test_percentile_argument_checks(L):
     assert f(A, 0, 256, 256, 0.5, 1, A, A, A, ws, None) == SHAPE
     assert f(A, 100, 256, 256, 0.5, 257, A, A, A, ws, None) == SHAPE
     assert f(A, 100, 256, 200, 0.5, 1, A, A, A, ws, None) == SHAPE
+    assert f(A, 100, 256, (1 << 22) + 8, 0.5, 1, A, A, A, ws, None) == SHAPE  # ld limit
     assert f(A, 100, 256, 256, 1.5, 1, A, A, A, ws, None) == ARG
     assert f(A, 100, 256, 256, float("nan"), 1, A, A, A, ws, None) == ARG
     assert f(A, 100, 256, 256, 0.5, 1, None, A, A, ws, None) == NULL

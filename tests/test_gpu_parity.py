@@ -313,6 +313,18 @@ def test_percentile_constant_and_tied_channels(hip):
     run_pct_case(hip, x, 0.5, 128)
 
 
+def test_percentile_ties_across_many_channels(hip):
+    """Most channels share one statistic: the protected ties are the lowest
+    channel indices, counted across every thread of the mask kernel."""
+    r = np.random.default_rng(57)
+    c = 3000
+    x = np.full((40, c), uc.to_bits([1.5])[0], dtype=np.uint16)
+    x[:, r.choice(c, 9, replace=False)] = uc.to_bits([3.0])[0]   # 9 channels above the tie
+    x[:, r.choice(c, 30, replace=False)] = uc.to_bits([0.5])[0]  # some below it
+    for n in (9, 10, 700, 2500):
+        run_pct_case(hip, x, 0.9, n)
+
+
 def test_percentile_wide_magnitude_range(hip):
     """Values spanning subnormals to huge bf16, and rank boundaries that fall
     exactly at coarse-bin edges."""
