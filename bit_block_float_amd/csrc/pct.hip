@@ -381,22 +381,34 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
 }
 
 // Top-n mask by radix select over the stats' bit patterns (stats are >= 0,
-// so unsigned order = numeric order). One workgroup: four 8-bit digit passes
-// (most significant first) find tau, the n-th largest value; channels above
-// tau are protected, and of the channels equal to tau the lowest-indexed
-// (n - count_above) are protected (ties go to the lower index).
+// so unsigned order = numeric order). One workgroup; thread t keeps the
+// statistics of its contiguous chunk of channels [t * per, (t + 1) * per)
+// (per <= kPer, c <= 1024 kPer) in registers. Four 8-bit digit passes (most significant first) find
+// tau, the n-th largest value; channels above tau are protected, and of the
+// channels equal to tau the lowest-indexed (n - count_above) are protected
+// (ties go to the lower index).
 constexpr int kMaskThreads = 1024;
+
+template <int kPer>
 __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __restrict__ stats,
                                                                  int c, int n_protect,
                                                                  uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_prefix, s_need, s_above;
   __shared__ uint32_t part[kMaskThreads / 64];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   if (n_protect <= 0 || n_protect >= c) {
     const uint8_t v = n_protect <= 0 ? 0 : 1;
     for (int i = tid; i < c; i += kMaskThreads) mask[i] = v;
     return;
+  }
+  const int per = (c + kMaskThreads - 1) / kMaskThreads;  // uniform, <= kPer
+  const int i0 = tid * per;
+  uint32_t u[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = i0 + j;
+    u[j] = (j < per && i < c) ? __float_as_uint(stats[i]) : 0u;
   }
   // rank (0-based, descending) of the element we look for
   if (tid == 0) {
@@ -404,13 +416,16 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
     s_need = (uint32_t)(n_protect - 1);
   }
   uint32_t prefix_mask = 0u;
+#pragma unroll
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
     const uint32_t pre = s_prefix;
-    for (int i = tid; i < c; i += kMaskThreads) {
-      const uint32_t u = __float_as_uint(stats[i]);
-      if ((u & prefix_mask) == pre) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = i0 + j;
+      if (j < per && i < c && (u[j] & prefix_mask) == pre)
+        atomicAdd(&hist[(u[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -419,7 +434,7 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
       const uint32_t need = s_need;
       uint32_t cnt[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - (tid * 4 + i)];
+      for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - (lane * 4 + i)];
       uint32_t pos;
       int64_t before;
       wave_find_rank<4>(cnt, (int64_t)need, &pos, &before);
@@ -432,37 +447,37 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
     __syncthreads();
   }
   const uint32_t tau = s_prefix;
-  // count_above and, per thread chunk, the number of ties (for the index-ordered tie rank)
-  const int chunk = (c + kMaskThreads - 1) / kMaskThreads;
-  const int b0 = min(c, tid * chunk), b1 = min(c, b0 + chunk);
+  // count_above, and the ties of each thread's chunk (thread order = channel
+  // order, so an exclusive scan of the tie counts ranks the ties by index)
   uint32_t above = 0, ties = 0;
-  for (int i = b0; i < b1; ++i) {
-    const uint32_t u = __float_as_uint(stats[i]);
-    above += u > tau;
-    ties += u == tau;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const bool ok = j < per && i0 + j < c;
+    above += (ok && u[j] > tau) ? 1u : 0u;
+    ties += (ok && u[j] == tau) ? 1u : 0u;
   }
   if (tid == 0) s_above = 0u;
-  // exclusive scan of the tie counts in thread order (= channel order):
-  // within each wave, then over the wave totals
   const uint32_t incl = wave_incl_scan(ties);
-  if ((tid & 63) == 63) part[tid >> 6] = incl;
+  if (lane == 63) part[tid >> 6] = incl;
   __syncthreads();
   atomicAdd(&s_above, above);
-  uint32_t wave_base = 0;
-  for (int w = 0; w < (tid >> 6); ++w) wave_base += part[w];
+  uint32_t tie_rank = incl - ties;
+  for (int w = 0; w < (tid >> 6); ++w) tie_rank += part[w];
   __syncthreads();
   const uint32_t take = (uint32_t)n_protect - s_above;  // ties to protect
-  uint32_t tie_rank = wave_base + incl - ties;
-  for (int i = b0; i < b1; ++i) {
-    const uint32_t u = __float_as_uint(stats[i]);
-    uint8_t m = 0;
-    if (u > tau) {
-      m = 1;
-    } else if (u == tau) {
-      m = tie_rank < take ? 1 : 0;
-      ++tie_rank;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = i0 + j;
+    if (j < per && i < c) {
+      uint8_t m = 0;
+      if (u[j] > tau) {
+        m = 1;
+      } else if (u[j] == tau) {
+        m = tie_rank < take ? 1 : 0;
+        ++tie_rank;
+      }
+      mask[i] = m;
     }
-    mask[i] = m;
   }
 }
 
@@ -532,7 +547,11 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
   hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel, minkey,
                      rows, ci, q, stats);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topn_mask_kernel, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,
-                     (int)n_protect, mask);
+  if (ci <= 8 * kMaskThreads)
+    hipLaunchKernelGGL(topn_mask_kernel<8>, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,
+                       (int)n_protect, mask);
+  else
+    hipLaunchKernelGGL(topn_mask_kernel<64>, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,
+                       (int)n_protect, mask);
   return hipGetLastError();
 }

@@ -296,7 +296,8 @@ def test_percentile_tiny_workload(hip):
 
 @pytest.mark.parametrize("rows,c,q,n", [(1, 64, 0.99, 3), (2, 128, 0.5, 0), (1000, 200, 0.999, 2),
                                         (777, 77, 0.0, 77), (4096, 384, 1.0, 10),
-                                        (5000, 256, 0.75, 13)])
+                                        (5000, 256, 0.75, 13), (50, 9000, 0.9, 90),
+                                        (3, 65536, 0.5, 655)])
 def test_percentile_ragged(hip, rows, c, q, n):
     bits = workloads.bits(workloads.heavy_tailed_x(rows, c, seed=rows + c, outlier_channels=2))
     ld = ((c + 7) // 8) * 8 if c % 8 else None
