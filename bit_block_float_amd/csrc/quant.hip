@@ -1,6 +1,6 @@
-// quant.hip -- HiF4 quantize (bf16 -> codes + meta), its fake-quant variant
-// (bf16 -> bf16 on the HiF4 grid), the protected-channel gather, and the
-// dequantize kernel. All are HBM-streaming kernels for gfx950.
+// quant.hip -- HiF4 quantize (bf16 -> codes + meta, optionally with
+// protected channels), and the dequantize kernel. HBM-streaming kernels for
+// gfx950.
 //
 // Format: HiFloat4 calibration article (hwcomputing.csdn.net), section
 // "一：HiFloat4 (HiF4) 格式". Exponent order and per-group statistics: same
@@ -13,8 +13,12 @@
 // maximum and the metadata word are formed with DPP moves inside the quad.
 // Each lane emits two 32-bit code words (a level-2 group each, its two
 // level-3 groups as low/high nibbles), so a wave writes 512 contiguous code
-// bytes and 64 contiguous meta bytes. The element rounding runs in fp32 with
-// a two-term reciprocal (inv_mant_hi/lo) that makes it exact.
+// bytes and 64 contiguous meta bytes. Maxima, thresholds and the element
+// rounding run on packed 16-bit pairs (bit-pattern maxima, an exact fp16
+// quotient; see kpair): the kernel would otherwise be bound by its VALU work
+// rather than by HBM.
+#include <algorithm>
+
 #include "hif4_dev.h"
 
 namespace hif4 {
@@ -49,40 +53,94 @@ __device__ __forceinline__ uint32_t or4_u32(uint32_t v) {
   return v;
 }
 
+// ---- packed 16-bit element arithmetic
+//
+// The element step works on two bf16 values per 32-bit word with packed
+// 16-bit instructions. For a level-3 quad with exponent sum E under a unit of
+// code c (e = c >> 2, m = c & 3), the S1P2 magnitude is k = min(RNE(t), 7)
+// with t = 4|x| / D = y * 4/(4+m), y = |x| 2^(33-e-E). Below range
+// saturation every y lies under 7 * 1.75 (the level-3 rule bounds the quad
+// maximum by 1.75 s 2^E), and any y of 16 or more gives k = 7, so y capped
+// at 16 is an fp16 number: its bf16 bits become fp16 bits by one saturating
+// subtract of ((e + E + 79) << 7) (exponent rebias and 2^(33-e-E) together;
+// values too small for an fp16 normal saturate to 0 or land among the fp16
+// subnormals, all of which round to k = 0) and a shift left by 3. Then
+// t = fma(y, hi, y lo) in fp16, with hi = RN16(4/(4+m)) and
+// lo = RN16(4/(4+m) - hi): within 2^-19 of the real quotient, while a
+// non-tie quotient is at least 9 fp16 half-ulps from the nearest half-integer
+// and a tie is an fp16 number, so t rounds on the same side as the real
+// quotient and ties come out exact. Adding 1024 (fp16 spacing 1 there)
+// rounds to nearest even; min(., 1031) saturates k at 7 and leaves k in the
+// low byte of each half. (Checked on the CPU for every bf16 y below 14 and
+// every m, and by the element-rounding parity tests.)
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t kpair(uint32_t absw, uint32_t csub, uint32_t hi2,
+                                          uint32_t lo2) {
+  u16x2_t y = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, absw),
+                                            __builtin_bit_cast(u16x2_t, csub));
+  // range saturation (c = 255 below a unit maximum above 7 v(255)) lets y
+  // exceed the fp16 range: cap it at 16 (pattern 0x0980 before the shift),
+  // which still rounds to k = 7
+  y = __builtin_elementwise_min(y, (u16x2_t)(0x0980));
+  y = y << (u16x2_t)(3);
+  const f16x2_t yf = __builtin_bit_cast(f16x2_t, y);
+  const f16x2_t pl = yf * __builtin_bit_cast(f16x2_t, lo2);
+  f16x2_t t = __builtin_elementwise_fma(yf, __builtin_bit_cast(f16x2_t, hi2), pl);
+  t = t + (f16x2_t)((_Float16)1024.0f);
+  t = __builtin_elementwise_min(t, (f16x2_t)((_Float16)1031.0f));
+  return __builtin_bit_cast(uint32_t, t);  // k in bytes 0 and 2
+}
+
+// Larger of the two u16 halves.
+__device__ __forceinline__ uint32_t hmax_u16(uint32_t v) { return max(v & 0xFFFFu, v >> 16); }
+// Per-half maximum of two words of u16 halves.
+__device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+
+// RN16(4/(4+m)) and the fp16 remainder, both halves.
+__device__ __forceinline__ uint32_t kinv_hi2(uint32_t m) {
+  return select4(m, 0x3C003C00u, 0x3A663A66u, 0x39553955u, 0x38923892u);
+}
+__device__ __forceinline__ uint32_t kinv_lo2(uint32_t m) {
+  return select4(m, 0x00000000u, 0x0A660A66u, 0x09550955u, 0x08920892u);
+}
+
+// Level-3 quad maxima of a level-2 group, as |x| bf16 bits: `a` = the group's
+// 4 words with the sign bits cleared.
+struct QuadMax {
+  uint32_t a, b;
+};
+__device__ __forceinline__ QuadMax quad_max(uint4 a) {
+  return QuadMax{hmax_u16(pkmax_u16(a.x, a.y)), hmax_u16(pkmax_u16(a.z, a.w))};
+}
+
 // One level-2 group (8 elements, one code word): steps 3-5 given the unit's
-// level-1 scale. w: the group's 8 bf16 values (element 2i in the low half of
-// word i). Returns the code word; e2 and e3 bits by reference.
-__device__ __forceinline__ uint32_t encode_group(uint4 w, float s, int p, float rh, float rl,
-                                                 uint32_t& e2, uint32_t& e3a, uint32_t& e3b) {
-  const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y),
-                      bf16hi_to_f32(w.y), bf16lo_to_f32(w.z), bf16hi_to_f32(w.z),
-                      bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
-  const float m4a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  const float m4b = fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7])));
-  // steps 3-4: level-2 / level-3 bits (exact compares)
-  e2 = fmaxf(m4a, m4b) > 3.5f * s;
-  const float t3 = (e2 ? 3.5f : 1.75f) * s;
-  e3a = m4a > t3;
-  e3b = m4b > t3;
-  // step 5: k = RNE(4|x| / D), D = s 2^E, 4/D = (16/(4+m)) 2^(31-e-E) (inv_mant_hi)
-  const int pa = p - (int)(e2 + e3a), pb = p - (int)(e2 + e3b);
-  const float rha = ldexpf(rh, pa), rla = ldexpf(rl, pa);
-  const float rhb = ldexpf(rh, pb), rlb = ldexpf(rl, pb);
-  float kf[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float ax = fabsf(v[i]);
-    const float t = i < 4 ? fmaf(ax, rha, ax * rla) : fmaf(ax, rhb, ax * rlb);
-    kf[i] = fminf(rintf(t), 7.0f);
-  }
+// level-1 code. w: the group's 8 bf16 values (element 2i in the low half of
+// word i), a: the same with the sign bits cleared, qm: its quad maxima;
+// thr2 / thr175: bf16 bits of 3.5 s and 1.75 s (exact: s has at most three
+// significant bits). Returns the code word; e2 and e3 bits by reference.
+__device__ __forceinline__ uint32_t encode_group(uint4 w, uint4 a, QuadMax qm, uint32_t e,
+                                                 uint32_t hi2, uint32_t lo2, uint32_t thr2,
+                                                 uint32_t thr175, uint32_t& e2, uint32_t& e3a,
+                                                 uint32_t& e3b) {
+  // steps 3-4: level-2 / level-3 bits (exact compares of bf16 bit patterns)
+  e2 = max(qm.a, qm.b) > thr2;
+  const uint32_t t3 = e2 ? thr2 : thr175;
+  e3a = qm.a > t3;
+  e3b = qm.b > t3;
+  // step 5: k = RNE(4|x| / D), two elements per packed operation
+  const uint32_t ca = ((e + e2 + e3a + 79u) << 7) * 0x00010001u;
+  const uint32_t cb = ((e + e2 + e3b + 79u) << 7) * 0x00010001u;
+  const uint32_t k01 = kpair(a.x, ca, hi2, lo2), k23 = kpair(a.y, ca, hi2, lo2);
+  const uint32_t k45 = kpair(a.z, cb, hi2, lo2), k67 = kpair(a.w, cb, hi2, lo2);
   // magnitudes: element b of the low level-3 group -> low nibble of byte b,
   // element 4+b -> high nibble of byte b
-  uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    lo = __builtin_amdgcn_cvt_pk_u8_f32(kf[b], b, lo);
-    hi = __builtin_amdgcn_cvt_pk_u8_f32(kf[4 + b], b, hi);
-  }
+  const uint32_t lo = __builtin_amdgcn_perm(k23, k01, 0x06040200u);
+  const uint32_t hi = __builtin_amdgcn_perm(k67, k45, 0x06040200u);
   const uint32_t mag = lo | (hi << 4);
   // signs: the high byte of each bf16 carries its sign in bit 7
   const uint32_t sl = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);  // elements 0..3
@@ -99,121 +157,211 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
   return ((hi >> 7) | (hi >> 14) | (hi >> 21) | (hi >> 28)) & 0xFu;
 }
 
-constexpr int kMaxMaskChunks = 65536 / 16;  // masked rows are at most 65536 wide
-
-// Work mapping: one lane owns two level-2 groups (16 consecutive elements,
-// two 16-byte loads), 4 aligned lanes own a unit; unit maximum and metadata
-// word via DPP inside the quad. A wave covers 16 units.
-//
-// kMask: protected channels become +0 in the HiF4 stream and their bf16
-// values go to kept[row][rank], rank = the channel's position among the
-// masked channels. Each workgroup first builds the rank of every 16-channel
-// chunk of the mask in LDS (a prefix count), so the lanes that meet masked
-// channels store their values directly: no second pass over X.
+// One 16-element item (two level-2 groups, words w0 and w1) of row `row`:
+// item j of the row, it = its index over all rows (code words 2it, 2it+1;
+// the unit's meta word it/4, written by the quad's first lane). Steps 1-5 of
+// the rule. kMask: `info` = the 16 mask bits of the item's channels (high
+// half) and the rank of its first masked channel among all masked channels
+// (low half), z0/z1 = the words' keep masks (0 on masked halves): masked
+// channels are quantized as +0 and do not enter the maxima, and their bf16
+// values go to kept[row][rank] once the item's codes are out (the data are
+// in registers by then, so no load wait is needed for that rare branch).
 template <bool kMask>
+__device__ __forceinline__ void quantize_item(uint4 w0, uint4 w1, uint4 z0, uint4 z1,
+                                              uint32_t info, uint32_t row, uint32_t j,
+                                              uint32_t it, uint32_t* __restrict__ codes32,
+                                              uint32_t* __restrict__ meta,
+                                              uint16_t* __restrict__ kept, int n_mask) {
+  const uint32_t q = j & 3u;  // item within the unit (groups 2q, 2q+1)
+  const uint4 v0 = kMask ? make_uint4(w0.x & z0.x, w0.y & z0.y, w0.z & z0.z, w0.w & z0.w) : w0;
+  const uint4 v1 = kMask ? make_uint4(w1.x & z1.x, w1.y & z1.y, w1.z & z1.z, w1.w & z1.w) : w1;
+
+  // step 1: level-3 / level-2 maxima of |x| as bf16 bit patterns (sign bits
+  // dropped; monotone in |x|), then the unit maximum over the quad of lanes
+  const uint4 a0 = make_uint4(v0.x & 0x7FFF7FFFu, v0.y & 0x7FFF7FFFu, v0.z & 0x7FFF7FFFu,
+                              v0.w & 0x7FFF7FFFu);
+  const uint4 a1 = make_uint4(v1.x & 0x7FFF7FFFu, v1.y & 0x7FFF7FFFu, v1.z & 0x7FFF7FFFu,
+                              v1.w & 0x7FFF7FFFu);
+  const QuadMax q0 = quad_max(a0), q1 = quad_max(a1);
+  const uint32_t am = max(max(q0.a, q0.b), max(q1.a, q1.b));
+  const float amax = __uint_as_float(max4_u32(am) << 16);
+
+  // step 2: level-1 code (shared by the quad)
+  const uint32_t c = level1_code(amax);
+  const float s = e6m2_f32(c);
+  const uint32_t thr2 = __float_as_uint(3.5f * s) >> 16;
+  const uint32_t thr175 = __float_as_uint(1.75f * s) >> 16;
+  const uint32_t hi2 = kinv_hi2(c & 3u), lo2 = kinv_lo2(c & 3u);
+
+  uint32_t e2a, e3a0, e3b0, e2b, e3a1, e3b1;
+  const uint32_t cw0 = encode_group(v0, a0, q0, c >> 2, hi2, lo2, thr2, thr175, e2a, e3a0, e3b0);
+  const uint32_t cw1 = encode_group(v1, a1, q1, c >> 2, hi2, lo2, thr2, thr175, e2b, e3a1, e3b1);
+
+  reinterpret_cast<uint2*>(codes32)[it] = make_uint2(cw0, cw1);
+  const uint32_t g0 = 2 * q, g1 = 2 * q + 1;
+  const uint32_t mb = (e2a << (8 + g0)) | (e2b << (8 + g1)) | (e3a0 << (16 + 2 * g0)) |
+                      (e3b0 << (17 + 2 * g0)) | (e3a1 << (16 + 2 * g1)) |
+                      (e3b1 << (17 + 2 * g1));
+  const uint32_t mw = or4_u32(mb) | c;
+  if (q == 0u) meta[it >> 2] = mw;
+
+  if (kMask) {
+    const uint32_t m16 = info >> 16;
+    if (m16) {  // rare: only lanes whose channels include masked ones
+      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      uint32_t mm = m16;
+      while (mm) {
+        const uint32_t e = __ffs(mm) - 1;
+        const uint32_t rank = (info & 0xFFFFu) + __popc(m16 & ((1u << e) - 1u));
+        if (rank < (uint32_t)n_mask)
+          kept[(int64_t)row * n_mask + rank] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+        mm &= mm - 1;
+      }
+    }
+  }
+}
+
+// Unmasked quantize. Work mapping: one lane owns one item (16 consecutive
+// elements, two 16-byte loads), 4 aligned lanes own a unit; unit maximum and
+// metadata word via DPP inside the quad. A wave covers 16 units.
 __global__ __launch_bounds__(256) void quantize_kernel(
     const uint16_t* __restrict__ x, int64_t ld, uint32_t items_per_row, FastDiv item_div,
-    uint32_t total_items, const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta, uint16_t* __restrict__ kept, int n_mask) {
-  // per 16-channel chunk: rank of its first masked channel (low 16 bits) and
-  // its 16 mask bits (high 16 bits)
-  __shared__ uint32_t chunk_info[kMask ? kMaxMaskChunks : 1];
-  __shared__ uint32_t part[kMask ? 256 : 1];
-  if (kMask) {
-    // chunks t*per .. t*per+per-1 belong to thread t
-    const int chunks = (int)items_per_row, tid = threadIdx.x;
-    const int per = (chunks + 255) / 256;
-    const int c0 = min(chunks, tid * per), c1 = min(chunks, c0 + per);
-    uint32_t run = 0;
-    for (int c = c0; c < c1; ++c) {
-      const uint4 mk = *reinterpret_cast<const uint4*>(mask + (size_t)c * 16);
-      const uint32_t m16 = nonzero_bytes(mk.x) | (nonzero_bytes(mk.y) << 4) |
-                           (nonzero_bytes(mk.z) << 8) | (nonzero_bytes(mk.w) << 12);
-      chunk_info[c] = m16 << 16;
-      run += __popc(m16);
-    }
-    part[tid] = run;
-    __syncthreads();
-    if (tid == 0) {  // exclusive prefix over the 256 thread totals
-      uint32_t acc = 0;
-      for (int i = 0; i < 256; ++i) {
-        const uint32_t v = part[i];
-        part[i] = acc;
-        acc += v;
-      }
-    }
-    __syncthreads();
-    run = part[tid];
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t m16 = chunk_info[c] >> 16;
-      chunk_info[c] |= run & 0xFFFFu;
-      run += __popc(m16);
-    }
-    __syncthreads();
-  }
+    uint32_t total_items, uint32_t* __restrict__ codes32, uint32_t* __restrict__ meta) {
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t it = blockIdx.x * blockDim.x + threadIdx.x; it < total_items; it += stride) {
+  // two register buffers: the loads of item it + stride go out before item
+  // it is encoded, into the buffer that is not being read. Past the end the
+  // last item is read again (never encoded): the loads are unconditional, so
+  // the compiler can wait for one buffer while the other is in flight.
+  auto load = [&](uint4& v0, uint4& v1, uint32_t it) {
+    it = min(it, total_items - 1u);
     const uint32_t row = fdiv(it, item_div);
-    const uint32_t j = it - row * items_per_row;  // 16-element item within the row
-    const uint32_t q = j & 3u;                    // item within the unit (groups 2q, 2q+1)
-
+    const uint32_t j = it - row * items_per_row;
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)row * ld + (int64_t)j * 16);
-    uint4 w0 = src[0], w1 = src[1];
-    if (kMask) {
-      // Protected channels are quantized as +0 and do not enter the maxima;
-      // their values go to kept (rare: only lanes whose chunk has any).
-      const uint32_t info = chunk_info[j];
-      const uint32_t m16 = info >> 16;
-      if (m16) {
-        uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        uint32_t mm = m16;
-        while (mm) {
-          const uint32_t e = __ffs(mm) - 1;
-          const uint32_t rank = (info & 0xFFFFu) + __popc(m16 & ((1u << e) - 1u));
-          if (rank < (uint32_t)n_mask)
-            kept[(int64_t)row * n_mask + rank] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
-          mm &= mm - 1;
-        }
+    v0 = src[0];
+    v1 = src[1];
+  };
+  auto encode = [&](uint4 v0, uint4 v1, uint32_t it) {
+    const uint32_t row = fdiv(it, item_div);
+    const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
+    quantize_item<false>(v0, v1, ones, ones, 0u, row, it - row * items_per_row, it, codes32, meta,
+                         nullptr, 0);
+  };
+  uint32_t it = blockIdx.x * blockDim.x + threadIdx.x;
+  uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+  load(a0, a1, it);
+  while (it < total_items) {
+    load(b0, b1, it + stride);
+    encode(a0, a1, it);
+    it += stride;
+    if (it >= total_items) break;
+    load(a0, a1, it + stride);
+    encode(b0, b1, it);
+    it += stride;
+  }
+}
+
+// Masked quantize, row-mapped. A workgroup of B threads (a multiple of 64)
+// covers a row in kRounds rounds: thread t owns items t, t + B, ... of every
+// row it visits, so the rank/mask word of its items is computed once, in
+// registers, by a workgroup prefix count over the mask before the row loop:
+// the loop itself has no table lookup. Workgroup g visits rows g, g + G, ...
+template <int kRounds>
+__global__ __launch_bounds__(1024) void quantize_masked_kernel(
+    const uint16_t* __restrict__ x, int64_t ld, uint32_t rows, uint32_t items_per_row,
+    const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
+    uint32_t* __restrict__ meta, uint16_t* __restrict__ kept, int n_mask) {
+  __shared__ uint32_t part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const uint32_t B = blockDim.x;
+  // (loads past the last row or item read the last one again, unconditionally)
+  auto load = [&](uint4& v0, uint4& v1, uint32_t row, int r) {
+    const uint32_t j = min(tid + r * B, items_per_row - 1u);
+    row = min(row, rows - 1u);
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)row * ld + (int64_t)j * 16);
+    v0 = src[0];
+    v1 = src[1];
+  };
+  // The mask words go out first, then the first item's loads, so that the
+  // prologue below waits for the mask only while the item is in flight
+  // (both loads unconditional: clamped indexes, out-of-range items masked
+  // off afterwards).
+  uint4 mk[kRounds];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t lo = (m16 >> (2 * i)) & 1u, hi = (m16 >> (2 * i + 1)) & 1u;
-          ww[i] &= ~((lo * 0x0000FFFFu) | (hi * 0xFFFF0000u));
-        }
-        w0 = make_uint4(ww[0], ww[1], ww[2], ww[3]);
-        w1 = make_uint4(ww[4], ww[5], ww[6], ww[7]);
-      }
-    }
-
-    // step 1: unit maximum of |x|, compared as bit patterns of non-negative
-    // floats (sign bits dropped), over the lane's 16 values, then the quad
-    uint32_t am = 0u;
-    {
-      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  for (int r = 0; r < kRounds; ++r)
+    mk[r] = *reinterpret_cast<const uint4*>(mask +
+                                            (size_t)min(tid + r * B, items_per_row - 1u) * 16);
+  uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+  load(a0, a1, blockIdx.x, 0);
+  uint32_t info[kRounds];
+  uint4 zk0[kRounds], zk1[kRounds];  // keep masks of the item's words
+  uint32_t run = 0;  // masked channels in the rounds before the current one
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        am = max(am, (ww[i] << 16) & 0x7FFFFFFFu);
-        am = max(am, ww[i] & 0x7FFF0000u);
-      }
+  for (int r = 0; r < kRounds; ++r) {
+    const uint32_t j = tid + r * B;
+    uint32_t m16 = nonzero_bytes(mk[r].x) | (nonzero_bytes(mk[r].y) << 4) |
+                   (nonzero_bytes(mk[r].z) << 8) | (nonzero_bytes(mk[r].w) << 12);
+    if (j >= items_per_row) m16 = 0;
+    // exclusive prefix of the popcounts over the round's items (thread order)
+    const uint32_t cnt = __popc(m16);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)incl, d, 64);
+      if (lane >= d) incl += o;
     }
-    const float amax = __uint_as_float(max4_u32(am));
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    uint32_t base = run + incl - cnt, total = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const uint32_t pw = part[w];
+      if (w < wave) base += pw;
+      total += pw;
+    }
+    __syncthreads();
+    info[r] = (m16 << 16) | (base & 0xFFFFu);
+    run += total;
+    uint32_t z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = (m16 >> (2 * i)) & 1u, hi = (m16 >> (2 * i + 1)) & 1u;
+      z[i] = ~((lo * 0x0000FFFFu) | (hi * 0xFFFF0000u));
+    }
+    zk0[r] = make_uint4(z[0], z[1], z[2], z[3]);
+    zk1[r] = make_uint4(z[4], z[5], z[6], z[7]);
+  }
 
-    // step 2: level-1 code (shared by the quad)
-    const uint32_t c = level1_code(amax);
-    const float s = e6m2_f32(c);
-    const int p = 31 - (int)(c >> 2);
-    const float rh = inv_mant_hi(c & 3u), rl = inv_mant_lo(c & 3u);
-
-    uint32_t e2a, e3a0, e3b0, e2b, e3a1, e3b1;
-    const uint32_t cw0 = encode_group(w0, s, p, rh, rl, e2a, e3a0, e3b0);
-    const uint32_t cw1 = encode_group(w1, s, p, rh, rl, e2b, e3a1, e3b1);
-
-    reinterpret_cast<uint2*>(codes32)[it] = make_uint2(cw0, cw1);
-    const uint32_t g0 = 2 * q, g1 = 2 * q + 1;
-    const uint32_t mb = (e2a << (8 + g0)) | (e2b << (8 + g1)) | (e3a0 << (16 + 2 * g0)) |
-                        (e3b0 << (17 + 2 * g0)) | (e3a1 << (16 + 2 * g1)) |
-                        (e3b1 << (17 + 2 * g1));
-    const uint32_t mw = or4_u32(mb) | c;
-    if (q == 0u) meta[it >> 2] = mw;
+  // items in the order (row, round); the next item's loads go out before the
+  // current one is encoded, into the register buffer that is not being read
+  auto encode = [&](uint4 v0, uint4 v1, uint32_t row, int r) {
+    const uint32_t j = tid + r * B;
+    if (j < items_per_row)
+      quantize_item<true>(v0, v1, zk0[r], zk1[r], info[r], row, j, row * items_per_row + j, codes32,
+                          meta, kept, n_mask);
+  };
+  // (row, round) after (row, r)
+  auto next = [&](uint32_t& row, int& r) {
+    if (++r == kRounds) {
+      r = 0;
+      row += gridDim.x;
+    }
+  };
+  uint32_t row = blockIdx.x;
+  int r = 0;
+  while (row < rows) {
+    uint32_t row2 = row;
+    int r2 = r;
+    next(row2, r2);
+    load(b0, b1, row2, r2);
+    encode(a0, a1, row, r);
+    row = row2;
+    r = r2;
+    if (row >= rows) break;
+    next(row2, r2);
+    load(a0, a1, row2, r2);
+    encode(b0, b1, row, r);
+    row = row2;
+    r = r2;
   }
 }
 
@@ -257,9 +405,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t* __restr
   }
 }
 
-static unsigned grid_for(uint64_t threads) {
+// Blocks for a grid-stride launch over `threads` work items, at most `cap`.
+// Far more blocks than fit at once (2048 of 256 threads on 256 CUs): as
+// blocks retire, new ones land on whichever CUs are ahead, which balances
+// CUs and XCDs that stream at different rates (measured on the FFN-up
+// activation: 2048 blocks 175 us, 16384 blocks 143 us, 32768 blocks 139 us).
+static unsigned grid_for(uint64_t threads, uint64_t cap = 256ull * 128) {
   const uint64_t blocks = (threads + 255) / 256;
-  const uint64_t cap = 256ull * 64;  // enough blocks to fill 256 CUs many times over
   return (unsigned)(blocks < cap ? (blocks ? blocks : 1) : cap);
 }
 
@@ -281,16 +433,39 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
     const uint16_t* xs = x + r0 * ld;
     uint32_t* cs = reinterpret_cast<uint32_t*>(codes + r0 * (k / 2));
     uint32_t* ms = meta + r0 * (k / 64);
-    const dim3 block(256);
     if (mask) {
-      // fewer, longer-lived workgroups: each builds the mask's rank table once
-      const unsigned g = grid_for(total);
-      const dim3 grid(g < 256u * 8u ? g : 256u * 8u);
-      hipLaunchKernelGGL(quantize_kernel<true>, grid, block, 0, stream, xs, ld, gpr, fd, total,
-                         mask, cs, ms, kept ? kept + r0 * n_mask : nullptr, (int)n_mask);
+      // one round per 1024 items of a row; B = the round's items rounded up to
+      // a whole wave; enough workgroups to fill the chip several times
+      const int rounds = (int)((gpr + 1023) / 1024);
+      const uint32_t per = (gpr + rounds - 1) / rounds;
+      const dim3 block((per + 63) / 64 * 64);
+      // at least ~4 rows per workgroup (the mask prologue is paid per
+      // workgroup), at most 48 workgroups per CU
+      const int64_t want = std::min<int64_t>(256 * 48, (nr + 3) / 4);
+      const dim3 grid((unsigned)std::max<int64_t>(1, want));
+      uint16_t* ks = kept ? kept + r0 * n_mask : nullptr;
+      const uint32_t nrow = (uint32_t)nr;
+      switch (rounds) {
+        case 1:
+          hipLaunchKernelGGL(quantize_masked_kernel<1>, grid, block, 0, stream, xs, ld, nrow, gpr,
+                             mask, cs, ms, ks, (int)n_mask);
+          break;
+        case 2:
+          hipLaunchKernelGGL(quantize_masked_kernel<2>, grid, block, 0, stream, xs, ld, nrow, gpr,
+                             mask, cs, ms, ks, (int)n_mask);
+          break;
+        case 3:
+          hipLaunchKernelGGL(quantize_masked_kernel<3>, grid, block, 0, stream, xs, ld, nrow, gpr,
+                             mask, cs, ms, ks, (int)n_mask);
+          break;
+        default:
+          hipLaunchKernelGGL(quantize_masked_kernel<4>, grid, block, 0, stream, xs, ld, nrow, gpr,
+                             mask, cs, ms, ks, (int)n_mask);
+          break;
+      }
     } else {
-      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(total)), block, 0, stream, xs, ld,
-                         gpr, fd, total, mask, cs, ms, nullptr, 0);
+      hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total)), dim3(256), 0, stream, xs, ld,
+                         gpr, fd, total, cs, ms);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

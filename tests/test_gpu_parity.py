@@ -103,6 +103,18 @@ def test_quantize_with_mask_and_kept(hip):
         assert_same_quant(hip, bits, mask)
 
 
+@pytest.mark.parametrize("rows,k,n", [(3, 13824, 52), (5, 16448, 300), (2, 40960, 9),
+                                      (2, 65536, 655), (4, 1024, 1024)])
+def test_quantize_with_mask_wide_rows(hip, rows, k, n):
+    """Masked rows of 1 to 4 rounds of the row-mapped masked kernel, with idle
+    lanes in the last wave (k / 16 not a multiple of 64), and a fully masked row."""
+    bits = uc.random_bits(rows * k // 64, seed=k + n).reshape(rows, k)
+    r = np.random.default_rng(k)
+    mask = np.zeros(k, np.uint8)
+    mask[r.choice(k, size=n, replace=False)] = 1
+    assert_same_quant(hip, bits, mask)
+
+
 def test_quantize_deterministic(hip):
     bits = uc.random_bits(2048, seed=13).reshape(256, 512)
     a = gpu_quantize(hip, bits)
