@@ -34,6 +34,7 @@ namespace hif4 {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 256, kBN = 256;
@@ -515,22 +516,63 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
     }
   }
 
-  const int col_in = lane & 31, row_in = (lane >> 5) * 4;
+  // Epilogue. In the 32x32 MFMA output a lane holds one column and, per
+  // group g of 4 accumulator registers, 4 consecutive rows. A 4x4 transpose
+  // across each aligned quad of lanes (two DPP exchange steps) gives every
+  // lane 4 consecutive columns of one row instead, stored as one 16-byte
+  // (fp32) or 8-byte (bf16) write: a quarter of the store instructions of
+  // element-wise stores, each row segment written whole. Rows are
+  // 16-byte aligned when ldy % 4 == 0 (and Y is); otherwise, and for a
+  // column group that crosses N, the values go out one by one.
+  const int col_in = lane & 31, row_in = (lane >> 5) * 4, qt = lane & 3;
+  const bool q_odd = (qt & 1) != 0, q_hi = (qt & 2) != 0;
+  const bool vec_ok = (ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + col_in;
-      if (col >= N) continue;
+      const int colq = n0 + wn * 128 + j * 32 + (col_in & ~3);  // the quad's first column
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
-        if (row < M) {
-          if (y_bf16)
-            reinterpret_cast<uint16_t*>(Y)[(size_t)row * ldy + col] =
-                (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-          else
-            reinterpret_cast<float*>(Y)[(size_t)row * ldy + col] = acc[i][j][r];
+      for (int g = 0; g < 4; ++g) {
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        // step 1 (lanes t, t^1): c[t][k] = a[t^1][k^1] where bit 0 of k and t differ
+        const float x0 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v1)));
+        const float x1 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v0)));
+        const float x2 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v3)));
+        const float x3 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v2)));
+        const float c0 = q_odd ? x0 : v0, c1 = q_odd ? v1 : x1;
+        const float c2 = q_odd ? x2 : v2, c3 = q_odd ? v3 : x3;
+        // step 2 (lanes t, t^2): d[t][k] = c[t^2][k^2] where bit 1 of k and t differ
+        const float y0 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c2)));
+        const float y1 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c3)));
+        const float y2 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c0)));
+        const float y3 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c1)));
+        const float d0 = q_hi ? y0 : c0, d1 = q_hi ? y1 : c1;
+        const float d2 = q_hi ? c2 : y2, d3 = q_hi ? c3 : y3;
+        // lane t of the quad: row (group row + t), columns colq .. colq + 3
+        const int row = m0 + wm * 128 + i * 32 + 8 * g + row_in + qt;
+        if (row >= M || colq >= N) continue;
+        const size_t off = (size_t)row * ldy + colq;
+        if (vec_ok && colq + 4 <= N) {
+          if (y_bf16) {
+            const uint32_t lo = f32_to_bf16_rne(d0) | (f32_to_bf16_rne(d1) << 16);
+            const uint32_t hi = f32_to_bf16_rne(d2) | (f32_to_bf16_rne(d3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Y) + off) =
+                f32x4_t{d0, d1, d2, d3};
+          }
+        } else {
+          const float d[4] = {d0, d1, d2, d3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (colq + e >= N) break;
+            if (y_bf16)
+              reinterpret_cast<uint16_t*>(Y)[off + e] = (uint16_t)f32_to_bf16_rne(d[e]);
+            else
+              reinterpret_cast<float*>(Y)[off + e] = d[e];
+          }
         }
       }
     }
