@@ -39,6 +39,10 @@ def _lib():
         lib.hif4o_percentile.restype = ctypes.c_int
         lib.hif4o_topn_mask.argtypes = [p, i64, i64, p]
         lib.hif4o_topn_mask.restype = ctypes.c_int
+        lib.hif4o_quantize_f32.argtypes = [p, i64, i64, i64, p, p]
+        lib.hif4o_quantize_f32.restype = ctypes.c_int
+        lib.hif4o_higptq_unit.argtypes = [p, i64, i64, p, i64, p, p]
+        lib.hif4o_higptq_unit.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -170,3 +174,42 @@ def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     """Exact float32 values of bf16 bit patterns (a plain bit move)."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_f32(x: np.ndarray):
+    """HiF4-quantize rows of float32 values [rows][k] along k (same rule as
+    ``quantize``, on the exact values of the floats). Returns (codes, meta)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, k = x.shape
+    codes = np.zeros((rows, k // 2), np.uint8)
+    meta = np.zeros((rows, k // 64), np.uint32)
+    _check(_lib().hif4o_quantize_f32(_ptr(x), rows, k, k, _ptr(codes), _ptr(meta)),
+           "quantize_f32")
+    return codes, meta
+
+
+def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta: np.ndarray):
+    """One HiGPTQ scheme-1 step in place (see hif4_oracle.c): quantize group
+    ``unit`` of the working weights ``w`` (float64 [n][k], C-contiguous) and
+    compensate the later columns with the upper factor ``u`` (H^-1 = u^T u)."""
+    n, k = w.shape
+    if w.dtype != np.float64 or not w.flags.c_contiguous:
+        raise OracleError("higptq_unit: w must be C-contiguous float64")
+    uu = np.ascontiguousarray(u, dtype=np.float64)
+    _shape(uu, (k, k), "higptq_unit u")
+    _shape(codes, (n, k // 2), "higptq_unit codes")
+    _shape(meta, (n, k // 64), "higptq_unit meta")
+    _check(_lib().hif4o_higptq_unit(_ptr(w), n, k, _ptr(uu), int(unit), _ptr(codes), _ptr(meta)),
+           "higptq_unit")
+
+
+def higptq(w: np.ndarray, u: np.ndarray):
+    """HiGPTQ scheme 1 over every group of ``w`` [n][k] (any float dtype):
+    returns (codes, meta, final working weights as float64)."""
+    ww = np.array(w, dtype=np.float64, order="C")
+    n, k = ww.shape
+    codes = np.zeros((n, k // 2), np.uint8)
+    meta = np.zeros((n, k // 64), np.uint32)
+    for unit in range(k // 64):
+        higptq_unit(ww, u, unit, codes, meta)
+    return codes, meta, ww

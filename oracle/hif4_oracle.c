@@ -22,6 +22,9 @@
  *              of the activations build a channel-protection mask.
  *  [TA-abs]    arXiv 2605.26628 record, abstract: W4A4 HiFloat4 fake
  *              quantization of the main linear layers.
+ *  GPTQ        Frantar et al., "GPTQ: Accurate Post-Training Quantization
+ *              for Generative Pre-trained Transformers" (2022): the
+ *              published error-compensation update HiGPTQ adapts.
  *
  * The element formula of [HiF4-fmt] is an image that did not survive; the
  * readings this file takes where the pages are silent are marked READING.
@@ -369,4 +372,87 @@ int hif4o_topn_mask(const float *stats, int64_t c, int64_t n_protect, uint8_t *m
     for (int64_t i = 0; i < n_protect; ++i) mask[idx[i]] = 1;
     free(idx);
     return HIF4O_OK;
+}
+
+/* -------------------------------------------------------------- HiGPTQ */
+
+/* fp32 rows [rows][ld] -> codes [rows][k/2], meta [rows][k/64]: the same
+ * encoding rule as hif4o_quantize, applied to the exact values of floats
+ * (HiGPTQ's working weights are real numbers, not bf16). */
+int hif4o_quantize_f32(const float *x, int64_t rows, int64_t k, int64_t ld, uint8_t *codes,
+                       uint32_t *meta)
+{
+    if (rows < 0 || k < 0 || k % UNIT != 0 || ld < k) return HIF4O_ERR_ARG;
+    int64_t units = k / UNIT;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t u = 0; u < units; ++u) {
+            double v[UNIT];
+            for (int j = 0; j < UNIT; ++j) {
+                v[j] = (double)x[r * ld + u * UNIT + j];
+                if (!isfinite(v[j])) {
+                    bad = 1;
+                    v[j] = 0.0;
+                }
+            }
+            quantize_unit(v, codes + r * (k / 2) + u * 32, meta + r * units + u);
+        }
+    }
+    return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* One step of HiGPTQ, scheme 1 ([HiGPTQ], section 3.1: groups of 64 columns,
+ * one HiF4 unit each; scheme 1 quantizes the 64 columns of a group at once,
+ * with the level-1, level-2 and level-3 exponents all fixed from those
+ * columns, and then updates the weights not yet quantized).
+ *
+ * The update is the one of GPTQ (Frantar et al., "GPTQ: Accurate
+ * Post-Training Quantization for Generative Pre-trained Transformers", 2022),
+ * restated for a set S of columns fixed together: with H the layer's Hessian
+ * over the input channels and H^-1 = U^T U (U upper triangular, the caller's
+ * factor), fixing S to Q_S moves the remaining columns R (those after S) by
+ *     W_R -= E U_SS^-1 U_SR,   E = W_S - deq(Q(W_S)),
+ * the optimal compensation of the quadratic loss once the earlier columns are
+ * fixed (for the trailing block, (H_{>=s})^-1 = U_{>=s}^T U_{>=s}).
+ * F = E U_SS^-1 is formed by forward substitution over the 64 columns
+ * (F U_SS = E with U_SS upper triangular), in double.
+ *
+ *  w      double [n][k], the working weights; columns of R are updated in
+ *         place (S and earlier columns are left as they are).
+ *  u      double [k][k], row-major, upper triangular.
+ *  unit   the group index (columns 64 unit .. 64 unit + 63).
+ *  codes  [n][k/2], meta [n][k/64]: unit `unit` of every row is written. */
+int hif4o_higptq_unit(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
+                      uint8_t *codes, uint32_t *meta)
+{
+    if (n < 0 || k <= 0 || k % UNIT != 0 || unit < 0 || unit >= k / UNIT) return HIF4O_ERR_ARG;
+    const int64_t s0 = unit * UNIT, r0 = s0 + UNIT, units = k / UNIT;
+    for (int j = 0; j < UNIT; ++j)
+        if (!(u[(s0 + j) * k + (s0 + j)] != 0.0)) return HIF4O_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < n; ++r) {
+        double *wr = w + r * k;
+        double v[UNIT], e[UNIT], f[UNIT];
+        for (int j = 0; j < UNIT; ++j) {
+            v[j] = wr[s0 + j];
+            if (!isfinite(v[j])) bad = 1;
+        }
+        uint8_t *uc = codes + r * (k / 2) + unit * 32;
+        quantize_unit(v, uc, meta + r * units + unit);
+        for (int j = 0; j < UNIT; ++j) e[j] = v[j] - unit_element(uc, meta[r * units + unit], j);
+        /* forward substitution: f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj */
+        for (int j = 0; j < UNIT; ++j) {
+            double acc = e[j];
+            for (int i = 0; i < j; ++i) acc -= f[i] * u[(s0 + i) * k + (s0 + j)];
+            f[j] = acc / u[(s0 + j) * k + (s0 + j)];
+        }
+        for (int64_t c = r0; c < k; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < UNIT; ++i) acc += f[i] * u[(s0 + i) * k + c];
+            wr[c] -= acc;
+        }
+    }
+    return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
 }

@@ -588,3 +588,113 @@ def test_topn_mask_ties_prefer_lower_index():
     s = np.float32([1, 3, 3, 2, 3, 0])
     assert list(oracle.topn_mask(s, 2)) == [0, 1, 1, 0, 0, 0]
     assert list(oracle.topn_mask(s, 3)) == [0, 1, 1, 0, 1, 0]
+
+
+# ------------------------------------------------------------------- HiGPTQ
+# [HiGPTQ] (the calibration article, section 3.1), scheme 1: every group of
+# 64 columns (one HiF4 unit) is quantized at once with all its exponents
+# fixed from it; the columns not yet quantized are then compensated, as in
+# GPTQ. The working weights are real numbers, so the quantizer's fp32 entry
+# is pinned first.
+
+def _check_values_exact(xs, codes_row, meta_word, deq_row):
+    """Exact-rational RNE check of one unit given its input values."""
+    c, e2, e3 = unit_fields(int(meta_word))
+    s = Fraction(oracle.e6m2_value(c))
+    for j in range(UNIT):
+        x = Fraction(float(xs[j]))
+        D = s * 2 ** (e2[j // 8] + e3[j // 4])
+        k = nibble(codes_row, j) & 7
+        assert Fraction(float(deq_row[j])) == (k * D / 4) * (-1 if (x < 0 and k) else 1)
+        err = abs(abs(x) - k * D / 4)
+        assert abs(x) <= 7 * D / 4 and err <= D / 8
+        if err == D / 8:
+            assert k % 2 == 0
+    # the rule's scales: the smallest level-1 code that covers the maximum
+    A = max(abs(Fraction(float(v))) for v in xs)
+    assert 7 * s >= A and (c == 0 or 7 * Fraction(oracle.e6m2_value(c - 1)) < A)
+
+
+def test_quantize_f32_on_bf16_values_equals_bf16_quantize():
+    bits = _random_bits(400, seed=71)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    c1, m1 = oracle.quantize_f32(f)
+    c0, m0, _ = oracle.quantize(bits)
+    assert np.array_equal(c1, c0) and np.array_equal(m1, m0)
+
+
+def test_quantize_f32_is_exact_rne_on_full_precision_floats():
+    r = np.random.default_rng(72)
+    x = (r.standard_t(3, size=(600, UNIT)) * np.exp(r.normal(0, 3, size=(600, 1)))).astype(np.float32)
+    # ties: fp32 elements exactly on grid midpoints (2m+1) D/8 of their unit
+    for i in range(200):
+        c = int(r.integers(20, 230))
+        s = Fraction(oracle.e6m2_value(c))
+        x[i, :] = 0
+        x[i, 0] = float(7 * s)
+        for j in range(8, UNIT):
+            x[i, j] = float((2 * int(r.integers(0, 7)) + 1) * s / 8) * (1 if r.random() < 0.5 else -1)
+    codes, meta = oracle.quantize_f32(x)
+    deq = oracle.dequantize(codes, meta)
+    for i in range(x.shape[0]):
+        _check_values_exact(x[i], codes[i], meta[i, 0], deq[i])
+
+
+def _gptq_problem(n, k, seed):
+    """Correlated synthetic calibration inputs -> Hessian H = 2 X^T X / rows
+    (+1% mean-diagonal damping) and the upper factor U of H^-1 = U^T U."""
+    r = np.random.default_rng(seed)
+    A = r.standard_normal((k, k)) / np.sqrt(k)
+    X = r.standard_normal((4 * k, k)) @ (np.eye(k) + 0.8 * A)
+    X *= np.exp(r.normal(0, 1, size=(1, k)))
+    H = 2 * X.T @ X / X.shape[0]
+    H += 0.01 * np.mean(np.diag(H)) * np.eye(k)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T
+    W = (r.standard_normal((n, k)) * 0.02).astype(np.float32)
+    return W, H, U
+
+
+def test_higptq_step_is_the_obs_update_for_a_group():
+    """Each step equals the closed-form optimal compensation when a set S of
+    weights is fixed (the multi-weight form of the OBS/GPTQ update), computed
+    with explicit inverses of the trailing Hessian block -- a route that does
+    not use the Cholesky factor."""
+    n, k = 24, 256
+    W, H, U = _gptq_problem(n, k, 73)
+    w = W.astype(np.float64)
+    codes = np.zeros((n, k // 2), np.uint8)
+    meta = np.zeros((n, k // 64), np.uint32)
+    for unit in range(k // 64):
+        s0, r0 = 64 * unit, 64 * unit + 64
+        before = w.copy()
+        oracle.higptq_unit(w, U, unit, codes, meta)
+        # the group is the rule's quantization of the current weights
+        c_ref, m_ref = oracle.quantize_f32(before[:, s0:r0].astype(np.float32))
+        assert np.array_equal(codes[:, unit * 32:unit * 32 + 32], c_ref)
+        assert np.array_equal(meta[:, unit], m_ref[:, 0])
+        E = before[:, s0:r0] - oracle.dequantize(c_ref, m_ref)
+        Hinv_rem = np.linalg.inv(H[s0:, s0:])
+        S, R = slice(0, 64), slice(64, k - s0)
+        delta = -E @ np.linalg.solve(Hinv_rem[S, S], Hinv_rem[S, R])
+        assert np.allclose(w[:, r0:], before[:, r0:] + delta, rtol=0, atol=1e-9 * np.abs(before).max())
+        assert np.array_equal(w[:, :r0], before[:, :r0])
+
+
+def test_higptq_with_identity_hessian_is_direct_quantization():
+    W, _, _ = _gptq_problem(32, 256, 74)
+    codes, meta, wf = oracle.higptq(W, np.eye(256))
+    c0, m0 = oracle.quantize_f32(W)
+    assert np.array_equal(codes, c0) and np.array_equal(meta, m0)
+    assert np.array_equal(wf, W.astype(np.float64))
+
+
+def test_higptq_lowers_the_layer_output_error():
+    """The point of the method: tr(E H E^T), the layer-output error on the
+    calibration inputs, drops against direct quantization."""
+    for seed in (75, 76):
+        W, H, U = _gptq_problem(64, 256, seed)
+        codes, meta, _ = oracle.higptq(W, U)
+        c0, m0 = oracle.quantize_f32(W)
+        E = W - oracle.dequantize(codes, meta)
+        E0 = W - oracle.dequantize(c0, m0)
+        assert np.trace(E @ H @ E.T) < 0.8 * np.trace(E0 @ H @ E0.T)
