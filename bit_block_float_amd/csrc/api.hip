@@ -246,4 +246,39 @@ hif4_status hif4_percentile_mask(const void* x, int64_t rows, int64_t c, int64_t
                                          workspace, stream));
 }
 
+hif4_status hif4_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
+                              uint8_t* codes, uint32_t* meta, hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 64 != 0 || ld < k) return HIF4_ERR_SHAPE;
+  if (rows == 0 || k == 0) return HIF4_OK;
+  if (!x || !codes || !meta) return HIF4_ERR_NULL;
+  if (!aligned(x, 16) || ld % 4 != 0 || !aligned(codes, 16) || !aligned(meta, 4))
+    return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_quantize_f32(x, rows, k, ld, codes, meta, stream));
+}
+
+size_t hif4_higptq_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return align256((size_t)n * 64 * sizeof(float));
+}
+
+hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
+                             int64_t ldu, int64_t unit, uint8_t* codes, uint32_t* meta,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n < 0 || k <= 0 || k % 64 != 0 || ldw < k || ldu < k) return HIF4_ERR_SHAPE;
+  if (unit < 0 || unit >= k / 64) return HIF4_ERR_ARG;
+  if (n == 0) return HIF4_OK;
+  if (!w || !u || !codes || !meta) return HIF4_ERR_NULL;
+  if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(u, 16) || ldu % 4 != 0 || !aligned(codes, 16) ||
+      !aligned(meta, 4))
+    return HIF4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hif4_higptq_workspace_bytes(n)) return HIF4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_higptq_unit(w, n, k, ldw, u, ldu, unit, codes, meta,
+                                          (float*)workspace, stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,231 @@
+// gptq.hip -- HiF4 quantize of fp32 values and the HiGPTQ scheme-1 step.
+//
+// HiGPTQ: HiFloat4 calibration article (hwcomputing.csdn.net), section 3.1
+// "HiGPTQ", scheme 1: the 64 columns of one group (one HiF4 unit) are
+// quantized at once, with the level-1, level-2 and level-3 exponents all
+// fixed from those columns; the weights not yet quantized are then updated
+// to compensate. The update is GPTQ's (Frantar et al., "GPTQ: Accurate
+// Post-Training Quantization for Generative Pre-trained Transformers", 2022)
+// for a set S of columns fixed together, with H^-1 = U^T U (U upper
+// triangular, given by the caller):
+//     E = W_S - deq(Q(W_S)),   F = E U_SS^-1,   W_R -= F U_SR
+// for R = the columns after S.
+//
+// The working weights are fp32, so the quantizer here takes fp32 values: the
+// rule is the one of quant.hip (hif4.h states it), with the element rounding
+// done by counting grid midpoints -- (2m+1) D/8 has at most 7 significant
+// bits, exact in fp32, so the comparisons are exact for any fp32 input.
+#include "hif4_dev.h"
+
+namespace hif4 {
+
+// One 64-element unit of fp32 values (v, in registers) -> its 8 code words
+// and meta word, and the dequantized values (deq, exact in fp32).
+__device__ __forceinline__ void quantize_unit_f32(const float (&v)[64], uint32_t (&cw)[8],
+                                                  uint32_t& meta, float (&deq)[64]) {
+  // step 1: maxima of |x| per level-3 group (4), level-2 group (8), unit
+  float m4[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    m4[q] = fmaxf(fmaxf(fabsf(v[4 * q]), fabsf(v[4 * q + 1])),
+                  fmaxf(fabsf(v[4 * q + 2]), fabsf(v[4 * q + 3])));
+  float a = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) a = fmaxf(a, m4[q]);
+  // step 2: level-1 code
+  const uint32_t c = level1_code(a);
+  const float s = e6m2_f32(c);
+  uint32_t mw = c;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    // steps 3-4: level-2 / level-3 bits (exact compares)
+    const uint32_t e2 = fmaxf(m4[2 * g], m4[2 * g + 1]) > 3.5f * s;
+    const float t3 = (e2 ? 3.5f : 1.75f) * s;
+    const uint32_t e3a = m4[2 * g] > t3, e3b = m4[2 * g + 1] > t3;
+    mw |= (e2 << (8 + g)) | (e3a << (16 + 2 * g)) | (e3b << (17 + 2 * g));
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 8 * g + i;
+      const uint32_t e3 = i < 4 ? e3a : e3b;
+      const float D = ldexpf(s, (int)(e2 + e3));
+      const float ax = fabsf(v[j]);
+      // step 5: k = midpoints (2m+1) D/8 below |x|; at a midpoint the even
+      // neighbour wins (> for even m, >= for odd m); 7 beyond the last one
+      uint32_t k = 0u;
+#pragma unroll
+      for (int m = 0; m < 7; ++m) {
+        const float mid = D * (0.125f * (float)(2 * m + 1));
+        k += (m & 1) ? (ax >= mid ? 1u : 0u) : (ax > mid ? 1u : 0u);
+      }
+      const uint32_t sgn = (v[j] < 0.0f && k != 0u) ? 8u : 0u;
+      word |= (k | sgn) << (i < 4 ? 8 * i : 8 * (i - 4) + 4);
+      const float mag = D * (0.25f * (float)k);
+      deq[j] = sgn ? -mag : mag;
+    }
+    cw[g] = word;
+  }
+  meta = mw;
+}
+
+// fp32 quantize: one thread per (row, unit); lanes of a wave take
+// consecutive units of a row.
+__global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restrict__ x,
+                                                           int64_t ld, int64_t rows,
+                                                           int64_t units,
+                                                           uint32_t* __restrict__ codes32,
+                                                           uint32_t* __restrict__ meta) {
+  const int64_t total = rows * units;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / units, u = t - r * units;
+    const float4* src = reinterpret_cast<const float4*>(x + r * ld + u * 64);
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 q = src[i];
+      v[4 * i] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+    uint32_t cw[8], mw;
+    float deq[64];
+    quantize_unit_f32(v, cw, mw, deq);
+    uint4* dst = reinterpret_cast<uint4*>(codes32 + t * 8);
+    dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+    meta[t] = mw;
+  }
+}
+
+// HiGPTQ group step, part 1: one thread per row. Quantize W[r][s0..s0+63],
+// write unit `unit` of the row's codes and meta, and F[r] = E U_SS^-1 by
+// forward substitution (F U_SS = E, U_SS upper triangular, in LDS).
+__global__ __launch_bounds__(256) void higptq_group_kernel(
+    const float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u,
+    int64_t ldu, int64_t s0, int64_t units, int64_t unit, uint32_t* __restrict__ codes32,
+    uint32_t* __restrict__ meta, float* __restrict__ f) {
+  __shared__ float uss[64 * 65];  // U_SS, row i at uss[65 i] (padded)
+  for (int t = threadIdx.x; t < 64 * 64; t += blockDim.x) {
+    const int i = t >> 6, j = t & 63;
+    uss[65 * i + j] = u[(s0 + i) * ldu + s0 + j];
+  }
+  __syncthreads();
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  const float4* src = reinterpret_cast<const float4*>(w + r * ldw + s0);
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 q = src[i];
+    v[4 * i] = q.x;
+    v[4 * i + 1] = q.y;
+    v[4 * i + 2] = q.z;
+    v[4 * i + 3] = q.w;
+  }
+  uint32_t cw[8], mw;
+  float deq[64];
+  quantize_unit_f32(v, cw, mw, deq);
+  uint4* dst = reinterpret_cast<uint4*>(codes32 + (r * units + unit) * 8);
+  dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+  meta[r * units + unit] = mw;
+  // E = W_S - deq (exact: the two differ by at most half a grid step), then
+  // f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj, overwriting v
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    float acc = v[j] - deq[j];
+#pragma unroll
+    for (int i = 0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
+    v[j] = acc / uss[65 * j + j];
+  }
+  float4* fo = reinterpret_cast<float4*>(f + r * 64);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) fo[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+// HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
+// update. Workgroup tile: 64 rows x 128 columns; thread: 8 rows x 4 columns;
+// F (64 x 64) and the U panel (64 x 128) staged in LDS.
+constexpr int kUpdRows = 64, kUpdCols = 128;
+__global__ __launch_bounds__(256) void higptq_update_kernel(
+    float* __restrict__ w, int64_t ldw, int64_t n, int64_t k, const float* __restrict__ u,
+    int64_t ldu, int64_t s0, int64_t c0, const float* __restrict__ f) {
+  __shared__ float fs[64][kUpdRows + 1];   // fs[i][row]
+  __shared__ __align__(16) float us[64][kUpdCols];  // us[i][col] (16-byte rows for float4 reads)
+  const int64_t row0 = (int64_t)blockIdx.y * kUpdRows;
+  const int64_t col0 = c0 + (int64_t)blockIdx.x * kUpdCols;
+  for (int t = threadIdx.x; t < 64 * kUpdRows; t += blockDim.x) {
+    const int rr = t >> 6, i = t & 63;
+    const int64_t row = row0 + rr;
+    fs[i][rr] = row < n ? f[row * 64 + i] : 0.0f;
+  }
+  for (int t = threadIdx.x; t < 64 * kUpdCols; t += blockDim.x) {
+    const int i = t / kUpdCols, cc = t % kUpdCols;
+    const int64_t col = col0 + cc;
+    us[i][cc] = col < k ? u[(s0 + i) * ldu + col] : 0.0f;
+  }
+  __syncthreads();
+  const int tc = threadIdx.x & 31, tr = threadIdx.x >> 5;  // 32 column quads x 8 row groups
+  float acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  for (int i = 0; i < 64; ++i) {
+    const float4 uq = *reinterpret_cast<const float4*>(&us[i][4 * tc]);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const float fv = fs[i][tr * 8 + a];
+      acc[a][0] = fmaf(fv, uq.x, acc[a][0]);
+      acc[a][1] = fmaf(fv, uq.y, acc[a][1]);
+      acc[a][2] = fmaf(fv, uq.z, acc[a][2]);
+      acc[a][3] = fmaf(fv, uq.w, acc[a][3]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int64_t row = row0 + tr * 8 + a;
+    if (row >= n) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t col = col0 + 4 * tc + b;
+      if (col < k) w[row * ldw + col] -= acc[a][b];
+    }
+  }
+}
+
+}  // namespace hif4
+
+using namespace hif4;
+
+hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
+                                    uint8_t* codes, uint32_t* meta, hipStream_t stream) {
+  if (rows == 0 || k == 0) return hipSuccess;
+  const int64_t units = k / 64, total = rows * units;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(quantize_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, ld,
+                     rows, units, reinterpret_cast<uint32_t*>(codes), meta);
+  return hipGetLastError();
+}
+
+hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
+                                   int64_t ldu, int64_t unit, uint8_t* codes, uint32_t* meta,
+                                   float* f, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t s0 = unit * 64, units = k / 64;
+  hipLaunchKernelGGL(higptq_group_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     w, ldw, n, u, ldu, s0, units, unit, reinterpret_cast<uint32_t*>(codes), meta,
+                     f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t c0 = s0 + 64;
+  if (c0 >= k) return hipSuccess;
+  const dim3 grid((unsigned)((k - c0 + kUpdCols - 1) / kUpdCols),
+                  (unsigned)((n + kUpdRows - 1) / kUpdRows));
+  hipLaunchKernelGGL(higptq_update_kernel, grid, dim3(256), 0, stream, w, ldw, n, k, u, ldu, s0,
+                     c0, (const float*)f);
+  return hipGetLastError();
+}

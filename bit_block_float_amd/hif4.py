@@ -54,6 +54,12 @@ def lib():
         L.hif4_percentile_workspace_bytes.restype = sz
         L.hif4_percentile_mask.argtypes = [p, i64, i64, i64, ctypes.c_double, i64, p, p, p, sz, p]
         L.hif4_percentile_mask.restype = ctypes.c_int
+        L.hif4_quantize_f32.argtypes = [p, i64, i64, i64, p, p, p]
+        L.hif4_quantize_f32.restype = ctypes.c_int
+        L.hif4_higptq_workspace_bytes.argtypes = [i64]
+        L.hif4_higptq_workspace_bytes.restype = sz
+        L.hif4_higptq_unit.argtypes = [p, i64, i64, i64, p, i64, i64, p, p, p, sz, p]
+        L.hif4_higptq_unit.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -197,3 +203,52 @@ def percentile_mask(x, q, n_protect, stats=None, mask=None, workspace=None, stre
                                     _stream(stream))
     _ok(st, "hif4_percentile_mask")
     return stats, mask
+
+
+def _check_f32_rows(x, name):
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D fp32 CUDA tensor with unit column stride")
+
+
+def quantize_f32(x, codes=None, meta=None, stream=None):
+    """HiF4-quantize fp32 x [rows][k] along k -> (codes u8, meta int32)."""
+    _check_f32_rows(x, "x")
+    rows, k = x.shape
+    dev = x.device
+    codes = codes if codes is not None else torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    meta = meta if meta is not None else torch.empty((rows, k // 64), dtype=torch.int32, device=dev)
+    st = lib().hif4_quantize_f32(_ptr(x), rows, k, x.stride(0), _ptr(codes), _ptr(meta),
+                                 _stream(stream))
+    _ok(st, "hif4_quantize_f32")
+    return codes, meta
+
+
+def higptq_workspace_bytes(n):
+    return int(lib().hif4_higptq_workspace_bytes(n))
+
+
+def higptq_unit(w, u, unit, codes, meta, workspace=None, stream=None):
+    """One HiGPTQ scheme-1 step in place on the fp32 working weights w [n][k]
+    with the upper factor u [k][k] (H^-1 = u^T u): writes unit ``unit`` of
+    codes/meta and updates the later columns of w."""
+    _check_f32_rows(w, "w")
+    _check_f32_rows(u, "u")
+    n, k = w.shape
+    if workspace is None:
+        workspace = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
+    st = lib().hif4_higptq_unit(_ptr(w), n, k, w.stride(0), _ptr(u), u.stride(0), int(unit),
+                                _ptr(codes), _ptr(meta), _ptr(workspace), workspace.numel(),
+                                _stream(stream))
+    _ok(st, "hif4_higptq_unit")
+
+
+def higptq(w, u, stream=None):
+    """HiGPTQ scheme 1 over all groups: returns (codes, meta); w is updated in
+    place (its final contents are the compensated working weights)."""
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    meta = torch.empty((n, k // 64), dtype=torch.int32, device=w.device)
+    ws = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
+    for unit in range(k // 64):
+        higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream)
+    return codes, meta

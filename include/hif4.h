@@ -212,6 +212,48 @@ HIF4_EXPORT hif4_status hif4_percentile_mask(const void *x, int64_t rows, int64_
                                  int64_t n_protect, float *stats, uint8_t *mask,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * hif4_quantize_f32 -- HiF4-quantize rows of fp32 values along k, with the
+ * same rule as hif4_quantize applied to the exact fp32 values (HiGPTQ's
+ * working weights are real numbers, not bf16).
+ *
+ *  x      fp32 [rows][ld], 16-byte aligned, ld % 4 == 0, ld >= k; finite.
+ *  codes  u8 [rows][k/2], 16-byte aligned.    meta  u32 [rows][k/64].
+ *  rows >= 0, k % 64 == 0.
+ */
+HIF4_EXPORT hif4_status hif4_quantize_f32(const float *x, int64_t rows, int64_t k, int64_t ld,
+                              uint8_t *codes, uint32_t *meta, hipStream_t stream);
+
+/* hif4_higptq_workspace_bytes -- workspace of hif4_higptq_unit for n rows. */
+HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
+
+/*
+ * hif4_higptq_unit -- one step of HiGPTQ scheme 1 (the calibration article,
+ * section 3.1 "HiGPTQ": a group of 64 columns, one HiF4 unit, is quantized at
+ * once with all its exponents fixed from it; the weights not yet quantized
+ * are then updated). The update is GPTQ's (Frantar et al., 2022) for the set
+ * S of the group's columns, with H^-1 = U^T U (H the layer's Hessian over
+ * the input channels, U upper triangular):
+ *     E = W_S - deq(Q(W_S)),   W_R -= E U_SS^-1 U_SR,
+ * R = the columns after the group. Call it for unit = 0, 1, ... in order
+ * (scheme 1 over the whole row); codes/meta then hold the HiGPTQ result.
+ *
+ *  w      fp32 [n][ldw] working weights (in: the current values; out: the
+ *         columns after the group updated in place; the group and earlier
+ *         columns are not modified), 16-byte aligned, ldw % 4 == 0.
+ *  u      fp32 [k][ldu], upper triangular factor, 16-byte aligned,
+ *         ldu % 4 == 0; its diagonal in the group must be nonzero (a zero
+ *         gives non-finite weights, not a fault).
+ *  unit   0 <= unit < k/64: the group's columns are 64 unit .. 64 unit + 63.
+ *  codes  u8 [n][k/2], meta u32 [n][k/64]: unit `unit` of every row written.
+ *  workspace >= hif4_higptq_workspace_bytes(n) bytes, 256-byte aligned.
+ *  The fp32 compensation is within rounding of the fp64 formula above; the
+ *  group's codes are exactly the quantization of the weights as given.
+ */
+HIF4_EXPORT hif4_status hif4_higptq_unit(float *w, int64_t n, int64_t k, int64_t ldw, const float *u,
+                             int64_t ldu, int64_t unit, uint8_t *codes, uint32_t *meta,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,8 @@ def L():
 def test_header_declares_the_four_entry_points():
     names = declared()
     for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
-               "hif4_linear_xcodes_wbf16",
+               "hif4_linear_xcodes_wbf16", "hif4_quantize_f32", "hif4_higptq_unit",
+               "hif4_higptq_workspace_bytes",
                "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
                "hif4_status_string", "hif4_version"):
         assert fn in names
@@ -163,6 +164,43 @@ def test_percentile_argument_checks(L):
     assert f(A, 100, 256, 256, 0.5, 1, None, A, A, ws, None) == NULL
     assert f(A, 100, 256, 260, 0.5, 1, A, A, A, ws, None) == ALIGN
     assert f(A, 100, 256, 256, 0.5, 1, A, A, A, ws - 1, None) == WORKSPACE
+
+
+def test_quantize_f32_argument_checks(L):
+    q = L.hif4_quantize_f32
+    assert q(A, 4, 65, 72, A, A, None) == SHAPE
+    assert q(A, 4, 128, 64, A, A, None) == SHAPE            # ld < k
+    assert q(A, 0, 64, 64, None, None, None) == OK         # empty: no work
+    assert q(None, 4, 64, 64, A, A, None) == NULL
+    assert q(A, 4, 64, 64, None, A, None) == NULL
+    assert q(A + 4, 4, 64, 64, A, A, None) == ALIGN
+    assert q(A, 4, 64, 66, A, A, None) == ALIGN             # ld % 4
+    assert q(A, 4, 64, 64, A + 8, A, None) == ALIGN
+
+
+def test_higptq_argument_checks(L):
+    f = L.hif4_higptq_unit
+    ws = L.hif4_higptq_workspace_bytes(10)
+    assert ws == 2560  # 10 rows x 64 fp32 (a multiple of 256 bytes)
+    assert L.hif4_higptq_workspace_bytes(-1) == 0
+
+    def call(w=A, n=10, k=128, ldw=128, u=A, ldu=128, unit=0, c=A, m=A, wsp=A, wb=None):
+        return f(w, n, k, ldw, u, ldu, unit, c, m, wsp, ws if wb is None else wb, None)
+
+    assert call(k=96) == SHAPE
+    assert call(k=0) == SHAPE
+    assert call(ldw=64) == SHAPE
+    assert call(ldu=64) == SHAPE
+    assert call(unit=2) == ARG
+    assert call(unit=-1) == ARG
+    assert call(n=0, w=None) == OK
+    assert call(w=None) == NULL
+    assert call(u=None) == NULL
+    assert call(w=A + 4) == ALIGN
+    assert call(ldw=130) == ALIGN
+    assert call(wsp=None) == WORKSPACE
+    assert call(wb=ws - 1) == WORKSPACE
+    assert call(wsp=A + 16) == ALIGN
 
 
 def test_valid_call_without_gfx950_reports_device_error():
