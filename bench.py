@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 HiF4 linear TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak
 
 
 def log(msg):
@@ -96,6 +97,39 @@ def torch_index(idx):
     return torch.from_numpy(idx).to(torch.long)
 
 
+def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
+    """HiGPTQ scheme 1 over the whole weight (80 groups of 64 columns): one
+    untimed pass, then `reps` timed passes from the same start. Reported apart
+    from the hot-path step (it is a calibration pass, run once per layer)."""
+    spec = workloads.WORKLOADS["higptq"]
+    n, k = w_bf16.shape
+    u = workloads.higptq_factor(k, device="cuda", seed=spec["index"])
+    w0 = w_bf16.float()
+    w = torch.empty_like(w0)
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    meta = torch.empty((n, k // 64), dtype=torch.int32, device=dev)
+    ws = torch.empty((hif4.higptq_workspace_bytes(n),), dtype=torch.uint8, device=dev)
+    units = k // 64
+    times = []
+    for rep in range(reps + 1):
+        w.copy_(w0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for unit in range(units):
+            hif4.higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(e0.elapsed_time(e1))
+    ms = sum(times) / len(times)
+    # compensation flops: 2 n 64 (k - 64 (u + 1)) per group
+    flops = sum(2.0 * n * 64 * (k - 64 * (g + 1)) for g in range(units))
+    log(f"HiGPTQ over W {n}x{k}: {ms:.2f} ms")
+    return {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
+            "ms": ms, "groups": units, "update_TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6144)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the HiGPTQ timing that follows the hot-path steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -243,6 +279,8 @@ def main():
         "quantize": parts["quantize_x_masked"],
         "parts": parts,
     }
+    if not args.no_extras:
+        out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, stream)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(x.cpu(), w.cpu(), mask.cpu().numpy(), args.cpu_rows)

@@ -151,3 +151,18 @@ def test_percentile_calibration_pass_and_masked_weight(hip):
     assert np.array_equal(host_u32(meta), m_o)
     assert np.array_equal(codes.cpu().numpy(), c_o)
     assert np.array_equal(kept.cpu().view(torch.int16).numpy().view(np.uint16), k_o)
+
+
+def test_higptq_full_weight_sampled_rows(hip):
+    """HiGPTQ scheme 1 over the full 13,824 x 5120 weight (80 groups) with a
+    random inverse-Hessian factor: every step checked on 96 sampled rows
+    against the oracle started from the GPU's own weights (the rows of the
+    method are independent of each other)."""
+    from test_gpu_higptq import _check_steps
+
+    spec = workloads.WORKLOADS["higptq"]
+    n, k = spec["N"], spec["K"]
+    w = workloads.normal_bf16(n, k, 0.02, device="cpu", seed=spec["index"]).float().numpy()
+    u = workloads.higptq_factor(k, device="cpu", seed=spec["index"]).numpy()
+    rows = np.linspace(0, n - 1, 96).astype(np.int64)
+    _check_steps(hip, w, u, rows=rows)

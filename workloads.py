@@ -20,6 +20,9 @@ Workloads (seed = workload index unless given):
   calib     16 batches of 57600x5120: Student-t(2.5) * c[ch] * d_b[ch],
             c ~ LogNormal(0,1), d_b ~ LogNormal(0,0.5); q=0.999, 52 protected;
             W 13824x5120 ~0.02 N(0,1) quantized with that mask.
+  higptq    W 13824x5120 ~0.02 N(0,1) and a random upper-triangular factor U
+            of a synthetic inverse Hessian (H^-1 = U^T U): drawn directly, since
+            any upper-triangular U with a positive diagonal is one.
 """
 import math
 
@@ -32,6 +35,7 @@ WORKLOADS = {
     "ffn_down": dict(index=3, M=57600, N=5120, K=13824),
     "calib": dict(index=4, rows_per_batch=57600, batches=16, C=5120, N=13824,
                   q=0.999, n_protect=52),
+    "higptq": dict(index=5, N=13824, K=5120),
 }
 
 
@@ -150,3 +154,15 @@ def bits(t: torch.Tensor):
     """uint16 numpy view of a bf16 tensor's bit patterns (host copy)."""
     import numpy as np
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def higptq_factor(k, device="cpu", seed=5, spread=0.5, coupling=1.0):
+    """Random upper-triangular U [k][k] (fp32) with a positive diagonal: the
+    factor of a synthetic inverse Hessian H^-1 = U^T U. Row i is scaled by
+    d_i ~ LogNormal(0, spread) (channel scales); the entries above the diagonal
+    are d_i * coupling * N(0,1) / sqrt(k) (channel correlations)."""
+    g = _gen(device, seed)
+    d = _lognormal((k, 1), spread, g, device)
+    z = torch.randn((k, k), generator=g, device=device, dtype=torch.float32) * (coupling / math.sqrt(k))
+    u = torch.triu(z, diagonal=1) + torch.eye(k, device=device, dtype=torch.float32)
+    return (u * d).contiguous()
