@@ -146,16 +146,35 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
 }
 
 // HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
-// update. Workgroup tile: 64 rows x 128 columns; thread: 8 rows x 4 columns;
-// F (64 x 64) and the U panel (64 x 128) staged in LDS.
+// update. Workgroup tile: 64 rows x 128 columns; thread: 8 rows x 4 columns.
+// The thread's 8 x 4 block of W is loaded first, so that its latency
+// overlaps the staging of F (64 x 64) and of the U panel (64 x 128) in LDS
+// and the 64-step product; per step a thread reads one float4 of U and two
+// of F for 32 FMAs.
 constexpr int kUpdRows = 64, kUpdCols = 128;
 __global__ __launch_bounds__(256) void higptq_update_kernel(
     float* __restrict__ w, int64_t ldw, int64_t n, int64_t k, const float* __restrict__ u,
     int64_t ldu, int64_t s0, int64_t c0, const float* __restrict__ f) {
-  __shared__ float fs[64][kUpdRows + 1];   // fs[i][row]
-  __shared__ __align__(16) float us[64][kUpdCols];  // us[i][col] (16-byte rows for float4 reads)
+  __shared__ __align__(16) float fs[64][kUpdRows];  // fs[i][row]
+  __shared__ __align__(16) float us[64][kUpdCols];  // us[i][col]
   const int64_t row0 = (int64_t)blockIdx.y * kUpdRows;
   const int64_t col0 = c0 + (int64_t)blockIdx.x * kUpdCols;
+  const int tc = threadIdx.x & 31, tr = threadIdx.x >> 5;  // 32 column quads x 8 row groups
+  const int64_t colq = col0 + 4 * tc;
+  const bool vec = colq + 4 <= k;  // a whole float4 of this row segment lies inside W
+  float wv[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int64_t row = row0 + tr * 8 + a;
+    if (row < n && vec) {
+      const float4 q = *reinterpret_cast<const float4*>(w + row * ldw + colq);
+      wv[a][0] = q.x; wv[a][1] = q.y; wv[a][2] = q.z; wv[a][3] = q.w;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        wv[a][b] = (row < n && colq + b < k) ? w[row * ldw + colq + b] : 0.0f;
+    }
+  }
   for (int t = threadIdx.x; t < 64 * kUpdRows; t += blockDim.x) {
     const int rr = t >> 6, i = t & 63;
     const int64_t row = row0 + rr;
@@ -167,31 +186,37 @@ __global__ __launch_bounds__(256) void higptq_update_kernel(
     us[i][cc] = col < k ? u[(s0 + i) * ldu + col] : 0.0f;
   }
   __syncthreads();
-  const int tc = threadIdx.x & 31, tr = threadIdx.x >> 5;  // 32 column quads x 8 row groups
   float acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+#pragma unroll 4
   for (int i = 0; i < 64; ++i) {
     const float4 uq = *reinterpret_cast<const float4*>(&us[i][4 * tc]);
+    const float4 f0 = *reinterpret_cast<const float4*>(&fs[i][tr * 8]);
+    const float4 f1 = *reinterpret_cast<const float4*>(&fs[i][tr * 8 + 4]);
+    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const float fv = fs[i][tr * 8 + a];
-      acc[a][0] = fmaf(fv, uq.x, acc[a][0]);
-      acc[a][1] = fmaf(fv, uq.y, acc[a][1]);
-      acc[a][2] = fmaf(fv, uq.z, acc[a][2]);
-      acc[a][3] = fmaf(fv, uq.w, acc[a][3]);
+      acc[a][0] = fmaf(fv[a], uq.x, acc[a][0]);
+      acc[a][1] = fmaf(fv[a], uq.y, acc[a][1]);
+      acc[a][2] = fmaf(fv[a], uq.z, acc[a][2]);
+      acc[a][3] = fmaf(fv[a], uq.w, acc[a][3]);
     }
   }
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
     const int64_t row = row0 + tr * 8 + a;
     if (row >= n) continue;
+    if (vec) {
+      *reinterpret_cast<float4*>(w + row * ldw + colq) =
+          make_float4(wv[a][0] - acc[a][0], wv[a][1] - acc[a][1], wv[a][2] - acc[a][2],
+                      wv[a][3] - acc[a][3]);
+    } else {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t col = col0 + 4 * tc + b;
-      if (col < k) w[row * ldw + col] -= acc[a][b];
+      for (int b = 0; b < 4; ++b)
+        if (colq + b < k) w[row * ldw + colq + b] = wv[a][b] - acc[a][b];
     }
   }
 }
