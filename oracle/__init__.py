@@ -43,6 +43,8 @@ def _lib():
         lib.hif4o_quantize_f32.restype = ctypes.c_int
         lib.hif4o_higptq_unit.argtypes = [p, i64, i64, p, i64, p, p]
         lib.hif4o_higptq_unit.restype = ctypes.c_int
+        lib.hif4o_higptq_unit_scheme.argtypes = [p, i64, i64, p, i64, ctypes.c_int, p, p]
+        lib.hif4o_higptq_unit_scheme.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -188,10 +190,12 @@ def quantize_f32(x: np.ndarray):
     return codes, meta
 
 
-def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta: np.ndarray):
-    """One HiGPTQ scheme-1 step in place (see hif4_oracle.c): quantize group
-    ``unit`` of the working weights ``w`` (float64 [n][k], C-contiguous) and
-    compensate the later columns with the upper factor ``u`` (H^-1 = u^T u)."""
+def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta: np.ndarray,
+                scheme: int = 1):
+    """One HiGPTQ step (scheme 1, 2 or 3) in place (see hif4_oracle.c):
+    quantize group ``unit`` of the working weights ``w`` (float64 [n][k],
+    C-contiguous) and compensate the later columns with the upper factor
+    ``u`` (H^-1 = u^T u)."""
     n, k = w.shape
     if w.dtype != np.float64 or not w.flags.c_contiguous:
         raise OracleError("higptq_unit: w must be C-contiguous float64")
@@ -199,17 +203,17 @@ def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta
     _shape(uu, (k, k), "higptq_unit u")
     _shape(codes, (n, k // 2), "higptq_unit codes")
     _shape(meta, (n, k // 64), "higptq_unit meta")
-    _check(_lib().hif4o_higptq_unit(_ptr(w), n, k, _ptr(uu), int(unit), _ptr(codes), _ptr(meta)),
-           "higptq_unit")
+    _check(_lib().hif4o_higptq_unit_scheme(_ptr(w), n, k, _ptr(uu), int(unit), int(scheme),
+                                           _ptr(codes), _ptr(meta)), "higptq_unit")
 
 
-def higptq(w: np.ndarray, u: np.ndarray):
-    """HiGPTQ scheme 1 over every group of ``w`` [n][k] (any float dtype):
-    returns (codes, meta, final working weights as float64)."""
+def higptq(w: np.ndarray, u: np.ndarray, scheme: int = 1):
+    """HiGPTQ over every group of ``w`` [n][k] (any float dtype): returns
+    (codes, meta, final working weights as float64)."""
     ww = np.array(w, dtype=np.float64, order="C")
     n, k = ww.shape
     codes = np.zeros((n, k // 2), np.uint8)
     meta = np.zeros((n, k // 64), np.uint32)
     for unit in range(k // 64):
-        higptq_unit(ww, u, unit, codes, meta)
+        higptq_unit(ww, u, unit, codes, meta, scheme)
     return codes, meta, ww

@@ -402,52 +402,136 @@ int hif4o_quantize_f32(const float *x, int64_t rows, int64_t k, int64_t ld, uint
     return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
 }
 
-/* One step of HiGPTQ, scheme 1 ([HiGPTQ], section 3.1: groups of 64 columns,
- * one HiF4 unit each; scheme 1 quantizes the 64 columns of a group at once,
- * with the level-1, level-2 and level-3 exponents all fixed from those
- * columns, and then updates the weights not yet quantized).
+/* HiGPTQ ([HiGPTQ], section 3.1): one group of 64 columns (one HiF4 unit)
+ * per call, under one of the article's three schemes.
+ *
+ *  scheme 1  the 64 columns are quantized at once, with the level-1,
+ *            level-2 and level-3 exponents all fixed from them;
+ *  scheme 2  the level-1 exponent (1-0) is fixed from the group first; then
+ *            8 columns at a time: their level-2 and level-3 exponents are
+ *            fixed from their current values, they are quantized, and the
+ *            weights not yet quantized are updated before the next 8;
+ *  scheme 3  the level-1 exponent is fixed first; for each level-2 group,
+ *            its level-2 exponent is fixed from its 8 current values, its
+ *            first 4 columns are quantized (level-3 fixed from them), the
+ *            weights not yet quantized are updated, and the second 4
+ *            columns re-estimate their level-3 exponent and are quantized.
  *
  * The update is the one of GPTQ (Frantar et al., "GPTQ: Accurate
  * Post-Training Quantization for Generative Pre-trained Transformers", 2022),
- * restated for a set S of columns fixed together: with H the layer's Hessian
+ * restated for a set T of columns fixed together: with H the layer's Hessian
  * over the input channels and H^-1 = U^T U (U upper triangular, the caller's
- * factor), fixing S to Q_S moves the remaining columns R (those after S) by
- *     W_R -= E U_SS^-1 U_SR,   E = W_S - deq(Q(W_S)),
+ * factor), fixing T to Q_T moves the columns after T by
+ *     W_R -= F U_TR,   F = E U_TT^-1,   E = W_T - deq(Q_T),
  * the optimal compensation of the quadratic loss once the earlier columns are
- * fixed (for the trailing block, (H_{>=s})^-1 = U_{>=s}^T U_{>=s}).
- * F = E U_SS^-1 is formed by forward substitution over the 64 columns
- * (F U_SS = E with U_SS upper triangular), in double.
+ * fixed (for a trailing block, (H_{>=t})^-1 = U_{>=t}^T U_{>=t}). F is formed
+ * by forward substitution (F U_TT = E, U_TT upper triangular), in double.
+ * Schemes 2 and 3 apply it per 8 or per 4 columns; the columns after the
+ * group receive the sum of those updates, F U_SR with F the group's 64 F
+ * values side by side.
  *
- *  w      double [n][k], the working weights; columns of R are updated in
- *         place (S and earlier columns are left as they are).
- *  u      double [k][k], row-major, upper triangular.
+ *  w      double [n][k], the working weights; the group's columns end holding
+ *         the values they were quantized from, the columns after it are
+ *         updated in place.
+ *  u      double [k][k], row-major, upper triangular (nonzero diagonal).
  *  unit   the group index (columns 64 unit .. 64 unit + 63).
  *  codes  [n][k/2], meta [n][k/64]: unit `unit` of every row is written. */
-int hif4o_higptq_unit(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
-                      uint8_t *codes, uint32_t *meta)
+
+/* Level-2 / level-3 bits and element rounding (steps 3-5 of the rule) for
+ * elements j0 .. j0 + len - 1 of a unit under level-1 scale s; e2 of their
+ * level-2 group is the given one when e2_fixed >= 0. Writes the nibbles, the
+ * meta bits and the dequantized values. */
+static void encode_span(const double x[UNIT], int j0, int len, double s, int e2_fixed,
+                        uint8_t codes[32], uint32_t *meta, double deq[UNIT])
+{
+    int g = j0 / 8;
+    double m8 = 0.0;
+    for (int j = 8 * g; j < 8 * g + 8; ++j) m8 = fabs(x[j]) > m8 ? fabs(x[j]) : m8;
+    int e2 = e2_fixed >= 0 ? e2_fixed : (m8 > 1.75 * 2.0 * s);
+    for (int q = j0 / 4; q < (j0 + len) / 4; ++q) {
+        double m4 = 0.0;
+        for (int j = 4 * q; j < 4 * q + 4; ++j) m4 = fabs(x[j]) > m4 ? fabs(x[j]) : m4;
+        int e3 = m4 > 1.75 * e1_factor(e2) * s;
+        *meta |= (uint32_t)e3 << (16 + q);
+        double D = s * e1_factor(e2) * e1_factor(e3);
+        for (int j = 4 * q; j < 4 * q + 4; ++j) {
+            double a = fabs(x[j]);
+            int k = 0;
+            for (int m = 0; m < 7; ++m) {
+                double mid = (double)(2 * m + 1) * D / 8.0;
+                if (a > mid) {
+                    k = m + 1;
+                } else {
+                    if (a == mid) k = (m % 2 == 0) ? m : m + 1;
+                    break;
+                }
+            }
+            int sign = (x[j] < 0.0) && (k != 0);
+            codes[code_byte(j)] |= (uint8_t)((k | (sign << 3)) << code_shift(j));
+            deq[j] = (sign ? -1.0 : 1.0) * (double)k * D / 4.0;
+        }
+    }
+    *meta |= (uint32_t)e2 << (8 + g);
+}
+
+int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
+                             int scheme, uint8_t *codes, uint32_t *meta)
 {
     if (n < 0 || k <= 0 || k % UNIT != 0 || unit < 0 || unit >= k / UNIT) return HIF4O_ERR_ARG;
+    if (scheme < 1 || scheme > 3) return HIF4O_ERR_ARG;
     const int64_t s0 = unit * UNIT, r0 = s0 + UNIT, units = k / UNIT;
     for (int j = 0; j < UNIT; ++j)
         if (!(u[(s0 + j) * k + (s0 + j)] != 0.0)) return HIF4O_ERR_ARG;
+    const int span = scheme == 1 ? 64 : (scheme == 2 ? 8 : 4);
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t r = 0; r < n; ++r) {
         double *wr = w + r * k;
-        double v[UNIT], e[UNIT], f[UNIT];
+        double v[UNIT], deq[UNIT], f[UNIT];
         for (int j = 0; j < UNIT; ++j) {
             v[j] = wr[s0 + j];
             if (!isfinite(v[j])) bad = 1;
         }
         uint8_t *uc = codes + r * (k / 2) + unit * 32;
-        quantize_unit(v, uc, meta + r * units + unit);
-        for (int j = 0; j < UNIT; ++j) e[j] = v[j] - unit_element(uc, meta[r * units + unit], j);
-        /* forward substitution: f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj */
-        for (int j = 0; j < UNIT; ++j) {
-            double acc = e[j];
-            for (int i = 0; i < j; ++i) acc -= f[i] * u[(s0 + i) * k + (s0 + j)];
-            f[j] = acc / u[(s0 + j) * k + (s0 + j)];
+        uint32_t *um = meta + r * units + unit;
+        if (scheme == 1) {
+            quantize_unit(v, uc, um); /* all exponents from the group at once */
+            for (int j = 0; j < UNIT; ++j) deq[j] = unit_element(uc, *um, j);
+        } else {
+            /* level-1 from the group as it stands before any update */
+            double amax = 0.0;
+            for (int j = 0; j < UNIT; ++j) amax = fabs(v[j]) > amax ? fabs(v[j]) : amax;
+            int c = 255;
+            for (int cc = 0; cc < 256; ++cc)
+                if (7.0 * hif4o_e6m2_value(cc) >= amax) {
+                    c = cc;
+                    break;
+                }
+            memset(uc, 0, 32);
+            *um = (uint32_t)c;
         }
+        for (int t0 = 0; t0 < UNIT; t0 += span) {
+            if (scheme == 2) {
+                encode_span(v, t0, 8, hif4o_e6m2_value((int)(*um & 255u)), -1, uc, um, deq);
+            } else if (scheme == 3) {
+                int e2 = -1;
+                if (t0 % 8 == 4) e2 = (int)((*um >> (8 + t0 / 8)) & 1u); /* fixed before the group's first 4 */
+                encode_span(v, t0, 4, hif4o_e6m2_value((int)(*um & 255u)), e2, uc, um, deq);
+            }
+            /* forward substitution over the span: f_j = (e_j - sum f_i U_ij) / U_jj */
+            for (int j = t0; j < t0 + span; ++j) {
+                double acc = v[j] - deq[j];
+                for (int i = t0; i < j; ++i) acc -= f[i] * u[(s0 + i) * k + (s0 + j)];
+                f[j] = acc / u[(s0 + j) * k + (s0 + j)];
+            }
+            /* update the group's columns after the span */
+            for (int j = t0 + span; j < UNIT; ++j) {
+                double acc = 0.0;
+                for (int i = t0; i < t0 + span; ++i) acc += f[i] * u[(s0 + i) * k + (s0 + j)];
+                v[j] -= acc;
+            }
+        }
+        for (int j = 0; j < UNIT; ++j) wr[s0 + j] = v[j];
         for (int64_t c = r0; c < k; ++c) {
             double acc = 0.0;
             for (int i = 0; i < UNIT; ++i) acc += f[i] * u[(s0 + i) * k + c];
@@ -455,4 +539,11 @@ int hif4o_higptq_unit(double *w, int64_t n, int64_t k, const double *u, int64_t 
         }
     }
     return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* Scheme 1 (kept as its own entry). */
+int hif4o_higptq_unit(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
+                      uint8_t *codes, uint32_t *meta)
+{
+    return hif4o_higptq_unit_scheme(w, n, k, u, unit, 1, codes, meta);
 }

@@ -698,3 +698,84 @@ def test_higptq_lowers_the_layer_output_error():
         E = W - oracle.dequantize(codes, meta)
         E0 = W - oracle.dequantize(c0, m0)
         assert np.trace(E @ H @ E.T) < 0.8 * np.trace(E0 @ H @ E0.T)
+
+
+def _simulate_schemes(W, H, codes, meta, w_after, unit, scheme):
+    """Re-derive one oracle step of scheme 2 or 3 with explicit inverses of
+    the trailing Hessian blocks (no Cholesky factor), checking the scheme's
+    exponent rules on the values each span was quantized from."""
+    n, k = W.shape
+    s0, r0 = 64 * unit, 64 * unit + 64
+    span = 8 if scheme == 2 else 4
+    state = W.astype(np.float64).copy()
+    deq = oracle.dequantize(codes[:, 32 * unit:32 * unit + 32], meta[:, unit:unit + 1])
+    for r in range(n):
+        c, e2, e3 = unit_fields(int(meta[r, unit]))
+        A = max(abs(Fraction(float(v))) for v in W[r, s0:r0])
+        # level-1 fixed from the group before any update
+        assert 7 * Fraction(oracle.e6m2_value(c)) >= A
+        assert c == 0 or 7 * Fraction(oracle.e6m2_value(c - 1)) < A
+    e2_seen = {}
+    for t0 in range(0, 64, span):
+        T = slice(s0 + t0, s0 + t0 + span)
+        vals = state[:, T]
+        # the span was quantized from exactly these values
+        assert np.allclose(w_after[:, T], vals, rtol=0, atol=1e-12 * max(1.0, np.abs(W).max()))
+        for r in range(n):
+            c, e2, e3 = unit_fields(int(meta[r, unit]))
+            s = oracle.e6m2_value(c)
+            g = t0 // 8
+            if t0 % 8 == 0:  # e2 fixed from the level-2 group's values at its first span
+                m8 = np.abs(state[r, s0 + 8 * g:s0 + 8 * g + 8]).max()
+                assert e2[g] == int(m8 > 3.5 * s)
+            for q in range(t0 // 4, (t0 + span) // 4):
+                m4 = np.abs(state[r, s0 + 4 * q:s0 + 4 * q + 4]).max()
+                assert e3[q] == int(m4 > 1.75 * 2 ** e2[g] * s)
+                D = s * 2 ** (e2[g] + e3[q])
+                for j in range(4 * q, 4 * q + 4):
+                    x = abs(state[r, s0 + j])
+                    kk = abs(deq[r, j]) / (D / 4)
+                    assert kk == int(kk) and 0 <= kk <= 7
+                    err = abs(x - kk * D / 4)
+                    if x > 7.5 * D / 4:
+                        assert kk == 7  # fixed level-1 exponent: clipped
+                    else:
+                        assert err <= D / 8 + 1e-300
+        E = vals - deq[:, t0:t0 + span]
+        Hinv_rem = np.linalg.inv(H[s0 + t0:, s0 + t0:])
+        S, R = slice(0, span), slice(span, None)
+        state[:, s0 + t0 + span:] -= E @ np.linalg.solve(Hinv_rem[S, S], Hinv_rem[S, R])
+    assert np.allclose(w_after[:, r0:], state[:, r0:], rtol=0, atol=1e-9 * np.abs(W).max())
+
+
+@pytest.mark.parametrize("scheme", [2, 3])
+def test_higptq_schemes_2_and_3_follow_their_rules_and_the_obs_update(scheme):
+    n, k = 12, 192
+    W, H, U = _gptq_problem(n, k, 77 + scheme)
+    w = W.astype(np.float64)
+    codes = np.zeros((n, k // 2), np.uint8)
+    meta = np.zeros((n, k // 64), np.uint32)
+    for unit in range(k // 64):
+        before = w.copy()
+        oracle.higptq_unit(w, U, unit, codes, meta, scheme)
+        _simulate_schemes(before, H, codes, meta, w, unit, scheme)
+
+
+@pytest.mark.parametrize("scheme", [2, 3])
+def test_higptq_schemes_with_identity_hessian_are_direct_quantization(scheme):
+    W, _, _ = _gptq_problem(32, 256, 78)
+    codes, meta, wf = oracle.higptq(W, np.eye(256), scheme)
+    c0, m0 = oracle.quantize_f32(W)
+    assert np.array_equal(codes, c0) and np.array_equal(meta, m0)
+    assert np.array_equal(wf, W.astype(np.float64))
+
+
+def test_higptq_all_schemes_lower_the_layer_output_error():
+    W, H, U = _gptq_problem(64, 256, 79)
+    c0, m0 = oracle.quantize_f32(W)
+    E0 = W - oracle.dequantize(c0, m0)
+    base = np.trace(E0 @ H @ E0.T)
+    for scheme in (1, 2, 3):
+        codes, meta, _ = oracle.higptq(W, U, scheme)
+        E = W - oracle.dequantize(codes, meta)
+        assert np.trace(E @ H @ E.T) < 0.8 * base
