@@ -98,9 +98,10 @@ def torch_index(idx):
 
 
 def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
-    """HiGPTQ scheme 1 over the whole weight (80 groups of 64 columns): one
-    untimed pass, then `reps` timed passes from the same start. Reported apart
-    from the hot-path step (it is a calibration pass, run once per layer)."""
+    """HiGPTQ over the whole weight (80 groups of 64 columns), each of the
+    three schemes: one untimed pass, then `reps` timed passes from the same
+    start. Reported apart from the hot-path step (it is a calibration pass,
+    run once per layer)."""
     spec = workloads.WORKLOADS["higptq"]
     n, k = w_bf16.shape
     u = workloads.higptq_factor(k, device="cuda", seed=spec["index"])
@@ -110,24 +111,29 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
     meta = torch.empty((n, k // 64), dtype=torch.int32, device=dev)
     ws = torch.empty((hif4.higptq_workspace_bytes(n),), dtype=torch.uint8, device=dev)
     units = k // 64
-    times = []
-    for rep in range(reps + 1):
-        w.copy_(w0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for unit in range(units):
-            hif4.higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if rep:
-            times.append(e0.elapsed_time(e1))
-    ms = sum(times) / len(times)
     # compensation flops: 2 n 64 (k - 64 (u + 1)) per group
     flops = sum(2.0 * n * 64 * (k - 64 * (g + 1)) for g in range(units))
-    log(f"HiGPTQ over W {n}x{k}: {ms:.2f} ms")
-    return {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
-            "ms": ms, "groups": units, "update_TFLOP/s": flops / (ms * 1e-3) / 1e12,
-            "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+    out = {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
+           "groups": units}
+    for scheme in (1, 2, 3):
+        times = []
+        for rep in range(reps + 1):
+            w.copy_(w0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for unit in range(units):
+                hif4.higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream,
+                                 scheme=scheme)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                times.append(e0.elapsed_time(e1))
+        ms = sum(times) / len(times)
+        log(f"HiGPTQ scheme {scheme} over W {n}x{k}: {ms:.2f} ms")
+        out[f"scheme{scheme}"] = {"ms": ms, "update_TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                                  "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 /
+                                  FP32_VECTOR_PEAK_TFLOPS}
+    return out
 
 
 def main():

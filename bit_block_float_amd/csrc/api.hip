@@ -264,10 +264,11 @@ size_t hif4_higptq_workspace_bytes(int64_t n) {
 }
 
 hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
-                             int64_t ldu, int64_t unit, uint8_t* codes, uint32_t* meta,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             int64_t ldu, int64_t unit, int scheme, uint8_t* codes,
+                             uint32_t* meta, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   if (n < 0 || k <= 0 || k % 64 != 0 || ldw < k || ldu < k) return HIF4_ERR_SHAPE;
-  if (unit < 0 || unit >= k / 64) return HIF4_ERR_ARG;
+  if (unit < 0 || unit >= k / 64 || scheme < 1 || scheme > 3) return HIF4_ERR_ARG;
   if (n == 0) return HIF4_OK;
   if (!w || !u || !codes || !meta) return HIF4_ERR_NULL;
   if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(u, 16) || ldu % 4 != 0 || !aligned(codes, 16) ||
@@ -277,7 +278,7 @@ hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const 
   if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
   hif4_status st = check_device();
   if (st != HIF4_OK) return st;
-  return launched(hif4_launch_higptq_unit(w, n, k, ldw, u, ldu, unit, codes, meta,
+  return launched(hif4_launch_higptq_unit(w, n, k, ldw, u, ldu, unit, scheme, codes, meta,
                                           (float*)workspace, stream));
 }
 

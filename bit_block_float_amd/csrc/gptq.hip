@@ -1,10 +1,10 @@
 // gptq.hip -- HiF4 quantize of fp32 values and the HiGPTQ scheme-1 step.
 //
 // HiGPTQ: HiFloat4 calibration article (hwcomputing.csdn.net), section 3.1
-// "HiGPTQ", scheme 1: the 64 columns of one group (one HiF4 unit) are
-// quantized at once, with the level-1, level-2 and level-3 exponents all
-// fixed from those columns; the weights not yet quantized are then updated
-// to compensate. The update is GPTQ's (Frantar et al., "GPTQ: Accurate
+// "HiGPTQ": groups of 64 columns (one HiF4 unit each) quantized under one of
+// three schemes (64 columns at once; 8 at a time; 4 at a time, the level-1
+// exponent fixed first in the latter two), the weights not yet quantized
+// updated to compensate after each quantized set. The update is GPTQ's (Frantar et al., "GPTQ: Accurate
 // Post-Training Quantization for Generative Pre-trained Transformers", 2022)
 // for a set S of columns fixed together, with H^-1 = U^T U (U upper
 // triangular, given by the caller):
@@ -99,9 +99,19 @@ __global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restri
   }
 }
 
-// HiGPTQ group step, part 1: one thread per row. Quantize W[r][s0..s0+63],
-// write unit `unit` of the row's codes and meta, and F[r] = E U_SS^-1 by
-// forward substitution (F U_SS = E, U_SS upper triangular, in LDS).
+// HiGPTQ group step, part 1: one thread per row, the group's 64 values in
+// registers, U_SS in LDS. Writes unit `unit` of the row's codes and meta and
+// the row's 64 values of F (the compensation of the columns after the group
+// is F U_SR, part 2).
+//   scheme 1: quantize the 64 values at once (all exponents from them), then
+//             F = E U_SS^-1 by forward substitution;
+//   scheme 2: level-1 from the 64 values first; then per 8 columns: level-2
+//             and level-3 from their current values, quantize, F over the 8
+//             (forward substitution on their diagonal block of U), and update
+//             the group's later columns by F U before the next 8;
+//   scheme 3: as scheme 2 per 4 columns, with each level-2 exponent fixed
+//             from its 8 current values before its first 4 columns.
+template <int kScheme>
 __global__ __launch_bounds__(256) void higptq_group_kernel(
     const float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u,
     int64_t ldu, int64_t s0, int64_t units, int64_t unit, uint32_t* __restrict__ codes32,
@@ -125,21 +135,86 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
     v[4 * i + 3] = q.w;
   }
   uint32_t cw[8], mw;
-  float deq[64];
-  quantize_unit_f32(v, cw, mw, deq);
+  if constexpr (kScheme == 1) {
+    float deq[64];
+    quantize_unit_f32(v, cw, mw, deq);
+    // E = W_S - deq (exact: the two differ by at most half a grid step), then
+    // f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj, overwriting v
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      float acc = v[j] - deq[j];
+#pragma unroll
+      for (int i = 0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
+      v[j] = acc / uss[65 * j + j];
+    }
+  } else {
+    constexpr int kSpan = kScheme == 2 ? 8 : 4;
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(v[j]));
+    const uint32_t c = level1_code(a);  // fixed from the group before any update
+    const float s = e6m2_f32(c);
+    mw = c;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) cw[g] = 0u;
+    uint32_t e2 = 0u;
+#pragma unroll
+    for (int t0 = 0; t0 < 64; t0 += kSpan) {
+      const int g = t0 / 8;
+      if (t0 % 8 == 0) {  // level-2 of group g from its 8 current values
+        float m8 = 0.0f;
+#pragma unroll
+        for (int j = 8 * g; j < 8 * g + 8; ++j) m8 = fmaxf(m8, fabsf(v[j]));
+        e2 = m8 > 3.5f * s;
+        mw |= e2 << (8 + g);
+      }
+      float e[kSpan];
+#pragma unroll
+      for (int q = t0 / 4; q < (t0 + kSpan) / 4; ++q) {
+        float m4 = 0.0f;
+#pragma unroll
+        for (int j = 4 * q; j < 4 * q + 4; ++j) m4 = fmaxf(m4, fabsf(v[j]));
+        const uint32_t e3 = m4 > (e2 ? 3.5f : 1.75f) * s;
+        mw |= e3 << (16 + q);
+        const float D = ldexpf(s, (int)(e2 + e3));
+#pragma unroll
+        for (int j = 4 * q; j < 4 * q + 4; ++j) {
+          const float ax = fabsf(v[j]);
+          uint32_t k = 0u;
+#pragma unroll
+          for (int m = 0; m < 7; ++m) {
+            const float mid = D * (0.125f * (float)(2 * m + 1));
+            k += (m & 1) ? (ax >= mid ? 1u : 0u) : (ax > mid ? 1u : 0u);
+          }
+          const uint32_t sgn = (v[j] < 0.0f && k != 0u) ? 8u : 0u;
+          const int i8 = j % 8;
+          cw[g] |= (k | sgn) << (i8 < 4 ? 8 * i8 : 8 * (i8 - 4) + 4);
+          const float mag = D * (0.25f * (float)k);
+          e[j - t0] = v[j] - (sgn ? -mag : mag);  // exact, as in scheme 1
+        }
+      }
+      // F over the span (forward substitution), stored over the span's values
+#pragma unroll
+      for (int j = t0; j < t0 + kSpan; ++j) {
+        float acc = e[j - t0];
+#pragma unroll
+        for (int i = t0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
+        v[j] = acc / uss[65 * j + j];
+      }
+      // the group's later columns, before they are quantized
+#pragma unroll
+      for (int j = t0 + kSpan; j < 64; ++j) {
+        float acc = v[j];
+#pragma unroll
+        for (int i = t0; i < t0 + kSpan; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
+        v[j] = acc;
+      }
+    }
+  }
   uint4* dst = reinterpret_cast<uint4*>(codes32 + (r * units + unit) * 8);
   dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
   dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
   meta[r * units + unit] = mw;
-  // E = W_S - deq (exact: the two differ by at most half a grid step), then
-  // f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj, overwriting v
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    float acc = v[j] - deq[j];
-#pragma unroll
-    for (int i = 0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
-    v[j] = acc / uss[65 * j + j];
-  }
   float4* fo = reinterpret_cast<float4*>(f + r * 64);
 #pragma unroll
   for (int i = 0; i < 16; ++i) fo[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -237,13 +312,21 @@ hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int
 }
 
 hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
-                                   int64_t ldu, int64_t unit, uint8_t* codes, uint32_t* meta,
-                                   float* f, hipStream_t stream) {
+                                   int64_t ldu, int64_t unit, int scheme, uint8_t* codes,
+                                   uint32_t* meta, float* f, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t s0 = unit * 64, units = k / 64;
-  hipLaunchKernelGGL(higptq_group_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     w, ldw, n, u, ldu, s0, units, unit, reinterpret_cast<uint32_t*>(codes), meta,
-                     f);
+  const dim3 gg((unsigned)((n + 255) / 256)), gb(256);
+  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
+  if (scheme == 1)
+    hipLaunchKernelGGL(higptq_group_kernel<1>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f);
+  else if (scheme == 2)
+    hipLaunchKernelGGL(higptq_group_kernel<2>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f);
+  else
+    hipLaunchKernelGGL(higptq_group_kernel<3>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t c0 = s0 + 64;

@@ -116,5 +116,5 @@ hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
                                     uint8_t* codes, uint32_t* meta, hipStream_t stream);
 hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
-                                   int64_t ldu, int64_t unit, uint8_t* codes, uint32_t* meta,
-                                   float* f, hipStream_t stream);
+                                   int64_t ldu, int64_t unit, int scheme, uint8_t* codes,
+                                   uint32_t* meta, float* f, hipStream_t stream);

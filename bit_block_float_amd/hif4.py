@@ -58,7 +58,7 @@ def lib():
         L.hif4_quantize_f32.restype = ctypes.c_int
         L.hif4_higptq_workspace_bytes.argtypes = [i64]
         L.hif4_higptq_workspace_bytes.restype = sz
-        L.hif4_higptq_unit.argtypes = [p, i64, i64, i64, p, i64, i64, p, p, p, sz, p]
+        L.hif4_higptq_unit.argtypes = [p, i64, i64, i64, p, i64, i64, ctypes.c_int, p, p, p, sz, p]
         L.hif4_higptq_unit.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,28 +227,28 @@ def higptq_workspace_bytes(n):
     return int(lib().hif4_higptq_workspace_bytes(n))
 
 
-def higptq_unit(w, u, unit, codes, meta, workspace=None, stream=None):
-    """One HiGPTQ scheme-1 step in place on the fp32 working weights w [n][k]
-    with the upper factor u [k][k] (H^-1 = u^T u): writes unit ``unit`` of
-    codes/meta and updates the later columns of w."""
+def higptq_unit(w, u, unit, codes, meta, workspace=None, stream=None, scheme=1):
+    """One HiGPTQ group step (scheme 1, 2 or 3) in place on the fp32 working
+    weights w [n][k] with the upper factor u [k][k] (H^-1 = u^T u): writes
+    unit ``unit`` of codes/meta and updates the later columns of w."""
     _check_f32_rows(w, "w")
     _check_f32_rows(u, "u")
     n, k = w.shape
     if workspace is None:
         workspace = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
     st = lib().hif4_higptq_unit(_ptr(w), n, k, w.stride(0), _ptr(u), u.stride(0), int(unit),
-                                _ptr(codes), _ptr(meta), _ptr(workspace), workspace.numel(),
-                                _stream(stream))
+                                int(scheme), _ptr(codes), _ptr(meta), _ptr(workspace),
+                                workspace.numel(), _stream(stream))
     _ok(st, "hif4_higptq_unit")
 
 
-def higptq(w, u, stream=None):
-    """HiGPTQ scheme 1 over all groups: returns (codes, meta); w is updated in
-    place (its final contents are the compensated working weights)."""
+def higptq(w, u, stream=None, scheme=1):
+    """HiGPTQ over all groups: returns (codes, meta); w is updated in place
+    (its final contents are the compensated working weights)."""
     n, k = w.shape
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     meta = torch.empty((n, k // 64), dtype=torch.int32, device=w.device)
     ws = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
     for unit in range(k // 64):
-        higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream)
+        higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream, scheme=scheme)
     return codes, meta

@@ -228,31 +228,43 @@ HIF4_EXPORT hif4_status hif4_quantize_f32(const float *x, int64_t rows, int64_t 
 HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
 
 /*
- * hif4_higptq_unit -- one step of HiGPTQ scheme 1 (the calibration article,
- * section 3.1 "HiGPTQ": a group of 64 columns, one HiF4 unit, is quantized at
- * once with all its exponents fixed from it; the weights not yet quantized
- * are then updated). The update is GPTQ's (Frantar et al., 2022) for the set
- * S of the group's columns, with H^-1 = U^T U (H the layer's Hessian over
- * the input channels, U upper triangular):
- *     E = W_S - deq(Q(W_S)),   W_R -= E U_SS^-1 U_SR,
- * R = the columns after the group. Call it for unit = 0, 1, ... in order
- * (scheme 1 over the whole row); codes/meta then hold the HiGPTQ result.
+ * hif4_higptq_unit -- one group step of HiGPTQ (the calibration article,
+ * section 3.1 "HiGPTQ": groups of 64 columns, one HiF4 unit each, with three
+ * schemes for fixing the exponents):
+ *   scheme 1: the group's 64 columns are quantized at once, all exponents
+ *             fixed from them;
+ *   scheme 2: the level-1 exponent is fixed from the group first; then 8
+ *             columns at a time: level-2 and level-3 fixed from their current
+ *             values, quantized, and the weights not yet quantized updated;
+ *   scheme 3: level-1 fixed first; per level-2 group, its exponent is fixed
+ *             from its 8 current values, its first 4 columns are quantized,
+ *             the rest updated, and the second 4 columns re-estimate their
+ *             level-3 exponent and are quantized.
+ * The update after a set T of columns is GPTQ's (Frantar et al., 2022), with
+ * H^-1 = U^T U (H the layer's Hessian over the input channels, U upper
+ * triangular):  E = W_T - deq(Q_T),  W_after -= E U_TT^-1 U_T,after.
+ * Call it for unit = 0, 1, ... in order; codes/meta then hold the result.
  *
  *  w      fp32 [n][ldw] working weights (in: the current values; out: the
- *         columns after the group updated in place; the group and earlier
+ *         columns after the group updated in place; the group's and earlier
  *         columns are not modified), 16-byte aligned, ldw % 4 == 0.
  *  u      fp32 [k][ldu], upper triangular factor, 16-byte aligned,
  *         ldu % 4 == 0; its diagonal in the group must be nonzero (a zero
  *         gives non-finite weights, not a fault).
  *  unit   0 <= unit < k/64: the group's columns are 64 unit .. 64 unit + 63.
+ *  scheme 1, 2 or 3 (HIF4_ERR_ARG otherwise).
  *  codes  u8 [n][k/2], meta u32 [n][k/64]: unit `unit` of every row written.
- *  workspace >= hif4_higptq_workspace_bytes(n) bytes, 256-byte aligned.
- *  The fp32 compensation is within rounding of the fp64 formula above; the
- *  group's codes are exactly the quantization of the weights as given.
+ *  workspace >= hif4_higptq_workspace_bytes(n) bytes, 256-byte aligned; on
+ *         return it holds F, fp32 [n][64] row-major (the group's
+ *         compensation coefficients, E U^-1 per quantized set).
+ *  The fp32 compensation is within rounding of the fp64 formula above; under
+ *  scheme 1 the group's codes are exactly the quantization of the weights as
+ *  given (schemes 2 and 3 quantize values updated within the group).
  */
 HIF4_EXPORT hif4_status hif4_higptq_unit(float *w, int64_t n, int64_t k, int64_t ldw, const float *u,
-                             int64_t ldu, int64_t unit, uint8_t *codes, uint32_t *meta,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+                             int64_t ldu, int64_t unit, int scheme, uint8_t *codes,
+                             uint32_t *meta, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

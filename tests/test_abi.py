@@ -184,8 +184,8 @@ def test_higptq_argument_checks(L):
     assert ws == 2560  # 10 rows x 64 fp32 (a multiple of 256 bytes)
     assert L.hif4_higptq_workspace_bytes(-1) == 0
 
-    def call(w=A, n=10, k=128, ldw=128, u=A, ldu=128, unit=0, c=A, m=A, wsp=A, wb=None):
-        return f(w, n, k, ldw, u, ldu, unit, c, m, wsp, ws if wb is None else wb, None)
+    def call(w=A, n=10, k=128, ldw=128, u=A, ldu=128, unit=0, scheme=1, c=A, m=A, wsp=A, wb=None):
+        return f(w, n, k, ldw, u, ldu, unit, scheme, c, m, wsp, ws if wb is None else wb, None)
 
     assert call(k=96) == SHAPE
     assert call(k=0) == SHAPE
@@ -193,6 +193,8 @@ def test_higptq_argument_checks(L):
     assert call(ldu=64) == SHAPE
     assert call(unit=2) == ARG
     assert call(unit=-1) == ARG
+    assert call(scheme=0) == ARG
+    assert call(scheme=4) == ARG
     assert call(n=0, w=None) == OK
     assert call(w=None) == NULL
     assert call(u=None) == NULL

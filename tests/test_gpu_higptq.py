@@ -1,13 +1,15 @@
-"""GPU parity of the fp32 quantizer and of HiGPTQ scheme 1, through the C ABI.
+"""GPU parity of the fp32 quantizer and of HiGPTQ, through the C ABI.
 
-HiGPTQ (the calibration article, section 3.1, scheme 1) quantizes one group
-of 64 columns at once and then compensates the columns not yet quantized
-(GPTQ's update with the upper factor U of H^-1). Each step is checked on the
-GPU's own trajectory: the group's codes and meta must be exactly the oracle's
+HiGPTQ (the calibration article, section 3.1) quantizes groups of 64 columns
+and compensates the columns not yet quantized (GPTQ's update with the upper
+factor U of H^-1). Scheme 1 (a group at once) is checked on the GPU's own
+trajectory: the group's codes and meta must be exactly the oracle's
 quantization of the weights the step started from, and the compensated
 weights must match the oracle's fp64 step from the same start within
 1e-5 * (sum_i |F_i||U_ic| + |W_c|) per entry (F = E U_SS^-1; the fp32
 arithmetic's error measured on the CPU is below 4e-7 of that scale).
+Schemes 2 and 3 (8 or 4 columns at a time, with fp32 updates inside the
+group) are checked as described above their tests.
 """
 import numpy as np
 import pytest
@@ -152,4 +154,109 @@ def test_higptq_lowers_the_layer_output_error(hip):
     q = oracle.dequantize(codes.cpu().numpy(), host_u32(meta))
     c0, m0 = oracle.quantize_f32(W)
     E, E0 = W - q, W - oracle.dequantize(c0, m0)
+    assert np.trace(E @ H @ E.T) < 0.8 * np.trace(E0 @ H @ E0.T)
+
+
+# ----------------------------------------------------- schemes 2 and 3 on the GPU
+# Under schemes 2 and 3 the group's later columns are updated in fp32 inside
+# the group before they are quantized, so a code can legitimately differ from
+# an fp64 run where a value lies within rounding of a decision boundary. Each
+# step is therefore checked on the GPU's own trajectory, rebuilt from the F
+# values the step leaves in its workspace: the level-1 code exactly; every
+# exponent bit and element code against the rule applied to the rebuilt
+# values, except within 1e-5 of the value's error scale from a boundary; F
+# against the forward substitution of the rebuilt errors; and the later
+# columns against W_R - F U_SR.
+
+def _check_scheme_step(before, after, codes_u, meta_u, F, U64, unit, scheme):
+    from fractions import Fraction
+
+    n = before.shape[0]
+    s0, r0 = 64 * unit, 64 * unit + 64
+    span = 8 if scheme == 2 else 4
+    v = before[:, s0:r0].astype(np.float64).copy()
+    sc = np.abs(v).copy()  # error scale of each rebuilt value
+    deq = oracle.dequantize(codes_u, meta_u[:, None])
+    c = (meta_u & 255).astype(np.int64)
+    e2b = (meta_u[:, None] >> (8 + np.arange(8))) & 1
+    e3b = (meta_u[:, None] >> (16 + np.arange(16))) & 1
+    for r in range(n):  # level-1 from the group before any update: exact
+        A = Fraction(float(np.abs(before[r, s0:r0]).max()))
+        assert 7 * Fraction(oracle.e6m2_value(int(c[r]))) >= A
+        assert c[r] == 0 or 7 * Fraction(oracle.e6m2_value(int(c[r]) - 1)) < A
+    s = np.array([oracle.e6m2_value(int(x)) for x in c])
+    tol = 1e-5
+    for t0 in range(0, 64, span):
+        g = t0 // 8
+        if t0 % 8 == 0:
+            m8 = np.abs(v[:, 8 * g:8 * g + 8]).max(axis=1)
+            near = np.abs(m8 - 3.5 * s) <= tol * sc[:, 8 * g:8 * g + 8].max(axis=1)
+            assert np.all((e2b[:, g] == (m8 > 3.5 * s)) | near)
+        for q in range(t0 // 4, (t0 + span) // 4):
+            m4 = np.abs(v[:, 4 * q:4 * q + 4]).max(axis=1)
+            t3 = 1.75 * 2.0 ** e2b[:, g] * s
+            near = np.abs(m4 - t3) <= tol * sc[:, 4 * q:4 * q + 4].max(axis=1)
+            assert np.all((e3b[:, q] == (m4 > t3)) | near)
+            D = s * 2.0 ** (e2b[:, g] + e3b[:, q])
+            for j in range(4 * q, 4 * q + 4):
+                x = np.abs(v[:, j])
+                k = np.rint(np.abs(deq[:, j]) / (D / 4)).astype(np.int64)
+                assert np.all(np.abs(deq[:, j]) == k * D / 4)
+                mids = (2 * np.arange(7) + 1)[None, :] * D[:, None] / 8
+                k_rule = np.minimum((x[:, None] > mids).sum(axis=1) +
+                                    ((x[:, None] == mids) & (np.arange(7)[None, :] % 2 == 1)).sum(axis=1), 7)
+                near = np.min(np.abs(x[:, None] - mids), axis=1) <= tol * sc[:, j]
+                assert np.all((k == k_rule) | near), f"scheme {scheme} unit {unit} element {j}"
+        # F over the span from the rebuilt errors
+        E = v[:, t0:t0 + span] - deq[:, t0:t0 + span]
+        Uab = U64[s0 + t0:s0 + t0 + span, s0 + t0:s0 + t0 + span]
+        F_ref = np.linalg.solve(Uab.T, E.T).T
+        # row-wise: |dF| <= 1e-4 |F| + |U_tt^-1| * tol * (the rebuilt values' error
+        # scale): E = v - deq cancels, so the values' own error carries into F
+        inv_norm = np.abs(np.linalg.inv(Uab)).sum(axis=0).max()
+        bound = 1e-4 * np.abs(F_ref).max(axis=1) + inv_norm * tol * sc[:, t0:t0 + span].max(axis=1)
+        assert np.all(np.abs(F[:, t0:t0 + span] - F_ref).max(axis=1) <= bound)
+        # follow the GPU: update the group's later columns with its F
+        Ul = U64[s0 + t0:s0 + t0 + span, s0 + t0 + span:r0]
+        v[:, t0 + span:] -= F[:, t0:t0 + span] @ Ul
+        sc[:, t0 + span:] += np.abs(F[:, t0:t0 + span]) @ np.abs(Ul)
+    assert np.array_equal(after[:, :r0], before[:, :r0])
+    if r0 < before.shape[1]:
+        Us = U64[s0:r0, r0:]
+        ref = before[:, r0:].astype(np.float64) - F @ Us
+        scale = np.abs(F) @ np.abs(Us) + np.abs(before[:, r0:])
+        assert np.all(np.abs(after[:, r0:] - ref) <= 1e-5 * scale)
+
+
+@pytest.mark.parametrize("scheme", [2, 3])
+def test_higptq_schemes_2_and_3_steps(hip, scheme):
+    W, _, U = _gptq_problem(200, 448, 97 + scheme)
+    n, k = W.shape
+    w = dev(W)
+    u = dev(U.astype(np.float32))
+    U64 = U.astype(np.float32).astype(np.float64)
+    codes = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
+    ws = torch.empty((hip.higptq_workspace_bytes(n),), dtype=torch.uint8, device="cuda")
+    for unit in range(k // 64):
+        before = w.cpu().numpy()
+        hip.higptq_unit(w, u, unit, codes, meta, workspace=ws, scheme=scheme)
+        torch.cuda.synchronize()
+        F = ws[:n * 64 * 4].view(torch.float32).view(n, 64).cpu().numpy().astype(np.float64)
+        _check_scheme_step(before, w.cpu().numpy(), codes[:, 32 * unit:32 * unit + 32].cpu().numpy(),
+                           host_u32(meta)[:, unit], F, U64, unit, scheme)
+
+
+@pytest.mark.parametrize("scheme", [2, 3])
+def test_higptq_schemes_2_and_3_identity_and_layer_error(hip, scheme):
+    W, H, U = _gptq_problem(256, 512, 96)
+    c0, m0 = oracle.quantize_f32(W)
+    w = dev(W)
+    codes, meta = hip.higptq(w, dev(np.eye(512, dtype=np.float32)), scheme=scheme)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), c0) and np.array_equal(host_u32(meta), m0)
+    codes, meta = hip.higptq(dev(W), dev(U.astype(np.float32)), scheme=scheme)
+    torch.cuda.synchronize()
+    E = W - oracle.dequantize(codes.cpu().numpy(), host_u32(meta))
+    E0 = W - oracle.dequantize(c0, m0)
     assert np.trace(E @ H @ E.T) < 0.8 * np.trace(E0 @ H @ E0.T)
