@@ -166,3 +166,27 @@ def test_higptq_full_weight_sampled_rows(hip):
     u = workloads.higptq_factor(k, device="cpu", seed=spec["index"]).numpy()
     rows = np.linspace(0, n - 1, 96).astype(np.int64)
     _check_steps(hip, w, u, rows=rows)
+
+
+def test_higptq_scheme3_full_weight_sampled_rows(hip):
+    """Scheme 3 (4 columns at a time) over the full weight: every step checked
+    on 64 sampled rows on the GPU's own trajectory (see test_gpu_higptq)."""
+    from test_gpu_higptq import _check_scheme_step
+
+    spec = workloads.WORKLOADS["higptq"]
+    n, k = spec["N"], spec["K"]
+    w = workloads.normal_bf16(n, k, 0.02, device="cuda", seed=spec["index"]).float().contiguous()
+    u = workloads.higptq_factor(k, device="cuda", seed=spec["index"])
+    U64 = u.cpu().numpy().astype(np.float64)
+    codes = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
+    ws = torch.empty((hip.higptq_workspace_bytes(n),), dtype=torch.uint8, device="cuda")
+    rows = torch.from_numpy(np.linspace(0, n - 1, 64).astype(np.int64)).cuda()
+    for unit in range(k // 64):
+        before = w[rows].cpu().numpy()
+        hip.higptq_unit(w, u, unit, codes, meta, workspace=ws, scheme=3)
+        torch.cuda.synchronize()
+        F = ws[:n * 64 * 4].view(torch.float32).view(n, 64)[rows].cpu().numpy().astype(np.float64)
+        _check_scheme_step(before, w[rows].cpu().numpy(),
+                           codes[rows, 32 * unit:32 * unit + 32].cpu().numpy(),
+                           host_u32(meta[rows])[:, unit], F, U64, unit, 3)
