@@ -136,6 +136,49 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
     return out
 
 
+def time_calibration(torch, workloads, hif4, dev, stream, reps=3):
+    """The calibration pass: percentile + top-n mask over 16 calibration
+    batches (921,600 x 5120 bf16 = 9.4 GB), then the masked quantize of the
+    13,824 x 5120 weight. Reported apart from the hot-path step."""
+    spec = workloads.WORKLOADS["calib"]
+    rows, c, n = spec["batches"] * spec["rows_per_batch"], spec["C"], spec["N"]
+    x = workloads.calib_x(spec["batches"], spec["rows_per_batch"], c, device="cuda",
+                          seed=spec["index"])
+    w = workloads.normal_bf16(n, c, 0.02, device="cuda", seed=spec["index"] + 1000)
+    stats = torch.empty((c,), dtype=torch.float32, device=dev)
+    mask = torch.empty((c,), dtype=torch.uint8, device=dev)
+    pws = torch.empty((hif4.percentile_workspace_bytes(rows, c),), dtype=torch.uint8, device=dev)
+    codes = torch.empty((n, c // 2), dtype=torch.uint8, device=dev)
+    meta = torch.empty((n, c // 64), dtype=torch.int32, device=dev)
+    kept = torch.empty((n, spec["n_protect"]), dtype=torch.bfloat16, device=dev)
+    tp, tq = [], []
+    for rep in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        hif4.percentile_mask(x, spec["q"], spec["n_protect"], stats=stats, mask=mask,
+                             workspace=pws, stream=stream)
+        e[1].record(stream)
+        st = hif4.lib().hif4_quantize(hif4._ptr(w), n, c, c, hif4._ptr(mask), spec["n_protect"],
+                                      hif4._ptr(kept), hif4._ptr(codes), hif4._ptr(meta),
+                                      hif4._stream(stream))
+        hif4._ok(st, "hif4_quantize(W)")
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            tp.append(e[0].elapsed_time(e[1]))
+            tq.append(e[1].elapsed_time(e[2]))
+    t_p, t_q = sum(tp) / len(tp), sum(tq) / len(tq)
+    pbytes = rows * c * 2
+    log(f"calibration pass: percentile over {rows}x{c} {t_p:.2f} ms, masked W quantize {t_q:.3f} ms")
+    del x
+    return {"workload": f"{spec['batches']} batches x {spec['rows_per_batch']} x {c} bf16 "
+                        f"(Student-t(2.5) x per-channel and per-batch LogNormal scales), q = "
+                        f"{spec['q']}, {spec['n_protect']} protected; W {n}x{c}",
+            "percentile_mask_ms": t_p, "percentile_GB/s": pbytes / t_p / 1e6,
+            "percentile_frac_hbm": pbytes / t_p / 1e6 / HBM_PEAK_GBS,
+            "quantize_w_masked_ms": t_q}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +330,7 @@ def main():
     }
     if not args.no_extras:
         out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, stream)}
+        out["extensions"]["calibration"] = time_calibration(torch, workloads, hif4, dev, stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(x.cpu(), w.cpu(), mask.cpu().numpy(), args.cpu_rows)
