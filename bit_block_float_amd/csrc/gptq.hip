@@ -250,15 +250,32 @@ __global__ __launch_bounds__(256) void higptq_update_kernel(
         wv[a][b] = (row < n && colq + b < k) ? w[row * ldw + colq + b] : 0.0f;
     }
   }
-  for (int t = threadIdx.x; t < 64 * kUpdRows; t += blockDim.x) {
-    const int rr = t >> 6, i = t & 63;
+  // staging with 16-byte loads: F rows (64 floats each) transposed into
+  // fs[i][row], U panel rows copied as they are
+  for (int t = threadIdx.x; t < 16 * kUpdRows; t += blockDim.x) {
+    const int rr = t >> 4, i4 = (t & 15) * 4;
     const int64_t row = row0 + rr;
-    fs[i][rr] = row < n ? f[row * 64 + i] : 0.0f;
+    float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (row < n) q = *reinterpret_cast<const float4*>(f + row * 64 + i4);
+    fs[i4][rr] = q.x;
+    fs[i4 + 1][rr] = q.y;
+    fs[i4 + 2][rr] = q.z;
+    fs[i4 + 3][rr] = q.w;
   }
-  for (int t = threadIdx.x; t < 64 * kUpdCols; t += blockDim.x) {
-    const int i = t / kUpdCols, cc = t % kUpdCols;
-    const int64_t col = col0 + cc;
-    us[i][cc] = col < k ? u[(s0 + i) * ldu + col] : 0.0f;
+  for (int t = threadIdx.x; t < 64 * (kUpdCols / 4); t += blockDim.x) {
+    const int i = t / (kUpdCols / 4), c4 = (t % (kUpdCols / 4)) * 4;
+    const int64_t col = col0 + c4;
+    const float* src = u + (s0 + i) * ldu + col;
+    float4 q;
+    if (col + 4 <= k) {
+      q = *reinterpret_cast<const float4*>(src);
+    } else {
+      q.x = col < k ? src[0] : 0.0f;
+      q.y = col + 1 < k ? src[1] : 0.0f;
+      q.z = col + 2 < k ? src[2] : 0.0f;
+      q.w = col + 3 < k ? src[3] : 0.0f;
+    }
+    *reinterpret_cast<float4*>(&us[i][c4]) = q;
   }
   __syncthreads();
   float acc[8][4];
