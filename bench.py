@@ -176,6 +176,7 @@ def time_calibration(torch, workloads, hif4, dev, stream, reps=3):
                         f"{spec['q']}, {spec['n_protect']} protected; W {n}x{c}",
             "percentile_mask_ms": t_p, "percentile_GB/s": pbytes / t_p / 1e6,
             "percentile_frac_hbm": pbytes / t_p / 1e6 / HBM_PEAK_GBS,
+            "percentile_exact_pass_channels": hif4.percentile_exact_channels(pws, rows, c),
             "quantize_w_masked_ms": t_q}
 
 
@@ -287,7 +288,8 @@ def main():
     gemm_tflops = flops / (t_lin * 1e-3) / 1e12
     parts = {
         "percentile_mask": {"ms": t_pct, "GB/s": pct_bytes / t_pct / 1e6,
-                            "frac_hbm": pct_bytes / t_pct / 1e6 / HBM_PEAK_GBS},
+                            "frac_hbm": pct_bytes / t_pct / 1e6 / HBM_PEAK_GBS,
+                            "exact_pass_channels": hif4.percentile_exact_channels(pws, M, K)},
         "quantize_w_masked": {"ms": t_wq, "GB/s": wq_bytes / t_wq / 1e6,
                               "note": "W (141.6 MB bf16) fits the 256 MB MALL"},
         "quantize_x_masked": {"ms": t_xq, "GB/s": q_bytes / t_xq / 1e6,

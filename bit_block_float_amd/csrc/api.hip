@@ -224,15 +224,15 @@ hif4_status hif4_linear_xcodes_wbf16(const uint8_t* x_codes, const uint32_t* x_m
 }
 
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {
-  (void)rows;
-  if (c < 0) return 0;
-  return hif4_percentile_ws_bytes(c);
+  if (c < 0 || rows < 0) return 0;
+  return hif4_percentile_ws_bytes(rows, c);
 }
 
 hif4_status hif4_percentile_mask(const void* x, int64_t rows, int64_t c, int64_t ld, double q,
                                  int64_t n_protect, float* stats, uint8_t* mask, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  if (rows < 1 || c < 1 || c > 65536 || ld < c || ld > (1 << 22)) return HIF4_ERR_SHAPE;
+  if (rows < 1 || rows > 0xFFFFFFFFll || c < 1 || c > 65536 || ld < c || ld > (1 << 22))
+    return HIF4_ERR_SHAPE;
   if (n_protect < 0 || n_protect > c) return HIF4_ERR_SHAPE;
   if (!(q >= 0.0 && q <= 1.0)) return HIF4_ERR_ARG;
   if (!x || !stats || !mask) return HIF4_ERR_NULL;

@@ -111,7 +111,7 @@ hipError_t hif4_launch_pack_kept(const uint16_t* kept, int64_t rows, int64_t nk,
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
                                   double q, int64_t n_protect, float* stats, uint8_t* mask,
                                   void* workspace, hipStream_t stream);
-size_t hif4_percentile_ws_bytes(int64_t c);
+size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c);
 hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
                                     uint8_t* codes, uint32_t* meta, hipStream_t stream);

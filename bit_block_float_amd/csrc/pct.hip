@@ -52,18 +52,6 @@ __device__ __forceinline__ int chan_of_col(int col) {
   return (col < 64) ? 2 * col : 2 * (col - 64) + 1;
 }
 
-// Zero the histograms, reset the per-channel minimum keys.
-__global__ void pct_init_kernel(uint32_t* __restrict__ h1, uint32_t* __restrict__ h2,
-                                uint32_t* __restrict__ minkey, int c) {
-  const int64_t n1 = (int64_t)c * 256, n2 = (int64_t)c * 128;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1; i += stride) {
-    h1[i] = 0u;
-    if (i < n2) h2[i] = 0u;
-    if (i < c) minkey[i] = 0xFFFFFFFFu;
-  }
-}
-
 // Element offset of the 32-bit word (channels ch, ch + 1) a lane reads in
 // each row. Lanes past the last channel read channel 0 instead (a valid
 // address); when c is odd the last lane's word also covers element c, which
@@ -164,8 +152,9 @@ __device__ __forceinline__ void for_segments(int64_t rows, int cblocks, int64_t 
 // bits 23..30: one bit-field extract and one shift-or per channel.
 __global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
-    uint32_t* __restrict__ h1) {
+    uint32_t* __restrict__ h1, const uint32_t* __restrict__ gate) {
   __shared__ uint32_t hist[256 * kPctCh];  // [bin][column]
+  if (gate != nullptr && *gate == 0u) return;  // fallback pass not needed
   for (int i = threadIdx.x; i < 256 * kPctCh; i += kPctThreads) hist[i] = 0u;
   __syncthreads();
 
@@ -251,12 +240,16 @@ __device__ __forceinline__ void wave_find_rank(const uint32_t (&cnt)[kPer], int6
 }
 
 // Between passes: one wave per channel finds the coarse bins (and ranks
-// inside them) of lo and hi.
+// inside them) of lo and hi. When n_exact is given (the two passes run for
+// every channel), it receives c.
 __global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restrict__ h1,
                                                          int64_t rows, int c, double q,
-                                                         PctSel* __restrict__ sel) {
+                                                         PctSel* __restrict__ sel,
+                                                         const uint32_t* __restrict__ gate,
+                                                         uint32_t* __restrict__ n_exact) {
+  if (n_exact != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *n_exact = (uint32_t)c;
   const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ch >= c) return;
+  if (ch >= c || (gate != nullptr && *gate == 0u)) return;
   const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
@@ -280,9 +273,11 @@ __global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restr
 // merges it once per segment.
 __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
-    const PctSel* __restrict__ sel, uint32_t* __restrict__ h2, uint32_t* __restrict__ minkey) {
+    const PctSel* __restrict__ sel, uint32_t* __restrict__ h2, uint32_t* __restrict__ minkey,
+    const uint32_t* __restrict__ gate) {
   __shared__ uint32_t hist[129 * kPctCh];  // [fine bin, spare][column]
   __shared__ uint32_t mins[kPctCh];
+  if (gate != nullptr && *gate == 0u) return;
   for (int i = threadIdx.x; i < 129 * kPctCh; i += kPctThreads) hist[i] = 0u;
   for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) mins[i] = 0xFFFFFFFFu;
   __syncthreads();
@@ -349,9 +344,12 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
                                                         const PctSel* __restrict__ sel,
                                                         const uint32_t* __restrict__ minkey,
                                                         int64_t rows, int c, double q,
-                                                        float* __restrict__ stats) {
+                                                        float* __restrict__ stats,
+                                                        const uint32_t* __restrict__ gate,
+                                                        const uint8_t* __restrict__ only) {
   const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ch >= c) return;
+  if (ch >= c || (gate != nullptr && *gate == 0u)) return;
+  if (only != nullptr && only[ch] == 0) return;  // this channel's statistic is already set
   const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
@@ -378,6 +376,214 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
     const double r = __dadd_rn(vlo, t);
     stats[ch] = __double2float_rn(r);
   }
+}
+
+// ---- one-pass path with a sampled window (large inputs)
+//
+// Pass 1 over every 8th row gives each channel's coarse bin b_s of the
+// quantile's rank in the sample; the window is the 512 consecutive keys of
+// coarse bins b_s - 1 .. b_s + 2. One pass over all rows then counts, per
+// channel, the keys below the window and a histogram of every key inside it.
+// When ranks lo and hi of the full column both fall inside the window (their
+// keys are then exact), the statistic is final; a channel whose ranks fall
+// outside (a sample that misled) is flagged, and only then do the two exact
+// passes run (gated on the device, no host round trip), for the flagged
+// channels' statistics.
+constexpr int kWin = 512;          // keys in the window
+constexpr int kPartStride = 260;   // u32 per column of a partial: 256 packed words, below, pad
+constexpr int64_t kPartWords = (int64_t)kPctCh * kPartStride;  // one partial (a segment's counts)
+
+// Window start per channel from the sample's coarse histogram; block 0 also
+// clears the flagged-channel count.
+__global__ __launch_bounds__(256) void pct_select_window_kernel(const uint32_t* __restrict__ h1,
+                                                                int64_t rows_s, int c, double q,
+                                                                uint32_t* __restrict__ wlo,
+                                                                uint32_t* __restrict__ n_failed) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_failed = 0u;
+  const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (ch >= c) return;
+  const int lane = threadIdx.x & 63;
+  int64_t lo, hi;
+  double f;
+  type7_ranks(rows_s, q, &lo, &hi, &f);
+  const uint4 w = reinterpret_cast<const uint4*>(h1 + (int64_t)ch * 256)[lane];
+  const uint32_t cnt[4] = {w.x, w.y, w.z, w.w};
+  uint32_t b;
+  int64_t before;
+  wave_find_rank<4>(cnt, lo, &b, &before);
+  if (lane == 0) wlo[ch] = (b > 0 ? b - 1 : 0u) << 7;
+}
+
+// The window pass. A key below the window only adds to its lane's register
+// count (most keys of a tail quantile do: as LDS atomics they would all hit
+// one word per column, a chain of dependent read-modify-writes); a key inside
+// adds to its bin, an LDS u16 pair counter (a segment never exceeds 65535
+// rows) in 256 words per column; a key above is not counted. The atomic is
+// issued under the lane mask of in-window keys. Lanes past the last channel
+// see a window at 0xFFFF: every key is below, counted in registers whose
+// partial is never read.
+//
+// Merging across workgroups without atomics: the (channel block, row) work
+// sequence is cut into units, one per (slab, channel block) (see
+// for_segments); a unit is at most per_wg rows long, so at most one slice
+// boundary falls inside it and it is processed as one or two segments. Each
+// segment stores its counts with plain 16-byte stores into its own partial:
+// part[2 unit + 0] for the segment that starts the unit, part[2 unit + 1] for
+// the other one. Partials are column-major ([column][word]): the final kernel
+// reads a channel's 1 KiB of packed counts per partial contiguously.
+// (Global atomics from the ~6 workgroups sharing a channel block, on lines
+// that move between the chip's L2 caches, cost more than the streaming pass
+// itself when every workgroup flushes at once.)
+__global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
+    const uint32_t* __restrict__ wlo, uint32_t* __restrict__ part) {
+  __shared__ uint32_t hist[(kWin / 2) * kPctCh];  // [bin/2][column]
+  __shared__ uint32_t below[kPctCh];
+  for (int i = threadIdx.x; i < (kWin / 2) * kPctCh; i += kPctThreads) hist[i] = 0u;
+  for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) below[i] = 0u;
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
+  const int cblocks = (c + kPctCh - 1) / kPctCh;
+
+  for_segments(rows, cblocks, per_wg, [&](int c0, int64_t r0, int64_t r1) {
+    const int ch = c0 + 2 * lane;
+    const uint32_t wA = ch < c ? wlo[ch] : 0xFFFFu;
+    const uint32_t wB = ch + 1 < c ? wlo[ch + 1] : 0xFFFFu;
+    uint32_t nA = 0, nB = 0;
+    auto count = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
+#pragma unroll
+      for (int u = 0; u < kPctUnroll; ++u) {
+        if (tail && rb + (int64_t)u * kPctWaves >= r1) continue;  // clamped row
+        const uint32_t ka = v[u] & 0x7FFFu, kb = (v[u] >> 16) & 0x7FFFu;
+        // keys and window starts are below 2^16: the difference wraps (top
+        // bit set) exactly for keys below the window
+        const uint32_t da = ka - wA, db = kb - wB;
+        nA += da >> 31;
+        nB += db >> 31;
+        if (da < (uint32_t)kWin) atomicAdd(&hist[(da >> 1) * kPctCh + colA], 1u << (16 * (da & 1u)));
+        if (db < (uint32_t)kWin) atomicAdd(&hist[(db >> 1) * kPctCh + colB], 1u << (16 * (db & 1u)));
+      }
+    };
+    stream_rows(x, lane_offset(ch, c), ld, r0, r1, wave, count);
+    if (nA) atomicAdd(&below[colA], nA);
+    if (nB) atomicAdd(&below[colB], nB);
+    __syncthreads();
+    // this segment's partial: unit (slab, channel block), first or second part
+    const int64_t slab = r0 / per_wg;
+    const int64_t unit = slab * cblocks + c0 / kPctCh;
+    uint32_t* dst = part + (2 * unit + (r0 == slab * per_wg ? 0 : 1)) * kPartWords;
+    for (int i = threadIdx.x; i < (kWin / 8) * kPctCh; i += kPctThreads) {
+      const int col = i % kPctCh, quad = i / kPctCh;  // words 4 quad .. 4 quad + 3
+      uint4 w;
+      w.x = hist[(4 * quad + 0) * kPctCh + col];
+      w.y = hist[(4 * quad + 1) * kPctCh + col];
+      w.z = hist[(4 * quad + 2) * kPctCh + col];
+      w.w = hist[(4 * quad + 3) * kPctCh + col];
+      hist[(4 * quad + 0) * kPctCh + col] = 0u;
+      hist[(4 * quad + 1) * kPctCh + col] = 0u;
+      hist[(4 * quad + 2) * kPctCh + col] = 0u;
+      hist[(4 * quad + 3) * kPctCh + col] = 0u;
+      *reinterpret_cast<uint4*>(dst + col * kPartStride + 4 * quad) = w;
+    }
+    for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) {
+      dst[i * kPartStride + kWin / 2] = below[i];
+      below[i] = 0u;
+    }
+    __syncthreads();
+  });
+}
+
+// Per channel: the window counts summed over the partials of its channel
+// block; the keys of ranks lo and hi when both lie in the window. Otherwise
+// the channel is flagged for the two exact passes (which gate on n_failed),
+// and its buffers of those passes are cleared here (the passes count every
+// channel, but only flagged channels' counts are read).
+__global__ __launch_bounds__(256) void pct_final_window_kernel(
+    const uint32_t* __restrict__ part, const uint32_t* __restrict__ wlo, int64_t rows, int c,
+    int64_t per_wg, double q, float* __restrict__ stats, uint8_t* __restrict__ failed,
+    uint32_t* __restrict__ n_failed, uint32_t* __restrict__ h1, uint32_t* __restrict__ h2,
+    uint32_t* __restrict__ minkey) {
+  __shared__ uint32_t nf[4];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ch = blockIdx.x * 4 + wv;
+  bool fail = false;
+  if (ch < c) {
+    const int cblocks = (c + kPctCh - 1) / kPctCh;
+    const int cb = ch / kPctCh, col = col_of(ch % kPctCh);
+    const int64_t full_slabs = rows / per_wg;
+    const int64_t n_slabs = (rows + per_wg - 1) / per_wg;
+    uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t nbelow = 0;
+    for (int64_t slab = 0; slab < n_slabs; ++slab) {
+      // the unit's place in the work sequence; split when a slice boundary
+      // (a multiple of per_wg) falls strictly inside it
+      const int64_t rn = slab < full_slabs ? per_wg : rows - full_slabs * per_wg;
+      const int64_t s0 = slab * cblocks * per_wg + cb * rn;
+      const int nparts = (s0 / per_wg != (s0 + rn - 1) / per_wg) ? 2 : 1;
+      const int64_t unit = slab * cblocks + cb;
+      for (int k = 0; k < nparts; ++k) {
+        const uint32_t* src = part + (2 * unit + k) * kPartWords + (int64_t)col * kPartStride;
+        const uint4 w = reinterpret_cast<const uint4*>(src)[lane];
+        cnt[0] += w.x & 0xFFFFu;
+        cnt[1] += w.x >> 16;
+        cnt[2] += w.y & 0xFFFFu;
+        cnt[3] += w.y >> 16;
+        cnt[4] += w.z & 0xFFFFu;
+        cnt[5] += w.z >> 16;
+        cnt[6] += w.w & 0xFFFFu;
+        cnt[7] += w.w >> 16;
+        nbelow += src[kWin / 2];
+      }
+    }
+    int64_t lo, hi;
+    double f;
+    type7_ranks(rows, q, &lo, &hi, &f);
+    uint32_t in_win = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in_win += cnt[i];
+    for (int d = 32; d >= 1; d >>= 1) in_win += (uint32_t)__shfl_xor((int)in_win, d, 64);
+    fail = !(lo >= nbelow && hi < nbelow + (int64_t)in_win);
+    if (fail) {
+      reinterpret_cast<uint4*>(h1 + (int64_t)ch * 256)[lane] = make_uint4(0u, 0u, 0u, 0u);
+      reinterpret_cast<uint2*>(h2 + (int64_t)ch * 128)[lane] = make_uint2(0u, 0u);
+      if (lane == 0) {
+        minkey[ch] = 0xFFFFFFFFu;
+        failed[ch] = 1;
+      }
+    } else {
+      uint32_t blo, bhi;
+      int64_t before;
+      wave_find_rank<8>(cnt, lo - nbelow, &blo, &before);
+      wave_find_rank<8>(cnt, hi - nbelow, &bhi, &before);
+      if (lane == 0) {
+        const uint32_t w0 = wlo[ch];
+        const double vlo = (double)__uint_as_float((w0 + blo) << 16);
+        const double vhi = (double)__uint_as_float((w0 + bhi) << 16);
+        const double d = __dsub_rn(vhi, vlo);
+        const double t = __dmul_rn(f, d);
+        const double r = __dadd_rn(vlo, t);
+        stats[ch] = __double2float_rn(r);
+        failed[ch] = 0;
+      }
+    }
+  }
+  // one count update per block (a single counter hit by every failing wave
+  // would serialize)
+  if (lane == 0) nf[wv] = fail ? 1u : 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t n = nf[0] + nf[1] + nf[2] + nf[3];
+    if (n) atomicAdd(n_failed, n);
+  }
+}
+
+// Fill n words with a value (the buffers of the exact passes, before they run
+// for every channel).
+__global__ void pct_zero_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = value;
 }
 
 // Top-n mask by radix select over the stats' bit patterns (stats are >= 0,
@@ -500,11 +706,43 @@ int cu_count() {
 }
 }  // namespace
 
-size_t hif4_percentile_ws_bytes(int64_t c) {
-  // h1 [c][256] + h2 [c][128] + minkey [c] (u32) + sel [c] (16 B), 256-B aligned parts
+namespace {
+// Grid of a streaming pass over `rows` rows: a whole number of waves of
+// `resident` workgroups (one per CU), each taking an equal slice of the
+// (channel block, row) sequence of at most 65535 rows.
+bool pass_grid(int64_t rows, int ci, int64_t resident, int64_t* per_wg, int64_t* grid) {
+  const int cblocks = (ci + kPctCh - 1) / kPctCh;
+  const int64_t total = (int64_t)cblocks * rows;
+  const int64_t waves = (total + resident * 65535 - 1) / (resident * 65535);
+  *per_wg = (total + resident * waves - 1) / (resident * waves);
+  *grid = (total + *per_wg - 1) / *per_wg;
+  return *grid <= 0x7FFFFFFF;
+}
+
+// The window pass runs on a grid for 256 resident workgroups (MI355X's CU
+// count) whatever the device reports, so that its partials -- two per unit,
+// one unit per (slab of per_wg rows, channel block) -- depend only on rows
+// and c and the workspace size can be stated without a device.
+constexpr int64_t kWindowResident = 256;
+constexpr int64_t kWindowMinRows = 8192;
+
+int64_t window_partials(int64_t rows, int64_t c) {
+  if (rows < kWindowMinRows) return 0;
+  int64_t per_wg, grid;
+  pass_grid(rows, (int)c, kWindowResident, &per_wg, &grid);
+  const int64_t cblocks = (c + kPctCh - 1) / kPctCh;
+  return 2 * ((rows + per_wg - 1) / per_wg) * cblocks;
+}
+}  // namespace
+
+size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c) {
+  // h1 [c][256] + h2 [c][128] + minkey [c] + sel [c] (16 B) + window start [c]
+  // + window partials + failed [c] (u8) + exact-channel count (last part),
+  // 256-B aligned parts
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   return al((size_t)c * 256 * 4) + al((size_t)c * 128 * 4) + al((size_t)c * 4) +
-         al((size_t)c * sizeof(PctSel));
+         al((size_t)c * sizeof(PctSel)) + al((size_t)c * 4) +
+         al((size_t)window_partials(rows, c) * kPartWords * 4) + al((size_t)c) + al(4);
 }
 
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
@@ -519,33 +757,64 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
   uint32_t* minkey = (uint32_t*)ws;
   ws += al((size_t)c * 4);
   PctSel* sel = (PctSel*)ws;
+  ws += al((size_t)c * sizeof(PctSel));
+  uint32_t* wlo = (uint32_t*)ws;
+  ws += al((size_t)c * 4);
+  uint32_t* part = (uint32_t*)ws;
+  ws += al((size_t)window_partials(rows, c) * kPartWords * 4);
+  uint8_t* failed = (uint8_t*)ws;
+  ws += al((size_t)c);
+  uint32_t* n_exact = (uint32_t*)ws;  // channels resolved by the two exact passes
 
   const int ci = (int)c;
-  hipLaunchKernelGGL(pct_init_kernel, dim3(256), dim3(256), 0, stream, h1, h2, minkey, ci);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  // Grid: a whole number of waves of resident workgroups (one per CU), each
-  // taking an equal slice of the (channel block, row) sequence of at most
-  // 65535 rows.
-  const int cblocks = (ci + kPctCh - 1) / kPctCh;
-  const int64_t total = (int64_t)cblocks * rows;
-  const int64_t resident = (int64_t)cu_count();
-  const int64_t waves = (total + resident * 65535 - 1) / (resident * 65535);
-  const int64_t per_wg = (total + resident * waves - 1) / (resident * waves);
-  const int64_t grid = (total + per_wg - 1) / per_wg;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipError_t e;
+  int64_t per_wg, grid;
+  if (!pass_grid(rows, ci, cu_count(), &per_wg, &grid)) return hipErrorInvalidValue;
+  // The sampled window pays off on long columns; the sample (every 8th row)
+  // is read with an 8x row stride, which must keep the pass's 32-bit buffer
+  // offsets in range (ld <= 2^19).
+  const bool window = rows >= kWindowMinRows && ld <= ((int64_t)1 << 19);
+  const uint32_t* gate = nullptr;
+  if (window) {
+    const int64_t rows_s = (rows + 7) / 8;
+    int64_t per_s, grid_s;
+    int64_t per_w, grid_w;
+    if (!pass_grid(rows_s, ci, cu_count(), &per_s, &grid_s) ||
+        !pass_grid(rows, ci, kWindowResident, &per_w, &grid_w))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h1, (int64_t)c * 256, 0u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid_s), dim3(kPctThreads), 0, stream, x,
+                       rows_s, ci, ld * 8, per_s, h1, (const uint32_t*)nullptr);
+    hipLaunchKernelGGL(pct_select_window_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1,
+                       rows_s, ci, q, wlo, n_exact);
+    hipLaunchKernelGGL(pct_window_kernel, dim3((unsigned)grid_w), dim3(kPctThreads), 0, stream, x,
+                       rows, ci, ld, per_w, (const uint32_t*)wlo, part);
+    hipLaunchKernelGGL(pct_final_window_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream,
+                       (const uint32_t*)part, (const uint32_t*)wlo, rows, ci, per_w, q, stats, failed,
+                       n_exact, h1, h2, minkey);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // The exact passes below run only if a channel was flagged; the flagged
+    // channels' buffers were cleared by the final window kernel.
+    gate = n_exact;
+  } else {
+    hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h1, (int64_t)c * 256, 0u);
+    hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h2, (int64_t)c * 128, 0u);
+    hipLaunchKernelGGL(pct_zero_kernel, dim3(64), dim3(256), 0, stream, minkey, (int64_t)c,
+                       0xFFFFFFFFu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
-                     rows, ci, ld, per_wg, h1);
+                     rows, ci, ld, per_wg, h1, gate);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1, rows, ci, q,
-                     sel);
+                     sel, gate, window ? (uint32_t*)nullptr : n_exact);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pct_pass2_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
-                     rows, ci, ld, per_wg, sel, h2, minkey);
+                     rows, ci, ld, per_wg, sel, h2, minkey, gate);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel, minkey,
-                     rows, ci, q, stats);
+                     rows, ci, q, stats, gate, window ? (const uint8_t*)failed : nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ci <= 8 * kMaskThreads)
     hipLaunchKernelGGL(topn_mask_kernel<8>, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,

@@ -189,6 +189,14 @@ def percentile_workspace_bytes(rows, c):
     return int(lib().hif4_percentile_workspace_bytes(rows, c))
 
 
+def percentile_exact_channels(workspace, rows, c):
+    """Channels of the last hif4_percentile_mask call on `workspace` whose
+    statistic came from the two exact passes (c unless the one-pass window
+    path ran; then the channels it missed). Reads the count from the device."""
+    off = percentile_workspace_bytes(rows, c) - 256
+    return int(workspace[off:off + 4].view(torch.int32).item())
+
+
 def percentile_mask(x, q, n_protect, stats=None, mask=None, workspace=None, stream=None):
     """Per-channel type-7 quantile of |x| over rows -> (stats fp32 [c], mask u8 [c])."""
     _check_bf16_rows(x, "x")

@@ -185,7 +185,7 @@ HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16(const uint8_t *x_codes, const u
 
 /*
  * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask
- * over c channels.
+ * over rows x c values (depends on rows from 8192 rows on; no device needed).
  */
 HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
 
@@ -201,12 +201,28 @@ HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
  *  mask[ch] = 1 for the n_protect largest stats (ties: lower ch first), else 0.
  *
  *  x         bf16 [rows][ld], 16-byte aligned, ld % 8 == 0, c <= ld <= 2^22,
- *            rows >= 1.
+ *            1 <= rows < 2^32.
  *  c         number of channels, 1 <= c <= 65536.   q in [0, 1].
  *  n_protect 0 <= n_protect <= c (e.g. ceil(p * c) for a top-p mask).
  *  stats     fp32 [c];  mask  u8 [c].
  *  workspace >= hif4_percentile_workspace_bytes(rows, c) bytes, 256-byte
- *            aligned; scratch.
+ *            aligned; scratch. Below 8192 rows about 1.6 KiB per channel;
+ *            from 8192 rows on it also holds the one-pass path's partial
+ *            counts, 133,120 bytes each, about 512 of them per 2^24
+ *            (row, 128-channel block) pairs or part thereof: 75 MB for
+ *            57,600 x 5120, 213 MB for 921,600 x 5120. On completion the u32 at byte offset
+ *            hif4_percentile_workspace_bytes(rows, c) - 256 holds the number
+ *            of channels whose statistic came from the two exact radix
+ *            passes: c when rows < 8192 or ld > 2^19; otherwise the channels
+ *            for which the one-pass window (see below) missed rank lo or hi.
+ *
+ *  Long columns (rows >= 8192, ld <= 2^19) first take a one-pass path: the
+ *  coarse histogram of every 8th row places, per channel, a window of 512
+ *  consecutive magnitude keys around the quantile; one pass over all rows
+ *  counts the keys below the window and each key inside it. Channels whose
+ *  ranks lo and hi both fall inside are final; the rest are recomputed by the
+ *  two exact passes (launched always, skipped on the device when no channel
+ *  needs them). Results are identical either way.
  */
 HIF4_EXPORT hif4_status hif4_percentile_mask(const void *x, int64_t rows, int64_t c, int64_t ld, double q,
                                  int64_t n_protect, float *stats, uint8_t *mask,

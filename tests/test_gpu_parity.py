@@ -287,18 +287,43 @@ def test_linear_empty_k_gives_zero(hip):
 
 # -------------------------------------------------------------- percentile
 
+def window_misses(bits, q):
+    """Channels the one-pass window path leaves to the exact passes, by the
+    rule the header states: the window is the 512 keys starting one coarse bin
+    (128 keys) below the coarse bin of rank floor(q (n_s - 1)) among every 8th
+    row; a channel misses when its ranks lo or hi fall outside the window."""
+    rows, c = bits.shape
+    if rows < 8192:
+        return c
+    k = (bits & 0x7FFF).astype(np.int64)
+    s = np.sort(k[::8], axis=0)
+    b = s[int(np.floor(q * (s.shape[0] - 1)))] >> 7
+    w = np.maximum(b - 1, 0) << 7
+    lo = int(np.floor(q * (rows - 1)))
+    hi = min(lo + 1, rows - 1)
+    below = (k < w).sum(axis=0)
+    inside = ((k >= w) & (k < w + 512)).sum(axis=0)
+    return int((~((lo >= below) & (hi < below + inside))).sum())
+
+
 def run_pct_case(hip, bits, q, n_protect, ld=None):
     x = dev_bf16(bits)
     if ld is not None:
         full = torch.zeros((bits.shape[0], ld), dtype=torch.bfloat16, device="cuda")
         full[:, :bits.shape[1]] = x
         x = full[:, :bits.shape[1]]
-    stats, mask = hip.percentile_mask(x, q, n_protect)
+    rows, c = bits.shape
+    ws = torch.empty((hip.percentile_workspace_bytes(rows, c),), dtype=torch.uint8, device="cuda")
+    stats, mask = hip.percentile_mask(x, q, n_protect, workspace=ws)
     s_ref = oracle.percentile(bits, q)
     m_ref = oracle.topn_mask(s_ref, n_protect)
     s_gpu = stats.cpu().numpy()
     assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(mask.cpu().numpy(), m_ref)
+    # which path produced each statistic: the count is exact integer work too
+    exact = hip.percentile_exact_channels(ws, rows, c)
+    assert exact == window_misses(bits, q), (exact, window_misses(bits, q))
+    return exact
 
 
 def test_percentile_tiny_workload(hip):
@@ -324,6 +349,35 @@ def test_percentile_constant_and_tied_channels(hip):
     x[:, 40] = x[:, 30] ^ np.uint16(0x8000)   # sign-flipped duplicate: same |x|
     run_pct_case(hip, x, 0.99, 40)
     run_pct_case(hip, x, 0.5, 128)
+
+
+@pytest.mark.parametrize("rows,c,q,n", [(8192, 64, 0.999, 3), (10000, 300, 0.999, 3),
+                                        (20000, 130, 0.5, 13), (9000, 64, 1.0, 5),
+                                        (9001, 200, 0.0, 7), (12345, 77, 0.9, 1)])
+def test_percentile_sampled_window_path(hip, rows, c, q, n):
+    """Long columns (>= 8192 rows) take the one-pass path: a window of keys
+    around the quantile of every 8th row, exact whenever both ranks land in it."""
+    bits = workloads.bits(workloads.heavy_tailed_x(rows, c, seed=rows + c, outlier_channels=2))
+    ld = ((c + 7) // 8) * 8 if c % 8 else None
+    exact = run_pct_case(hip, bits, q, n, ld=ld)
+    if 0.0 < q < 1.0:
+        assert exact == 0  # the window resolved every channel of these columns
+
+
+def test_percentile_sampled_window_misled_falls_back(hip):
+    """Channels whose sampled rows (every 8th) are unrepresentative: the
+    window misses the true ranks, the exact passes run for those channels,
+    and every statistic still matches."""
+    r = np.random.default_rng(61)
+    rows, c = 16384, 192
+    x = np.abs(r.standard_normal((rows, c))).astype(np.float32)
+    x[0::8, :40] *= 1e-6           # the sample sees tiny values, the rest is large
+    x[1::8, 40:80] *= 1e6          # the sample misses a block of huge values
+    x[:, 80:100] = 0.0
+    x[0::8, 80:100] = 3.0          # only the sampled rows are non-zero
+    bits = uc.truncate_to_bits(x.astype(np.float64))
+    for q in (0.999, 0.5, 0.05):
+        assert run_pct_case(hip, bits, q, 9) >= 20  # at least the 20 zero columns fall back
 
 
 def test_percentile_ties_across_many_channels(hip):
