@@ -14,8 +14,11 @@
 //           lo, plus the smallest key of the coarse bin of rank hi when that
 //           is a different bin -> the exact keys of ranks lo and hi;
 //   final   type-7 interpolation in double, rounded once to fp32.
-// Histograms are integers (LDS atomics per workgroup, then global atomics):
-// results do not depend on scheduling.
+// Long columns first take a one-pass path (a window of keys placed by a
+// sample of every 8th row; see the section further down) and fall back to
+// the two passes only for channels the window missed.
+// Histograms are integers (LDS atomics per workgroup, then global atomics or
+// per-segment partials): results do not depend on scheduling.
 //
 // Mapping: the work of a pass is the sequence of (channel block, row) pairs,
 // a channel block being 128 channels. The grid is a whole number of waves of
