@@ -35,6 +35,7 @@ namespace hif4 {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 256, kBN = 256;
@@ -68,14 +69,16 @@ __device__ __forceinline__ void stage_barrier() {
 // Decode (HiF4 element = S1P2 nibble k/4 x 2^E x v(c), E = e2 + e3 in
 // {0, 1, 2}, v(c) = 2^(e-31) (1 + m/4) with e = c >> 2, m = c & 3): write
 // e = 2a + p. Then |x| = [k (1 + m/4) 2^(E + p - 33)] 2^(2a), and the bracket
-// takes one of 24 x 8 values, all exact in bf16 (k (4 + m) <= 49). A 24-entry
-// LDS table holds, per (m, E, p), the low and high bytes of the bracket's
-// bf16 for k = 0..7 as two byte planes. Multiplying by 2^(2a) adds a to the
+// depends on m and s = E + p only (s in 0..3) and takes one of 16 x 8
+// values, all exact in bf16 (k (4 + m) <= 49). A 16-entry LDS table holds,
+// per (m, s), the low and high bytes of the bracket's bf16 for k = 0..7 as
+// two byte planes. Multiplying by 2^(2a) adds a to the
 // high byte of every non-zero value (the exponent's low bit stays put), so a
 // level-3 quad decodes as: add a to the high plane (sparing k = 0), two
 // v_perm_b32 plane lookups by the 4 magnitudes, OR the 4 signs into the high
-// bytes, two v_perm_b32 to interleave into 4 bf16. The table is 384 B: the
-// lanes of a read either share an entry (broadcast) or hit distinct banks.
+// bytes, two v_perm_b32 to interleave into 4 bf16. The table is 256 B, one
+// entry per 16-byte bank group: the 16 lanes served together either share an
+// entry (broadcast) or hit distinct bank groups.
 //
 // Thread t decodes row t of the tile, whose codes its own wave fetched.
 // LDS map (bytes):
@@ -83,7 +86,7 @@ __device__ __forceinline__ void stage_barrier() {
 //   [64K, 96K)        decoded A: 2 buffers x 256 rows x 64 B (same swizzle)
 //   [96K, 144K)       A code ring: 3 slots x 2 units x 256 rows x 32 B
 //   [144K, 152K)      A meta ring: 2 slots x 4 units x 256 rows x 4 B
-//   [152K, +384)      decode table
+//   [152K, +256)      decode table
 // Code bytes are fetched two units (64 B) per row and meta four units (16 B)
 // per row, so that one DMA instruction touches 16 (codes) or 64 (meta) rows
 // instead of 32-64 rows for 32 or 4 bytes each: the vector L1 looks up far
@@ -104,7 +107,7 @@ constexpr int kCodeSlotBytes = 256 * 64;                     // 16384: 2 units
 constexpr int kLdsAMeta = kLdsACodes + 3 * kCodeSlotBytes;   // 147456
 constexpr int kMetaSlotBytes = 256 * 16;                     // 4096: 4 units
 constexpr int kLdsTable = kLdsAMeta + 2 * kMetaSlotBytes;    // 155648
-constexpr int kLdsW4A4Bytes = kLdsTable + 24 * 16;           // 156032
+constexpr int kLdsW4A4Bytes = kLdsTable + 16 * 16;           // 155904
 
 // 16-byte LDS access through a native vector type. (Through the uint4
 // struct it is split into four i32 accesses and re-merged, and the compiler
@@ -169,10 +172,10 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // ---- decode table: entry (m, E, p) at 16 ((3m + E) 2 + p), built by threads 0..23
-  if (tid < 24) {
-    const int m = tid / 6, E = (tid >> 1) % 3, p = tid & 1;
-    const float d = ldexpf(1.0f + 0.25f * (float)m, E + p - 33);  // value of k = 1
+  // ---- decode table: entry (m, s = E + p) at 16 (4m + s), built by threads 0..15
+  if (tid < 16) {
+    const int m = tid >> 2, sx = tid & 3;
+    const float d = ldexpf(1.0f + 0.25f * (float)m, sx - 33);  // value of k = 1
     uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
 #pragma unroll
     for (int k = 1; k < 8; ++k) {
@@ -288,7 +291,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   auto dec_unit = [&]() {
     const uint32_t c = dmw & 255u;
     const uint32_t a = c >> 3, p = (c >> 2) & 1u, m = c & 3u;
-    dbase = lds + kLdsTable + (m * 6u + p) * 16u;
+    dbase = lds + kLdsTable + (m * 4u + p) * 16u;  // entry (m, p); + E selects s = E + p
     dd = __builtin_amdgcn_perm(a, a, 0u);
     dd0 = dd & 0xFFFFFF00u;
   };
@@ -296,7 +299,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   auto dec_tab = [&](int hn_odd, int q) {
     const int g = hn_odd * 4 + (q >> 1);
     const uint32_t E = ((dmw >> (8 + g)) & 1u) + ((dmw >> (16 + 2 * g + (q & 1))) & 1u);
-    t8[q] = lds_u32x4(dbase + 32 * E);
+    t8[q] = lds_u32x4(dbase + 16 * E);
   };
   // decode quad q of half hn; the second quad of a group writes the group
   auto dec_quad = [&](int hn, int q) {
@@ -555,13 +558,16 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
         if (row >= M || colq >= N) continue;
         const size_t off = (size_t)row * ldy + colq;
         if (vec_ok && colq + 4 <= N) {
+          // non-temporal: Y is written once and read by no one in this
+          // kernel, so it should not push the operand tiles out of L2/MALL
           if (y_bf16) {
             const uint32_t lo = f32_to_bf16_rne(d0) | (f32_to_bf16_rne(d1) << 16);
             const uint32_t hi = f32_to_bf16_rne(d2) | (f32_to_bf16_rne(d3) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) = make_uint2(lo, hi);
+            __builtin_nontemporal_store(
+                u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(Y) + off));
           } else {
-            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Y) + off) =
-                f32x4_t{d0, d1, d2, d3};
+            __builtin_nontemporal_store(
+                f32x4_t{d0, d1, d2, d3}, reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Y) + off));
           }
         } else {
           const float d[4] = {d0, d1, d2, d3};
