@@ -40,6 +40,7 @@ def _lib():
         lib.hif4o_topn_mask.argtypes = [p, i64, i64, p]
         lib.hif4o_topn_mask.restype = ctypes.c_int
         lib.hif4o_quantize_f32.argtypes = [p, i64, i64, i64, p, p]
+        lib.hif4o_quantize_offsets.argtypes = [p, i64, i64, i64, p, p, p, p]
         lib.hif4o_quantize_f32.restype = ctypes.c_int
         lib.hif4o_higptq_unit.argtypes = [p, i64, i64, p, i64, p, p]
         lib.hif4o_higptq_unit.restype = ctypes.c_int
@@ -187,6 +188,25 @@ def quantize_f32(x: np.ndarray):
     meta = np.zeros((rows, k // 64), np.uint32)
     _check(_lib().hif4o_quantize_f32(_ptr(x), rows, k, k, _ptr(codes), _ptr(meta)),
            "quantize_f32")
+    return codes, meta
+
+
+def quantize_offsets(x_bits: np.ndarray, koff: np.ndarray, moff: np.ndarray):
+    """HiF4-quantize bf16 rows [rows][k] with given HiAutoRound offsets
+    (HiFloat4 calibration article, section 3.2): koff float32 [rows][k/4], one
+    per level-3 group, shifts the level-3 exponent by RZ(K); moff float32
+    [rows][k] is added to each element's scaled magnitude before rounding.
+    Returns (codes, meta)."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, k = x_bits.shape
+    koff = np.ascontiguousarray(koff, dtype=np.float32)
+    moff = np.ascontiguousarray(moff, dtype=np.float32)
+    if koff.shape != (rows, k // 4) or moff.shape != (rows, k):
+        raise ValueError("koff must be [rows][k/4] and moff [rows][k]")
+    codes = np.zeros((rows, k // 2), np.uint8)
+    meta = np.zeros((rows, k // 64), np.uint32)
+    _check(_lib().hif4o_quantize_offsets(_ptr(x_bits), rows, k, k, _ptr(koff), _ptr(moff),
+                                         _ptr(codes), _ptr(meta)), "quantize_offsets")
     return codes, meta
 
 

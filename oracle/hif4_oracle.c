@@ -16,6 +16,10 @@
  *              statistics of the data it covers.
  *  [HiFlat]    same article, section 3.3 "HiFlatQuant": HiF4's range is wide
  *              enough that no clipping thresholds are needed.
+ *  [HiAR]      same article, section 3.2 "HiAutoRound": learnable offsets K
+ *              (16 per unit, added to the level-3 exponents, E' = E + RZ(K))
+ *              and M (mantissa compensation, shifted M' = M >> RZ(K) before
+ *              it is added), and the quantize step of its training loop.
  *  [TA-method] "Tail-Aware HiFloat4: W4A4 PTQ calibration for Wan2.2"
  *              (agents-report.net), sections "方法概述" and
  *              "尾部百分位統計的動機": per-channel tail percentile statistics
@@ -94,7 +98,9 @@ static double s1p2_value(int nib)
  * covers, [HiFlat] says no clipping is needed): choose every scale as small
  * as it can be without any element exceeding its grid maximum, then round
  * each element to the nearest grid point, ties to even. */
-static void quantize_unit(const double x[UNIT], uint8_t codes[32], uint32_t *meta)
+/* Steps 1-4 of the unit encoding: the level-1 code c and the level-2 and
+ * level-3 bits, each from the maxima of the values it covers. */
+static void unit_scales(const double x[UNIT], int *c_out, int e2[8], int e3[16])
 {
     /* step 1: the maxima of |x| over the unit, each level-2 group (8) and
      * each level-3 group (4). */
@@ -122,13 +128,19 @@ static void quantize_unit(const double x[UNIT], uint8_t codes[32], uint32_t *met
 
     /* step 3: level-2 bit of group g is set iff the group does not fit
      * under 1.75 * 2 * s (its largest magnitude with e2 = 0). */
-    int e2[8];
     for (int g = 0; g < 8; ++g) e2[g] = M8[g] > 1.75 * 2.0 * s;
 
     /* step 4: level-3 bit of group q is set iff the group does not fit
      * under 1.75 * 2^e2 * s (its largest magnitude with e3 = 0). */
-    int e3[16];
     for (int q = 0; q < 16; ++q) e3[q] = M4[q] > 1.75 * e1_factor(e2[q / 2]) * s;
+    *c_out = c;
+}
+
+static void quantize_unit(const double x[UNIT], uint8_t codes[32], uint32_t *meta)
+{
+    int c, e2[8], e3[16];
+    unit_scales(x, &c, e2, e3);
+    double s = hif4o_e6m2_value(c);
 
     /* step 5: round |x| onto the grid {k D / 4 : k = 0..7}, D = s 2^e2 2^e3,
      * to nearest with ties to even k. The grid midpoints are (2m+1) D / 8;
@@ -196,6 +208,88 @@ int hif4o_quantize(const uint16_t *x, int64_t rows, int64_t k, int64_t ld,
                 v[j] = val;
             }
             quantize_unit(v, codes + r * (k / 2) + u * 32, meta + r * units + u);
+        }
+    }
+    return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* ------------------------------------------------- HiAutoRound offsets */
+
+/* The quantize step of [HiAR] with given offsets (the training loop that
+ * learns them is out of scope). Per unit: c and the level-2 bits as in
+ * hif4o_quantize; each level-3 bit e3 of the 16 groups, then its offset.
+ * READINGS ([HiAR] gives the two formulas only):
+ *  - K and M are real-valued. K has one entry per level-3 group, K [rows][k/4];
+ *    M one per element ("independent mantissa" in the section's comparison),
+ *    M [rows][k].
+ *  - RZ is rounding toward zero. The level-3 exponent is a 1-bit field, so
+ *    e3' = e3 + RZ(K) is held to {0, 1}.
+ *  - "M >> RZ(K)" on a real M is M * 2^-d with d = e3' - e3, the change of
+ *    the exponent actually applied: that is what keeps M' on the scale of
+ *    the element's new step, the continuity the section asks for.
+ *  - M' is added to the element's magnitude in units of its step (as
+ *    AutoRound adds its rounding offset to W / s), then rounded to the
+ *    nearest k, ties to even, held to 0..7; the sign is kept; a zero element
+ *    has no sign.
+ *  - Precision: the decision is taken in IEEE binary32, as the kernel takes
+ *    it: t = fl(|x| / (D / 4)) with D = s 2^(e2 + e3') (exact in binary32),
+ *    u = fl(t + M'), k = rint(u). For bf16 x, fl(t) never crosses a
+ *    rounding tie (t has at most 8 significant bits over a divisor of
+ *    4 + m), so with K = 0 and M = 0 this is exactly hif4o_quantize. */
+static int offset_e3(int e3, float K)
+{
+    float t = (float)e3 + truncf(K);
+    return t >= 1.0f ? 1 : 0; /* t is a whole number; NaN gives 0 */
+}
+
+int hif4o_quantize_offsets(const uint16_t *x, int64_t rows, int64_t k, int64_t ld,
+                           const float *koff, const float *moff, uint8_t *codes,
+                           uint32_t *meta)
+{
+    if (rows < 0 || k < 0 || k % UNIT != 0 || ld < k) return HIF4O_ERR_ARG;
+    int64_t units = k / UNIT;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t u = 0; u < units; ++u) {
+            double v[UNIT];
+            for (int j = 0; j < UNIT; ++j) {
+                double val = bf16_value(x[r * ld + u * UNIT + j]);
+                if (!isfinite(val)) {
+                    bad = 1;
+                    val = 0.0;
+                }
+                v[j] = val;
+            }
+            int c, e2[8], e3[16];
+            unit_scales(v, &c, e2, e3);
+            const float *ku = koff + r * (k / 4) + u * 16;
+            const float *mu = moff + r * k + u * UNIT;
+            int e3n[16];
+            for (int q = 0; q < 16; ++q) e3n[q] = offset_e3(e3[q], ku[q]);
+            float s = (float)hif4o_e6m2_value(c); /* exact in binary32 */
+            uint8_t *uc = codes + r * (k / 2) + u * 32;
+            memset(uc, 0, 32);
+            for (int j = 0; j < UNIT; ++j) {
+                int q = j / 4;
+                float D = ldexpf(s, e2[j / 8] + e3n[q]);
+                float ax = (float)fabs(v[j]); /* exact: v is a bf16 value */
+                int d = e3n[q] - e3[q];
+                float mp = d > 0 ? mu[j] * 0.5f : (d < 0 ? mu[j] * 2.0f : mu[j]);
+                float t = ax / (D * 0.25f);
+                float uu = t + mp;
+                int kk = 0;
+                if (uu > 0.0f) {
+                    float rr = rintf(uu);
+                    kk = rr >= 7.0f ? 7 : (int)rr;
+                }
+                int sign = (v[j] < 0.0) && (kk != 0);
+                uc[code_byte(j)] |= (uint8_t)((kk | (sign << 3)) << code_shift(j));
+            }
+            uint32_t m = (uint32_t)c;
+            for (int g = 0; g < 8; ++g) m |= (uint32_t)e2[g] << (8 + g);
+            for (int q = 0; q < 16; ++q) m |= (uint32_t)e3n[q] << (16 + q);
+            meta[r * units + u] = m;
         }
     }
     return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
