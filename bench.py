@@ -136,6 +136,33 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
     return out
 
 
+def time_autoround(torch, hif4, dev, w_bf16, stream, reps=10):
+    """The quantize step of HiAutoRound (given offsets K per level-3 group, M
+    per element) over the whole weight, as each iteration of its training loop
+    runs it. Algorithmic bytes: read 2 (x) + 4 (M) + 1 (K) B per element,
+    write 0.5 + 1/16 B (codes, meta)."""
+    n, k = w_bf16.shape
+    g = torch.Generator(device="cuda").manual_seed(5)
+    koff = torch.rand((n, k // 4), generator=g, device=dev) * 5.0 - 2.5
+    moff = torch.rand((n, k), generator=g, device=dev) * 2.0 - 1.0
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    meta = torch.empty((n, k // 64), dtype=torch.int32, device=dev)
+    hif4.quantize_offsets(w_bf16, koff, moff, codes=codes, meta=meta, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        hif4.quantize_offsets(w_bf16, koff, moff, codes=codes, meta=meta, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = n * k * (2 + 4 + 1 + 0.5 + 1 / 16)
+    log(f"HiAutoRound quantize step over W {n}x{k}: {ms:.3f} ms")
+    return {"workload": f"W {n}x{k} bf16 (the FFN-up weight), K uniform in [-2.5, 2.5), "
+                        "M uniform in [-1, 1)",
+            "ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def time_calibration(torch, workloads, hif4, dev, stream, reps=3):
     """The calibration pass: percentile + top-n mask over 16 calibration
     batches (921,600 x 5120 bf16 = 9.4 GB), then the masked quantize of the
@@ -333,6 +360,7 @@ def main():
     if not args.no_extras:
         out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, stream)}
         out["extensions"]["calibration"] = time_calibration(torch, workloads, hif4, dev, stream)
+        out["extensions"]["hiautoround_quantize"] = time_autoround(torch, hif4, dev, w, stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(x.cpu(), w.cpu(), mask.cpu().numpy(), args.cpu_rows)

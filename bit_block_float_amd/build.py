@@ -12,7 +12,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhif4.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "pct.hip", "gptq.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "pct.hip", "gptq.hip", "autoround.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 

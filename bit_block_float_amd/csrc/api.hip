@@ -258,6 +258,21 @@ hif4_status hif4_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t l
   return launched(hif4_launch_quantize_f32(x, rows, k, ld, codes, meta, stream));
 }
 
+hif4_status hif4_quantize_offsets(const void* x, int64_t rows, int64_t k, int64_t ld,
+                                  const float* koff, const float* moff, uint8_t* codes,
+                                  uint32_t* meta, hipStream_t stream) {
+  if (rows < 0 || k < 0 || k % 64 != 0 || ld < k) return HIF4_ERR_SHAPE;
+  if (rows == 0 || k == 0) return HIF4_OK;
+  if (!x || !koff || !moff || !codes || !meta) return HIF4_ERR_NULL;
+  if (!aligned(x, 16) || ld % 8 != 0 || !aligned(koff, 16) || !aligned(moff, 16) ||
+      !aligned(codes, 16) || !aligned(meta, 4))
+    return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_quantize_offsets((const uint16_t*)x, rows, k, ld, koff, moff, codes,
+                                               meta, stream));
+}
+
 size_t hif4_higptq_workspace_bytes(int64_t n) {
   if (n < 0) return 0;
   return align256((size_t)n * 64 * sizeof(float));

@@ -113,6 +113,9 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
                                   void* workspace, hipStream_t stream);
 size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c);
 hipError_t hif4_launch_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t hif4_launch_quantize_offsets(const uint16_t* x, int64_t rows, int64_t k, int64_t ld,
+                                        const float* koff, const float* moff, uint8_t* codes,
+                                        uint32_t* meta, hipStream_t stream);
 hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int64_t ld,
                                     uint8_t* codes, uint32_t* meta, hipStream_t stream);
 hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,

@@ -55,6 +55,8 @@ def lib():
         L.hif4_percentile_mask.argtypes = [p, i64, i64, i64, ctypes.c_double, i64, p, p, p, sz, p]
         L.hif4_percentile_mask.restype = ctypes.c_int
         L.hif4_quantize_f32.argtypes = [p, i64, i64, i64, p, p, p]
+        L.hif4_quantize_offsets.argtypes = [p, i64, i64, i64, p, p, p, p, p]
+        L.hif4_quantize_offsets.restype = ctypes.c_int
         L.hif4_quantize_f32.restype = ctypes.c_int
         L.hif4_higptq_workspace_bytes.argtypes = [i64]
         L.hif4_higptq_workspace_bytes.restype = sz
@@ -216,6 +218,25 @@ def percentile_mask(x, q, n_protect, stats=None, mask=None, workspace=None, stre
 def _check_f32_rows(x, name):
     if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D fp32 CUDA tensor with unit column stride")
+
+
+def quantize_offsets(x, koff, moff, codes=None, meta=None, stream=None):
+    """HiF4-quantize bf16 x [rows][k] with given HiAutoRound offsets: koff fp32
+    [rows][k/4] (level-3 exponents), moff fp32 [rows][k] (mantissas).
+    Returns (codes u8, meta int32)."""
+    _check_bf16_rows(x, "x")
+    rows, k = x.shape
+    for t, name, shape in ((koff, "koff", (rows, k // 4)), (moff, "moff", (rows, k))):
+        if (t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != shape
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor of shape {shape}")
+    dev = x.device
+    codes = codes if codes is not None else torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    meta = meta if meta is not None else torch.empty((rows, k // 64), dtype=torch.int32, device=dev)
+    st = lib().hif4_quantize_offsets(_ptr(x), rows, k, x.stride(0), _ptr(koff), _ptr(moff),
+                                     _ptr(codes), _ptr(meta), _stream(stream))
+    _ok(st, "hif4_quantize_offsets")
+    return codes, meta
 
 
 def quantize_f32(x, codes=None, meta=None, stream=None):

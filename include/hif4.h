@@ -240,6 +240,34 @@ HIF4_EXPORT hif4_status hif4_percentile_mask(const void *x, int64_t rows, int64_
 HIF4_EXPORT hif4_status hif4_quantize_f32(const float *x, int64_t rows, int64_t k, int64_t ld,
                               uint8_t *codes, uint32_t *meta, hipStream_t stream);
 
+/*
+ * hif4_quantize_offsets -- the quantize step of HiAutoRound (the calibration
+ * article, section 3.2 "HiAutoRound": learnable offsets K on the level-3
+ * exponents, E' = E + RZ(K), 16 per unit, and M on the mantissas, shifted as
+ * M' = M >> RZ(K) before being added), with the offsets given; the training
+ * loop that learns them is not part of this library.
+ * Readings (the section gives the two formulas only):
+ *   - the level-1 code and level-2 bits are chosen as in hif4_quantize; each
+ *     level-3 bit e3 too, then e3' = clamp(e3 + trunc(K[q]), 0, 1);
+ *   - with d = e3' - e3, M' = M * 2^-d (the shift follows the exponent
+ *     change actually applied);
+ *   - k = clamp(rint(fl(t + M')), 0, 7), t = fl(|x| / (D / 4)),
+ *     D = v(c) 2^(e2 + e3'), each operation IEEE binary32 with round to
+ *     nearest even; the sign of x is kept, a zero code has no sign.
+ * With K = 0 and M = 0 the output equals hif4_quantize's (unmasked).
+ *
+ *  x      bf16 [rows][ld], 16-byte aligned, ld % 8 == 0, ld >= k; finite.
+ *  koff   fp32 [rows][k/4], row stride k/4 (one K per level-3 group, groups
+ *         in K order), 16-byte aligned; finite.
+ *  moff   fp32 [rows][k], row stride k (one M per element), 16-byte aligned;
+ *         finite.
+ *  codes  u8 [rows][k/2], 16-byte aligned.    meta  u32 [rows][k/64].
+ *  rows >= 0, k % 64 == 0. Non-finite inputs give unspecified codes.
+ */
+HIF4_EXPORT hif4_status hif4_quantize_offsets(const void *x, int64_t rows, int64_t k, int64_t ld,
+                                  const float *koff, const float *moff, uint8_t *codes,
+                                  uint32_t *meta, hipStream_t stream);
+
 /* hif4_higptq_workspace_bytes -- workspace of hif4_higptq_unit for n rows. */
 HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
 

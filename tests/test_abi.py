@@ -37,6 +37,7 @@ def test_header_declares_the_four_entry_points():
     names = declared()
     for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
                "hif4_linear_xcodes_wbf16", "hif4_quantize_f32", "hif4_higptq_unit",
+               "hif4_quantize_offsets",
                "hif4_higptq_workspace_bytes",
                "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
                "hif4_status_string", "hif4_version"):
@@ -187,6 +188,26 @@ def test_quantize_f32_argument_checks(L):
     assert q(A + 4, 4, 64, 64, A, A, None) == ALIGN
     assert q(A, 4, 64, 66, A, A, None) == ALIGN             # ld % 4
     assert q(A, 4, 64, 64, A + 8, A, None) == ALIGN
+
+
+def test_quantize_offsets_argument_checks(L):
+    q = L.hif4_quantize_offsets
+
+    def call(x=A, rows=4, k=64, ld=64, ko=A, mo=A, c=A, m=A):
+        return q(x, rows, k, ld, ko, mo, c, m, None)
+    assert call(k=65, ld=72) == SHAPE
+    assert call(k=128, ld=64) == SHAPE                      # ld < k
+    assert call(rows=-1) == SHAPE
+    assert call(rows=0, x=None, ko=None, mo=None, c=None, m=None) == OK  # empty
+    assert call(x=None) == NULL
+    assert call(ko=None) == NULL
+    assert call(mo=None) == NULL
+    assert call(c=None) == NULL
+    assert call(x=A + 8) == ALIGN
+    assert call(ld=68) == ALIGN                             # ld % 8
+    assert call(ko=A + 8) == ALIGN
+    assert call(mo=A + 4) == ALIGN
+    assert call(m=A + 2) == ALIGN
 
 
 def test_higptq_argument_checks(L):
