@@ -14,7 +14,11 @@
 //
 // Tiling: 256x256 output tile per workgroup (4 waves, 2x2, each 128x128 =
 // 4x4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane in
-// AGPRs), one workgroup per CU. Operands reach LDS by direct-to-LDS buffer
+// AGPRs), one workgroup per CU. Two schedules share this design: steps of
+// one HiF4 unit (64 K values, one barrier per step) when K is a multiple of
+// 256 (gemm_w4a4_u64_kernel), else steps of half a unit
+// (gemm_w4a4_kernel); both issue the MFMAs of an output block in the same
+// K order, so they give the same bits. Operands reach LDS by direct-to-LDS buffer
 // DMA (buffer_load ... lds): no VGPR staging, the K offset rides in an SGPR,
 // rows past M / N read as zero through the buffer range check.
 //
@@ -130,16 +134,16 @@ __device__ __forceinline__ uint2 decode_quad(uint32_t nib, uint4 t) {
                     __builtin_amdgcn_perm(hib, lob, 0x07030602u));
 }
 
-// kMeta16: meta rows are 16-byte aligned (K a multiple of 256 and an aligned
-// base), so a unit quad is one 16-byte load per row; otherwise four 4-byte
-// loads, one per unit.
+// This 32-wide schedule serves the shapes the unit-step kernel below does
+// not take (K not a multiple of 256, or meta rows not 16-byte aligned): a
+// unit quad of meta is four 4-byte loads per row, one per unit.
 //
 // kResid: protected channels ([TA-method]: kept in high precision). Xr [M][KR]
 // and Wr [N][KR] hold their bf16 values, zero-padded to KR (a multiple of
 // 64); Y += Xr Wr^T is computed after the main loop, 64 columns at a time,
 // in the B ring: the first 64 columns are fetched by the last four steps of
 // the loop (whose B stages would lie past K), the rest after it.
-template <bool kMeta16, bool kResid>
+template <bool kResid>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
                       const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
@@ -240,20 +244,15 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)(slot + wave * 4096 + i * 1024),
                                              16, voffAc[i] + (uint32_t)P * 64u, 0, 0, 0);
   };
-  // meta slot layout: kMeta16 -> [row][4 units]; else [wave][unit][64 rows]
+  // meta slot layout: [wave][unit][64 rows]
   auto dma_meta = [&](int Q) {  // unit quad Q into slot Q % 2
     char* slot = lds + kLdsAMeta + (Q & 1) * kMetaSlotBytes + wave * 1024;
-    if constexpr (kMeta16) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)slot, 16,
-                                               voffAm + (uint32_t)Q * 16u, 0, 0, 0);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)(slot + j * 256), 4,
-                                                 voffAm + (uint32_t)(4 * Q + j) * 4u, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)(slot + j * 256), 4,
+                                               voffAm + (uint32_t)(4 * Q + j) * 4u, 0, 0, 0);
   };
-  constexpr int kMetaLoads = kMeta16 ? 1 : 4;
+  constexpr int kMetaLoads = 4;
 
   // Residual tiles, laid out like B stages (16-row swizzle) in B-ring slot
   // `slot`: part = 0/1 -> Wr columns 64c + 32part.., 2/3 -> Xr columns
@@ -281,9 +280,8 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   auto dec_in = [&](int hn) {    // meta + codes of half hn (all zero past the end of K)
     const char* ms = lds + kLdsAMeta + ((hn >> 3) & 1) * kMetaSlotBytes;
     const char* cs = lds + kLdsACodes + ((hn >> 2) % 3) * kCodeSlotBytes;
-    dmw = kMeta16 ? *reinterpret_cast<const uint32_t*>(ms + tid * 16 + ((hn >> 1) & 3) * 4)
-                  : *reinterpret_cast<const uint32_t*>(ms + (tid >> 6) * 1024 +
-                                                       ((hn >> 1) & 3) * 256 + (tid & 63) * 4);
+    dmw = *reinterpret_cast<const uint32_t*>(ms + (tid >> 6) * 1024 + ((hn >> 1) & 3) * 256 +
+                                             (tid & 63) * 4);
     const uint4 w = lds_u32x4(cs + tid * 64 + (((hn & 3) ^ dsw) * 16));
     const bool live = hn < KH;
     dcw = make_uint4(live ? w.x : 0u, live ? w.y : 0u, live ? w.z : 0u, live ? w.w : 0u);
@@ -427,10 +425,8 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    static_assert(kLoads1 + kLoads2 == 10 || kLoads1 + kLoads2 == 11 ||
-                  kLoads1 + kLoads2 == 14, "vmcnt");
+    static_assert(kLoads1 + kLoads2 == 10 || kLoads1 + kLoads2 == 14, "vmcnt");
     if constexpr (kLoads1 + kLoads2 == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else if constexpr (kLoads1 + kLoads2 == 11) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();
@@ -585,6 +581,428 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same contraction in steps of one HiF4 unit (64 K values): four 16-wide
+// MFMA K-chunks per step and ONE barrier per step (half the barriers and
+// waits of the 32-wide schedule). Needs K % 256 == 0 and 16-byte meta rows.
+//
+// LDS map (bytes):
+//   [0, 64K)       B ring: 2 stages x 256 rows x 128 B, chunk c (16 B) of row
+//                  r in slot c ^ ((r >> 1) & 7)
+//   [64K, 128K)    decoded A: 2 buffers x 256 rows x 128 B (same swizzle)
+//   [128K, 152K)   A code ring: 3 slots x 256 rows x 32 B, chunk c of row r in
+//                  slot c ^ ((r >> 3) & 1)
+//   [152K, 156K)   A meta: 1 slot, 256 rows x 16 B (4 units)
+//   [156K, +256)   decode table
+// Step u: loops L0..L2 run the MFMAs of chunks 0..2 of stage u while unit
+// u+1 is decoded into the other buffer; then s_waitcnt vmcnt(0) +
+// lgkmcnt(0) + barrier; L3 runs chunk 3 while the chunk-0 fragments of
+// stage u+1 load, B stage u+2 and the codes of unit u+3 go out (and, every
+// fourth step, the next meta quad), and unit u+2 is read and prepared.
+// Ring reuse after the barrier of step u: B slot u&1 and decoded buffer u&1
+// (stage / unit u, last read before the barrier), code slot u%3 (unit u,
+// read in step u-2), the meta slot (its quad's last unit was read in this
+// step's L3 before the next quad is issued, behind an lgkmcnt(0)).
+constexpr int kRowBytes2 = 128;
+constexpr int kTileBytes2 = 256 * kRowBytes2;              // 32 KiB
+constexpr int kL2B = 0;
+constexpr int kL2X = 2 * kTileBytes2;                      // 65536
+constexpr int kL2C = 4 * kTileBytes2;                      // 131072
+constexpr int kCodeSlot2 = 256 * 32;                       // 8192
+constexpr int kL2M = kL2C + 3 * kCodeSlot2;                // 155648
+constexpr int kL2T = kL2M + 256 * 16;                      // 159744
+constexpr int kLds2Bytes = kL2T + 16 * 16;                 // 160000
+
+template <bool kResid>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
+                          const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
+                          const uint16_t* __restrict__ B, int M, int N, int K,
+                          void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLds2Bytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  {
+    const int per_xcd = ntiles / 8;
+    if (t < per_xcd * 8) t = (t & 7) * per_xcd + (t >> 3);
+    const int group = 8;
+    const int tiles_per_group = group * tiles_n;
+    const int gidx = t / tiles_per_group;
+    const int first_m = gidx * group;
+    const int gsize = min(tiles_m - first_m, group);
+    const int in = t - gidx * tiles_per_group;
+    t = (first_m + in % gsize) * tiles_n + in / gsize;
+  }
+  const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+
+  // decode table: entry (m, s = E + p) at 16 (4m + s)
+  if (tid < 16) {
+    const int m = tid >> 2, sx = tid & 3;
+    const float d = ldexpf(1.0f + 0.25f * (float)m, sx - 33);
+    uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const uint32_t bits = __float_as_uint((float)k * d) >> 16;
+      const uint32_t lb = bits & 0xFFu, hb = bits >> 8;
+      if (k < 4) {
+        lo0 |= lb << (8 * k);
+        hi0 |= hb << (8 * k);
+      } else {
+        lo1 |= lb << (8 * (k - 4));
+        hi1 |= hb << (8 * (k - 4));
+      }
+    }
+    const u32x4_t v = {lo0, lo1, hi0, hi1};
+    *reinterpret_cast<u32x4_t*>(lds + kL2T + 16 * tid) = v;
+  }
+
+  const __amdgpu_buffer_rsrc_t rsAc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Ac, (short)0, M * (K / 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsAm =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Am, (short)0, M * (K / 64) * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * K * 2, kRsrcWord3);
+  // B: wave w rows 64w.. of the stage, 8 x 1 KiB (8 rows each); lane l ->
+  // row 8i + (l >> 3), LDS slot l & 7 holding global chunk (l & 7) ^ ((row >> 1) & 7)
+  uint32_t voffB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 8 * i + (lane >> 3));
+    voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 8u)) * 2u;
+  }
+  // codes: wave w rows 64w.., 2 x 1 KiB (32 rows each); lane l -> row 32i + (l >> 1),
+  // slot l & 1 holding chunk (l & 1) ^ ((row >> 3) & 1) of the row's unit
+  uint32_t voffC[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 32 * i + (lane >> 1));
+    voffC[i] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (((uint32_t)(lane & 1) ^ ((r >> 3) & 1u)) * 16u);
+  }
+  const uint32_t KU = (uint32_t)(K / 64);
+  const uint32_t voffM = (uint32_t)(m0 + wave * 64 + lane) * KU * 4u;
+  const int KUi = K / 64;
+
+  auto dma_b = [&](int st, int i) {  // part i of B stage min(st, KU-1) into slot st & 1
+    char* dst = lds + kL2B + (st & 1) * kTileBytes2 + wave * 64 * kRowBytes2 + i * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)dst, 16, voffB[i],
+                                             min(st, KUi - 1) * kRowBytes2, 0, 0);
+  };
+  auto dma_codes = [&](int un, int i) {  // part i of unit un's codes into slot un % 3
+    char* dst = lds + kL2C + (un % 3) * kCodeSlot2 + wave * 2048 + i * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)dst, 16,
+                                             voffC[i] + (uint32_t)un * 32u, 0, 0, 0);
+  };
+  auto dma_meta = [&](int q) {  // units 4q..4q+3, 16 B per row
+    char* dst = lds + kL2M + wave * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)dst, 16,
+                                             voffM + (uint32_t)q * 16u, 0, 0, 0);
+  };
+  // residual chunk c: Wr columns 64c.. into B slot 0, Xr columns 64c.. into
+  // decoded buffer 0, both with the stage swizzle; rows past M / N read zeros
+  auto dma_resid = [&](int c, bool is_x, int i) {
+    const uint32_t r = (uint32_t)(wave * 64 + 8 * i + (lane >> 3));
+    const uint32_t row = (uint32_t)((is_x ? m0 : n0)) + r;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(is_x ? (const void*)Xr : (const void*)Wr), (short)0, (is_x ? M : N) * KR * 2,
+        kRsrcWord3);
+    char* dst = lds + (is_x ? kL2X : kL2B) + wave * 64 * kRowBytes2 + i * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_t*)dst, 16,
+        row * (uint32_t)(KR * 2) + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 16u),
+        c * 128, 0, 0);
+  };
+
+  // ---- decode state: thread tid decodes row tid of unit un
+  const int csw = (tid >> 3) & 1;  // code chunk swizzle of this row
+  const int xsw = (tid >> 1) & 7;  // decoded-row chunk swizzle of this row
+  uint32_t dmw = 0;
+  uint4 dca = make_uint4(0, 0, 0, 0), dcb = make_uint4(0, 0, 0, 0);  // code words 0-3, 4-7
+  uint4 t8[8];
+  const char* dbase = lds;
+  uint32_t dd = 0, dd0 = 0;
+  uint2 dq0 = make_uint2(0, 0);
+  auto dec_in = [&](int un) {
+    dmw = *reinterpret_cast<const uint32_t*>(lds + kL2M + tid * 16 + (un & 3) * 4);
+    const char* cs = lds + kL2C + (un % 3) * kCodeSlot2 + tid * 32;
+    const uint4 wa = lds_u32x4(cs + ((0 ^ csw) * 16));
+    const uint4 wb = lds_u32x4(cs + ((1 ^ csw) * 16));
+    const bool live = un < KUi;
+    dca = make_uint4(live ? wa.x : 0u, live ? wa.y : 0u, live ? wa.z : 0u, live ? wa.w : 0u);
+    dcb = make_uint4(live ? wb.x : 0u, live ? wb.y : 0u, live ? wb.z : 0u, live ? wb.w : 0u);
+  };
+  auto dec_unit = [&]() {
+    const uint32_t c = dmw & 255u;
+    const uint32_t a = c >> 3, p = (c >> 2) & 1u, m = c & 3u;
+    dbase = lds + kL2T + (m * 4u + p) * 16u;
+    dd = __builtin_amdgcn_perm(a, a, 0u);
+    dd0 = dd & 0xFFFFFF00u;
+  };
+  // table entry of quad q (0..15) into t8[q & 7]
+  auto dec_tab = [&](int q) {
+    const int g = q >> 1;
+    const uint32_t E = ((dmw >> (8 + g)) & 1u) + ((dmw >> (16 + q)) & 1u);
+    t8[q & 7] = lds_u32x4(dbase + 16 * E);
+  };
+  uint32_t qlo = 0, qhi = 0, qnib = 0;
+  auto dec_quad_a = [&](int q) {
+    const uint32_t words[8] = {dca.x, dca.y, dca.z, dca.w, dcb.x, dcb.y, dcb.z, dcb.w};
+    qnib = words[q >> 1] >> (4 * (q & 1));
+    uint4 tq = t8[q & 7];
+    tq.z += dd0;
+    tq.w += dd;
+    const uint32_t sel = qnib & 0x07070707u;
+    qlo = __builtin_amdgcn_perm(tq.y, tq.x, sel);
+    qhi = __builtin_amdgcn_perm(tq.w, tq.z, sel);
+  };
+  auto dec_quad_b = [&](int un, int q) {  // the second quad of a pair writes chunk q >> 1
+    const uint32_t hib = qhi | ((qnib << 4) & 0x80808080u);
+    const uint2 v = make_uint2(__builtin_amdgcn_perm(hib, qlo, 0x05010400u),
+                               __builtin_amdgcn_perm(hib, qlo, 0x07030602u));
+    if ((q & 1) == 0) {
+      dq0 = v;
+    } else {
+      char* dst = lds + kL2X + (un & 1) * kTileBytes2 + tid * kRowBytes2;
+      const u32x4_t w = {dq0.x, dq0.y, v.x, v.y};
+      *reinterpret_cast<u32x4_t*>(dst + (((q >> 1) ^ xsw) * 16)) = w;
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int frow = lane & 31;
+  const int fsw = (frow >> 1) & 7;
+  const int fhalf = lane >> 5;
+  // fragment f of K-chunk s (0..3) of stage/unit st: f < 4 -> A rows wm*128 + 32f,
+  // else B rows wn*128 + 32(f-4); slot parity st & 1
+  auto frag = [&](int st, int s, int f) {
+    const char* p = f < 4
+        ? lds + kL2X + (st & 1) * kTileBytes2 + (wm * 128 + f * 32 + frow) * kRowBytes2
+        : lds + kL2B + (st & 1) * kTileBytes2 + (wn * 128 + (f - 4) * 32 + frow) * kRowBytes2;
+    return *reinterpret_cast<const bf16x8_t*>(p + (((2 * s + fhalf) ^ fsw) * 16));
+  };
+  bf16x8_t f0[8], f1[8];
+
+  // ---- prologue: B stages 0, 1; codes of units 0..2; meta quad 0; unit 0
+  // decoded; unit 1 read and its first table entries in flight; chunk-0
+  // fragments of stage 0.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma_b(0, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma_b(1, i);
+#pragma unroll
+  for (int un = 0; un < 3; ++un) {
+    dma_codes(un, 0);
+    dma_codes(un, 1);
+  }
+  dma_meta(0);
+  wait_vmcnt0();
+  __syncthreads();  // table + every wave's loads visible
+  dec_in(0);
+  dec_unit();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dec_tab(8 * h + q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dec_quad_a(8 * h + q);
+      dec_quad_b(0, 8 * h + q);
+    }
+  }
+  dec_in(1);
+  dec_unit();
+  dec_tab(0);
+  dec_tab(1);
+  dec_tab(2);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();  // unit 0 decoded by every wave
+#pragma unroll
+  for (int f = 0; f < 8; ++f) f0[f] = frag(0, 0, f);
+
+  auto step = [&](int u, auto phase) {
+    constexpr int kPh = decltype(phase)::value;  // u mod 4
+    // L0: chunk 0 (f0); chunk-1 fragments -> f1; table entries of quads 3..7
+    // of unit u+1; quads 0..5 of unit u+1
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8) f1[c] = frag(kPh, 1, c);
+      if (c < 5) dec_tab(3 + c);
+      if (c >= 2 && c < 14) {
+        if (((c - 2) & 1) == 0) dec_quad_a((c - 2) >> 1);
+        else dec_quad_b(u + 1, (c - 2) >> 1);
+      }
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // L1: chunk 1 (f1); chunk-2 fragments -> f0; quads 6, 7; table entries of
+    // quads 8..15 (into the slots quads 0..7 no longer need)
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8) f0[c] = frag(kPh, 2, c);
+      if (c < 4) {
+        if ((c & 1) == 0) dec_quad_a(6 + (c >> 1));
+        else dec_quad_b(u + 1, 6 + (c >> 1));
+      }
+      if (c >= 4 && c < 12) dec_tab(8 + (c - 4));
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // L2: chunk 2 (f0); chunk-3 fragments -> f1; quads 8..15
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8) f1[c] = frag(kPh, 3, c);
+      if ((c & 1) == 0) dec_quad_a(8 + (c >> 1));
+      else dec_quad_b(u + 1, 8 + (c >> 1));
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // L3: chunk 3 (f1); chunk-0 fragments of stage u+1 -> f0; B stage u+2;
+    // codes of unit u+3; unit u+2 read; every fourth step the next meta quad
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (c < 8) {
+        f0[c] = frag(kPh + 1, 0, c);
+        dma_b(u + 2, c);
+      }
+      if (c == 8) dma_codes(u + 3, 0);
+      if (c == 9) dma_codes(u + 3, 1);
+      if (c == 10) dec_in(u + 2);
+      if constexpr (kPh == 1) {  // u + 3 = 4q: the quad holding units u+3.. (u+2 was its predecessor's last)
+        if (c == 11) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          dma_meta((u + 3) >> 2);
+        }
+      }
+      if (c == 12) dec_unit();
+      if (c >= 13) dec_tab(c - 13);
+      const int i = c >> 2, j = c & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int KUp = (KUi + 3) & ~3;
+  for (int u = 0; u < KUp; u += 4) {
+    step(u + 0, std::integral_constant<int, 0>{});
+    step(u + 1, std::integral_constant<int, 1>{});
+    step(u + 2, std::integral_constant<int, 2>{});
+    step(u + 3, std::integral_constant<int, 3>{});
+  }
+  wait_vmcnt0();  // no LDS-DMA may outlive the workgroup (or overlap the residual's)
+
+  if constexpr (kResid) {
+    // Y += Xr Wr^T, 64 columns per chunk: Wr in B slot 0, Xr in decoded buffer 0
+    const int chunks = KR / 64;
+    for (int c = 0; c < chunks; ++c) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      stage_barrier();  // every wave is done with the previous contents
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dma_resid(c, false, i);
+        dma_resid(c, true, i);
+      }
+      wait_vmcnt0();
+      stage_barrier();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t fr[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) fr[f] = frag(0, s, f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], fr[4 + j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // Epilogue. In the 32x32 MFMA output a lane holds one column and, per
+  // group g of 4 accumulator registers, 4 consecutive rows. A 4x4 transpose
+  // across each aligned quad of lanes (two DPP exchange steps) gives every
+  // lane 4 consecutive columns of one row instead, stored as one 16-byte
+  // (fp32) or 8-byte (bf16) write: a quarter of the store instructions of
+  // element-wise stores, each row segment written whole. Rows are
+  // 16-byte aligned when ldy % 4 == 0 (and Y is); otherwise, and for a
+  // column group that crosses N, the values go out one by one.
+  const int col_in = lane & 31, row_in = (lane >> 5) * 4, qt = lane & 3;
+  const bool q_odd = (qt & 1) != 0, q_hi = (qt & 2) != 0;
+  const bool vec_ok = (ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int colq = n0 + wn * 128 + j * 32 + (col_in & ~3);  // the quad's first column
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        // step 1 (lanes t, t^1): c[t][k] = a[t^1][k^1] where bit 0 of k and t differ
+        const float x0 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v1)));
+        const float x1 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v0)));
+        const float x2 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v3)));
+        const float x3 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v2)));
+        const float c0 = q_odd ? x0 : v0, c1 = q_odd ? v1 : x1;
+        const float c2 = q_odd ? x2 : v2, c3 = q_odd ? v3 : x3;
+        // step 2 (lanes t, t^2): d[t][k] = c[t^2][k^2] where bit 1 of k and t differ
+        const float y0 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c2)));
+        const float y1 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c3)));
+        const float y2 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c0)));
+        const float y3 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c1)));
+        const float d0 = q_hi ? y0 : c0, d1 = q_hi ? y1 : c1;
+        const float d2 = q_hi ? c2 : y2, d3 = q_hi ? c3 : y3;
+        // lane t of the quad: row (group row + t), columns colq .. colq + 3
+        const int row = m0 + wm * 128 + i * 32 + 8 * g + row_in + qt;
+        if (row >= M || colq >= N) continue;
+        const size_t off = (size_t)row * ldy + colq;
+        if (vec_ok && colq + 4 <= N) {
+          // non-temporal: Y is written once and read by no one in this
+          // kernel, so it should not push the operand tiles out of L2/MALL
+          if (y_bf16) {
+            const uint32_t lo = f32_to_bf16_rne(d0) | (f32_to_bf16_rne(d1) << 16);
+            const uint32_t hi = f32_to_bf16_rne(d2) | (f32_to_bf16_rne(d3) << 16);
+            __builtin_nontemporal_store(
+                u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(Y) + off));
+          } else {
+            __builtin_nontemporal_store(
+                f32x4_t{d0, d1, d2, d3}, reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(Y) + off));
+          }
+        } else {
+          const float d[4] = {d0, d1, d2, d3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (colq + e >= N) break;
+            if (y_bf16)
+              reinterpret_cast<uint16_t*>(Y)[off + e] = (uint16_t)f32_to_bf16_rne(d[e]);
+            else
+              reinterpret_cast<float*>(Y)[off + e] = d[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+
 // Protected-channel values for the residual: kept [rows][nk] (dense, any
 // nk) -> out [rows][kr] zero-padded, kr a multiple of 64, so that the
 // residual tiles load like B stages (16-byte rows chunks, 16-byte aligned).
@@ -646,12 +1064,12 @@ hipError_t hif4_launch_pack_kept(const uint16_t* kept, int64_t rows, int64_t nk,
 
 // A in HiF4 codes (+ meta), B bf16, optional residual xr/wr [.][kr] (kr = 0:
 // none). Same row-block split as before: all 32-bit offsets stay in range.
-template <bool kMeta16, bool kResid>
+template <bool kResid>
 static void launch_w4a4(dim3 grid, hipStream_t stream, const uint16_t* xr, const uint16_t* wr,
                         int kr, const uint8_t* ac, const uint32_t* am, const uint16_t* b, int mc,
                         int nc, int k, void* ys, int64_t ldy, int y_bf16, int tiles_m,
                         int tiles_n) {
-  hipLaunchKernelGGL((gemm_w4a4_kernel<kMeta16, kResid>), grid, dim3(256), 0, stream, xr, wr, kr,
+  hipLaunchKernelGGL((gemm_w4a4_kernel<kResid>), grid, dim3(256), 0, stream, xr, wr, kr,
                      ac, am, b, mc, nc, k, ys, ldy, y_bf16, tiles_m, tiles_n);
 }
 
@@ -677,17 +1095,20 @@ hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
       const uint16_t* xs = kr ? xr + m0 * kr : nullptr;
       const uint16_t* ws = kr ? wr + n0 * kr : nullptr;
       const bool meta16 = (k / 64) % 4 == 0 && ((uintptr_t)am & 15) == 0;
+      // K % 256 == 0 with 16-byte meta rows: the unit-step schedule; other
+      // shapes take the 32-wide schedule
       if (meta16 && kr)
-        launch_w4a4<true, true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
-                                (int)k, ys, n, y_bf16, tiles_m, tiles_n);
+        hipLaunchKernelGGL((gemm_w4a4_u64_kernel<true>), grid, dim3(256), 0, stream, xs, ws,
+                           (int)kr, ac, am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16,
+                           tiles_m, tiles_n);
       else if (meta16)
-        launch_w4a4<true, false>(grid, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k, ys,
-                                 n, y_bf16, tiles_m, tiles_n);
+        hipLaunchKernelGGL((gemm_w4a4_u64_kernel<false>), grid, dim3(256), 0, stream, xs, ws, 0, ac,
+                           am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16, tiles_m, tiles_n);
       else if (kr)
-        launch_w4a4<false, true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
+        launch_w4a4<true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
                                  (int)k, ys, n, y_bf16, tiles_m, tiles_n);
       else
-        launch_w4a4<false, false>(grid, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k,
+        launch_w4a4<false>(grid, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k,
                                   ys, n, y_bf16, tiles_m, tiles_n);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -194,7 +194,9 @@ def random_units(rows, k, seed):
 
 
 @pytest.mark.parametrize("m,n,k,y_dtype", [(300, 200, 320, torch.float32), (513, 257, 640, torch.float32),
-                                           (260, 300, 128, torch.bfloat16)])
+                                           (260, 300, 128, torch.bfloat16),
+                                           (300, 200, 512, torch.float32),   # K % 256 == 0: the
+                                           (129, 257, 768, torch.bfloat16)])  # unit-step kernel
 def test_linear_random_codes(hip, m, n, k, y_dtype):
     """Decode inside the GEMM over every level-1 code and exponent pattern."""
     xc, xm = random_units(m, k, 5)
