@@ -731,11 +731,12 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
   auto dec_in = [&](int un) {
     dmw = *reinterpret_cast<const uint32_t*>(lds + kL2M + tid * 16 + (un & 3) * 4);
     const char* cs = lds + kL2C + (un % 3) * kCodeSlot2 + tid * 32;
-    const uint4 wa = lds_u32x4(cs + ((0 ^ csw) * 16));
-    const uint4 wb = lds_u32x4(cs + ((1 ^ csw) * 16));
-    const bool live = un < KUi;
-    dca = make_uint4(live ? wa.x : 0u, live ? wa.y : 0u, live ? wa.z : 0u, live ? wa.w : 0u);
-    dcb = make_uint4(live ? wb.x : 0u, live ? wb.y : 0u, live ? wb.z : 0u, live ? wb.w : 0u);
+    // no masking of units past K: K % 256 == 0 leaves no padding steps, and
+    // the only such units (decoded in the last two steps) are never read by
+    // an MFMA; using the words only at their consumers keeps this read off
+    // the critical path
+    dca = lds_u32x4(cs + ((0 ^ csw) * 16));
+    dcb = lds_u32x4(cs + ((1 ^ csw) * 16));
   };
   auto dec_unit = [&]() {
     const uint32_t c = dmw & 255u;
@@ -884,16 +885,16 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
         f0[c] = frag(kPh + 1, 0, c);
         dma_b(u + 2, c);
       }
+      if (c == 0) dec_in(u + 2);
       if (c == 8) dma_codes(u + 3, 0);
       if (c == 9) dma_codes(u + 3, 1);
-      if (c == 10) dec_in(u + 2);
       if constexpr (kPh == 1) {  // u + 3 = 4q: the quad holding units u+3.. (u+2 was its predecessor's last)
         if (c == 11) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           dma_meta((u + 3) >> 2);
         }
       }
-      if (c == 12) dec_unit();
+      if (c == 4) dec_unit();
       if (c >= 13) dec_tab(c - 13);
       const int i = c >> 2, j = c & 3;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
