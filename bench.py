@@ -11,7 +11,7 @@ FFN-up weight (13,824 x 5120), each stage one C-ABI call:
   4. hif4_dequantize(W codes -> bf16): the weight operand, decoded once;
   5. hif4_linear_xcodes_wbf16(X codes, W, kept): the W4A4 contraction plus the
      bf16 residual over the 52 protected channels, Y fp32 [57600][13824]
-     (two small packing kernels and one gemm_w4a4_kernel launch, which
+     (two small packing kernels and one gemm_w4a4_u64_kernel launch, which
      decodes X per tile and adds the residual before its epilogue).
 Inputs are resident in HBM before the timed region. `value` is whole-step
 throughput counted as the linear layer's 2*M*N*K flops per step time.
@@ -72,11 +72,11 @@ def cpu_baseline(x, w, mask_np, rows_sample):
 
 
 GEMM_SRC = os.path.join(ROOT, "bit_block_float_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_kernel_ffn_up_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_u64_kernel_ffn_up_traffic.txt")
 
 
 def measured_traffic():
-    """HBM bytes per launch of gemm_w4a4_kernel from the committed counter
+    """HBM bytes per launch of gemm_w4a4_u64_kernel from the committed counter
     summary, or None if it is missing or the kernel source has changed."""
     try:
         fields = {}
@@ -346,7 +346,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_w4a4_kernel (hif4_linear_xcodes_wbf16, one launch per step), "
+            "kernel": "gemm_w4a4_u64_kernel (hif4_linear_xcodes_wbf16, one launch per step), "
                       "2*M*N*K flops per launch over its HIP-event time",
             "achieved": gemm_tflops,
             "peak": BF16_MFMA_PEAK_TFLOPS,
