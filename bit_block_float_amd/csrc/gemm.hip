@@ -217,7 +217,7 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   // row), block i = rows 64w+16i..+15 (1 KiB): lane l -> row 64w+16i+(l>>2),
   // LDS chunk l&3 holding global chunk (l&3) ^ ((row>>2)&3), so that the
   // decode reads of 16 consecutive rows hit 16 distinct bank groups. Meta,
-  // unit quad Q (16 B per row): lane l -> row 64w+l. The K offsets ride in
+  // unit quad Q: four 4-byte loads per row, lane l -> row 64w+l. The K offsets ride in
   // the range-checked vector offset: past the end of a row they read the
   // next row (never decoded), past the end of the matrix they read zeros.
   const uint32_t KU = (uint32_t)(K / 64);  // units per row
