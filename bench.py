@@ -36,7 +36,6 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 HiF4 linear TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak
 
 
 def log(msg):
@@ -111,8 +110,10 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
     meta = torch.empty((n, k // 64), dtype=torch.int32, device=dev)
     ws = torch.empty((hif4.higptq_workspace_bytes(n),), dtype=torch.uint8, device=dev)
     units = k // 64
-    # compensation flops: 2 n 64 (k - 64 (u + 1)) per group
+    # compensation per group: 2 n 64 flops and 8 bytes of W (read + write)
+    # per element after the group, 64 (u + 1) .. k
     flops = sum(2.0 * n * 64 * (k - 64 * (g + 1)) for g in range(units))
+    wbytes = sum(8.0 * n * (k - 64 * (g + 1)) for g in range(units))
     out = {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
            "groups": units}
     for scheme in (1, 2, 3):
@@ -130,9 +131,11 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
                 times.append(e0.elapsed_time(e1))
         ms = sum(times) / len(times)
         log(f"HiGPTQ scheme {scheme} over W {n}x{k}: {ms:.2f} ms")
+        # rates over the whole pass (group kernels included): the compensation
+        # streams W, so its bound is HBM
         out[f"scheme{scheme}"] = {"ms": ms, "update_TFLOP/s": flops / (ms * 1e-3) / 1e12,
-                                  "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 /
-                                  FP32_VECTOR_PEAK_TFLOPS}
+                                  "W_GB/s": wbytes / ms / 1e6,
+                                  "frac_hbm": wbytes / ms / 1e6 / HBM_PEAK_GBS}
     return out
 
 

@@ -221,96 +221,158 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
 }
 
 // HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
-// update. Workgroup tile: 64 rows x 128 columns; thread: 8 rows x 4 columns.
-// The thread's 8 x 4 block of W is loaded first, so that its latency
-// overlaps the staging of F (64 x 64) and of the U panel (64 x 128) in LDS
-// and the 64-step product; per step a thread reads one float4 of U and two
-// of F for 32 FMAs.
-constexpr int kUpdRows = 64, kUpdCols = 128;
-__global__ __launch_bounds__(256) void higptq_update_kernel(
-    float* __restrict__ w, int64_t ldw, int64_t n, int64_t k, const float* __restrict__ u,
-    int64_t ldu, int64_t s0, int64_t c0, const float* __restrict__ f) {
-  __shared__ __align__(16) float fs[64][kUpdRows];  // fs[i][row]
-  __shared__ __align__(16) float us[64][kUpdCols];  // us[i][col]
-  const int64_t row0 = (int64_t)blockIdx.y * kUpdRows;
-  const int64_t col0 = c0 + (int64_t)blockIdx.x * kUpdCols;
-  const int tc = threadIdx.x & 31, tr = threadIdx.x >> 5;  // 32 column quads x 8 row groups
-  const int64_t colq = col0 + 4 * tc;
-  const bool vec = colq + 4 <= k;  // a whole float4 of this row segment lies inside W
-  float wv[8][4];
+// update on the fp32 matrix cores (v_mfma_f32_32x32x2_f32). Each element of
+// W is read and written once and takes 128 flops, 16 per byte: the matrix
+// cores would need more than HBM delivers, so the kernel is built to stream W
+// and to keep enough of it in flight.
+//
+// The product is taken transposed, W^T -= U^T (-F)^T: in the instruction's
+// output layout (lane l, register r: row 8(r/4) + 4(l/32) + r%4, column l%32)
+// a lane then holds one row of W and, per register quad, four consecutive
+// columns. The contraction index is split by lane half (step t: lanes 0-31
+// contribute index t, lanes 32-63 index 32 + t), so a lane's -F operand is 32
+// consecutive values of its F row and its U operand 32 rows of one column.
+//
+// Workgroup: 4 waves, each 64 rows x 64 columns (two 32-column blocks); the
+// column range after a group is a multiple of 64, so every block is whole.
+// W and the U block travel as 16-byte loads of whole 128-byte row pieces
+// (instruction i: rows 8i + l/8, bytes 16 (l%8)) and are reordered through a
+// wave-private LDS slice (no barrier): W rows padded to 36 floats; U rows 32..63
+// shifted by 32 floats so that the two lane halves read different banks. The
+// second block's loads are issued before the first block is computed, F's
+// together with the first block's; the code is straight-line so that every
+// wait counts exactly the loads it needs.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4u_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3Upd = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kUpdWaveRows = 64, kUpdRows = 4 * kUpdWaveRows, kUpdCols = 64;
+constexpr int kUpdWStride = 36;                        // floats per LDS row of the W block
+constexpr int kUpdUFloats = 64 * 32 + 32;              // U block, rows 32..63 shifted by 32
+constexpr int kUpdSlice = 64 * kUpdWStride + kUpdUFloats;  // floats per wave
+
+template <bool kFull>
+__device__ __forceinline__ void higptq_update_wave(float* __restrict__ w, int64_t ldw, int64_t n,
+                                                   int64_t k, const float* __restrict__ u,
+                                                   int64_t ldu, int64_t s0, int64_t cb0,
+                                                   const float* __restrict__ f, int64_t r0,
+                                                   float* __restrict__ sl) {
+  const int lane = threadIdx.x & 63, li = lane & 31, h = lane >> 5;
+  // F rows r0 + 32b + li, values 32h .. 32h + 31 (rows past n read as zero)
+  float4 fr[2][8];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int64_t row = row0 + tr * 8 + a;
-    if (row < n && vec) {
-      const float4 q = *reinterpret_cast<const float4*>(w + row * ldw + colq);
-      wv[a][0] = q.x; wv[a][1] = q.y; wv[a][2] = q.z; wv[a][3] = q.w;
-    } else {
+  for (int b = 0; b < 2; ++b) {
+    const int64_t row = r0 + 32 * b + li;
+    const float4* src = reinterpret_cast<const float4*>(f + row * 64 + 32 * h);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        wv[a][b] = (row < n && colq + b < k) ? w[row * ldw + colq + b] : 0.0f;
+    for (int q = 0; q < 8; ++q)
+      fr[b][q] = (kFull || row < n) ? src[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  // Buffer resources at the wave's corner of W and of the U panel; the lane
+  // offsets are 32-bit (ldw, ldu < 2^22 keep every offset below 2^30).
+  const int64_t wrows = n - r0 < kUpdWaveRows ? n - r0 : kUpdWaveRows;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w + r0 * ldw + cb0), (short)0, (int)(((wrows - 1) * ldw + (k - cb0)) * 4),
+      kRsrcWord3Upd);
+  const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(u + s0 * ldu + cb0), (short)0, (int)((63 * ldu + (k - cb0)) * 4), kRsrcWord3Upd);
+  const int cr = lane >> 3, cc = 4 * (lane & 7);
+  const int vw = (int)((cr * ldw + cc) * 4), sw8 = (int)(8 * ldw * 4);
+  const int vu = (int)((cr * ldu + cc) * 4), su8 = (int)(8 * ldu * 4);
+  const int64_t rem = n - r0 - cr;  // W row 8i + cr of the wave is live when 8i < rem
+  float* const su = sl + 64 * kUpdWStride;
+  struct Blk {
+    f32x4u_t w[8], u[8];
+  };
+  auto load = [&](Blk& B, int j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) B.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, vu, i * su8 + 128 * j, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f32x4u_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (kFull || 8 * i < rem) x = __builtin_amdgcn_raw_buffer_load_b128(rw, vw, i * sw8 + 128 * j, 0);
+      B.w[i] = x;
     }
-  }
-  // staging with 16-byte loads: F rows (64 floats each) transposed into
-  // fs[i][row], U panel rows copied as they are
-  for (int t = threadIdx.x; t < 16 * kUpdRows; t += blockDim.x) {
-    const int rr = t >> 4, i4 = (t & 15) * 4;
-    const int64_t row = row0 + rr;
-    float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (row < n) q = *reinterpret_cast<const float4*>(f + row * 64 + i4);
-    fs[i4][rr] = q.x;
-    fs[i4 + 1][rr] = q.y;
-    fs[i4 + 2][rr] = q.z;
-    fs[i4 + 3][rr] = q.w;
-  }
-  for (int t = threadIdx.x; t < 64 * (kUpdCols / 4); t += blockDim.x) {
-    const int i = t / (kUpdCols / 4), c4 = (t % (kUpdCols / 4)) * 4;
-    const int64_t col = col0 + c4;
-    const float* src = u + (s0 + i) * ldu + col;
-    float4 q;
-    if (col + 4 <= k) {
-      q = *reinterpret_cast<const float4*>(src);
-    } else {
-      q.x = col < k ? src[0] : 0.0f;
-      q.y = col + 1 < k ? src[1] : 0.0f;
-      q.z = col + 2 < k ? src[2] : 0.0f;
-      q.w = col + 3 < k ? src[3] : 0.0f;
+  };
+  auto stage = [&](const Blk& B) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<f32x4u_t*>(sl + (8 * i + cr) * kUpdWStride + cc) = B.w[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<f32x4u_t*>(su + (8 * i + cr) * 32 + cc + (i >= 4 ? 32 : 0)) = B.u[i];
+  };
+  float a[2][32];  // -F
+  auto run = [&](int j) {
+    // accumulators: register 4q + e of block b holds W[32b + li][8q + 4h + e]
+    f32x16_t c[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4u_t x =
+            *reinterpret_cast<const f32x4u_t*>(sl + (32 * b + li) * kUpdWStride + 8 * q + 4 * h);
+        c[b][4 * q] = x[0];
+        c[b][4 * q + 1] = x[1];
+        c[b][4 * q + 2] = x[2];
+        c[b][4 * q + 3] = x[3];
+      }
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const float uv = su[(32 * h + t) * 32 + li + 32 * h];
+      c[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, a[0][t], c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, a[1][t], c[1], 0, 0, 0);
     }
-    *reinterpret_cast<float4*>(&us[i][c4]) = q;
-  }
-  __syncthreads();
-  float acc[8][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-#pragma unroll 4
-  for (int i = 0; i < 64; ++i) {
-    const float4 uq = *reinterpret_cast<const float4*>(&us[i][4 * tc]);
-    const float4 f0 = *reinterpret_cast<const float4*>(&fs[i][tr * 8]);
-    const float4 f1 = *reinterpret_cast<const float4*>(&fs[i][tr * 8 + 4]);
-    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      for (int q = 0; q < 4; ++q) {
+        const f32x4u_t x = {c[b][4 * q], c[b][4 * q + 1], c[b][4 * q + 2], c[b][4 * q + 3]};
+        *reinterpret_cast<f32x4u_t*>(sl + (32 * b + li) * kUpdWStride + 8 * q + 4 * h) = x;
+      }
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      acc[a][0] = fmaf(fv[a], uq.x, acc[a][0]);
-      acc[a][1] = fmaf(fv[a], uq.y, acc[a][1]);
-      acc[a][2] = fmaf(fv[a], uq.z, acc[a][2]);
-      acc[a][3] = fmaf(fv[a], uq.w, acc[a][3]);
+    for (int i = 0; i < 8; ++i) {
+      const f32x4u_t x = *reinterpret_cast<const f32x4u_t*>(sl + (8 * i + cr) * kUpdWStride + cc);
+      if (kFull || 8 * i < rem) __builtin_amdgcn_raw_buffer_store_b128(x, rw, vw, i * sw8 + 128 * j, 0);
     }
-  }
+  };
+  // the scheduling barriers keep the loads ahead of the work they overlap
+  Blk P, Q;
+  load(P, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int64_t row = row0 + tr * 8 + a;
-    if (row >= n) continue;
-    if (vec) {
-      *reinterpret_cast<float4*>(w + row * ldw + colq) =
-          make_float4(wv[a][0] - acc[a][0], wv[a][1] - acc[a][1], wv[a][2] - acc[a][2],
-                      wv[a][3] - acc[a][3]);
-    } else {
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (colq + b < k) w[row * ldw + colq + b] = wv[a][b] - acc[a][b];
+    for (int q = 0; q < 8; ++q) {
+      a[b][4 * q] = -fr[b][q].x;
+      a[b][4 * q + 1] = -fr[b][q].y;
+      a[b][4 * q + 2] = -fr[b][q].z;
+      a[b][4 * q + 3] = -fr[b][q].w;
     }
-  }
+  load(Q, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  stage(P);
+  __builtin_amdgcn_sched_barrier(0);
+  run(0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage(Q);
+  __builtin_amdgcn_sched_barrier(0);
+  run(1);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+higptq_update_kernel(float* __restrict__ w, int64_t ldw, int64_t n, int64_t k,
+                     const float* __restrict__ u, int64_t ldu, int64_t s0, int64_t c0,
+                     const float* __restrict__ f) {
+  __shared__ __align__(16) float lds[4][kUpdSlice];
+  // wave-uniform by construction; said so, the buffer resources stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t r0 = (int64_t)blockIdx.y * kUpdRows + (int64_t)wave * kUpdWaveRows;
+  if (r0 >= n) return;  // the whole wave lies below W
+  const int64_t cb0 = c0 + (int64_t)blockIdx.x * kUpdCols;
+  if (n - r0 >= kUpdWaveRows)
+    higptq_update_wave<true>(w, ldw, n, k, u, ldu, s0, cb0, f, r0, lds[wave]);
+  else
+    higptq_update_wave<false>(w, ldw, n, k, u, ldu, s0, cb0, f, r0, lds[wave]);
 }
 
 }  // namespace hif4

@@ -291,9 +291,10 @@ HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
  *
  *  w      fp32 [n][ldw] working weights (in: the current values; out: the
  *         columns after the group updated in place; the group's and earlier
- *         columns are not modified), 16-byte aligned, ldw % 4 == 0.
+ *         columns are not modified), 16-byte aligned, ldw % 4 == 0,
+ *         k <= ldw < 2^22 (HIF4_ERR_SHAPE otherwise).
  *  u      fp32 [k][ldu], upper triangular factor, 16-byte aligned,
- *         ldu % 4 == 0; its diagonal in the group must be nonzero (a zero
+ *         ldu % 4 == 0, k <= ldu < 2^22; its diagonal in the group must be nonzero (a zero
  *         gives non-finite weights, not a fault).
  *  unit   0 <= unit < k/64: the group's columns are 64 unit .. 64 unit + 63.
  *  scheme 1, 2 or 3 (HIF4_ERR_ARG otherwise).

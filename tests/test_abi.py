@@ -223,6 +223,9 @@ def test_higptq_argument_checks(L):
     assert call(k=0) == SHAPE
     assert call(ldw=64) == SHAPE
     assert call(ldu=64) == SHAPE
+    assert call(ldw=1 << 22) == SHAPE  # strides below 2^22 (32-bit buffer offsets)
+    assert call(ldu=1 << 22) == SHAPE
+    assert call(ldw=(1 << 22) - 4) != SHAPE
     assert call(unit=2) == ARG
     assert call(unit=-1) == ARG
     assert call(scheme=0) == ARG
