@@ -1,4 +1,4 @@
-// gptq.hip -- HiF4 quantize of fp32 values and the HiGPTQ scheme-1 step.
+// gptq.hip -- HiF4 quantize of fp32 values and the HiGPTQ group step.
 //
 // HiGPTQ: HiFloat4 calibration article (hwcomputing.csdn.net), section 3.1
 // "HiGPTQ": groups of 64 columns (one HiF4 unit each) quantized under one of
@@ -99,125 +99,133 @@ __global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restri
   }
 }
 
-// HiGPTQ group step, part 1: one thread per row, the group's 64 values in
-// registers, U_SS in LDS. Writes unit `unit` of the row's codes and meta and
-// the row's 64 values of F (the compensation of the columns after the group
-// is F U_SR, part 2).
+// HiGPTQ group step, part 1: four lanes per row (a quad), lane q owning the
+// group's columns j = 4m + q (m = 0..15), so that a level-3 group is one
+// column per lane and its maximum a two-step quad reduction; U_SS in LDS.
+// Writes unit `unit` of the row's codes and meta and the row's 64 values of F
+// (the compensation of the columns after the group is F U_SR, part 2).
 //   scheme 1: quantize the 64 values at once (all exponents from them), then
-//             F = E U_SS^-1 by forward substitution;
+//             F = E U_SS^-1;
 //   scheme 2: level-1 from the 64 values first; then per 8 columns: level-2
-//             and level-3 from their current values, quantize, F over the 8
-//             (forward substitution on their diagonal block of U), and update
-//             the group's later columns by F U before the next 8;
+//             and level-3 from their current values, quantize, F over the 8,
+//             and the group's later columns updated by F U before the next 8;
 //   scheme 3: as scheme 2 per 4 columns, with each level-2 exponent fixed
 //             from its 8 current values before its first 4 columns.
+// F is formed right-looking: once f_i = v_i / U_ii is known (v_i broadcast
+// from its owner lane), every later column takes v_j -= f_i U_ij. Per column
+// that is the order of the forward substitution, i = 0, 1, ...: the same
+// operations in the same order as one thread per row would do.
+__device__ __forceinline__ float quad_maxf(float x) {
+  x = fmaxf(x, __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(x))));
+  return fmaxf(x, __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(x))));
+}
+template <int kLane>
+__device__ __forceinline__ float quad_bcastf(float x) {
+  return __uint_as_float(dpp<kLane * 0x55>(__float_as_uint(x)));  // quad_perm [o,o,o,o]
+}
+
 template <int kScheme>
 __global__ __launch_bounds__(256) void higptq_group_kernel(
     const float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u,
     int64_t ldu, int64_t s0, int64_t units, int64_t unit, uint32_t* __restrict__ codes32,
     uint32_t* __restrict__ meta, float* __restrict__ f) {
-  __shared__ float uss[64 * 65];  // U_SS, row i at uss[65 i] (padded)
+  // U_SS regrouped by owner lane: U[i][4m + q] at us[64 i + 16 q + m]
+  __shared__ __align__(16) float us[64 * 64];
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
+  const int q = threadIdx.x & 3;
+  // the row's values first, so that their latency overlaps the staging
+  float v[16];
+  if (r < n) {
+    const float* wr = w + r * ldw + s0 + q;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = wr[4 * m];
+  }
   for (int t = threadIdx.x; t < 64 * 64; t += blockDim.x) {
     const int i = t >> 6, j = t & 63;
-    uss[65 * i + j] = u[(s0 + i) * ldu + s0 + j];
+    us[64 * i + 16 * (j & 3) + (j >> 2)] = u[(s0 + i) * ldu + s0 + j];
   }
   __syncthreads();
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n) return;
-  const float4* src = reinterpret_cast<const float4*>(w + r * ldw + s0);
-  float v[64];
+  if (r >= n) return;  // the whole quad
+  // level-1 from the 64 values as given (every scheme)
+  float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float4 q = src[i];
-    v[4 * i] = q.x;
-    v[4 * i + 1] = q.y;
-    v[4 * i + 2] = q.z;
-    v[4 * i + 3] = q.w;
-  }
-  uint32_t cw[8], mw;
-  if constexpr (kScheme == 1) {
-    float deq[64];
-    quantize_unit_f32(v, cw, mw, deq);
-    // E = W_S - deq (exact: the two differ by at most half a grid step), then
-    // f_j = (e_j - sum_{i<j} f_i U_ij) / U_jj, overwriting v
+  for (int m = 0; m < 16; ++m) a = fmaxf(a, fabsf(v[m]));
+  a = quad_maxf(a);
+  const uint32_t c = level1_code(a);
+  const float s = e6m2_f32(c);
+  uint32_t mw = c;
+  uint32_t cw[8];  // this lane's byte (q) of each code word
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      float acc = v[j] - deq[j];
+  for (int g = 0; g < 8; ++g) cw[g] = 0u;
+  constexpr int kSpan = kScheme == 1 ? 64 : (kScheme == 2 ? 8 : 4);
+  uint32_t e2g[8];
 #pragma unroll
-      for (int i = 0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
-      v[j] = acc / uss[65 * j + j];
+  for (int t0 = 0; t0 < 64; t0 += kSpan) {
+    // level-2 exponents of the level-2 groups starting in the span, from
+    // their 8 current values (columns 8g + q, 8g + 4 + q on this lane)
+#pragma unroll
+    for (int g = t0 / 8; g < (t0 + kSpan + 7) / 8; ++g) {
+      if (8 * g < t0) continue;  // fixed before this span (scheme 3)
+      const float m8 = quad_maxf(fmaxf(fabsf(v[2 * g]), fabsf(v[2 * g + 1])));
+      e2g[g] = m8 > 3.5f * s;
+      mw |= e2g[g] << (8 + g);
     }
-  } else {
-    constexpr int kSpan = kScheme == 2 ? 8 : 4;
-    float a = 0.0f;
+    // level-3 exponents and element codes of the span's columns, E in place
 #pragma unroll
-    for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(v[j]));
-    const uint32_t c = level1_code(a);  // fixed from the group before any update
-    const float s = e6m2_f32(c);
-    mw = c;
+    for (int m = t0 / 4; m < (t0 + kSpan) / 4; ++m) {
+      const uint32_t e2 = e2g[m / 2];
+      const float m4 = quad_maxf(fabsf(v[m]));
+      const uint32_t e3 = m4 > (e2 ? 3.5f : 1.75f) * s;
+      mw |= e3 << (16 + m);
+      const float D = ldexpf(s, (int)(e2 + e3));
+      const float ax = fabsf(v[m]);
+      // k = midpoints (2t+1) D/8 below |x|; at a midpoint the even neighbour
+      // wins (> for even t, >= for odd t); 7 beyond the last one
+      uint32_t k = 0u;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) cw[g] = 0u;
-    uint32_t e2 = 0u;
-#pragma unroll
-    for (int t0 = 0; t0 < 64; t0 += kSpan) {
-      const int g = t0 / 8;
-      if (t0 % 8 == 0) {  // level-2 of group g from its 8 current values
-        float m8 = 0.0f;
-#pragma unroll
-        for (int j = 8 * g; j < 8 * g + 8; ++j) m8 = fmaxf(m8, fabsf(v[j]));
-        e2 = m8 > 3.5f * s;
-        mw |= e2 << (8 + g);
+      for (int t = 0; t < 7; ++t) {
+        const float mid = D * (0.125f * (float)(2 * t + 1));
+        k += (t & 1) ? (ax >= mid ? 1u : 0u) : (ax > mid ? 1u : 0u);
       }
-      float e[kSpan];
+      const uint32_t sgn = (v[m] < 0.0f && k != 0u) ? 8u : 0u;
+      // element 4m + q: word m/2, byte q, high nibble for odd m
+      cw[m / 2] |= (k | sgn) << (8 * q + 4 * (m & 1));
+      const float mag = D * (0.25f * (float)k);
+      v[m] = v[m] - (sgn ? -mag : mag);  // exact: within half a grid step
+    }
+    // F over the span, right-looking; the later columns updated as it goes
 #pragma unroll
-      for (int q = t0 / 4; q < (t0 + kSpan) / 4; ++q) {
-        float m4 = 0.0f;
+    for (int i = t0; i < t0 + kSpan; ++i) {
+      const int mi = i >> 2, oi = i & 3;
+      float vi;
+      if (oi == 0) vi = quad_bcastf<0>(v[mi]);
+      else if (oi == 1) vi = quad_bcastf<1>(v[mi]);
+      else if (oi == 2) vi = quad_bcastf<2>(v[mi]);
+      else vi = quad_bcastf<3>(v[mi]);
+      const float fi = vi / us[64 * i + 16 * oi + mi];
+      if (q == oi) v[mi] = fi;
+      const float* ur = us + 64 * i + 16 * q;
+      // column 4 mi + q is after i only on lanes q > oi
+      if (q > oi) v[mi] = fmaf(-fi, ur[mi], v[mi]);
 #pragma unroll
-        for (int j = 4 * q; j < 4 * q + 4; ++j) m4 = fmaxf(m4, fabsf(v[j]));
-        const uint32_t e3 = m4 > (e2 ? 3.5f : 1.75f) * s;
-        mw |= e3 << (16 + q);
-        const float D = ldexpf(s, (int)(e2 + e3));
-#pragma unroll
-        for (int j = 4 * q; j < 4 * q + 4; ++j) {
-          const float ax = fabsf(v[j]);
-          uint32_t k = 0u;
-#pragma unroll
-          for (int m = 0; m < 7; ++m) {
-            const float mid = D * (0.125f * (float)(2 * m + 1));
-            k += (m & 1) ? (ax >= mid ? 1u : 0u) : (ax > mid ? 1u : 0u);
-          }
-          const uint32_t sgn = (v[j] < 0.0f && k != 0u) ? 8u : 0u;
-          const int i8 = j % 8;
-          cw[g] |= (k | sgn) << (i8 < 4 ? 8 * i8 : 8 * (i8 - 4) + 4);
-          const float mag = D * (0.25f * (float)k);
-          e[j - t0] = v[j] - (sgn ? -mag : mag);  // exact, as in scheme 1
-        }
-      }
-      // F over the span (forward substitution), stored over the span's values
-#pragma unroll
-      for (int j = t0; j < t0 + kSpan; ++j) {
-        float acc = e[j - t0];
-#pragma unroll
-        for (int i = t0; i < j; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
-        v[j] = acc / uss[65 * j + j];
-      }
-      // the group's later columns, before they are quantized
-#pragma unroll
-      for (int j = t0 + kSpan; j < 64; ++j) {
-        float acc = v[j];
-#pragma unroll
-        for (int i = t0; i < t0 + kSpan; ++i) acc = fmaf(-v[i], uss[65 * i + j], acc);
-        v[j] = acc;
-      }
+      for (int m = mi + 1; m < 16; ++m) v[m] = fmaf(-fi, ur[m], v[m]);
     }
   }
-  uint4* dst = reinterpret_cast<uint4*>(codes32 + (r * units + unit) * 8);
-  dst[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-  dst[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-  meta[r * units + unit] = mw;
-  float4* fo = reinterpret_cast<float4*>(f + r * 64);
+  // code words: OR of the four lanes' bytes; lane q stores words 2q, 2q + 1
 #pragma unroll
-  for (int i = 0; i < 16; ++i) fo[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  for (int g = 0; g < 8; ++g) {
+    cw[g] |= dpp<kDppQuadXor1>(cw[g]);
+    cw[g] |= dpp<kDppQuadXor2>(cw[g]);
+  }
+  uint32_t w0 = cw[0], w1 = cw[1];
+#pragma unroll
+  for (int g = 1; g < 4; ++g)
+    if (q == g) { w0 = cw[2 * g]; w1 = cw[2 * g + 1]; }
+  *reinterpret_cast<uint2*>(codes32 + (r * units + unit) * 8 + 2 * q) = make_uint2(w0, w1);
+  if (q == 0) meta[r * units + unit] = mw;
+  float* fo = f + r * 64 + q;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) fo[4 * m] = v[m];
 }
 
 // HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
@@ -395,7 +403,7 @@ hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, 
                                    uint32_t* meta, float* f, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t s0 = unit * 64, units = k / 64;
-  const dim3 gg((unsigned)((n + 255) / 256)), gb(256);
+  const dim3 gg((unsigned)((4 * n + 255) / 256)), gb(256);  // four lanes per row
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
   if (scheme == 1)
     hipLaunchKernelGGL(higptq_group_kernel<1>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
