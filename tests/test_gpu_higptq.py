@@ -89,12 +89,22 @@ def test_quantize_f32_shapes(hip, rows, k, ld):
 
 # ---------------------------------------------------------------------- HiGPTQ
 
-def _check_steps(hip, W, U, rows=None):
+def _padded(a, pad):
+    """Device copy of a 2-D fp32 array as a view with row stride cols + pad."""
+    rows, cols = a.shape
+    t = torch.full((rows, cols + pad), float("nan"), dtype=torch.float32, device="cuda")
+    t[:, :cols] = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t[:, :cols]
+
+
+def _check_steps(hip, W, U, rows=None, pad_w=0, pad_u=0):
     """Run HiGPTQ on the GPU unit by unit; check every step (on `rows`, or all
-    rows) against the oracle started from the GPU's own weights."""
+    rows) against the oracle started from the GPU's own weights. pad_w / pad_u
+    give W and U row strides beyond their widths (the padding holds NaN, so a
+    read of it would show)."""
     n, k = W.shape
-    w = dev(W.astype(np.float32))
-    u = dev(U.astype(np.float32))
+    w = _padded(W, pad_w) if pad_w else dev(W.astype(np.float32))
+    u = _padded(U, pad_u) if pad_u else dev(U.astype(np.float32))
     U64 = U.astype(np.float32).astype(np.float64)  # the values the GPU works with
     codes = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
     meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
@@ -131,10 +141,21 @@ def _check_steps(hip, W, U, rows=None):
 
 
 def test_higptq_steps_follow_the_oracle(hip):
-    """200 rows (ragged against 64-row update tiles), 448 columns (7 groups;
-    the column tiles of the updates end ragged)."""
+    """200 rows (ragged against the 64-row waves of the compensation and its
+    256-row workgroups), 448 columns (7 groups)."""
     W, _, U = _gptq_problem(200, 448, 94)
     _check_steps(hip, W, U)
+
+
+@pytest.mark.parametrize("n,k,pad_w,pad_u", [(1, 128, 0, 0), (3, 192, 12, 4), (63, 192, 0, 0),
+                                             (65, 256, 4, 0), (130, 192, 0, 36)])
+def test_higptq_small_and_strided(hip, n, k, pad_w, pad_u):
+    """Row counts below, at and just past the compensation's 64-row waves
+    (and quads of the group step that end inside a wave), and W / U row
+    strides padded past their widths (32-bit buffer offsets are formed from
+    the strides): every step against the oracle's fp64 step."""
+    W, _, U = _gptq_problem(n, k, 97 + n)
+    _check_steps(hip, W, U, pad_w=pad_w, pad_u=pad_u)
 
 
 def test_higptq_identity_hessian_is_direct_quantization(hip):
