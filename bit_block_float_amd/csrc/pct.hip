@@ -97,13 +97,16 @@ __device__ __forceinline__ void stream_rows(const uint16_t* x, uint32_t loff, in
   if (full(rb)) {
     load(va, rb);
     for (;;) {
+      // the next block's loads are issued on every path (past the last full
+      // block they repeat the current one, unused), so that the waits before
+      // the current block count them exactly
       const bool nb = full(rb + step);
-      if (nb) load(vb, rb + step);
+      load(vb, nb ? rb + step : rb);
       body(va, rb, false);
       rb += step;
       if (!nb) break;
       const bool na = full(rb + step);
-      if (na) load(va, rb + step);
+      load(va, na ? rb + step : rb);
       body(vb, rb, false);
       rb += step;
       if (!na) break;
