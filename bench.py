@@ -224,7 +224,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the kernels shard by rows; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
