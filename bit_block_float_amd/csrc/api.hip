@@ -282,8 +282,8 @@ hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const 
                              int64_t ldu, int64_t unit, int scheme, uint8_t* codes,
                              uint32_t* meta, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  if (n < 0 || k <= 0 || k % 64 != 0 || ldw < k || ldu < k || ldw >= (int64_t(1) << 22) ||
-      ldu >= (int64_t(1) << 22))
+  if (n < 0 || n >= (int64_t(1) << 24) || k <= 0 || k % 64 != 0 || ldw < k || ldu < k ||
+      ldw >= (int64_t(1) << 22) || ldu >= (int64_t(1) << 22))
     return HIF4_ERR_SHAPE;
   if (unit < 0 || unit >= k / 64 || scheme < 1 || scheme > 3) return HIF4_ERR_ARG;
   if (n == 0) return HIF4_OK;

@@ -292,7 +292,7 @@ HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
  *  w      fp32 [n][ldw] working weights (in: the current values; out: the
  *         columns after the group updated in place; the group's and earlier
  *         columns are not modified), 16-byte aligned, ldw % 4 == 0,
- *         k <= ldw < 2^22 (HIF4_ERR_SHAPE otherwise).
+ *         k <= ldw < 2^22 and n < 2^24 (HIF4_ERR_SHAPE otherwise).
  *  u      fp32 [k][ldu], upper triangular factor, 16-byte aligned,
  *         ldu % 4 == 0, k <= ldu < 2^22; its diagonal in the group must be nonzero (a zero
  *         gives non-finite weights, not a fault).

@@ -226,6 +226,7 @@ def test_higptq_argument_checks(L):
     assert call(ldw=1 << 22) == SHAPE  # strides below 2^22 (32-bit buffer offsets)
     assert call(ldu=1 << 22) == SHAPE
     assert call(ldw=(1 << 22) - 4) != SHAPE
+    assert call(n=1 << 24) == SHAPE  # the compensation's grid holds 2^16 tiles of 256 rows
     assert call(unit=2) == ARG
     assert call(unit=-1) == ARG
     assert call(scheme=0) == ARG
