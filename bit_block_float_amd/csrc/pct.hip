@@ -449,32 +449,96 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
   for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) below[i] = 0u;
   __syncthreads();
 
+  // Lane layout: 16 lanes per row, each reading 16 bytes (channels 8p .. 8p + 7
+  // of the block), so a wave's load covers 4 rows (row group g = lane / 16):
+  // wave w reads rows rb + 4w + g + 64u of a block of kWinUnroll steps.
+  constexpr int kWinUnroll = 4, kRowStep = 4 * kPctWaves;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int colA = col_of(2 * lane), colB = col_of(2 * lane + 1);
+  const int g = lane >> 4, p = lane & 15;
+  const int rw = 4 * wave + g;  // row of the lane inside a step
+  int col[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) col[e] = col_of(8 * p + e);
   const int cblocks = (c + kPctCh - 1) / kPctCh;
 
   for_segments(rows, cblocks, per_wg, [&](int c0, int64_t r0, int64_t r1) {
-    const int ch = c0 + 2 * lane;
-    const uint32_t wA = ch < c ? wlo[ch] : 0xFFFFu;
-    const uint32_t wB = ch + 1 < c ? wlo[ch + 1] : 0xFFFFu;
-    uint32_t nA = 0, nB = 0;
-    auto count = [&](const uint32_t (&v)[kPctUnroll], int64_t rb, bool tail) {
+    const int ch = c0 + 8 * p;
+    uint32_t wv[8];
 #pragma unroll
-      for (int u = 0; u < kPctUnroll; ++u) {
-        if (tail && rb + (int64_t)u * kPctWaves >= r1) continue;  // clamped row
-        const uint32_t ka = v[u] & 0x7FFFu, kb = (v[u] >> 16) & 0x7FFFu;
-        // keys and window starts are below 2^16: the difference wraps (top
-        // bit set) exactly for keys below the window
-        const uint32_t da = ka - wA, db = kb - wB;
-        nA += da >> 31;
-        nB += db >> 31;
-        if (da < (uint32_t)kWin) atomicAdd(&hist[(da >> 1) * kPctCh + colA], 1u << (16 * (da & 1u)));
-        if (db < (uint32_t)kWin) atomicAdd(&hist[(db >> 1) * kPctCh + colB], 1u << (16 * (db & 1u)));
+    for (int e = 0; e < 8; ++e) wv[e] = ch + e < c ? wlo[ch + e] : 0xFFFFu;
+    // lanes past the last channel read channel 0 of the row (a valid address;
+    // their window start 0xFFFF keeps every key below it, and below counts of
+    // channels >= c are never read)
+    const uint32_t vb = (uint32_t)((rw * ld + (ch < c ? ch : 0)) * 2);
+    const int sstep = (int)(kRowStep * ld * 2);
+    uint32_t nb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nb[e] = 0u;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    auto load = [&](u32x4_t (&v)[kWinUnroll], int64_t rb) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+#pragma unroll
+      for (int u = 0; u < kWinUnroll; ++u) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 0);
+        v[u] = *reinterpret_cast<const u32x4_t*>(&q);
       }
     };
-    stream_rows(x, lane_offset(ch, c), ld, r0, r1, wave, count);
-    if (nA) atomicAdd(&below[colA], nA);
-    if (nB) atomicAdd(&below[colB], nB);
+    auto count = [&](const u32x4_t (&v)[kWinUnroll], int64_t rb, bool tail) {
+#pragma unroll
+      for (int u = 0; u < kWinUnroll; ++u) {
+        if (tail && rb + rw + (int64_t)u * kRowStep >= r1) continue;  // row past the segment
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = v[u][e >> 1];
+          const uint32_t key = (e & 1) ? (word >> 16) & 0x7FFFu : word & 0x7FFFu;
+          // keys and window starts are below 2^16: the difference wraps (top
+          // bit set) exactly for keys below the window
+          const uint32_t d = key - wv[e];
+          nb[e] += d >> 31;
+          if (d < (uint32_t)kWin) atomicAdd(&hist[(d >> 1) * kPctCh + col[e]], 1u << (16 * (d & 1u)));
+        }
+      }
+    };
+    // whole blocks of kWinUnroll steps (every lane's rows inside the segment),
+    // the next block's loads issued on every path before the current block is
+    // counted; then one partial block with rows past r1 clamped and skipped
+    const int64_t blk = (int64_t)kWinUnroll * kRowStep;
+    int64_t rb = r0;
+    u32x4_t va[kWinUnroll], vc[kWinUnroll];
+    if (rb + blk <= r1) {
+      load(va, rb);
+      for (;;) {
+        const bool nxt = rb + 2 * blk <= r1;
+        load(vc, nxt ? rb + blk : rb);
+        count(va, rb, false);
+        rb += blk;
+        if (!nxt) break;
+        const bool nxt2 = rb + 2 * blk <= r1;
+        load(va, nxt2 ? rb + blk : rb);
+        count(vc, rb, false);
+        rb += blk;
+        if (!nxt2) break;
+      }
+    }
+    if (rb < r1) {
+      // rows past r1 - 1 read row r1 - 1 again (skipped by count); offsets
+      // from the block's row, below 256 rows
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+#pragma unroll
+      for (int u = 0; u < kWinUnroll; ++u) {
+        int64_t r = rb + rw + (int64_t)u * kRowStep;
+        if (r > r1 - 1) r = r1 - 1;
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 0);
+        va[u] = *reinterpret_cast<const u32x4_t*>(&q);
+      }
+      count(va, rb, true);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (nb[e]) atomicAdd(&below[col[e]], nb[e]);
     __syncthreads();
     // this segment's partial: unit (slab, channel block), first or second part
     const int64_t slab = r0 / per_wg;
