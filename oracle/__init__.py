@@ -46,6 +46,8 @@ def _lib():
         lib.hif4o_higptq_unit.restype = ctypes.c_int
         lib.hif4o_higptq_unit_scheme.argtypes = [p, i64, i64, p, i64, ctypes.c_int, p, p]
         lib.hif4o_higptq_unit_scheme.restype = ctypes.c_int
+        lib.hif4o_higptq_unit_scheme_margin.argtypes = [p, i64, i64, p, i64, ctypes.c_int, p, p, p]
+        lib.hif4o_higptq_unit_scheme_margin.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -211,11 +213,13 @@ def quantize_offsets(x_bits: np.ndarray, koff: np.ndarray, moff: np.ndarray):
 
 
 def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta: np.ndarray,
-                scheme: int = 1):
+                scheme: int = 1, margin: np.ndarray = None):
     """One HiGPTQ step (scheme 1, 2 or 3) in place (see hif4_oracle.c):
     quantize group ``unit`` of the working weights ``w`` (float64 [n][k],
     C-contiguous) and compensate the later columns with the upper factor
-    ``u`` (H^-1 = u^T u)."""
+    ``u`` (H^-1 = u^T u). ``margin`` (float64 [n], optional) receives each
+    row's smallest relative distance of a decision on updated values to its
+    boundary (+inf when no decision reads updated values)."""
     n, k = w.shape
     if w.dtype != np.float64 or not w.flags.c_contiguous:
         raise OracleError("higptq_unit: w must be C-contiguous float64")
@@ -223,8 +227,13 @@ def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta
     _shape(uu, (k, k), "higptq_unit u")
     _shape(codes, (n, k // 2), "higptq_unit codes")
     _shape(meta, (n, k // 64), "higptq_unit meta")
-    _check(_lib().hif4o_higptq_unit_scheme(_ptr(w), n, k, _ptr(uu), int(unit), int(scheme),
-                                           _ptr(codes), _ptr(meta)), "higptq_unit")
+    if margin is not None:
+        if margin.dtype != np.float64 or margin.shape != (n,) or not margin.flags.c_contiguous:
+            raise OracleError("higptq_unit: margin must be a contiguous float64 array [n]")
+    _check(_lib().hif4o_higptq_unit_scheme_margin(_ptr(w), n, k, _ptr(uu), int(unit), int(scheme),
+                                                  _ptr(codes), _ptr(meta),
+                                                  _ptr(margin) if margin is not None else None),
+           "higptq_unit")
 
 
 def higptq(w: np.ndarray, u: np.ndarray, scheme: int = 1):

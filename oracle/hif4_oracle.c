@@ -534,18 +534,52 @@ int hif4o_quantize_f32(const float *x, int64_t rows, int64_t k, int64_t ld, uint
 /* Level-2 / level-3 bits and element rounding (steps 3-5 of the rule) for
  * elements j0 .. j0 + len - 1 of a unit under level-1 scale s; e2 of their
  * level-2 group is the given one when e2_fixed >= 0. Writes the nibbles, the
- * meta bits and the dequantized values. */
+ * meta bits and the dequantized values.
+ *
+ * Decision margins (diagnostic output; no effect on the result): when
+ * `margin` is not NULL, each decision that reads a value some update has
+ * moved (moved[j] != 0) lowers *margin to its distance from the boundary it
+ * was decided against -- |M8 - 3.5 s| for a
+ * level-2 bit, |M4 - 1.75 2^e2 s| for a level-3 bit, the distance of |x| to
+ * the nearest rounding midpoint for an element -- divided by sc[] (the
+ * largest sc[j] of the values the decision reads), the size of the sums
+ * that produced those values. A run in other precision that starts from the
+ * same weights can only decide differently where this ratio is within its
+ * rounding error. */
 static void encode_span(const double x[UNIT], int j0, int len, double s, int e2_fixed,
-                        uint8_t codes[32], uint32_t *meta, double deq[UNIT])
+                        uint8_t codes[32], uint32_t *meta, double deq[UNIT],
+                        const double *sc, const int *moved, double *margin)
 {
     int g = j0 / 8;
-    double m8 = 0.0;
-    for (int j = 8 * g; j < 8 * g + 8; ++j) m8 = fabs(x[j]) > m8 ? fabs(x[j]) : m8;
+    double m8 = 0.0, sc8 = 0.0;
+    int mv8 = 0;
+    for (int j = 8 * g; j < 8 * g + 8; ++j) {
+        m8 = fabs(x[j]) > m8 ? fabs(x[j]) : m8;
+        if (margin) {
+            sc8 = sc[j] > sc8 ? sc[j] : sc8;
+            mv8 |= moved[j];
+        }
+    }
     int e2 = e2_fixed >= 0 ? e2_fixed : (m8 > 1.75 * 2.0 * s);
+    if (margin && mv8 && e2_fixed < 0) {
+        double r = fabs(m8 - 1.75 * 2.0 * s) / sc8;
+        if (r < *margin) *margin = r;
+    }
     for (int q = j0 / 4; q < (j0 + len) / 4; ++q) {
-        double m4 = 0.0;
-        for (int j = 4 * q; j < 4 * q + 4; ++j) m4 = fabs(x[j]) > m4 ? fabs(x[j]) : m4;
+        double m4 = 0.0, sc4 = 0.0;
+        int mv4 = 0;
+        for (int j = 4 * q; j < 4 * q + 4; ++j) {
+            m4 = fabs(x[j]) > m4 ? fabs(x[j]) : m4;
+            if (margin) {
+                sc4 = sc[j] > sc4 ? sc[j] : sc4;
+                mv4 |= moved[j];
+            }
+        }
         int e3 = m4 > 1.75 * e1_factor(e2) * s;
+        if (margin && mv4) {
+            double r = fabs(m4 - 1.75 * e1_factor(e2) * s) / sc4;
+            if (r < *margin) *margin = r;
+        }
         *meta |= (uint32_t)e3 << (16 + q);
         double D = s * e1_factor(e2) * e1_factor(e3);
         for (int j = 4 * q; j < 4 * q + 4; ++j) {
@@ -560,6 +594,12 @@ static void encode_span(const double x[UNIT], int j0, int len, double s, int e2_
                     break;
                 }
             }
+            if (margin && moved[j]) {
+                for (int m = 0; m < 7; ++m) {
+                    double r = fabs(a - (double)(2 * m + 1) * D / 8.0) / sc[j];
+                    if (r < *margin) *margin = r;
+                }
+            }
             int sign = (x[j] < 0.0) && (k != 0);
             codes[code_byte(j)] |= (uint8_t)((k | (sign << 3)) << code_shift(j));
             deq[j] = (sign ? -1.0 : 1.0) * (double)k * D / 4.0;
@@ -568,8 +608,15 @@ static void encode_span(const double x[UNIT], int j0, int len, double s, int e2_
     *meta |= (uint32_t)e2 << (8 + g);
 }
 
-int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
-                             int scheme, uint8_t *codes, uint32_t *meta)
+/* margin: NULL, or double [n]. Row r receives the smallest decision margin
+ * (see encode_span) over the decisions of schemes 2 and 3 that read updated
+ * values, with sc[j] = |w[j]| + sum over the updates of column j of
+ * sum_i |f_i| |U_ij|; +inf under scheme 1 and for decisions on the weights as
+ * given (scheme 1's, and every level-1 code), which any run starting from the
+ * same weights takes identically. */
+int hif4o_higptq_unit_scheme_margin(double *w, int64_t n, int64_t k, const double *u,
+                                    int64_t unit, int scheme, uint8_t *codes, uint32_t *meta,
+                                    double *margin)
 {
     if (n < 0 || k <= 0 || k % UNIT != 0 || unit < 0 || unit >= k / UNIT) return HIF4O_ERR_ARG;
     if (scheme < 1 || scheme > 3) return HIF4O_ERR_ARG;
@@ -581,9 +628,13 @@ int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, i
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t r = 0; r < n; ++r) {
         double *wr = w + r * k;
-        double v[UNIT], deq[UNIT], f[UNIT];
+        double v[UNIT], deq[UNIT], f[UNIT], sc[UNIT];
+        int moved[UNIT];
+        double mg = INFINITY;
         for (int j = 0; j < UNIT; ++j) {
             v[j] = wr[s0 + j];
+            sc[j] = fabs(v[j]);
+            moved[j] = 0;
             if (!isfinite(v[j])) bad = 1;
         }
         uint8_t *uc = codes + r * (k / 2) + unit * 32;
@@ -606,11 +657,13 @@ int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, i
         }
         for (int t0 = 0; t0 < UNIT; t0 += span) {
             if (scheme == 2) {
-                encode_span(v, t0, 8, hif4o_e6m2_value((int)(*um & 255u)), -1, uc, um, deq);
+                encode_span(v, t0, 8, hif4o_e6m2_value((int)(*um & 255u)), -1, uc, um, deq, sc,
+                            moved, margin ? &mg : NULL);
             } else if (scheme == 3) {
                 int e2 = -1;
                 if (t0 % 8 == 4) e2 = (int)((*um >> (8 + t0 / 8)) & 1u); /* fixed before the group's first 4 */
-                encode_span(v, t0, 4, hif4o_e6m2_value((int)(*um & 255u)), e2, uc, um, deq);
+                encode_span(v, t0, 4, hif4o_e6m2_value((int)(*um & 255u)), e2, uc, um, deq, sc,
+                            moved, margin ? &mg : NULL);
             }
             /* forward substitution over the span: f_j = (e_j - sum f_i U_ij) / U_jj */
             for (int j = t0; j < t0 + span; ++j) {
@@ -620,11 +673,17 @@ int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, i
             }
             /* update the group's columns after the span */
             for (int j = t0 + span; j < UNIT; ++j) {
-                double acc = 0.0;
-                for (int i = t0; i < t0 + span; ++i) acc += f[i] * u[(s0 + i) * k + (s0 + j)];
+                double acc = 0.0, mag = 0.0;
+                for (int i = t0; i < t0 + span; ++i) {
+                    acc += f[i] * u[(s0 + i) * k + (s0 + j)];
+                    mag += fabs(f[i]) * fabs(u[(s0 + i) * k + (s0 + j)]);
+                }
                 v[j] -= acc;
+                sc[j] += mag;
+                if (mag != 0.0) moved[j] = 1;
             }
         }
+        if (margin) margin[r] = mg;
         for (int j = 0; j < UNIT; ++j) wr[s0 + j] = v[j];
         for (int64_t c = r0; c < k; ++c) {
             double acc = 0.0;
@@ -633,6 +692,12 @@ int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, i
         }
     }
     return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
+                             int scheme, uint8_t *codes, uint32_t *meta)
+{
+    return hif4o_higptq_unit_scheme_margin(w, n, k, u, unit, scheme, codes, meta, NULL);
 }
 
 /* Scheme 1 (kept as its own entry). */

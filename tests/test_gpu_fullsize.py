@@ -168,10 +168,12 @@ def test_higptq_full_weight_sampled_rows(hip):
     _check_steps(hip, w, u, rows=rows)
 
 
-def test_higptq_scheme3_full_weight_sampled_rows(hip):
+def test_higptq_scheme3_full_weight_sampled_rows(hip, capsys):
     """Scheme 3 (4 columns at a time) over the full weight: every step checked
-    on 64 sampled rows on the GPU's own trajectory (see test_gpu_higptq)."""
-    from test_gpu_higptq import _check_scheme_step
+    on 64 sampled rows against the oracle's step from the same rows (the
+    trajectory check for rows within rounding of a decision; see
+    test_gpu_higptq)."""
+    from test_gpu_higptq import _check_scheme_step_oracle
 
     spec = workloads.WORKLOADS["higptq"]
     n, k = spec["N"], spec["K"]
@@ -182,11 +184,16 @@ def test_higptq_scheme3_full_weight_sampled_rows(hip):
     meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
     ws = torch.empty((hip.higptq_workspace_bytes(n),), dtype=torch.uint8, device="cuda")
     rows = torch.from_numpy(np.linspace(0, n - 1, 64).astype(np.int64)).cuda()
+    fallback = 0
     for unit in range(k // 64):
         before = w[rows].cpu().numpy()
         hip.higptq_unit(w, u, unit, codes, meta, workspace=ws, scheme=3)
         torch.cuda.synchronize()
         F = ws[:n * 64 * 4].view(torch.float32).view(n, 64)[rows].cpu().numpy().astype(np.float64)
-        _check_scheme_step(before, w[rows].cpu().numpy(),
-                           codes[rows, 32 * unit:32 * unit + 32].cpu().numpy(),
-                           host_u32(meta[rows])[:, unit], F, U64, unit, 3)
+        fallback += _check_scheme_step_oracle(before, w[rows].cpu().numpy(),
+                                              codes[rows, 32 * unit:32 * unit + 32].cpu().numpy(),
+                                              host_u32(meta[rows])[:, unit], F, U64, unit, 3)
+    with capsys.disabled():
+        print(f"\n[higptq scheme 3, full weight] row-steps checked on the trajectory instead of "
+              f"exactly against the oracle: {fallback} of {64 * (k // 64)}", flush=True)
+    assert fallback < 64 * (k // 64) // 20

@@ -9,7 +9,11 @@ weights must match the oracle's fp64 step from the same start within
 1e-5 * (sum_i |F_i||U_ic| + |W_c|) per entry (F = E U_SS^-1; the fp32
 arithmetic's error measured on the CPU is below 4e-7 of that scale).
 Schemes 2 and 3 (8 or 4 columns at a time, with fp32 updates inside the
-group) are checked as described above their tests.
+group) are checked against the oracle's step from the same starting rows:
+identical codes and meta on every row whose decisions all lie farther than
+1e-5 (relative) from their boundaries in the oracle's own values, F and the
+later columns within tolerance; the rows inside that band are checked on the
+GPU's own trajectory instead (see above those tests), and counted.
 """
 import numpy as np
 import pytest
@@ -181,13 +185,63 @@ def test_higptq_lowers_the_layer_output_error(hip):
 # ----------------------------------------------------- schemes 2 and 3 on the GPU
 # Under schemes 2 and 3 the group's later columns are updated in fp32 inside
 # the group before they are quantized, so a code can legitimately differ from
-# an fp64 run where a value lies within rounding of a decision boundary. Each
-# step is therefore checked on the GPU's own trajectory, rebuilt from the F
-# values the step leaves in its workspace: the level-1 code exactly; every
-# exponent bit and element code against the rule applied to the rebuilt
+# the fp64 oracle only where a value lies within rounding of a decision
+# boundary. Each step is checked against the oracle's step from the GPU's own
+# starting rows (_check_scheme_step_oracle): the oracle reports, per row, the
+# smallest distance of a decision on updated values to its boundary, relative
+# to the size of the sums behind those values; rows farther than 1e-5 (two
+# orders above fp32's rounding of such sums) must give the oracle's codes and
+# meta exactly, F and the later columns within tolerance. Rows inside the
+# band fall back to the trajectory check (_check_scheme_step), rebuilt from
+# the F values the step leaves in its workspace: the level-1 code exactly;
+# every exponent bit and element code against the rule applied to the rebuilt
 # values, except within 1e-5 of the value's error scale from a boundary; F
 # against the forward substitution of the rebuilt errors; and the later
 # columns against W_R - F U_SR.
+
+MARGIN = 1e-5
+
+
+def _check_scheme_step_oracle(before, after, codes_u, meta_u, F, U64, unit, scheme):
+    """One step of scheme 2/3 against the oracle started from `before`.
+    Returns the number of rows that fell back to the trajectory check."""
+    n, k = before.shape
+    s0, r0 = 64 * unit, 64 * unit + 64
+    span = 8 if scheme == 2 else 4
+    wo = np.ascontiguousarray(before, dtype=np.float64)
+    co = np.zeros((n, k // 2), np.uint8)
+    mo = np.zeros((n, k // 64), np.uint32)
+    mg = np.zeros(n, np.float64)
+    oracle.higptq_unit(wo, U64, unit, co, mo, scheme, margin=mg)
+    exact = mg > MARGIN
+    co_u, mo_u = co[:, 32 * unit:32 * unit + 32], mo[:, unit]
+    assert np.array_equal(codes_u[exact], co_u[exact]), f"scheme {scheme} unit {unit} codes"
+    assert np.array_equal(meta_u[exact], mo_u[exact]), f"scheme {scheme} unit {unit} meta"
+    # the oracle's F, span by span: F_T = E_T U_TT^-1 with E the oracle's own
+    # quantization error (its group columns hold the values each span was
+    # quantized from)
+    E = wo[:, s0:r0] - oracle.dequantize(co_u, mo_u[:, None])
+    F_o = np.zeros_like(E)
+    sc = np.abs(before[:, s0:r0]).astype(np.float64)
+    for t0 in range(0, 64, span):
+        Ut = U64[s0 + t0:s0 + t0 + span, s0 + t0:s0 + t0 + span]
+        F_o[:, t0:t0 + span] = np.linalg.solve(Ut.T, E[:, t0:t0 + span].T).T
+        inv_norm = np.abs(np.linalg.inv(Ut)).sum(axis=0).max()
+        bound = (1e-4 * np.abs(F_o[:, t0:t0 + span]).max(axis=1)
+                 + inv_norm * MARGIN * sc[:, t0:t0 + span].max(axis=1))
+        dF = np.abs(F[:, t0:t0 + span] - F_o[:, t0:t0 + span]).max(axis=1)
+        assert np.all((dF <= bound) | ~exact), f"scheme {scheme} unit {unit} F, span {t0}"
+        Ul = U64[s0 + t0:s0 + t0 + span, s0 + t0 + span:r0]
+        sc[:, t0 + span:] += np.abs(F_o[:, t0:t0 + span]) @ np.abs(Ul)
+    assert np.array_equal(after[:, :r0], before[:, :r0])
+    if r0 < k:
+        scale = np.abs(F_o) @ np.abs(U64[s0:r0, r0:]) + np.abs(before[:, r0:])
+        err = np.abs(after[:, r0:].astype(np.float64) - wo[:, r0:])
+        assert np.all((err <= 1e-5 * scale)[exact]), f"scheme {scheme} unit {unit} later columns"
+    fb = np.nonzero(~exact)[0]
+    if fb.size:
+        _check_scheme_step(before[fb], after[fb], codes_u[fb], meta_u[fb], F[fb], U64, unit, scheme)
+    return int(fb.size)
 
 def _check_scheme_step(before, after, codes_u, meta_u, F, U64, unit, scheme):
     from fractions import Fraction
@@ -250,7 +304,7 @@ def _check_scheme_step(before, after, codes_u, meta_u, F, U64, unit, scheme):
 
 
 @pytest.mark.parametrize("scheme", [2, 3])
-def test_higptq_schemes_2_and_3_steps(hip, scheme):
+def test_higptq_schemes_2_and_3_steps(hip, scheme, capsys):
     W, _, U = _gptq_problem(200, 448, 97 + scheme)
     n, k = W.shape
     w = dev(W)
@@ -259,13 +313,19 @@ def test_higptq_schemes_2_and_3_steps(hip, scheme):
     codes = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
     meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
     ws = torch.empty((hip.higptq_workspace_bytes(n),), dtype=torch.uint8, device="cuda")
+    fallback = 0
     for unit in range(k // 64):
         before = w.cpu().numpy()
         hip.higptq_unit(w, u, unit, codes, meta, workspace=ws, scheme=scheme)
         torch.cuda.synchronize()
         F = ws[:n * 64 * 4].view(torch.float32).view(n, 64).cpu().numpy().astype(np.float64)
-        _check_scheme_step(before, w.cpu().numpy(), codes[:, 32 * unit:32 * unit + 32].cpu().numpy(),
-                           host_u32(meta)[:, unit], F, U64, unit, scheme)
+        fallback += _check_scheme_step_oracle(before, w.cpu().numpy(),
+                                              codes[:, 32 * unit:32 * unit + 32].cpu().numpy(),
+                                              host_u32(meta)[:, unit], F, U64, unit, scheme)
+    with capsys.disabled():
+        print(f"\n[higptq scheme {scheme}] row-steps checked on the trajectory instead of "
+              f"exactly against the oracle: {fallback} of {n * (k // 64)}", flush=True)
+    assert fallback < n * (k // 64) // 20
 
 
 @pytest.mark.parametrize("scheme", [2, 3])

@@ -779,3 +779,50 @@ def test_higptq_all_schemes_lower_the_layer_output_error():
         codes, meta, _ = oracle.higptq(W, U, scheme)
         E = W - oracle.dequantize(codes, meta)
         assert np.trace(E @ H @ E.T) < 0.8 * base
+
+
+@pytest.mark.parametrize("scheme", [1, 2, 3])
+def test_higptq_decision_margin(scheme):
+    """The decision margin the oracle reports (the distance of a decision on
+    updated values to its boundary, relative to the size of the sums behind
+    them): +inf under scheme 1 and with no update at all (identity Hessian:
+    every decision reads the weights as given); 0 on a row where an updated
+    value lands exactly on a rounding midpoint; unchanged when the problem is
+    scaled by a power of two; positive on generic rows."""
+    n, k = 16, 128
+    W, _, U = _gptq_problem(n, k, 81)
+    mg = np.zeros(n)
+    w = W.astype(np.float64)
+    codes = np.zeros((n, k // 2), np.uint8)
+    meta = np.zeros((n, k // 64), np.uint32)
+    oracle.higptq_unit(w.copy(), np.eye(k), 0, codes, meta, scheme, margin=mg)
+    assert np.all(np.isinf(mg))
+    oracle.higptq_unit(w.copy(), U, 0, codes, meta, scheme, margin=mg)
+    if scheme == 1:
+        assert np.all(np.isinf(mg))
+        return
+    assert np.all(np.isfinite(mg)) and np.all(mg > 0)
+    mg2 = np.zeros(n)
+    oracle.higptq_unit(4.0 * w, U, 0, codes, meta, scheme, margin=mg2)
+    assert np.array_equal(mg, mg2)
+    # A factor whose only off-diagonal entry moves column 8 by -F_1 U[1, 8]
+    # once the first span is fixed; chosen so that column 8 lands exactly on
+    # the midpoint 3 D / 8 of its grid. x_0 = 7 sets v(c) = 1 and, with
+    # e2 = e3 = 1 (D = 4), quantizes exactly; x_1 = 0.25 rounds to 0 there,
+    # so E_1 = F_1 = 0.25 and column 8 becomes 0.25 + 0.25 * 0.5 = 0.375. Its
+    # own level-2 group then holds nothing larger: e2 = e3 = 0, D = 1, and
+    # 0.375 is the tie between k = 1 and k = 2.
+    x = np.zeros((1, k))
+    x[0, 0] = 7.0
+    x[0, 1] = 0.25
+    x[0, 8] = 0.25
+    uu = np.eye(k)
+    uu[1, 8] = -0.5
+    mg1 = np.zeros(1)
+    c1 = np.zeros((1, k // 2), np.uint8)
+    m1 = np.zeros((1, k // 64), np.uint32)
+    w1 = x.copy()
+    oracle.higptq_unit(w1, uu, 0, c1, m1, scheme, margin=mg1)
+    assert w1[0, 8] == 0.375
+    assert mg1[0] == 0.0
+    assert (nibble(c1[0], 8) & 7) == 2  # the tie went to the even k
