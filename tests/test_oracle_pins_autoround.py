@@ -11,8 +11,14 @@ binary32 path:
   element is the exact RNE of t on the new grid;
 * with K moving the exponent by d, the mantissa offset acts as M 2^-d.
 
-Elements whose exact t + M' lies within 2^-7 of a rounding decision are left
-out of the M checks (there the binary32 rounding of t may decide).
+The oracle forms t = fl(|x| / (D/4)) and fl(t + M') in binary32 (reading
+R16). |x| and D/4 are exact, so t carries at most 2^-24 t of error and the sum
+at most 2^-24 |t + M'| more: with t <= 14 and |M'| <= 1 in these pins, less
+than 2^-19 in all. Elements whose exact t + M' lies within 2^-18 of a
+half-integer are therefore left out of the M checks, and every other
+element must equal the exact-real round-to-nearest-even of t + M'. Exact
+ties (t + M' = n + 1/2 with t and M' exact in binary32) are pinned
+separately: they must go to the even n.
 """
 from fractions import Fraction
 import math
@@ -24,6 +30,7 @@ import oracle
 import unit_cases as uc
 
 UNIT = 64
+BAND = Fraction(1, 2 ** 18)  # binary32 error of fl(t + M') is below 2^-19 here
 pytestmark = pytest.mark.filterwarnings("ignore")
 
 
@@ -89,7 +96,7 @@ def test_half_mantissa_offset_is_ceil_or_floor(sign):
     codes, meta = oracle.quantize_offsets(x, np.zeros((rows, k // 4), np.float32),
                                           np.full((rows, k), float(mval), np.float32))
     assert np.array_equal(meta, meta0)  # K = 0: exponents untouched
-    checked = 0
+    checked = ceil_floor = 0
     for r in range(rows):
         steps = _element_steps(meta[r])
         nib = _nibbles(codes[r])
@@ -98,14 +105,22 @@ def test_half_mantissa_offset_is_ceil_or_floor(sign):
             t = 4 * a / steps[j]
             u = t + mval
             frac = u - math.floor(u)
-            if abs(frac - Fraction(1, 2)) < Fraction(1, 128):
-                continue  # too close to a rounding decision
-            want = min(7, max(0, math.ceil(t) if sign > 0 else math.floor(t)))
+            if abs(frac - Fraction(1, 2)) < BAND:
+                continue  # within binary32's error of a rounding decision
+            want = min(7, max(0, _rne(u)))
             assert nib[j] & 7 == want, (r, j, t, nib[j])
             neg = _bf16_value(x[r, j]) < 0
             assert (nib[j] >> 3) == (1 if (neg and want) else 0)
             checked += 1
-    assert checked > rows * k // 2
+            # the offset's purpose: ceil (floor) of t, except where the
+            # fractional part of t lies within delta of the other side
+            ft = t - math.floor(t)
+            if ft == 0 or (ft > delta if sign > 0 else ft < 1 - delta):
+                cf = min(7, max(0, math.ceil(t) if sign > 0 else math.floor(t)))
+                assert want == cf
+                ceil_floor += 1
+    assert checked > rows * k * 99 // 100
+    assert ceil_floor > rows * k * 9 // 10
 
 
 def test_k_offset_moves_level3_exponent_then_exact_rne():
@@ -162,12 +177,74 @@ def test_mantissa_offset_follows_the_exponent_change():
             mp = mval / 2 if d > 0 else mval * 2
             t = 4 * abs(_bf16_value(x[row, j])) / steps[j]
             u = t + mp
-            if abs((u - math.floor(u)) - Fraction(1, 2)) < Fraction(1, 128):
+            if abs((u - math.floor(u)) - Fraction(1, 2)) < BAND:
                 continue
             want = min(7, max(0, _rne(u)))
             assert nib[j] & 7 == want, (row, j, t, d)
             checked += 1
-    assert checked > rows * k // 2
+    assert checked > rows * k * 99 // 100
+
+
+def _tie_unit(r, with_d_minus):
+    """One unit, as bf16 bits, whose grid steps are known in advance: element
+    0 = 7 (v(c) = 1, c = 124; level-2 group 0 and level-3 group 0 get their
+    bits set); with_d_minus: element 4 = 4 sets the level-3 bit of elements
+    4..7 too (D = 4 there), else those elements stay small. Every other
+    element is a multiple of 1/16 in [0, 1.75] with a random sign, so the
+    groups 1..7 keep e2 = e3 = 0 (D = 1) and all t = 4|x| / D are exact."""
+    v = np.zeros(UNIT, np.float32)
+    v[0] = 7.0
+    mags = r.integers(0, 29, size=UNIT) / 16.0
+    v[1:] = (mags[1:] * np.where(r.random(UNIT - 1) < 0.5, -1.0, 1.0)).astype(np.float32)
+    v[1:4] = r.integers(0, 8, size=3) / 2.0  # quad 0 (D = 4): t = |x| exact
+    if with_d_minus:
+        v[4] = 4.0
+        v[5:8] = (r.integers(0, 8, size=3) / 8.0).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kmode", ["none", "up", "down"])
+def test_exact_ties_of_t_plus_offset_go_to_even(kmode):
+    """t + M' = n + 1/2 exactly (t and M' exact in binary32): the element is
+    the even neighbour, clamped to 0..7. kmode: level-3 offsets K = 0;
+    K = +1.5 on every level-3 group whose bit is 0 (d = +1, M' = M / 2);
+    K = -1.5 on the groups whose bit is 1 (d = -1, M' = 2 M). M is chosen per
+    element to land exactly on a tie: M' = n + 1/2 - t."""
+    r = np.random.default_rng({"none": 61, "up": 62, "down": 63}[kmode])
+    rows = 40
+    x = np.stack([_tie_unit(r, kmode == "down") for _ in range(rows)])
+    _, meta0, _ = oracle.quantize(x)
+    koff = np.zeros((rows, UNIT // 4), np.float32)
+    moff = np.zeros((rows, UNIT), np.float32)
+    want = np.zeros((rows, UNIT), np.int64)
+    tied = 0
+    for row in range(rows):
+        m0 = int(meta0[row, 0])
+        assert m0 & 255 == 124
+        e3 = [(m0 >> (16 + q)) & 1 for q in range(16)]
+        e3n = list(e3)
+        for q in range(16):
+            if kmode == "up" and e3[q] == 0:
+                koff[row, q], e3n[q] = 1.5, 1
+            if kmode == "down" and e3[q] == 1:
+                koff[row, q], e3n[q] = -1.5, 0
+        steps = _element_steps([m0], [e3n])
+        for j in range(UNIT):
+            t = 4 * abs(_bf16_value(x[row, j])) / steps[j]
+            n = int(r.integers(max(0, math.floor(t) - 1), math.floor(t) + 2))
+            mp = Fraction(2 * n + 1, 2) - t  # t is dyadic, so M' and M are exact
+            d = e3n[j // 4] - e3[j // 4]
+            m = mp * 2 ** d  # M' = M 2^-d
+            moff[row, j] = float(m)
+            assert Fraction(float(moff[row, j])) == m
+            want[row, j] = min(7, max(0, n + (n % 2)))  # tie -> even neighbour
+            tied += 1
+    codes, meta = oracle.quantize_offsets(x, koff, moff)
+    for row in range(rows):
+        nib = _nibbles(codes[row])
+        for j in range(UNIT):
+            assert nib[j] & 7 == want[row, j], (kmode, row, j)
+    assert tied == rows * UNIT
 
 
 def test_offsets_reject_bad_shapes():
