@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/hif4.h"
 #include "hif4_dev.h"
 
@@ -45,6 +47,8 @@ const char* hif4_status_string(int status) {
     case HIF4_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case HIF4_ERR_LAUNCH: return "kernel launch failed";
     case HIF4_ERR_ARG: return "argument out of range";
+    case HIF4_ERR_SCRATCH:
+      return "problem needs more than the allocation-free entry point's static scratch";
     default: return "unknown status";
   }
 }
@@ -221,6 +225,69 @@ hif4_status hif4_linear_xcodes_wbf16(const uint8_t* x_codes, const uint32_t* x_m
   return linear_tail(x_codes, x_meta, (const uint16_t*)w, (const uint16_t*)x_kept,
                      (const uint16_t*)w_kept, n_kept, m, n, k, y, y_dtype,
                      (char*)workspace + ws_x_kept(m, 0), stream);
+}
+
+}  // extern "C"
+
+// Static scratch of the allocation-free entry point: the zero-padded
+// protected-channel operands Xr [m][kr] and Wr [n][kr] of one call. Host code
+// never passes `scratch` itself to a kernel (in host code that name is a
+// host-side stand-in, not the device address): each device's copy is looked
+// up once with hipGetSymbolAddress, with that device current, and the cached
+// address is what the kernels receive.
+static __device__ __attribute__((aligned(256))) char scratch[HIF4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];
+
+// The current device's copy of `scratch` (looked up on first use). Two
+// threads racing on the first lookup both store the same address.
+hif4_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HIF4_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return HIF4_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = (char*)p;
+  return HIF4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+hif4_status hif4_linear_xcodes_wbf16_noalloc(const uint8_t* x_codes, const uint32_t* x_meta,
+                                             const void* w, const void* x_kept,
+                                             const void* w_kept, int64_t n_kept, int64_t m,
+                                             int64_t n, int64_t k, void* y, int y_dtype,
+                                             hipStream_t stream) {
+  hif4_status st = check_linear_common(m, n, k, n_kept, y_dtype);
+  if (st != HIF4_OK) return st;
+  if (m == 0 || n == 0) return HIF4_OK;
+  if (!y) return HIF4_ERR_NULL;
+  if (k > 0 && (!x_codes || !x_meta || !w)) return HIF4_ERR_NULL;
+  if (n_kept > 0 && (!x_kept || !w_kept)) return HIF4_ERR_NULL;
+  if (!aligned(y, 16)) return HIF4_ERR_ALIGN;
+  if (k > 0 && (!aligned(x_codes, 16) || !aligned(x_meta, 4) || !aligned(w, 16)))
+    return HIF4_ERR_ALIGN;
+  if (n_kept > 0 && (!aligned(x_kept, 2) || !aligned(w_kept, 2))) return HIF4_ERR_ALIGN;
+  if (ws_resid(m, n_kept) + ws_resid(n, n_kept) > HIF4_NOALLOC_SCRATCH_BYTES)
+    return HIF4_ERR_SCRATCH;
+  st = check_device();
+  if (st != HIF4_OK) return st;
+  if (k == 0) {
+    const size_t bytes = (size_t)m * (size_t)n * (y_dtype == HIF4_BF16 ? 2 : 4);
+    return launched(hif4_launch_zero(y, bytes, stream));
+  }
+  char* ws = nullptr;
+  if (n_kept > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != HIF4_OK) return st;
+  }
+  return linear_tail(x_codes, x_meta, (const uint16_t*)w, (const uint16_t*)x_kept,
+                     (const uint16_t*)w_kept, n_kept, m, n, k, y, y_dtype, ws, stream);
 }
 
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {

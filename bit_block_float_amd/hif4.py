@@ -50,6 +50,9 @@ def lib():
         L.hif4_linear_xcodes_wbf16.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, ctypes.c_int, p,
                                                sz, p]
         L.hif4_linear_xcodes_wbf16.restype = ctypes.c_int
+        L.hif4_linear_xcodes_wbf16_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p,
+                                                       ctypes.c_int, p]
+        L.hif4_linear_xcodes_wbf16_noalloc.restype = ctypes.c_int
         L.hif4_percentile_workspace_bytes.argtypes = [i64, i64]
         L.hif4_percentile_workspace_bytes.restype = sz
         L.hif4_percentile_mask.argtypes = [p, i64, i64, i64, ctypes.c_double, i64, p, p, p, sz, p]
@@ -184,6 +187,28 @@ def linear_xcodes_wbf16(x_codes, x_meta, w, x_kept=None, w_kept=None, y_dtype=to
                                         _ptr(w_kept), n_kept, m, n, k, _ptr(y), dt,
                                         _ptr(workspace), ws_bytes, _stream(stream))
     _ok(st, "hif4_linear_xcodes_wbf16")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # HIF4_NOALLOC_SCRATCH_BYTES
+
+
+def linear_xcodes_wbf16_noalloc(x_codes, x_meta, w, y, x_kept=None, w_kept=None, stream=None):
+    """hif4_linear_xcodes_wbf16 without a workspace (the library's static
+    scratch holds the protected-channel operands): Y into the caller's `y`
+    ([m][n], fp32 or bf16). Allocates no device memory."""
+    _check_bf16_rows(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous (row stride k)")
+    m, n, k = x_codes.shape[0], w.shape[0], w.shape[1]
+    if y.shape != (m, n) or not y.is_contiguous() or y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("y must be a contiguous fp32 or bf16 tensor [m][n]")
+    n_kept = _kept_count(x_kept, w_kept)
+    dt = HIF4_F32 if y.dtype == torch.float32 else HIF4_BF16
+    st = lib().hif4_linear_xcodes_wbf16_noalloc(_ptr(x_codes), _ptr(x_meta), _ptr(w),
+                                                _ptr(x_kept), _ptr(w_kept), n_kept, m, n, k,
+                                                _ptr(y), dt, _stream(stream))
+    _ok(st, "hif4_linear_xcodes_wbf16_noalloc")
     return y
 
 

@@ -36,7 +36,9 @@
  * CONVENTIONS (all entry points):
  *  - Every pointer argument is DEVICE memory owned by the caller; the library
  *    allocates nothing and keeps no state between calls (a per-device
- *    "is this gfx950" flag is cached). Calls are reentrant.
+ *    "is this gfx950" flag is cached). Calls are reentrant. The one exception
+ *    is hif4_linear_xcodes_wbf16_noalloc, which stages its scratch in a
+ *    static device array (see there).
  *  - Work is enqueued asynchronously on `stream` (NULL = the null stream); the
  *    library never synchronizes. Faults inside a kernel surface at the
  *    caller's next synchronization.
@@ -74,7 +76,8 @@ typedef enum hif4_status {
     HIF4_ERR_DTYPE = 5,     /* unknown hif4_dtype */
     HIF4_ERR_DEVICE = 6,    /* current device is not gfx950, or no device */
     HIF4_ERR_LAUNCH = 7,    /* a kernel failed to enqueue */
-    HIF4_ERR_ARG = 8        /* another argument is out of range (q outside [0,1], ...) */
+    HIF4_ERR_ARG = 8,       /* another argument is out of range (q outside [0,1], ...) */
+    HIF4_ERR_SCRATCH = 9    /* the allocation-free entry point's static scratch is too small */
 } hif4_status;
 
 typedef enum hif4_dtype { HIF4_F32 = 0, HIF4_BF16 = 1 } hif4_dtype;
@@ -182,6 +185,36 @@ HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16(const uint8_t *x_codes, const u
                                      int64_t n_kept, int64_t m, int64_t n, int64_t k, void *y,
                                      int y_dtype, void *workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * hif4_linear_xcodes_wbf16_noalloc -- hif4_linear_xcodes_wbf16 for callers
+ * that cannot allocate device memory: code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * result and error behaviour as hif4_linear_xcodes_wbf16 (bit for bit the
+ * same Y), minus the workspace: the protected-channel operands (Xr, Wr) are
+ * staged in a static device array of the library instead.
+ *
+ *  - That array holds HIF4_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, for the
+ *    life of the process. A call with n_kept > 0 needs m * 2 * kr + n * 2 * kr
+ *    bytes of it (kr = n_kept rounded up to 64; each of the two parts rounded
+ *    up to 256 bytes), none with n_kept == 0. A larger call returns
+ *    HIF4_ERR_SCRATCH and enqueues nothing.
+ *  - The call allocates nothing: no hipMalloc, hipFree or allocating library
+ *    routine. Its first call on a device looks up that device's copy of the
+ *    array once (hipGetSymbolAddress) and caches the address per device.
+ *  - Every call on one GPU shares that GPU's array. Calls whose execution
+ *    overlaps on one GPU (on different streams, or from several threads
+ *    without ordering) race on it and give undefined Y; calls ordered on one
+ *    stream are safe. Each call writes all of the array it reads, so the
+ *    previous call's contents never leak into a result.
+ */
+#define HIF4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16_noalloc(const uint8_t *x_codes,
+                                             const uint32_t *x_meta, const void *w,
+                                             const void *x_kept, const void *w_kept,
+                                             int64_t n_kept, int64_t m, int64_t n, int64_t k,
+                                             void *y, int y_dtype, hipStream_t stream);
 
 /*
  * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask

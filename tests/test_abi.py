@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hif4.h")
 LIB = os.path.join(ROOT, "bit_block_float_amd", "libhif4.so")
 
-OK, NULL, SHAPE, ALIGN, WORKSPACE, DTYPE, DEVICE, LAUNCH, ARG = range(9)
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DTYPE, DEVICE, LAUNCH, ARG, SCRATCH = range(10)
 A = 0x100000  # a 256-byte-aligned stand-in address; never dereferenced here
 
 
@@ -36,7 +36,8 @@ def L():
 def test_header_declares_the_four_entry_points():
     names = declared()
     for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
-               "hif4_linear_xcodes_wbf16", "hif4_quantize_f32", "hif4_higptq_unit",
+               "hif4_linear_xcodes_wbf16", "hif4_linear_xcodes_wbf16_noalloc",
+               "hif4_quantize_f32", "hif4_higptq_unit",
                "hif4_quantize_offsets",
                "hif4_higptq_workspace_bytes",
                "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
@@ -56,8 +57,8 @@ def test_library_exports_exactly_the_declared_symbols(L):
 
 def test_version_and_status_strings(L):
     assert L.hif4_version() == 1
-    for s in range(9):
-        assert L.hif4_status_string(s)
+    for s in range(10):
+        assert L.hif4_status_string(s) and L.hif4_status_string(s) != b"unknown status"
     assert L.hif4_status_string(12345) == b"unknown status"
 
 
@@ -150,6 +151,32 @@ def test_linear_xcodes_wbf16_argument_checks(L):
     assert call(nk=5, xk=A, wk=A, ws=A, wb=wsk - 1) == WORKSPACE
     assert call(nk=5, xk=A, wk=A, ws=A + 16, wb=wsk) == ALIGN
     assert call(nk=65, xk=A, wk=A, ws=A, wb=wsk) == SHAPE
+
+
+def test_linear_xcodes_wbf16_noalloc_argument_checks(L):
+    """The allocation-free variant: the same checks minus the workspace, and
+    problems whose protected-channel operands exceed the static scratch
+    (32 MiB) are refused before any device work."""
+    f = L.hif4_linear_xcodes_wbf16_noalloc
+    limit = 32 << 20
+
+    def call(xc=A, xm=A, w=A, xk=None, wk=None, nk=0, m=8, n=8, k=64, y=A, dt=0):
+        return f(xc, xm, w, xk, wk, nk, m, n, k, y, dt, None)
+
+    assert call(k=60) == SHAPE
+    assert call(dt=2) == DTYPE
+    assert call(xc=None) == NULL
+    assert call(y=None) == NULL
+    assert call(w=A + 8) == ALIGN
+    assert call(m=0, y=None) == OK
+    assert call(nk=5, xk=A) == NULL                      # w_kept missing
+    assert call(nk=5, xk=A, wk=A + 1) == ALIGN
+    assert call(nk=65, xk=A, wk=A) == SHAPE
+    # (m + n) * 2 * kr bytes (256-byte aligned parts) against the limit
+    rows = limit // (2 * 64)  # kr = 64: exactly the limit for m + n = rows
+    assert call(nk=64, xk=A, wk=A, m=rows - 256 + 1, n=256, k=64) == SCRATCH
+    assert call(nk=128, xk=A, wk=A, m=rows // 2, n=8, k=128) == SCRATCH
+    assert call(nk=65, xk=A, wk=A, m=rows // 2, n=8, k=128) == SCRATCH  # kr = 128
 
 
 def test_percentile_argument_checks(L):
