@@ -136,7 +136,11 @@ HIF4_EXPORT size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, 
  * mask protects stay in high precision):
  *     Y[i][j] = sum_t deq(Q(X))[i][t] * deq(Q(W))[j][t]
  *             + sum_{p < n_kept} x_kept[i][p] * w_kept[j][p],
- * accumulated in fp32 (|error| <= 1e-5 * sum |a||b| over both parts per output).
+ * accumulated in fp32: one accumulator per output, one rounding per 16-term
+ * matrix-core step. The worst case is (k + 64 ceil(n_kept / 64)) / 16 * 2^-24
+ * * sum |a||b| over both parts; rounding errors of independent sign keep the
+ * error far below that, and within 1e-5 * sum |a||b| on every shape tested
+ * (K up to 13,824, same-sign data included).
  *
  *  X is given EITHER as bf16 x [m][k] (row stride k; it is quantized along k
  *  into the workspace first, with `mask` applied when n_kept > 0) OR

@@ -75,6 +75,41 @@ def test_linear_full_shape_sampled_rows(hip, name, y_dtype, via_codes):
     assert np.all(err <= tol), f"max excess {np.max(err - tol)}"
 
 
+def test_linear_ffn_down_same_sign_full_k(hip, capsys):
+    """Same-sign contraction at the full FFN-down depth (K = 13,824: 864
+    sequential fp32 MFMA accumulations per output, whose worst-case bound
+    ~864 * 2^-24 = 5.1e-5 of sum |a||b| exceeds the tolerance): GELU
+    activations against |W|, so partial sums grow monotonically and rounding
+    errors cannot cancel by sign; eight rows are near-constant (every entry
+    within a few bf16 steps of 1). Sampled rows against the oracle within
+    1e-5 * sum |a||b|; the measured ratio is printed."""
+    w = workloads.WORKLOADS["ffn_down"]
+    M, N, K = w["M"], w["N"], w["K"]
+    print(f"[case] same-sign linear {M}x{N}x{K}", flush=True)
+    x = workloads.gelu_x(M, K, device="cuda", seed=w["index"])
+    # near-constant rows: every entry within a few bf16 steps of 1.0
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x[:8] = (1.0 + torch.randint(0, 4, (8, K), generator=g, device="cuda") * 2.0 ** -7).to(torch.bfloat16)
+    wt = workloads.normal_bf16(N, K, 0.015, device="cuda", seed=w["index"] + 1000).abs()
+    wcodes, wmeta, _ = hip.quantize(wt)
+    y = hip.linear_w4a4(wcodes, wmeta, x=x)
+    rows = np.unique(np.concatenate([np.arange(8), sample_rows(x)]))
+    xs = workloads.bits(x[torch.from_numpy(rows).cuda()])
+    y_rows = y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    wb = workloads.bits(wt)
+    del x, y
+    xc, xm, _ = oracle.quantize(xs)
+    wc, wm, _ = oracle.quantize(wb)
+    y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+    ratio = np.abs(y_rows - y_ref) / s_ref
+    with capsys.disabled():
+        print(f"\n[same-sign K=13824] max |dY|/S = {ratio.max():.3e}, mean {ratio.mean():.3e}, "
+              f"near-constant rows max {ratio[:8].max():.3e}, "
+              f"|Y|/S min {np.min(np.abs(y_ref) / s_ref):.3f}", flush=True)
+    assert np.all(ratio <= 1e-5), f"max |dY|/S {ratio.max():.3e}"
+
+
 def test_linear_ffn_up_protected_channels(hip):
     """The whole method at the FFN-up shape: the percentile mask of X (52
     channels), W and X quantized with it, the linear with the bf16 residual;
