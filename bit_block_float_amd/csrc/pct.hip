@@ -15,8 +15,8 @@
 //           is a different bin -> the exact keys of ranks lo and hi;
 //   final   type-7 interpolation in double, rounded once to fp32.
 // Long columns first take a one-pass path (a window of keys placed by a
-// sample of every 8th row; see the section further down) and fall back to
-// the two passes only for channels the window missed.
+// sample of every S-th row; see the section further down) and compute only
+// the channels the window missed exactly, from their own columns.
 // Histograms are integers (LDS atomics per workgroup, then global atomics or
 // per-segment partials): results do not depend on scheduling.
 //
@@ -158,9 +158,8 @@ __device__ __forceinline__ void for_segments(int64_t rows, int cblocks, int64_t 
 // bits 23..30: one bit-field extract and one shift-or per channel.
 __global__ __launch_bounds__(kPctThreads) void pct_pass1_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
-    uint32_t* __restrict__ h1, const uint32_t* __restrict__ gate) {
+    uint32_t* __restrict__ h1) {
   __shared__ uint32_t hist[256 * kPctCh];  // [bin][column]
-  if (gate != nullptr && *gate == 0u) return;  // fallback pass not needed
   for (int i = threadIdx.x; i < 256 * kPctCh; i += kPctThreads) hist[i] = 0u;
   __syncthreads();
 
@@ -246,16 +245,15 @@ __device__ __forceinline__ void wave_find_rank(const uint32_t (&cnt)[kPer], int6
 }
 
 // Between passes: one wave per channel finds the coarse bins (and ranks
-// inside them) of lo and hi. When n_exact is given (the two passes run for
-// every channel), it receives c.
+// inside them) of lo and hi; n_exact receives c (every channel's statistic
+// comes from the two exact passes on this path).
 __global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restrict__ h1,
                                                          int64_t rows, int c, double q,
                                                          PctSel* __restrict__ sel,
-                                                         const uint32_t* __restrict__ gate,
                                                          uint32_t* __restrict__ n_exact) {
-  if (n_exact != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *n_exact = (uint32_t)c;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_exact = (uint32_t)c;
   const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ch >= c || (gate != nullptr && *gate == 0u)) return;
+  if (ch >= c) return;
   const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
@@ -279,11 +277,9 @@ __global__ __launch_bounds__(256) void pct_select_kernel(const uint32_t* __restr
 // merges it once per segment.
 __global__ __launch_bounds__(kPctThreads) void pct_pass2_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
-    const PctSel* __restrict__ sel, uint32_t* __restrict__ h2, uint32_t* __restrict__ minkey,
-    const uint32_t* __restrict__ gate) {
+    const PctSel* __restrict__ sel, uint32_t* __restrict__ h2, uint32_t* __restrict__ minkey) {
   __shared__ uint32_t hist[129 * kPctCh];  // [fine bin, spare][column]
   __shared__ uint32_t mins[kPctCh];
-  if (gate != nullptr && *gate == 0u) return;
   for (int i = threadIdx.x; i < 129 * kPctCh; i += kPctThreads) hist[i] = 0u;
   for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) mins[i] = 0xFFFFFFFFu;
   __syncthreads();
@@ -350,12 +346,9 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
                                                         const PctSel* __restrict__ sel,
                                                         const uint32_t* __restrict__ minkey,
                                                         int64_t rows, int c, double q,
-                                                        float* __restrict__ stats,
-                                                        const uint32_t* __restrict__ gate,
-                                                        const uint8_t* __restrict__ only) {
+                                                        float* __restrict__ stats) {
   const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ch >= c || (gate != nullptr && *gate == 0u)) return;
-  if (only != nullptr && only[ch] == 0) return;  // this channel's statistic is already set
+  if (ch >= c) return;
   const int lane = threadIdx.x & 63;
   int64_t lo, hi;
   double f;
@@ -386,39 +379,18 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
 
 // ---- one-pass path with a sampled window (large inputs)
 //
-// Pass 1 over every 8th row gives each channel's coarse bin b_s of the
-// quantile's rank in the sample; the window is the 512 consecutive keys of
-// coarse bins b_s - 1 .. b_s + 2. One pass over all rows then counts, per
-// channel, the keys below the window and a histogram of every key inside it.
-// When ranks lo and hi of the full column both fall inside the window (their
-// keys are then exact), the statistic is final; a channel whose ranks fall
-// outside (a sample that misled) is flagged, and only then do the two exact
-// passes run (gated on the device, no host round trip), for the flagged
-// channels' statistics.
+// Pass 1 over every S-th row (S = max(8, ceil(rows / 8192)): at most ~8192
+// sampled rows) gives each channel's coarse bin b_s of the quantile's rank
+// in the sample; the window is the 512 consecutive keys of coarse bins
+// b_s - 1 .. b_s + 2. One pass over all rows then counts, per channel, the
+// keys below the window and a histogram of every key inside it. When ranks
+// lo and hi of the full column both fall inside the window (their keys are
+// then exact), the statistic is final; a channel whose ranks fall outside (a
+// sample that misled) is computed exactly from its column in the same final
+// kernel (pct_resolve_kernel), which also builds the mask.
 constexpr int kWin = 512;          // keys in the window
 constexpr int kPartStride = 260;   // u32 per column of a partial: 256 packed words, below, pad
 constexpr int64_t kPartWords = (int64_t)kPctCh * kPartStride;  // one partial (a segment's counts)
-
-// Window start per channel from the sample's coarse histogram; block 0 also
-// clears the flagged-channel count.
-__global__ __launch_bounds__(256) void pct_select_window_kernel(const uint32_t* __restrict__ h1,
-                                                                int64_t rows_s, int c, double q,
-                                                                uint32_t* __restrict__ wlo,
-                                                                uint32_t* __restrict__ n_failed) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_failed = 0u;
-  const int ch = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (ch >= c) return;
-  const int lane = threadIdx.x & 63;
-  int64_t lo, hi;
-  double f;
-  type7_ranks(rows_s, q, &lo, &hi, &f);
-  const uint4 w = reinterpret_cast<const uint4*>(h1 + (int64_t)ch * 256)[lane];
-  const uint32_t cnt[4] = {w.x, w.y, w.z, w.w};
-  uint32_t b;
-  int64_t before;
-  wave_find_rank<4>(cnt, lo, &b, &before);
-  if (lane == 0) wlo[ch] = (b > 0 ? b - 1 : 0u) << 7;
-}
 
 // The window pass. A key below the window only adds to its lane's register
 // count (most keys of a tail quantile do: as LDS atomics they would all hit
@@ -565,113 +537,31 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
   });
 }
 
-// Per channel: the window counts summed over the partials of its channel
-// block; the keys of ranks lo and hi when both lie in the window. Otherwise
-// the channel is flagged for the two exact passes (which gate on n_failed),
-// and its buffers of those passes are cleared here (the passes count every
-// channel, but only flagged channels' counts are read).
-__global__ __launch_bounds__(256) void pct_final_window_kernel(
-    const uint32_t* __restrict__ part, const uint32_t* __restrict__ wlo, int64_t rows, int c,
-    int64_t per_wg, double q, float* __restrict__ stats, uint8_t* __restrict__ failed,
-    uint32_t* __restrict__ n_failed, uint32_t* __restrict__ h1, uint32_t* __restrict__ h2,
-    uint32_t* __restrict__ minkey) {
-  __shared__ uint32_t nf[4];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ch = blockIdx.x * 4 + wv;
-  bool fail = false;
-  if (ch < c) {
-    const int cblocks = (c + kPctCh - 1) / kPctCh;
-    const int cb = ch / kPctCh, col = col_of(ch % kPctCh);
-    const int64_t full_slabs = rows / per_wg;
-    const int64_t n_slabs = (rows + per_wg - 1) / per_wg;
-    uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int64_t nbelow = 0;
-    for (int64_t slab = 0; slab < n_slabs; ++slab) {
-      // the unit's place in the work sequence; split when a slice boundary
-      // (a multiple of per_wg) falls strictly inside it
-      const int64_t rn = slab < full_slabs ? per_wg : rows - full_slabs * per_wg;
-      const int64_t s0 = slab * cblocks * per_wg + cb * rn;
-      const int nparts = (s0 / per_wg != (s0 + rn - 1) / per_wg) ? 2 : 1;
-      const int64_t unit = slab * cblocks + cb;
-      for (int k = 0; k < nparts; ++k) {
-        const uint32_t* src = part + (2 * unit + k) * kPartWords + (int64_t)col * kPartStride;
-        const uint4 w = reinterpret_cast<const uint4*>(src)[lane];
-        cnt[0] += w.x & 0xFFFFu;
-        cnt[1] += w.x >> 16;
-        cnt[2] += w.y & 0xFFFFu;
-        cnt[3] += w.y >> 16;
-        cnt[4] += w.z & 0xFFFFu;
-        cnt[5] += w.z >> 16;
-        cnt[6] += w.w & 0xFFFFu;
-        cnt[7] += w.w >> 16;
-        nbelow += src[kWin / 2];
-      }
-    }
-    int64_t lo, hi;
-    double f;
-    type7_ranks(rows, q, &lo, &hi, &f);
-    uint32_t in_win = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) in_win += cnt[i];
-    for (int d = 32; d >= 1; d >>= 1) in_win += (uint32_t)__shfl_xor((int)in_win, d, 64);
-    fail = !(lo >= nbelow && hi < nbelow + (int64_t)in_win);
-    if (fail) {
-      reinterpret_cast<uint4*>(h1 + (int64_t)ch * 256)[lane] = make_uint4(0u, 0u, 0u, 0u);
-      reinterpret_cast<uint2*>(h2 + (int64_t)ch * 128)[lane] = make_uint2(0u, 0u);
-      if (lane == 0) {
-        minkey[ch] = 0xFFFFFFFFu;
-        failed[ch] = 1;
-      }
-    } else {
-      uint32_t blo, bhi;
-      int64_t before;
-      wave_find_rank<8>(cnt, lo - nbelow, &blo, &before);
-      wave_find_rank<8>(cnt, hi - nbelow, &bhi, &before);
-      if (lane == 0) {
-        const uint32_t w0 = wlo[ch];
-        const double vlo = (double)__uint_as_float((w0 + blo) << 16);
-        const double vhi = (double)__uint_as_float((w0 + bhi) << 16);
-        const double d = __dsub_rn(vhi, vlo);
-        const double t = __dmul_rn(f, d);
-        const double r = __dadd_rn(vlo, t);
-        stats[ch] = __double2float_rn(r);
-        failed[ch] = 0;
-      }
-    }
-  }
-  // one count update per block (a single counter hit by every failing wave
-  // would serialize)
-  if (lane == 0) nf[wv] = fail ? 1u : 0u;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t n = nf[0] + nf[1] + nf[2] + nf[3];
-    if (n) atomicAdd(n_failed, n);
-  }
-}
-
-// Fill n words with a value (the buffers of the exact passes, before they run
-// for every channel).
+// Fill n words with a value (the buffers of the exact passes).
 __global__ void pct_zero_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = value;
 }
 
 // Top-n mask by radix select over the stats' bit patterns (stats are >= 0,
-// so unsigned order = numeric order). One workgroup; thread t keeps the
-// statistics of its contiguous chunk of channels [t * per, (t + 1) * per)
-// (per <= kPer, c <= 1024 kPer) in registers. Four 8-bit digit passes (most significant first) find
-// tau, the n-th largest value; channels above tau are protected, and of the
-// channels equal to tau the lowest-indexed (n - count_above) are protected
-// (ties go to the lower index).
+// so unsigned order = numeric order), run by one workgroup of kMaskThreads
+// threads; thread t keeps the statistics of its contiguous chunk of channels
+// [t * per, (t + 1) * per) (per <= kPer, c <= kMaskThreads * kPer) in
+// registers. Four 8-bit digit passes (most significant first) find tau, the
+// n-th largest value; channels above tau are protected, and of the channels
+// equal to tau the lowest-indexed (n - count_above) are protected (ties go
+// to the lower index).
 constexpr int kMaskThreads = 1024;
 
+struct TopnShared {
+  uint32_t hist[256];
+  uint32_t prefix, need;
+  uint32_t part[kMaskThreads / 64], part_above[kMaskThreads / 64];
+};
+
 template <int kPer>
-__global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __restrict__ stats,
-                                                                 int c, int n_protect,
-                                                                 uint8_t* __restrict__ mask) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_need, s_above;
-  __shared__ uint32_t part[kMaskThreads / 64];
+__device__ void topn_select(const float* __restrict__ stats, int c, int n_protect,
+                            uint8_t* __restrict__ mask, TopnShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (n_protect <= 0 || n_protect >= c) {
     const uint8_t v = n_protect <= 0 ? 0 : 1;
@@ -688,41 +578,41 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
   }
   // rank (0-based, descending) of the element we look for
   if (tid == 0) {
-    s_prefix = 0u;
-    s_need = (uint32_t)(n_protect - 1);
+    sh.prefix = 0u;
+    sh.need = (uint32_t)(n_protect - 1);
   }
   uint32_t prefix_mask = 0u;
 #pragma unroll
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
+    if (tid < 256) sh.hist[tid] = 0u;
     __syncthreads();
-    const uint32_t pre = s_prefix;
+    const uint32_t pre = sh.prefix;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = i0 + j;
       if (j < per && i < c && (u[j] & prefix_mask) == pre)
-        atomicAdd(&hist[(u[j] >> shift) & 255u], 1u);
+        atomicAdd(&sh.hist[(u[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      // the digit holding rank s_need, counting from the top digit down:
+      // the digit holding rank `need`, counting from the top digit down:
       // lane l holds digits 255 - 4l .. 252 - 4l
-      const uint32_t need = s_need;
+      const uint32_t need = sh.need;
       uint32_t cnt[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cnt[i] = hist[255 - (lane * 4 + i)];
+      for (int i = 0; i < 4; ++i) cnt[i] = sh.hist[255 - (lane * 4 + i)];
       uint32_t pos;
       int64_t before;
       wave_find_rank<4>(cnt, (int64_t)need, &pos, &before);
       if (tid == 0) {
-        s_prefix = pre | ((255u - pos) << shift);
-        s_need = need - (uint32_t)before;
+        sh.prefix = pre | ((255u - pos) << shift);
+        sh.need = need - (uint32_t)before;
       }
     }
     prefix_mask |= 255u << shift;
     __syncthreads();
   }
-  const uint32_t tau = s_prefix;
+  const uint32_t tau = sh.prefix;
   // count_above, and the ties of each thread's chunk (thread order = channel
   // order, so an exclusive scan of the tie counts ranks the ties by index)
   uint32_t above = 0, ties = 0;
@@ -732,15 +622,19 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
     above += (ok && u[j] > tau) ? 1u : 0u;
     ties += (ok && u[j] == tau) ? 1u : 0u;
   }
-  if (tid == 0) s_above = 0u;
   const uint32_t incl = wave_incl_scan(ties);
-  if (lane == 63) part[tid >> 6] = incl;
+  const uint32_t above_w = wave_incl_scan(above);  // lane 63: the wave's total
+  if (lane == 63) {
+    sh.part[tid >> 6] = incl;
+    sh.part_above[tid >> 6] = above_w;
+  }
   __syncthreads();
-  atomicAdd(&s_above, above);
-  uint32_t tie_rank = incl - ties;
-  for (int w = 0; w < (tid >> 6); ++w) tie_rank += part[w];
-  __syncthreads();
-  const uint32_t take = (uint32_t)n_protect - s_above;  // ties to protect
+  uint32_t tie_rank = incl - ties, above_all = 0;
+  for (int w = 0; w < kMaskThreads / 64; ++w) {
+    if (w < (tid >> 6)) tie_rank += sh.part[w];
+    above_all += sh.part_above[w];
+  }
+  const uint32_t take = (uint32_t)n_protect - above_all;  // ties to protect
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = i0 + j;
@@ -754,6 +648,308 @@ __global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __
       }
       mask[i] = m;
     }
+  }
+}
+
+template <int kPer>
+__global__ __launch_bounds__(kMaskThreads) void topn_mask_kernel(const float* __restrict__ stats,
+                                                                 int c, int n_protect,
+                                                                 uint8_t* __restrict__ mask) {
+  __shared__ TopnShared sh;
+  topn_select<kPer>(stats, c, n_protect, mask, sh);
+}
+
+// Exact type-7 statistic of one channel by the whole workgroup: two passes over the channel's column, a 256-bin histogram of
+// key >> 7, then a 128-bin histogram of key & 127 inside the coarse bin of
+// rank lo with the smallest key of the coarse bin of rank hi when that
+// differs; the interpolation as in pct_final_kernel. For the channels the
+// sampled window missed: rare, and each is one column read twice.
+struct ExactShared {
+  uint32_t coarse[256];
+  uint32_t fine[128];
+  uint32_t minkey;
+  PctSel sel;
+};
+
+__device__ void exact_channel(const uint16_t* __restrict__ x, int64_t ld, int64_t rows, int ch,
+                              double q, float* __restrict__ stats, ExactShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int kU = 8;  // loads in flight per thread
+  const int nthr = blockDim.x;
+  for (int i = tid; i < 256; i += nthr) sh.coarse[i] = 0u;
+  for (int i = tid; i < 128; i += nthr) sh.fine[i] = 0u;
+  if (tid == 0) sh.minkey = 0xFFFFFFFFu;
+  __syncthreads();
+  const uint16_t* col = x + ch;
+  const int64_t step = (int64_t)nthr * kU;
+  for (int64_t r0 = tid; r0 < rows; r0 += step) {
+    uint32_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t r = r0 + (int64_t)u * nthr;
+      v[u] = r < rows ? (uint32_t)col[r * ld] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (v[u] != 0xFFFFFFFFu) atomicAdd(&sh.coarse[(v[u] & 0x7FFFu) >> 7], 1u);
+  }
+  __syncthreads();
+  int64_t lo, hi;
+  double f;
+  type7_ranks(rows, q, &lo, &hi, &f);
+  if (wv == 0) {
+    const uint32_t cnt[4] = {sh.coarse[4 * lane], sh.coarse[4 * lane + 1], sh.coarse[4 * lane + 2],
+                             sh.coarse[4 * lane + 3]};
+    uint32_t blo, bhi;
+    int64_t before_lo, before_hi;
+    wave_find_rank<4>(cnt, lo, &blo, &before_lo);
+    wave_find_rank<4>(cnt, hi, &bhi, &before_hi);
+    if (lane == 0) sh.sel = PctSel{blo, (uint32_t)(lo - before_lo), bhi, (uint32_t)(hi - before_hi)};
+  }
+  __syncthreads();
+  const PctSel s = sh.sel;
+  uint32_t mn = 0xFFFFFFFFu;
+  for (int64_t r0 = tid; r0 < rows; r0 += step) {
+    uint32_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t r = r0 + (int64_t)u * nthr;
+      v[u] = r < rows ? (uint32_t)col[r * ld] & 0x7FFFu : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (v[u] == 0xFFFFFFFFu) continue;
+      if ((v[u] >> 7) == s.b_lo) atomicAdd(&sh.fine[v[u] & 127u], 1u);
+      if ((v[u] >> 7) == s.b_hi) mn = min(mn, v[u]);
+    }
+  }
+  if (s.b_hi != s.b_lo && mn != 0xFFFFFFFFu) atomicMin(&sh.minkey, mn);
+  __syncthreads();
+  if (wv == 0) {
+    const uint32_t cnt[2] = {sh.fine[2 * lane], sh.fine[2 * lane + 1]};
+    uint32_t flo, fhi;
+    int64_t before;
+    wave_find_rank<2>(cnt, (int64_t)s.r_lo, &flo, &before);
+    const uint32_t klo = (s.b_lo << 7) | flo;
+    uint32_t khi;
+    if (s.b_hi == s.b_lo) {
+      wave_find_rank<2>(cnt, (int64_t)s.r_hi, &fhi, &before);
+      khi = (s.b_lo << 7) | fhi;
+    } else {
+      khi = sh.minkey;
+    }
+    if (lane == 0) {
+      const double vlo = (double)__uint_as_float(klo << 16);
+      const double vhi = (double)__uint_as_float(khi << 16);
+      const double d = __dsub_rn(vhi, vlo);
+      const double t = __dmul_rn(f, d);
+      const double r = __dadd_rn(vlo, t);
+      stats[ch] = __double2float_rn(r);
+    }
+  }
+  __syncthreads();
+}
+
+// The window path's last kernel, one wave per channel (4 channels per
+// workgroup of 256 threads):
+//  1. each wave sums its channel's window counts over the partials of its
+//     channel block; when ranks lo and hi both lie in the window their keys
+//     are read off it and the statistic is final;
+//  2. the channels whose ranks fell outside (a sample that misled) are then
+//     computed exactly, one after another, by the whole workgroup
+//     (exact_channel), and counted in n_failed.
+constexpr int kResolveThreads = 256;
+
+__global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
+    const uint16_t* __restrict__ x, int64_t ld, const uint32_t* __restrict__ part,
+    const uint32_t* __restrict__ wlo, int64_t rows, int c, int64_t per_wg, double q,
+    float* __restrict__ stats, uint32_t* __restrict__ n_failed) {
+  __shared__ ExactShared sh;
+  __shared__ uint32_t s_fail;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ch = blockIdx.x * (kResolveThreads / 64) + wv;
+  if (threadIdx.x == 0) s_fail = 0u;
+  __syncthreads();
+  if (ch < c) {
+    const int cblocks = (c + kPctCh - 1) / kPctCh;
+    const int cb = ch / kPctCh, col = col_of(ch % kPctCh);
+    const int64_t full_slabs = rows / per_wg;
+    const int64_t n_slabs = (rows + per_wg - 1) / per_wg;
+    uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t nbelow = 0;
+    // The channel's partials, kBatch slabs at a time with every load issued
+    // before any is summed (a slab's second partial is read only when a
+    // slice boundary -- a multiple of per_wg -- falls strictly inside its
+    // unit; otherwise it is never written and its words are masked off).
+    constexpr int kBatch = 8;
+    for (int64_t sb = 0; sb < n_slabs; sb += kBatch) {
+      uint4 w[2 * kBatch];
+      uint32_t bl[2 * kBatch];
+      bool use[2 * kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t slab = min(sb + i, n_slabs - 1);
+        const int64_t rn = slab < full_slabs ? per_wg : rows - full_slabs * per_wg;
+        const int64_t s0 = slab * cblocks * per_wg + cb * rn;
+        const bool two = s0 / per_wg != (s0 + rn - 1) / per_wg;
+        const int64_t unit = slab * cblocks + cb;
+        use[2 * i] = sb + i < n_slabs;
+        use[2 * i + 1] = use[2 * i] && two;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          // an unused second partial reads the first one again (a valid address)
+          const uint32_t* src = part + (2 * unit + (use[2 * i + 1] ? k : 0)) * kPartWords +
+                                (int64_t)col * kPartStride;
+          w[2 * i + k] = reinterpret_cast<const uint4*>(src)[lane];
+          bl[2 * i + k] = src[kWin / 2];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * kBatch; ++i) {
+        if (!use[i]) continue;
+        cnt[0] += w[i].x & 0xFFFFu;
+        cnt[1] += w[i].x >> 16;
+        cnt[2] += w[i].y & 0xFFFFu;
+        cnt[3] += w[i].y >> 16;
+        cnt[4] += w[i].z & 0xFFFFu;
+        cnt[5] += w[i].z >> 16;
+        cnt[6] += w[i].w & 0xFFFFu;
+        cnt[7] += w[i].w >> 16;
+        nbelow += bl[i];
+      }
+    }
+    int64_t lo, hi;
+    double f;
+    type7_ranks(rows, q, &lo, &hi, &f);
+    uint32_t in_win = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in_win += cnt[i];
+    for (int d = 32; d >= 1; d >>= 1) in_win += (uint32_t)__shfl_xor((int)in_win, d, 64);
+    if (!(lo >= nbelow && hi < nbelow + (int64_t)in_win)) {
+      if (lane == 0) atomicOr(&s_fail, 1u << wv);
+    } else {
+      uint32_t blo, bhi;
+      int64_t before;
+      wave_find_rank<8>(cnt, lo - nbelow, &blo, &before);
+      wave_find_rank<8>(cnt, hi - nbelow, &bhi, &before);
+      if (lane == 0) {
+        const uint32_t w0 = wlo[ch];
+        const double vlo = (double)__uint_as_float((w0 + blo) << 16);
+        const double vhi = (double)__uint_as_float((w0 + bhi) << 16);
+        const double d = __dsub_rn(vhi, vlo);
+        const double t = __dmul_rn(f, d);
+        const double r = __dadd_rn(vlo, t);
+        stats[ch] = __double2float_rn(r);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t fails = s_fail;
+  for (uint32_t m = fails; m != 0u; m &= m - 1u)
+    exact_channel(x, ld, rows, blockIdx.x * (kResolveThreads / 64) + __builtin_ctz(m), q, stats,
+                  sh);
+  if (threadIdx.x == 0 && fails) atomicAdd(n_failed, (uint32_t)__builtin_popcount(fails));
+}
+
+// The window path's first kernel: the sample of every S-th row and the
+// window it places, one workgroup per block of 64 channels reading all of
+// that block's sampled rows (no cross-workgroup merge: no global atomics, no
+// histogram to clear beforehand). Lanes read 16 bytes (channels 8p .. 8p+7,
+// p = lane & 7), 8 lanes per row, so a wave's load covers 8 rows. The
+// coarse histogram (key >> 7, u32) is [bin][channel] with a row stride of
+// 65 words, so the 8 rows of a wave's atomic land in distinct banks. Then
+// wave w finds, for channels 4w .. 4w+3 of the block, the coarse bin b of
+// rank floor(q (n_s - 1)) of the sample; the window starts one coarse bin
+// below it. Workgroup 0 also clears the flagged-channel count.
+constexpr int kSampCh = 64;
+constexpr int kSampStride = kSampCh + 1;
+
+__global__ __launch_bounds__(kPctThreads) void pct_sample_window_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_s, int c, int64_t ld, double q,
+    uint32_t* __restrict__ wlo, uint32_t* __restrict__ n_failed) {
+  __shared__ uint32_t hist[256 * kSampStride];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_failed = 0u;
+  for (int i = threadIdx.x; i < 256 * kSampStride; i += kPctThreads) hist[i] = 0u;
+  __syncthreads();
+  constexpr int kUnroll = 4, kRowStep = 8 * kPctWaves;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 3, p = lane & 7;
+  const int rw = 8 * wave + g;  // row of the lane inside a step
+  const int c0 = blockIdx.x * kSampCh;
+  const int ch = c0 + 8 * p;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  // lanes past the last channel read channel 0 (a valid address); their
+  // columns are never read back. The row base of a block is wave-uniform;
+  // the lane's row and channel ride in its 32-bit offset (ld <= 2^20 here:
+  // below 2^31 over the 512 rows of a block of loads).
+  const uint32_t vb = (uint32_t)((rw * ld + (ch < c ? ch : 0)) * 2);
+  const int sstep = (int)(kRowStep * ld * 2);
+  auto load = [&](u32x4_t (&v)[kUnroll], int64_t rb) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 0);
+      v[u] = *reinterpret_cast<const u32x4_t*>(&qq);
+    }
+  };
+  auto count = [&](const u32x4_t (&v)[kUnroll], int64_t rb, bool tail) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (tail && rb + rw + (int64_t)u * kRowStep >= rows_s) continue;  // row past the end
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = v[u][e >> 1];
+        const uint32_t bin = (e & 1) ? (word >> 23) & 255u : (word >> 7) & 255u;
+        atomicAdd(&hist[bin * kSampStride + 8 * p + e], 1u);
+      }
+    }
+  };
+  const int64_t blk = (int64_t)kUnroll * kRowStep;
+  int64_t rb = 0;
+  u32x4_t va[kUnroll], vc[kUnroll];
+  if (rb + blk <= rows_s) {
+    load(va, rb);
+    for (;;) {
+      const bool nxt = rb + 2 * blk <= rows_s;
+      load(vc, nxt ? rb + blk : rb);
+      count(va, rb, false);
+      rb += blk;
+      if (!nxt) break;
+      const bool nxt2 = rb + 2 * blk <= rows_s;
+      load(va, nxt2 ? rb + blk : rb);
+      count(vc, rb, false);
+      rb += blk;
+      if (!nxt2) break;
+    }
+  }
+  if (rb < rows_s) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t r = rb + rw + (int64_t)u * kRowStep;
+      if (r > rows_s - 1) r = rows_s - 1;
+      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 0);
+      va[u] = *reinterpret_cast<const u32x4_t*>(&qq);
+    }
+    count(va, rb, true);
+  }
+  __syncthreads();
+  int64_t lo, hi;
+  double f;
+  type7_ranks(rows_s, q, &lo, &hi, &f);
+#pragma unroll
+  for (int k = 0; k < kSampCh / kPctWaves; ++k) {
+    const int cc = wave * (kSampCh / kPctWaves) + k;  // channel within the block
+    uint32_t cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt[i] = hist[(4 * lane + i) * kSampStride + cc];
+    uint32_t b;
+    int64_t before;
+    wave_find_rank<4>(cnt, lo, &b, &before);
+    if (lane == 0 && c0 + cc < c) wlo[c0 + cc] = (b > 0 ? b - 1 : 0u) << 7;
   }
 }
 
@@ -796,6 +992,13 @@ bool pass_grid(int64_t rows, int ci, int64_t resident, int64_t* per_wg, int64_t*
 constexpr int64_t kWindowResident = 256;
 constexpr int64_t kWindowMinRows = 8192;
 
+// Row stride of the window path's sample: every 8th row, and at most ~8192
+// sampled rows for very long columns.
+int64_t sample_stride(int64_t rows) {
+  const int64_t s = (rows + 8191) / 8192;
+  return s > 8 ? s : 8;
+}
+
 int64_t window_partials(int64_t rows, int64_t c) {
   if (rows < kWindowMinRows) return 0;
   int64_t per_wg, grid;
@@ -807,12 +1010,12 @@ int64_t window_partials(int64_t rows, int64_t c) {
 
 size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c) {
   // h1 [c][256] + h2 [c][128] + minkey [c] + sel [c] (16 B) + window start [c]
-  // + window partials + failed [c] (u8) + exact-channel count (last part),
-  // 256-B aligned parts
+  // + window partials + the exact-channel count (last part), 256-B aligned
+  // parts
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   return al((size_t)c * 256 * 4) + al((size_t)c * 128 * 4) + al((size_t)c * 4) +
          al((size_t)c * sizeof(PctSel)) + al((size_t)c * 4) +
-         al((size_t)window_partials(rows, c) * kPartWords * 4) + al((size_t)c) + al(4);
+         al((size_t)window_partials(rows, c) * kPartWords * 4) + al(4);
 }
 
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
@@ -832,60 +1035,51 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
   ws += al((size_t)c * 4);
   uint32_t* part = (uint32_t*)ws;
   ws += al((size_t)window_partials(rows, c) * kPartWords * 4);
-  uint8_t* failed = (uint8_t*)ws;
-  ws += al((size_t)c);
-  uint32_t* n_exact = (uint32_t*)ws;  // channels resolved by the two exact passes
+  uint32_t* n_exact = (uint32_t*)ws;  // channels resolved by exact passes
 
   const int ci = (int)c;
   hipError_t e;
-  int64_t per_wg, grid;
-  if (!pass_grid(rows, ci, cu_count(), &per_wg, &grid)) return hipErrorInvalidValue;
-  // The sampled window pays off on long columns; the sample (every 8th row)
-  // is read with an 8x row stride, which must keep the pass's 32-bit buffer
-  // offsets in range (ld <= 2^19).
-  const bool window = rows >= kWindowMinRows && ld <= ((int64_t)1 << 19);
-  const uint32_t* gate = nullptr;
+  const int64_t stride_s = sample_stride(rows);
+  // The sampled window pays off on long columns; the sample is read with an
+  // S-fold row stride, and the sample kernel's 32-bit buffer offsets span
+  // 512 sampled rows: ld * S <= 2^20 keeps them below 2^31.
+  const bool window = rows >= kWindowMinRows && ld * stride_s <= ((int64_t)1 << 20);
   if (window) {
-    const int64_t rows_s = (rows + 7) / 8;
-    int64_t per_s, grid_s;
+    const int64_t rows_s = (rows + stride_s - 1) / stride_s;
     int64_t per_w, grid_w;
-    if (!pass_grid(rows_s, ci, cu_count(), &per_s, &grid_s) ||
-        !pass_grid(rows, ci, kWindowResident, &per_w, &grid_w))
-      return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h1, (int64_t)c * 256, 0u);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid_s), dim3(kPctThreads), 0, stream, x,
-                       rows_s, ci, ld * 8, per_s, h1, (const uint32_t*)nullptr);
-    hipLaunchKernelGGL(pct_select_window_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1,
-                       rows_s, ci, q, wlo, n_exact);
+    if (!pass_grid(rows, ci, kWindowResident, &per_w, &grid_w)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pct_sample_window_kernel, dim3((unsigned)((ci + kSampCh - 1) / kSampCh)),
+                       dim3(kPctThreads), 0, stream, x, rows_s, ci, ld * stride_s, q, wlo,
+                       n_exact);
     hipLaunchKernelGGL(pct_window_kernel, dim3((unsigned)grid_w), dim3(kPctThreads), 0, stream, x,
                        rows, ci, ld, per_w, (const uint32_t*)wlo, part);
-    hipLaunchKernelGGL(pct_final_window_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream,
-                       (const uint32_t*)part, (const uint32_t*)wlo, rows, ci, per_w, q, stats, failed,
-                       n_exact, h1, h2, minkey);
+    hipLaunchKernelGGL(pct_resolve_kernel,
+                       dim3((unsigned)((ci + kResolveThreads / 64 - 1) / (kResolveThreads / 64))),
+                       dim3(kResolveThreads), 0, stream, x, ld, (const uint32_t*)part,
+                       (const uint32_t*)wlo, rows, ci, per_w, q, stats, n_exact);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // The exact passes below run only if a channel was flagged; the flagged
-    // channels' buffers were cleared by the final window kernel.
-    gate = n_exact;
   } else {
+    // Short columns: the two exact passes for every channel.
+    int64_t per_wg, grid;
+    if (!pass_grid(rows, ci, cu_count(), &per_wg, &grid)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h1, (int64_t)c * 256, 0u);
     hipLaunchKernelGGL(pct_zero_kernel, dim3(256), dim3(256), 0, stream, h2, (int64_t)c * 128, 0u);
     hipLaunchKernelGGL(pct_zero_kernel, dim3(64), dim3(256), 0, stream, minkey, (int64_t)c,
                        0xFFFFFFFFu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
+                       rows, ci, ld, per_wg, h1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1, rows, ci,
+                       q, sel, n_exact);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pct_pass2_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
+                       rows, ci, ld, per_wg, sel, h2, minkey);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel,
+                       minkey, rows, ci, q, stats);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pct_pass1_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
-                     rows, ci, ld, per_wg, h1, gate);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(pct_select_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h1, rows, ci, q,
-                     sel, gate, window ? (uint32_t*)nullptr : n_exact);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(pct_pass2_kernel, dim3((unsigned)grid), dim3(kPctThreads), 0, stream, x,
-                     rows, ci, ld, per_wg, sel, h2, minkey, gate);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(pct_final_kernel, dim3((ci + 3) / 4), dim3(256), 0, stream, h2, sel, minkey,
-                     rows, ci, q, stats, gate, window ? (const uint8_t*)failed : nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ci <= 8 * kMaskThreads)
     hipLaunchKernelGGL(topn_mask_kernel<8>, dim3(1), dim3(kMaskThreads), 0, stream, stats, ci,
                        (int)n_protect, mask);

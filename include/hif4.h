@@ -249,17 +249,19 @@ HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
  *            (row, 128-channel block) pairs or part thereof: 75 MB for
  *            57,600 x 5120, 213 MB for 921,600 x 5120. On completion the u32 at byte offset
  *            hif4_percentile_workspace_bytes(rows, c) - 256 holds the number
- *            of channels whose statistic came from the two exact radix
- *            passes: c when rows < 8192 or ld > 2^19; otherwise the channels
- *            for which the one-pass window (see below) missed rank lo or hi.
+ *            of channels whose statistic came from exact radix passes: c when
+ *            the one-pass window path below does not apply; otherwise the
+ *            channels for which the window missed rank lo or hi.
  *
- *  Long columns (rows >= 8192, ld <= 2^19) first take a one-pass path: the
- *  coarse histogram of every 8th row places, per channel, a window of 512
+ *  Long columns (rows >= 8192 and ld * S <= 2^20, with the sample stride
+ *  S = max(8, ceil(rows / 8192))) first take a one-pass path: the coarse
+ *  histogram of every S-th row places, per channel, a window of 512
  *  consecutive magnitude keys around the quantile; one pass over all rows
  *  counts the keys below the window and each key inside it. Channels whose
- *  ranks lo and hi both fall inside are final; the rest are recomputed by the
- *  two exact passes (launched always, skipped on the device when no channel
- *  needs them). Results are identical either way.
+ *  ranks lo and hi both fall inside are final; the rest are recomputed
+ *  exactly, each by two radix passes over its own column, inside the same
+ *  final kernel (slow per channel, and normally none). Results are identical
+ *  either way.
  */
 HIF4_EXPORT hif4_status hif4_percentile_mask(const void *x, int64_t rows, int64_t c, int64_t ld, double q,
                                  int64_t n_protect, float *stats, uint8_t *mask,

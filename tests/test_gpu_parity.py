@@ -292,13 +292,15 @@ def test_linear_empty_k_gives_zero(hip):
 def window_misses(bits, q):
     """Channels the one-pass window path leaves to the exact passes, by the
     rule the header states: the window is the 512 keys starting one coarse bin
-    (128 keys) below the coarse bin of rank floor(q (n_s - 1)) among every 8th
-    row; a channel misses when its ranks lo or hi fall outside the window."""
+    (128 keys) below the coarse bin of rank floor(q (n_s - 1)) among every
+    S-th row, S = max(8, ceil(rows / 8192)); a channel misses when its ranks
+    lo or hi fall outside the window."""
     rows, c = bits.shape
     if rows < 8192:
         return c
+    stride = max(8, -(-rows // 8192))
     k = (bits & 0x7FFF).astype(np.int64)
-    s = np.sort(k[::8], axis=0)
+    s = np.sort(k[::stride], axis=0)
     b = s[int(np.floor(q * (s.shape[0] - 1)))] >> 7
     w = np.maximum(b - 1, 0) << 7
     lo = int(np.floor(q * (rows - 1)))
@@ -355,10 +357,12 @@ def test_percentile_constant_and_tied_channels(hip):
 
 @pytest.mark.parametrize("rows,c,q,n", [(8192, 64, 0.999, 3), (10000, 300, 0.999, 3),
                                         (20000, 130, 0.5, 13), (9000, 64, 1.0, 5),
-                                        (9001, 200, 0.0, 7), (12345, 77, 0.9, 1)])
+                                        (9001, 200, 0.0, 7), (12345, 77, 0.9, 1),
+                                        (70001, 64, 0.999, 3), (200000, 24, 0.99, 2)])
 def test_percentile_sampled_window_path(hip, rows, c, q, n):
     """Long columns (>= 8192 rows) take the one-pass path: a window of keys
-    around the quantile of every 8th row, exact whenever both ranks land in it."""
+    around the quantile of every S-th row (S = 8 up to 65,536 rows, 9 and 25
+    for the two longest cases), exact whenever both ranks land in it."""
     bits = workloads.bits(workloads.heavy_tailed_x(rows, c, seed=rows + c, outlier_channels=2))
     ld = ((c + 7) // 8) * 8 if c % 8 else None
     exact = run_pct_case(hip, bits, q, n, ld=ld)
