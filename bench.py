@@ -36,14 +36,29 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 HiF4 linear TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, w, mask_np, rows_sample):
-    """The oracle, as it stands, on a bounded sample of the same step."""
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    masked quantize of all of W and of `rows_sample` evenly spaced rows of X,
+    then the fp64 linear (with the protected-channel residual) on those rows.
+    `value` is the step's rate (2 * rows * N * K flops over the whole sample
+    time); the quantize and linear rates are also given on their own."""
     import numpy as np
 
     import oracle
@@ -56,17 +71,24 @@ def cpu_baseline(x, w, mask_np, rows_sample):
     t0 = time.perf_counter()
     wc, wm, wk = oracle.quantize(wb, mask_np)
     xc, xm, xk = oracle.quantize(xs, mask_np)
+    t1 = time.perf_counter()
     oracle.linear_protected(xc, xm, xk, wc, wm, wk, with_mag=False)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
+    dt = t2 - t0
     n, k = w.shape
+    n_mask = int(mask_np.sum())
     flops = 2.0 * rows_sample * n * k
+    q_bytes = (rows_sample + n) * (k * (2 + 0.5 + 4 / 64) + n_mask * 2)
     omp = os.environ.get("OMP_NUM_THREADS")
     cores = min(threads, int(omp)) if omp and omp.isdigit() else threads
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{rows_sample} of {x.shape[0]} rows of X quantized (masked) + full W quantized "
                   f"(masked) + fp64 linear with the protected-channel residual on those rows; "
                   f"{dt:.1f} s",
+        "quantize_GB/s": q_bytes / (t1 - t0) / 1e9, "quantize_s": t1 - t0,
+        "linear_TFLOP/s": flops / (t2 - t1) / 1e12, "linear_s": t2 - t1,
     }
 
 
@@ -210,6 +232,151 @@ def time_calibration(torch, workloads, hif4, dev, stream, reps=3):
             "quantize_w_masked_ms": t_q}
 
 
+def time_shapes(torch, workloads, hif4, dev, stream, reps=5):
+    """The other target shapes, each call timed on its own (HIP events, mean
+    over `reps` after one untimed call), outside the step: the unmasked
+    activation quantize of the FFN-up and FFN-down activations, and the W4A4
+    contraction (hif4_linear_xcodes_wbf16, Y fp32, no protected channels) at
+    the attention-projection and FFN-down shapes."""
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    for name in ("ffn_up", "attn", "ffn_down"):
+        spec = workloads.WORKLOADS[name]
+        M, N, K = spec["M"], spec["N"], spec["K"]
+        x = (workloads.gelu_x(M, K, device="cuda", seed=spec["index"]) if name == "ffn_down"
+             else workloads.heavy_tailed_x(M, K, device="cuda", seed=spec["index"]))
+        xcodes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xmeta = torch.empty((M, K // 64), dtype=torch.int32, device=dev)
+        if name != "attn":
+            t = timed(lambda: hif4.quantize(x, codes=xcodes, meta=xmeta, stream=stream))
+            nbytes = M * K * (2 + 0.5 + 4 / 64)
+            out[f"quantize_x_unmasked_{name}"] = {
+                "shape": f"{M}x{K}", "ms": t, "GB/s": nbytes / t / 1e6,
+                "frac_hbm": nbytes / t / 1e6 / HBM_PEAK_GBS}
+            log(f"unmasked quantize of X {name} {M}x{K}: {t:.3f} ms")
+        else:
+            hif4.quantize(x, codes=xcodes, meta=xmeta, stream=stream)
+        if name == "ffn_up":
+            del x, xcodes, xmeta
+            continue
+        del x
+        wt = workloads.normal_bf16(N, K, 0.015 if name == "ffn_down" else 0.02, device="cuda",
+                                   seed=spec["index"] + 1000)
+        wc, wm, _ = hif4.quantize(wt, stream=stream)
+        wdeq = hif4.dequantize(wc, wm, out_dtype=torch.bfloat16, stream=stream)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        t = timed(lambda: hif4.linear_xcodes_wbf16(xcodes, xmeta, wdeq, y=y, stream=stream))
+        tf = 2.0 * M * N * K / (t * 1e-3) / 1e12
+        out[f"gemm_w4a4_{name}"] = {"shape": f"{M}x{N}x{K}", "ms": t, "TFLOP/s": tf,
+                                    "frac_bf16_mfma": tf / BF16_MFMA_PEAK_TFLOPS,
+                                    "frac_fp8_mfma": tf / FP8_MFMA_PEAK_TFLOPS}
+        log(f"W4A4 contraction {name} {M}x{N}x{K}: {t:.3f} ms, {tf:.0f} TFLOP/s")
+        del wt, wc, wm, wdeq, y, xcodes, xmeta
+    return out
+
+
+def ceilings(torch, dev, stream):
+    """Achievable ceilings on this GPU, for the rooflines: a device-to-device
+    copy of 2 GiB (HBM read + write, far beyond the 256 MB MALL) and the bf16
+    matrix-core probe (libhif4_probe.so) at the W4A4 kernel's launch shape."""
+    import ctypes
+
+    nbytes = 2 << 30
+    a = torch.empty((nbytes // 4,), dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+
+    def rate(fn, moved, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return ms, moved / ms / 1e6
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_block_float_amd", "libhif4_probe.so"))
+    lib.hif4_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.hif4_probe_mfma_bf16.restype = ctypes.c_int
+    lib.hif4_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.hif4_probe_copy.restype = ctypes.c_int
+    ms_c, gbs_c = rate(lambda: b.copy_(a), 2 * nbytes)
+    out = {"hbm_copy_torch": {"bytes": 2 * nbytes, "ms": ms_c, "GB/s": gbs_c,
+                              "frac_hbm": gbs_c / HBM_PEAK_GBS,
+                              "what": "torch copy_ of 2 GiB fp32 (read 2 GiB + write 2 GiB)"}}
+    log(f"HBM copy (torch): {gbs_c:.0f} GB/s")
+    best = None
+    for blocks in (2048, 8192, 32768):
+        def cp():
+            st = lib.hif4_probe_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                     nbytes, blocks, ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"hif4_probe_copy: status {st}")
+        ms, gbs = rate(cp, 2 * nbytes)
+        log(f"HBM copy (probe, {blocks} workgroups): {gbs:.0f} GB/s")
+        if best is None or gbs > best["GB/s"]:
+            best = {"bytes": 2 * nbytes, "ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                    "workgroups": blocks,
+                    "what": "grid-stride copy of 2 GiB, 16-byte non-temporal loads/stores, four "
+                            "loads in flight per lane (libhif4_probe.so)"}
+    out["hbm_copy"] = best
+    lib.hif4_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.hif4_probe_read.restype = ctypes.c_int
+    best = None
+    for blocks in (2048, 8192, 32768):
+        sink = torch.empty((blocks * 256,), dtype=torch.int32, device=dev)
+
+        def rd():
+            st = lib.hif4_probe_read(ctypes.c_void_p(a.data_ptr()), nbytes,
+                                     ctypes.c_void_p(sink.data_ptr()), blocks,
+                                     ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"hif4_probe_read: status {st}")
+        ms, gbs = rate(rd, nbytes)
+        log(f"HBM read (probe, {blocks} workgroups): {gbs:.0f} GB/s")
+        if best is None or gbs > best["GB/s"]:
+            best = {"bytes": nbytes, "ms": ms, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                    "workgroups": blocks,
+                    "what": "grid-stride read of 2 GiB, 16-byte non-temporal loads, four in "
+                            "flight per lane (libhif4_probe.so)"}
+    out["hbm_read"] = best
+    del a, b
+    blocks, iters = 12150, 324  # the FFN-up launch: 12,150 tiles x 4 waves x 5184 MFMAs
+    sink = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
+    flops = blocks * 4 * iters * 16 * 2.0 * 32 * 32 * 16
+
+    def probe():
+        st = lib.hif4_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hif4_probe_mfma_bf16: status {st}")
+
+    ms_m, _ = rate(probe, 0.0, reps=5)
+    tf = flops / (ms_m * 1e-3) / 1e12
+    out["mfma_bf16"] = {"ms": ms_m, "TFLOP/s": tf, "frac_bf16_mfma": tf / BF16_MFMA_PEAK_TFLOPS,
+                        "implied_clock_GHz": tf / BF16_MFMA_PEAK_TFLOPS * 2.4,
+                        "what": "v_mfma_f32_32x32x16_bf16 back to back from registers, 12,150 "
+                                "workgroups x 4 waves x 5184 MFMAs (the FFN-up launch's count)"}
+    log(f"MFMA-only bf16: {tf:.0f} TFLOP/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +386,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=6144)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the HiGPTQ timing that follows the hot-path steps")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the achievable ceilings (HBM copy, MFMA-only probe), print "
+                         "them as one JSON line and exit")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the other target shapes timed after the hot-path steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -244,6 +416,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy probe: 3 copies of {args.copy_probe} MiB done")
+        return
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(torch, dev, torch.cuda.current_stream(dev))}),
+              flush=True)
         return
     spec = workloads.WORKLOADS["ffn_up"]
     M, N, K = spec["M"], spec["N"], spec["K"]
@@ -326,7 +502,8 @@ def main():
                        "frac_hbm": q_bytes / t_xq / 1e6 / HBM_PEAK_GBS},
         "dequantize_w": {"ms": t_wd, "GB/s": wd_bytes / t_wd / 1e6},
         "gemm_w4a4": {"ms": t_lin, "TFLOP/s": gemm_tflops,
-                      "frac_bf16_mfma": gemm_tflops / BF16_MFMA_PEAK_TFLOPS},
+                      "frac_bf16_mfma": gemm_tflops / BF16_MFMA_PEAK_TFLOPS,
+                      "frac_fp8_mfma": gemm_tflops / FP8_MFMA_PEAK_TFLOPS},
     }
     out = {
         "metric": METRIC,
@@ -360,6 +537,8 @@ def main():
         "quantize": parts["quantize_x_masked"],
         "parts": parts,
     }
+    if not args.no_shapes:
+        parts.update(time_shapes(torch, workloads, hif4, dev, stream))
     if not args.no_extras:
         out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, stream)}
         out["extensions"]["calibration"] = time_calibration(torch, workloads, hif4, dev, stream)

@@ -30,8 +30,27 @@ def flags():
     ]
 
 
+PROBE_LIB = os.path.join(HERE, "libhif4_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile libhif4_probe.so (measurement probes used by bench.py --ceilings)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *flags(), "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    text = "\n".join(l for l in p.stdout.decode(errors="replace").splitlines()
+                     if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probe.hip:\n{text}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object, then link libhif4.so. Always rebuilds."""
+    """Compile every source to an object, then link libhif4.so (and the probe
+    library). Always rebuilds."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
@@ -52,6 +71,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -153,7 +153,8 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: the DMA destinations (M0) then come from scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // Tile order: consecutive workgroup ids go to different XCDs (round
@@ -623,7 +624,8 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: the DMA destinations (M0) then come from scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int ntiles = tiles_m * tiles_n;
