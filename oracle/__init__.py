@@ -48,6 +48,8 @@ def _lib():
         lib.hif4o_higptq_unit_scheme.restype = ctypes.c_int
         lib.hif4o_higptq_unit_scheme_margin.argtypes = [p, i64, i64, p, i64, ctypes.c_int, p, p, p]
         lib.hif4o_higptq_unit_scheme_margin.restype = ctypes.c_int
+        lib.hif4o_higptq_run_margin.argtypes = [p, i64, i64, p, i64, i64, ctypes.c_int, p, p, p, p]
+        lib.hif4o_higptq_run_margin.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -234,6 +236,30 @@ def higptq_unit(w: np.ndarray, u: np.ndarray, unit: int, codes: np.ndarray, meta
                                                   _ptr(codes), _ptr(meta),
                                                   _ptr(margin) if margin is not None else None),
            "higptq_unit")
+
+
+def higptq_run(w: np.ndarray, u: np.ndarray, unit0: int, units: int, codes: np.ndarray,
+               meta: np.ndarray, scheme: int, margin: np.ndarray, accmag: np.ndarray):
+    """Groups ``unit0 .. unit0 + units - 1`` in order, each exactly the step of
+    ``higptq_unit``, in place on ``w`` (float64 [n][k]); ``margin`` (float64
+    [n], start it at +inf) receives each row's smallest relative distance of a
+    decision on a moved value to its boundary over the whole run, and
+    ``accmag`` (float64 [n][k], start it at 0) the accumulated update sizes
+    sum |f||U| per entry (see hif4_oracle.c)."""
+    n, k = w.shape
+    if w.dtype != np.float64 or not w.flags.c_contiguous:
+        raise OracleError("higptq_run: w must be C-contiguous float64")
+    uu = np.ascontiguousarray(u, dtype=np.float64)
+    _shape(uu, (k, k), "higptq_run u")
+    _shape(codes, (n, k // 2), "higptq_run codes")
+    _shape(meta, (n, k // 64), "higptq_run meta")
+    for a, shp, name in ((margin, (n,), "margin"), (accmag, (n, k), "accmag")):
+        if a.dtype != np.float64 or a.shape != shp or not a.flags.c_contiguous:
+            raise OracleError(f"higptq_run: {name} must be a contiguous float64 array {shp}")
+    _check(_lib().hif4o_higptq_run_margin(_ptr(w), n, k, _ptr(uu), int(unit0), int(units),
+                                          int(scheme), _ptr(codes), _ptr(meta), _ptr(margin),
+                                          _ptr(accmag)),
+           "higptq_run")
 
 
 def higptq(w: np.ndarray, u: np.ndarray, scheme: int = 1):

@@ -608,15 +608,22 @@ static void encode_span(const double x[UNIT], int j0, int len, double s, int e2_
     *meta |= (uint32_t)e2 << (8 + g);
 }
 
-/* margin: NULL, or double [n]. Row r receives the smallest decision margin
- * (see encode_span) over the decisions of schemes 2 and 3 that read updated
- * values, with sc[j] = |w[j]| + sum over the updates of column j of
- * sum_i |f_i| |U_ij|; +inf under scheme 1 and for decisions on the weights as
- * given (scheme 1's, and every level-1 code), which any run starting from the
- * same weights takes identically. */
-int hif4o_higptq_unit_scheme_margin(double *w, int64_t n, int64_t k, const double *u,
-                                    int64_t unit, int scheme, uint8_t *codes, uint32_t *meta,
-                                    double *margin)
+/* Level-1 code of a unit whose largest magnitude is amax: the smallest c with
+ * 7 v(c) >= amax (255 when none). */
+static int level1_of(double amax)
+{
+    for (int cc = 0; cc < 256; ++cc)
+        if (7.0 * hif4o_e6m2_value(cc) >= amax) return cc;
+    return 255;
+}
+
+/* One group step; see hif4o_higptq_unit_scheme_margin and hif4o_higptq_run_margin
+ * for margin and accmag. With accmag, a value counts as moved from the start
+ * of the step when accmag of its entry is nonzero, and then the level-1 code
+ * and scheme 1's decisions read moved values too. */
+static int higptq_step(double *w, int64_t n, int64_t k, const double *u, int64_t unit,
+                       int scheme, uint8_t *codes, uint32_t *meta, double *margin,
+                       double *accmag)
 {
     if (n < 0 || k <= 0 || k % UNIT != 0 || unit < 0 || unit >= k / UNIT) return HIF4O_ERR_ARG;
     if (scheme < 1 || scheme > 3) return HIF4O_ERR_ARG;
@@ -631,29 +638,48 @@ int hif4o_higptq_unit_scheme_margin(double *w, int64_t n, int64_t k, const doubl
         double v[UNIT], deq[UNIT], f[UNIT], sc[UNIT];
         int moved[UNIT];
         double mg = INFINITY;
+        double *am = accmag ? accmag + r * k : NULL;
+        int any_moved = 0;
         for (int j = 0; j < UNIT; ++j) {
             v[j] = wr[s0 + j];
-            sc[j] = fabs(v[j]);
-            moved[j] = 0;
+            sc[j] = fabs(v[j]) + (am ? am[s0 + j] : 0.0);
+            moved[j] = am && am[s0 + j] != 0.0;
+            any_moved |= moved[j];
             if (!isfinite(v[j])) bad = 1;
         }
         uint8_t *uc = codes + r * (k / 2) + unit * 32;
         uint32_t *um = meta + r * units + unit;
+        double amax = 0.0, scmax = 0.0;
+        for (int j = 0; j < UNIT; ++j) {
+            amax = fabs(v[j]) > amax ? fabs(v[j]) : amax;
+            scmax = sc[j] > scmax ? sc[j] : scmax;
+        }
+        const int c1 = level1_of(amax);
+        if (margin && any_moved) {
+            /* level-1: amax against 7 v(c) and 7 v(c - 1) */
+            double r1 = fabs(7.0 * hif4o_e6m2_value(c1) - amax);
+            if (c1 > 0) {
+                double r0 = fabs(amax - 7.0 * hif4o_e6m2_value(c1 - 1));
+                r1 = r0 < r1 ? r0 : r1;
+            }
+            r1 /= scmax;
+            if (r1 < mg) mg = r1;
+        }
         if (scheme == 1) {
             quantize_unit(v, uc, um); /* all exponents from the group at once */
             for (int j = 0; j < UNIT; ++j) deq[j] = unit_element(uc, *um, j);
+            if (margin && any_moved) {
+                /* the same decisions again, for their margins only */
+                uint8_t cs[32] = {0};
+                uint32_t ms = (uint32_t)c1;
+                double ds[UNIT];
+                for (int t0 = 0; t0 < UNIT; t0 += 8)
+                    encode_span(v, t0, 8, hif4o_e6m2_value(c1), -1, cs, &ms, ds, sc, moved, &mg);
+            }
         } else {
             /* level-1 from the group as it stands before any update */
-            double amax = 0.0;
-            for (int j = 0; j < UNIT; ++j) amax = fabs(v[j]) > amax ? fabs(v[j]) : amax;
-            int c = 255;
-            for (int cc = 0; cc < 256; ++cc)
-                if (7.0 * hif4o_e6m2_value(cc) >= amax) {
-                    c = cc;
-                    break;
-                }
             memset(uc, 0, 32);
-            *um = (uint32_t)c;
+            *um = (uint32_t)c1;
         }
         for (int t0 = 0; t0 < UNIT; t0 += span) {
             if (scheme == 2) {
@@ -683,15 +709,56 @@ int hif4o_higptq_unit_scheme_margin(double *w, int64_t n, int64_t k, const doubl
                 if (mag != 0.0) moved[j] = 1;
             }
         }
-        if (margin) margin[r] = mg;
+        if (margin) margin[r] = accmag ? (mg < margin[r] ? mg : margin[r]) : mg;
         for (int j = 0; j < UNIT; ++j) wr[s0 + j] = v[j];
         for (int64_t c = r0; c < k; ++c) {
-            double acc = 0.0;
-            for (int i = 0; i < UNIT; ++i) acc += f[i] * u[(s0 + i) * k + c];
+            double acc = 0.0, mag = 0.0;
+            for (int i = 0; i < UNIT; ++i) {
+                acc += f[i] * u[(s0 + i) * k + c];
+                mag += fabs(f[i]) * fabs(u[(s0 + i) * k + c]);
+            }
             wr[c] -= acc;
+            if (am) am[c] += mag;
         }
     }
     return bad ? HIF4O_ERR_NONFINITE : HIF4O_OK;
+}
+
+/* margin: NULL, or double [n]. Row r receives the smallest decision margin
+ * (see encode_span) over the decisions of schemes 2 and 3 that read updated
+ * values, with sc[j] = |w[j]| + sum over the updates of column j of
+ * sum_i |f_i| |U_ij|; +inf under scheme 1 and for decisions on the weights as
+ * given (scheme 1's, and every level-1 code), which any run starting from the
+ * same weights takes identically. */
+int hif4o_higptq_unit_scheme_margin(double *w, int64_t n, int64_t k, const double *u,
+                                    int64_t unit, int scheme, uint8_t *codes, uint32_t *meta,
+                                    double *margin)
+{
+    return higptq_step(w, n, k, u, unit, scheme, codes, meta, margin, NULL);
+}
+
+/* HiGPTQ over groups unit0 .. unit0 + units - 1 in order, each exactly
+ * hif4o_higptq_unit_scheme's step (same arithmetic, same results). Margins
+ * over the whole run: accmag (double [n][k], in/out, zero for a run from
+ * weights as given) holds per entry the sum over the updates applied so far
+ * of sum_i |f_i| |U_ic|; a decision reads a moved value when an update of this
+ * run or an earlier one (accmag != 0) or of its own group has moved it, and
+ * then lowers margin[r] (in/out: start it at +inf) to its distance from its
+ * boundary over sc = |value| + accmag + the group's own update sizes. The
+ * level-1 code (amax against 7 v(c) and 7 v(c - 1)) and scheme 1's decisions
+ * count too once the group holds a moved value. A run in other precision from
+ * the same weights can decide differently from this one only on a row whose
+ * margin lies within its rounding error. */
+int hif4o_higptq_run_margin(double *w, int64_t n, int64_t k, const double *u, int64_t unit0,
+                            int64_t units, int scheme, uint8_t *codes, uint32_t *meta,
+                            double *margin, double *accmag)
+{
+    if (!margin || !accmag || units < 0 || unit0 < 0) return HIF4O_ERR_ARG;
+    for (int64_t t = 0; t < units; ++t) {
+        int st = higptq_step(w, n, k, u, unit0 + t, scheme, codes, meta, margin, accmag);
+        if (st != HIF4O_OK) return st;
+    }
+    return HIF4O_OK;
 }
 
 int hif4o_higptq_unit_scheme(double *w, int64_t n, int64_t k, const double *u, int64_t unit,

@@ -826,3 +826,73 @@ def test_higptq_decision_margin(scheme):
     assert w1[0, 8] == 0.375
     assert mg1[0] == 0.0
     assert (nibble(c1[0], 8) & 7) == 2  # the tie went to the even k
+
+
+@pytest.mark.parametrize("scheme", [1, 2, 3])
+def test_higptq_run_margin(scheme):
+    """The oracle's run over several groups with margins across them: the
+    same codes, meta and weights as its group steps one at a time (margins
+    change no arithmetic); with the identity Hessian no update sizes and
+    +inf; on generic rows finite and positive under every scheme (the later
+    groups read values the earlier ones moved) and unchanged by a power-of-two
+    scaling, with the update sizes scaled alike; under scheme 1 the update
+    sizes are sum |F| |U| with F = E U_SS^-1 per group; and a tie planted
+    across groups gives 0 where the per-group margin, which counts only moves
+    inside a group, gives +inf."""
+    n, k = 16, 256
+    W, _, U = _gptq_problem(n, k, 82)
+    w = W.astype(np.float64)
+    wr, cr, mr = w.copy(), np.zeros((n, k // 2), np.uint8), np.zeros((n, k // 64), np.uint32)
+    mg, am = np.full(n, np.inf), np.zeros((n, k))
+    oracle.higptq_run(wr, U, 0, k // 64, cr, mr, scheme, mg, am)
+    wu, cu, mu = w.copy(), np.zeros_like(cr), np.zeros_like(mr)
+    for unit in range(k // 64):
+        oracle.higptq_unit(wu, U, unit, cu, mu, scheme)
+    assert np.array_equal(wr, wu) and np.array_equal(cr, cu) and np.array_equal(mr, mu)
+    assert np.all(np.isfinite(mg)) and np.all(mg > 0)
+    mg4, am4 = np.full(n, np.inf), np.zeros((n, k))
+    oracle.higptq_run(4.0 * w, U, 0, k // 64, np.zeros_like(cr), np.zeros_like(mr), scheme, mg4,
+                      am4)
+    assert np.array_equal(mg, mg4) and np.array_equal(4.0 * am, am4)
+    if scheme == 1:
+        # update sizes from the F each group implies (E from the weights the
+        # group started from, which the run leaves in the group's columns)
+        ref = np.zeros((n, k))
+        for unit in range(k // 64):
+            s0, r0 = 64 * unit, 64 * unit + 64
+            E = wr[:, s0:r0] - oracle.dequantize(cr[:, 32 * unit:32 * unit + 32],
+                                                 mr[:, unit:unit + 1])
+            F = np.linalg.solve(U[s0:r0, s0:r0].T, E.T).T
+            ref[:, r0:] += np.abs(F) @ np.abs(U[s0:r0, r0:])
+        assert np.allclose(am, ref, rtol=1e-12, atol=0)
+        assert np.all(am[:, :64] == 0)
+    mgi, ami = np.full(n, np.inf), np.zeros((n, k))
+    oracle.higptq_run(w.copy(), np.eye(k), 0, k // 64, np.zeros_like(cr), np.zeros_like(mr),
+                      scheme, mgi, ami)
+    assert np.all(np.isinf(mgi)) and not ami.any()
+    # Planted tie across groups. Group 0: x_0 = 7 sets v(c) = 1, e2 = e3 = 1
+    # (D = 4) and quantizes exactly; x_1 = 0.25 rounds to 0, so F_1 = 0.25,
+    # and U[1, 64] = 2 moves column 64 by -0.5: 2.6875 -> 2.1875. Group 1:
+    # its largest value x_65 = 6 sets v(c) = 0.875 (7 v(c) = 6.125 >= 6),
+    # e2 = e3 = 1 (6 > 3.0625), D = 3.5, and 2.1875 = 5 D / 8 is the tie
+    # between k = 2 and k = 3; every other decision on column 64 is away
+    # from its boundary.
+    kk = 128
+    x = np.zeros((1, kk))
+    x[0, 0], x[0, 1], x[0, 64], x[0, 65] = 7.0, 0.25, 2.6875, 6.0
+    uu = np.eye(kk)
+    uu[1, 64] = 2.0
+    c1, m1 = np.zeros((1, kk // 2), np.uint8), np.zeros((1, kk // 64), np.uint32)
+    mg1, am1 = np.full(1, np.inf), np.zeros((1, kk))
+    w1 = x.copy()
+    oracle.higptq_run(w1, uu, 0, 2, c1, m1, scheme, mg1, am1)
+    assert w1[0, 64] == 2.1875 and oracle.e6m2_value(int(m1[0, 1] & 255)) == 0.875
+    assert mg1[0] == 0.0
+    assert (nibble(c1[0], 64) & 7) == 2  # the tie went to the even k
+    assert am1[0, 64] == 0.5 and np.count_nonzero(am1) == 1
+    # the per-group margin of the same second step sees no move inside it
+    w2 = x.copy()
+    oracle.higptq_unit(w2, uu, 0, c1, m1, scheme)
+    mg2 = np.zeros(1)
+    oracle.higptq_unit(w2, uu, 1, c1, m1, scheme, margin=mg2)
+    assert np.isinf(mg2[0])
