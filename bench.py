@@ -37,6 +37,7 @@ METRIC = "W4A4 HiF4 linear TFLOP/s + quantize GB/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 
 
 def log(msg):
@@ -118,11 +119,13 @@ def torch_index(idx):
     return torch.from_numpy(idx).to(torch.long)
 
 
-def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
+def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2, block_units=4):
     """HiGPTQ over the whole weight (80 groups of 64 columns), each of the
-    three schemes: one untimed pass, then `reps` timed passes from the same
-    start. Reported apart from the hot-path step (it is a calibration pass,
-    run once per layer)."""
+    three schemes, in blocks of `block_units` groups (blocksize 64 block_units:
+    the columns after a block are compensated once per block) and, for
+    comparison, one group per call (blocksize 64): one untimed pass, then
+    `reps` timed passes from the same start. Reported apart from the hot-path
+    step (it is a calibration pass, run once per layer)."""
     spec = workloads.WORKLOADS["higptq"]
     n, k = w_bf16.shape
     u = workloads.higptq_factor(k, device="cuda", seed=spec["index"])
@@ -130,34 +133,59 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2):
     w = torch.empty_like(w0)
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
     meta = torch.empty((n, k // 64), dtype=torch.int32, device=dev)
-    ws = torch.empty((hif4.higptq_workspace_bytes(n),), dtype=torch.uint8, device=dev)
     units = k // 64
-    # compensation per group: 2 n 64 flops and 8 bytes of W (read + write)
-    # per element after the group, 64 (u + 1) .. k
+    ws1 = torch.empty((hif4.higptq_workspace_bytes(n),), dtype=torch.uint8, device=dev)
+    wsb = torch.empty((hif4.higptq_block_workspace_bytes(n, block_units),), dtype=torch.uint8,
+                      device=dev)
+    # compensation: 2 n flops per (earlier column, later column) pair of each
+    # group, whatever the blocksize; W traffic (read + write, 8 bytes per
+    # element): per group every later column (blocksize 64), or per block the
+    # columns after it plus, per group, the block's own later columns
     flops = sum(2.0 * n * 64 * (k - 64 * (g + 1)) for g in range(units))
-    wbytes = sum(8.0 * n * (k - 64 * (g + 1)) for g in range(units))
-    out = {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
-           "groups": units}
-    for scheme in (1, 2, 3):
+    wbytes1 = sum(8.0 * n * (k - 64 * (g + 1)) for g in range(units))
+    wbytesb = 0.0
+    for b0 in range(0, units, block_units):
+        bu = min(block_units, units - b0)
+        wbytesb += 8.0 * n * (k - 64 * (b0 + bu)) + sum(8.0 * n * 64 * (bu - 1 - j) for j in range(bu))
+
+    def one_pass(scheme, bu):
+        if bu == 1:
+            for unit in range(units):
+                hif4.higptq_unit(w, u, unit, codes, meta, workspace=ws1, stream=stream,
+                                 scheme=scheme)
+        else:
+            for b0 in range(0, units, bu):
+                hif4.higptq_block(w, u, b0, min(bu, units - b0), codes, meta, workspace=wsb,
+                                  stream=stream, scheme=scheme)
+
+    def timed(scheme, bu):
         times = []
         for rep in range(reps + 1):
             w.copy_(w0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for unit in range(units):
-                hif4.higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream,
-                                 scheme=scheme)
+            one_pass(scheme, bu)
             e1.record(stream)
             torch.cuda.synchronize()
             if rep:
                 times.append(e0.elapsed_time(e1))
-        ms = sum(times) / len(times)
-        log(f"HiGPTQ scheme {scheme} over W {n}x{k}: {ms:.2f} ms")
-        # rates over the whole pass (group kernels included): the compensation
-        # streams W, so its bound is HBM
-        out[f"scheme{scheme}"] = {"ms": ms, "update_TFLOP/s": flops / (ms * 1e-3) / 1e12,
-                                  "W_GB/s": wbytes / ms / 1e6,
-                                  "frac_hbm": wbytes / ms / 1e6 / HBM_PEAK_GBS}
+        return sum(times) / len(times)
+
+    out = {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
+           "groups": units, "blocksize": 64 * block_units}
+    for scheme in (1, 2, 3):
+        ms = timed(scheme, block_units)
+        ms1 = timed(scheme, 1)
+        log(f"HiGPTQ scheme {scheme} over W {n}x{k}: {ms:.2f} ms in blocks of {64 * block_units} "
+            f"columns, {ms1:.2f} ms one group at a time")
+        # rates over the whole pass (group kernels included)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"scheme{scheme}"] = {"ms": ms, "update_TFLOP/s": tf,
+                                  "frac_fp32_mfma": tf / FP32_MFMA_PEAK_TFLOPS,
+                                  "W_GB/s": wbytesb / ms / 1e6,
+                                  "ms_blocksize64": ms1,
+                                  "W_GB/s_blocksize64": wbytes1 / ms1 / 1e6,
+                                  "frac_hbm_blocksize64": wbytes1 / ms1 / 1e6 / HBM_PEAK_GBS}
     return out
 
 

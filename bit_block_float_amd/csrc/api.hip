@@ -366,4 +366,33 @@ hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const 
                                           (float*)workspace, stream));
 }
 
+size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units) {
+  if (n < 0 || units < 1 || units > HIF4_HIGPTQ_MAX_BLOCK_UNITS) return 0;
+  return align256((size_t)n * 64 * (size_t)units * sizeof(float));
+}
+
+hif4_status hif4_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
+                              int64_t ldu, int64_t unit0, int64_t units, int scheme,
+                              uint8_t* codes, uint32_t* meta, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (n < 0 || n >= (int64_t(1) << 24) || k <= 0 || k % 64 != 0 || ldw < k || ldu < k ||
+      ldw >= (int64_t(1) << 22) || ldu >= (int64_t(1) << 22))
+    return HIF4_ERR_SHAPE;
+  if (units < 1 || units > HIF4_HIGPTQ_MAX_BLOCK_UNITS || unit0 < 0 || unit0 > k / 64 - units ||
+      scheme < 1 || scheme > 3)
+    return HIF4_ERR_ARG;
+  if (n == 0) return HIF4_OK;
+  if (!w || !u || !codes || !meta) return HIF4_ERR_NULL;
+  if (!aligned(w, 16) || ldw % 4 != 0 || !aligned(u, 16) || ldu % 4 != 0 || !aligned(codes, 16) ||
+      !aligned(meta, 4))
+    return HIF4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < hif4_higptq_block_workspace_bytes(n, units))
+    return HIF4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return HIF4_ERR_ALIGN;
+  hif4_status st = check_device();
+  if (st != HIF4_OK) return st;
+  return launched(hif4_launch_higptq_block(w, n, k, ldw, u, ldu, unit0, units, scheme, codes,
+                                           meta, (float*)workspace, stream));
+}
+
 }  // extern "C"

@@ -99,11 +99,14 @@ __global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restri
   }
 }
 
-// HiGPTQ group step, part 1: four lanes per row (a quad), lane q owning the
-// group's columns j = 4m + q (m = 0..15), so that a level-3 group is one
-// column per lane and its maximum a two-step quad reduction; U_SS in LDS.
-// Writes unit `unit` of the row's codes and meta and the row's 64 values of F
-// (the compensation of the columns after the group is F U_SR, part 2).
+// HiGPTQ group step, part 1: one row of 16 lanes (a DPP row) per weight row,
+// four weight rows per wave; lane p holds the group's columns p + 16 m in
+// v[m] (m = 0..3). A level-3 group (4 consecutive columns) is then one
+// register of a lane quad and a level-2 group one register of a half row, so
+// the maxima are DPP reductions and a set of 4 or 8 columns is quantized by 4
+// or 8 lanes at once. Writes unit `unit` of the row's codes and meta and the
+// row's 64 values of F (at f + r ldf; the compensation of the columns after
+// the group is F U_SR, part 2).
 //   scheme 1: quantize the 64 values at once (all exponents from them), then
 //             F = E U_SS^-1;
 //   scheme 2: level-1 from the 64 values first; then per 8 columns: level-2
@@ -111,73 +114,123 @@ __global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restri
 //             and the group's later columns updated by F U before the next 8;
 //   scheme 3: as scheme 2 per 4 columns, with each level-2 exponent fixed
 //             from its 8 current values before its first 4 columns.
-// F is formed right-looking: once f_i = v_i / U_ii is known (v_i broadcast
-// from its owner lane), every later column takes v_j -= f_i U_ij. Per column
-// that is the order of the forward substitution, i = 0, 1, ...: the same
-// operations in the same order as one thread per row would do.
+// F is formed right-looking, column i = 0, 1, ... in the order of the forward
+// substitution: once column i holds its final value v_i, every later column
+// takes v_j -= v_i (U_ij / U_ii), and f_i = v_i / U_ii. The workgroup stages
+// U_SS in LDS with each row scaled by its diagonal's reciprocal and zeros on
+// and below the diagonal, so the step of column i is the same four FMAs on
+// every lane (v_i broadcast over the row from its owner lane): the columns up
+// to i take -v_i * 0 and keep their values, and F is v times the reciprocals
+// once all steps are done. LDS holds row i of that matrix as lane p's four
+// values (columns p + 16 m) side by side.
+constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <-> 15-i in 16
 __device__ __forceinline__ float quad_maxf(float x) {
   x = fmaxf(x, __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(x))));
   return fmaxf(x, __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(x))));
 }
-template <int kLane>
-__device__ __forceinline__ float quad_bcastf(float x) {
-  return __uint_as_float(dpp<kLane * 0x55>(__float_as_uint(x)));  // quad_perm [o,o,o,o]
+__device__ __forceinline__ float half_row_maxf(float quad_max) {  // over 8 lanes
+  return fmaxf(quad_max, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(quad_max))));
+}
+__device__ __forceinline__ float row_maxf(float x) {
+  x = half_row_maxf(quad_maxf(x));
+  return fmaxf(x, __uint_as_float(dpp<kDppRowMirror>(__float_as_uint(x))));
+}
+// lane `src` of each row of 16 broadcast over its row (row_newbcast); `src`
+// is a constant once the caller's loop is unrolled, so the switch folds away
+__device__ __forceinline__ float row_bcastf(float x, int src) {
+  const uint32_t b = __float_as_uint(x);
+  uint32_t y;
+  switch (src) {
+    case 0: y = dpp<0x150>(b); break;
+    case 1: y = dpp<0x151>(b); break;
+    case 2: y = dpp<0x152>(b); break;
+    case 3: y = dpp<0x153>(b); break;
+    case 4: y = dpp<0x154>(b); break;
+    case 5: y = dpp<0x155>(b); break;
+    case 6: y = dpp<0x156>(b); break;
+    case 7: y = dpp<0x157>(b); break;
+    case 8: y = dpp<0x158>(b); break;
+    case 9: y = dpp<0x159>(b); break;
+    case 10: y = dpp<0x15A>(b); break;
+    case 11: y = dpp<0x15B>(b); break;
+    case 12: y = dpp<0x15C>(b); break;
+    case 13: y = dpp<0x15D>(b); break;
+    case 14: y = dpp<0x15E>(b); break;
+    default: y = dpp<0x15F>(b); break;
+  }
+  return __uint_as_float(y);
+}
+// the 16 bits of a wave-wide ballot that belong to this lane's row of 16
+__device__ __forceinline__ uint32_t row_bits(uint64_t ballot) {
+  return (uint32_t)(ballot >> (threadIdx.x & 48)) & 0xFFFFu;
+}
+// every fourth bit (0, 4, 8, 12) of x, packed into bits 0..3
+__device__ __forceinline__ uint32_t every4th(uint32_t x) {
+  x &= 0x1111u;
+  x = (x | (x >> 3)) & 0x0303u;
+  return (x | (x >> 6)) & 0x000Fu;
 }
 
 template <int kScheme>
 __global__ __launch_bounds__(256) void higptq_group_kernel(
     const float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u,
     int64_t ldu, int64_t s0, int64_t units, int64_t unit, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta, float* __restrict__ f) {
-  // U_SS regrouped by owner lane: U[i][4m + q] at us[64 i + 16 q + m]
-  __shared__ __align__(16) float us[64 * 64];
-  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
-  const int q = threadIdx.x & 3;
+    uint32_t* __restrict__ meta, float* __restrict__ f, int64_t ldf) {
+  __shared__ __align__(16) float us[64 * 64];  // row i: U_ij / U_ii for j > i, else 0
+  __shared__ __align__(16) float rinv[64];     // 1 / U_jj at 4 (j % 16) + j / 16
+  const int p = threadIdx.x & 15;
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   // the row's values first, so that their latency overlaps the staging
-  float v[16];
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (r < n) {
-    const float* wr = w + r * ldw + s0 + q;
+    const float* wr = w + r * ldw + s0 + p;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) v[m] = wr[4 * m];
+    for (int m = 0; m < 4; ++m) v[m] = wr[16 * m];
   }
-  for (int t = threadIdx.x; t < 64 * 64; t += blockDim.x) {
-    const int i = t >> 6, j = t & 63;
-    us[64 * i + 16 * (j & 3) + (j >> 2)] = u[(s0 + i) * ldu + s0 + j];
+#pragma unroll
+  for (int t = threadIdx.x; t < 64 * 16; t += 256) {
+    const int i = t >> 4, j = 4 * (t & 15);
+    const float* ui = u + (s0 + i) * ldu + s0;
+    const float4 x = *reinterpret_cast<const float4*>(ui + j);
+    const float ri = 1.0f / ui[i];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jj = j + e;  // lane jj % 16, register jj / 16
+      us[64 * i + 4 * (jj & 15) + (jj >> 4)] = jj > i ? xs[e] * ri : 0.0f;
+    }
+    if ((i >> 2) == (t & 15)) rinv[4 * (i & 15) + (i >> 4)] = ri;
   }
   __syncthreads();
-  if (r >= n) return;  // the whole quad
+  if (r >= n) return;  // the whole row of 16 lanes
   // level-1 from the 64 values as given (every scheme)
-  float a = 0.0f;
-#pragma unroll
-  for (int m = 0; m < 16; ++m) a = fmaxf(a, fabsf(v[m]));
-  a = quad_maxf(a);
+  const float a = row_maxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
   const uint32_t c = level1_code(a);
   const float s = e6m2_f32(c);
-  uint32_t mw = c;
-  uint32_t cw[8];  // this lane's byte (q) of each code word
-#pragma unroll
-  for (int g = 0; g < 8; ++g) cw[g] = 0u;
   constexpr int kSpan = kScheme == 1 ? 64 : (kScheme == 2 ? 8 : 4);
-  uint32_t e2g[8];
+  // per register: level-2 / level-3 bits of the lane's groups, element code
+  uint32_t e2[4] = {0u, 0u, 0u, 0u}, e3[4] = {0u, 0u, 0u, 0u}, nib[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t0 = 0; t0 < 64; t0 += kSpan) {
-    // level-2 exponents of the level-2 groups starting in the span, from
-    // their 8 current values (columns 8g + q, 8g + 4 + q on this lane)
+  for (int sp = 0; sp < 64 / kSpan; ++sp) {
+    // registers holding the set's columns sp kSpan .. + kSpan - 1
+    constexpr int kRegs = kSpan == 64 ? 4 : 1;
 #pragma unroll
-    for (int g = t0 / 8; g < (t0 + kSpan + 7) / 8; ++g) {
-      if (8 * g < t0) continue;  // fixed before this span (scheme 3)
-      const float m8 = quad_maxf(fmaxf(fabsf(v[2 * g]), fabsf(v[2 * g + 1])));
-      e2g[g] = m8 > 3.5f * s;
-      mw |= e2g[g] << (8 + g);
-    }
-    // level-3 exponents and element codes of the span's columns, E in place
-#pragma unroll
-    for (int m = t0 / 4; m < (t0 + kSpan) / 4; ++m) {
-      const uint32_t e2 = e2g[m / 2];
+    for (int mm = 0; mm < kRegs; ++mm) {
+      const int m = kSpan == 64 ? mm : (sp * kSpan) / 16;
+      const int col = p + 16 * m;
+      const bool in = col / kSpan == sp;
+      // the level-2 exponent of a half row is fixed at the first set that
+      // reaches it (scheme 3: the first of its two sets of 4), from its 8
+      // current values
       const float m4 = quad_maxf(fabsf(v[m]));
-      const uint32_t e3 = m4 > (e2 ? 3.5f : 1.75f) * s;
-      mw |= e3 << (16 + m);
-      const float D = ldexpf(s, (int)(e2 + e3));
+      if (kScheme != 3 || (sp & 1) == 0) {
+        const bool fix2 = kScheme == 3 ? col / 8 == sp / 2 : in;
+        const uint32_t t2 = half_row_maxf(m4) > 3.5f * s;
+        if (fix2) e2[m] = t2;
+      }
+      // level-3 exponent and element code of the lane's column, E in place
+      const uint32_t t3 = m4 > (e2[m] ? 3.5f : 1.75f) * s;
+      const float D = ldexpf(s, (int)(e2[m] + t3));
       const float ax = fabsf(v[m]);
       // k = midpoints (2t+1) D/8 below |x|; at a midpoint the even neighbour
       // wins (> for even t, >= for odd t); 7 beyond the last one
@@ -188,44 +241,55 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
         k += (t & 1) ? (ax >= mid ? 1u : 0u) : (ax > mid ? 1u : 0u);
       }
       const uint32_t sgn = (v[m] < 0.0f && k != 0u) ? 8u : 0u;
-      // element 4m + q: word m/2, byte q, high nibble for odd m
-      cw[m / 2] |= (k | sgn) << (8 * q + 4 * (m & 1));
       const float mag = D * (0.25f * (float)k);
-      v[m] = v[m] - (sgn ? -mag : mag);  // exact: within half a grid step
+      if (in) {
+        e3[m] = t3;
+        nib[m] = k | sgn;
+        v[m] = v[m] - (sgn ? -mag : mag);  // exact: within half a grid step
+      }
     }
-    // F over the span, right-looking; the later columns updated as it goes
+    // the set's columns, right-looking: every later column updated
 #pragma unroll
-    for (int i = t0; i < t0 + kSpan; ++i) {
-      const int mi = i >> 2, oi = i & 3;
-      float vi;
-      if (oi == 0) vi = quad_bcastf<0>(v[mi]);
-      else if (oi == 1) vi = quad_bcastf<1>(v[mi]);
-      else if (oi == 2) vi = quad_bcastf<2>(v[mi]);
-      else vi = quad_bcastf<3>(v[mi]);
-      const float fi = vi / us[64 * i + 16 * oi + mi];
-      if (q == oi) v[mi] = fi;
-      const float* ur = us + 64 * i + 16 * q;
-      // column 4 mi + q is after i only on lanes q > oi
-      if (q > oi) v[mi] = fmaf(-fi, ur[mi], v[mi]);
-#pragma unroll
-      for (int m = mi + 1; m < 16; ++m) v[m] = fmaf(-fi, ur[m], v[m]);
+    for (int i = sp * kSpan; i < sp * kSpan + kSpan; ++i) {
+      const float vi = row_bcastf(v[i >> 4], i & 15);
+      const float4 ur = *reinterpret_cast<const float4*>(us + 64 * i + 4 * p);
+      v[0] = fmaf(-vi, ur.x, v[0]);
+      v[1] = fmaf(-vi, ur.y, v[1]);
+      v[2] = fmaf(-vi, ur.z, v[2]);
+      v[3] = fmaf(-vi, ur.w, v[3]);
     }
   }
-  // code words: OR of the four lanes' bytes; lane q stores words 2q, 2q + 1
+  // code words: element j = p + 16 m sits in word j / 8 = 2 m + p / 8, byte
+  // p % 4, high nibble for p % 8 >= 4; OR over the half row gives word
+  // 2 m + p / 8 on all of its 8 lanes; lane 0 takes the odd words from lane 8
+  const int sh = 8 * (p & 3) + 4 * ((p >> 2) & 1);
+  uint32_t wd[4];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    cw[g] |= dpp<kDppQuadXor1>(cw[g]);
-    cw[g] |= dpp<kDppQuadXor2>(cw[g]);
+  for (int m = 0; m < 4; ++m) wd[m] = or8_u32(nib[m] << sh);
+  uint32_t wo[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) wo[m] = dpp<0x128>(wd[m]);  // row_ror:8: lane 0 <- lane 8
+  if (p == 0) {
+    uint4* dst = reinterpret_cast<uint4*>(codes32 + (r * units + unit) * 8);
+    dst[0] = make_uint4(wd[0], wo[0], wd[1], wo[1]);
+    dst[1] = make_uint4(wd[2], wo[2], wd[3], wo[3]);
   }
-  uint32_t w0 = cw[0], w1 = cw[1];
+  // meta: level-3 group 4 m + p / 4 (one bit per quad), level-2 group
+  // 2 m + p / 8 (one bit per half row)
+  uint32_t b3 = 0u, b2 = 0u;
 #pragma unroll
-  for (int g = 1; g < 4; ++g)
-    if (q == g) { w0 = cw[2 * g]; w1 = cw[2 * g + 1]; }
-  *reinterpret_cast<uint2*>(codes32 + (r * units + unit) * 8 + 2 * q) = make_uint2(w0, w1);
-  if (q == 0) meta[r * units + unit] = mw;
-  float* fo = f + r * 64 + q;
-#pragma unroll
-  for (int m = 0; m < 16; ++m) fo[4 * m] = v[m];
+  for (int m = 0; m < 4; ++m) {
+    b3 |= every4th(row_bits(__builtin_amdgcn_ballot_w64(e3[m] != 0u))) << (4 * m);
+    const uint32_t h2 = row_bits(__builtin_amdgcn_ballot_w64(e2[m] != 0u));
+    b2 |= ((h2 & 1u) | ((h2 >> 7) & 2u)) << (2 * m);
+  }
+  if (p == 0) meta[r * units + unit] = c | (b2 << 8) | (b3 << 16);
+  const float4 ri = *reinterpret_cast<const float4*>(rinv + 4 * p);
+  float* fr = f + r * ldf + p;
+  fr[0] = v[0] * ri.x;
+  fr[16] = v[1] * ri.y;
+  fr[32] = v[2] * ri.z;
+  fr[48] = v[3] * ri.w;
 }
 
 // HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
@@ -383,6 +447,109 @@ higptq_update_kernel(float* __restrict__ w, int64_t ldw, int64_t n, int64_t k,
     higptq_update_wave<false>(w, ldw, n, k, u, ldu, s0, cb0, f, r0, lds[wave]);
 }
 
+// HiGPTQ block update: W[:, c0..c1) -= F[:, 0..R) U[sk..sk+R, c0..c1) with
+// R = 64 units of F (the columns a block has quantized) on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32). At R = 256 an element of W takes 512 flops
+// per 8 bytes moved, so the matrix cores, not HBM, set the pace: the kernel
+// keeps W in the accumulators and streams only the operands, from L2.
+//
+// Product taken transposed, W^T -= U^T F^T: in the output layout (lane l,
+// register r: row 8(r/4) + 4(l/32) + r%4, column l%32) a lane holds one row of
+// W and, per register quad, four consecutive columns, so the W tile moves as
+// 16-byte loads and stores straight into and out of the accumulators. The
+// contraction order is permuted: step s of lane half h takes index
+// 8(s/4) + 4h + s%4, so that a lane's -F operands for four steps are four
+// consecutive values of its F row (one 16-byte load); its U operands are the
+// same four indices' rows of one column (lanes 0-31 and 32-63 each read 128
+// contiguous bytes of a U row).
+//
+// Workgroup (x, y): 4 waves, wave v on rows 256 y + 64 v .. + 63, all on the
+// columns c0 + 64 x .. + 63 (c1 - c0 is a multiple of 64). Each wave: four
+// 32x32 accumulator tiles (2 row blocks x 2 column blocks). Rows past n load
+// row n - 1 and are not stored. Operands go 16 contraction indices at a time,
+// two such chunks in flight.
+struct RankOps {
+  float4 fr[2][2];  // [row block][t % 2]: F[row][8t + 4h .. + 3]
+  float uc[2][8];   // [column block][4 (t % 2) + e]: U[8t + 4h + e][column]
+};
+
+__global__ __launch_bounds__(256, 2) void higptq_rank_update_kernel(
+    float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u, int64_t ldu,
+    int64_t sk, int64_t c0, const float* __restrict__ f, int64_t ldf, int R) {
+  const int lane = threadIdx.x & 63, li = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t r0 = (int64_t)blockIdx.y * 256 + (int64_t)wave * 64;
+  if (r0 >= n) return;  // the whole wave lies below W
+  const int64_t cb = c0 + (int64_t)blockIdx.x * 64;
+  const int64_t row[2] = {r0 + li, r0 + 32 + li};
+  const int64_t rl[2] = {row[0] < n ? row[0] : n - 1, row[1] < n ? row[1] : n - 1};
+  f32x16_t acc[2][2];  // [row block][column block]
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x =
+            *reinterpret_cast<const float4*>(w + rl[b] * ldw + cb + 32 * c + 8 * q + 4 * h);
+        acc[b][c][4 * q] = x.x;
+        acc[b][c][4 * q + 1] = x.y;
+        acc[b][c][4 * q + 2] = x.z;
+        acc[b][c][4 * q + 3] = x.w;
+      }
+  const float* fp[2] = {f + rl[0] * ldf + 4 * h, f + rl[1] * ldf + 4 * h};
+  const float* up = u + (sk + 4 * h) * ldu + cb + li;
+  RankOps A, B;
+  // chunk T: indices 16T .. 16T + 15 (t = 2T, 2T + 1)
+  auto load = [&](RankOps& X, int T) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        X.fr[b][tt] = *reinterpret_cast<const float4*>(fp[b] + 16 * T + 8 * tt);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          X.uc[c][4 * tt + e] = up[(int64_t)(16 * T + 8 * tt + e) * ldu + 32 * c];
+  };
+  auto run = [&](const RankOps& X) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float nf0 = -X.fr[0][tt][e], nf1 = -X.fr[1][tt][e];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float uv = X.uc[c][4 * tt + e];
+          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, nf0, acc[0][c], 0, 0, 0);
+          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, nf1, acc[1][c], 0, 0, 0);
+        }
+      }
+  };
+  const int chunks = R >> 4;  // even: R is a multiple of 64
+  load(A, 0);
+  for (int T = 0; T < chunks; T += 2) {
+    load(B, T + 1);
+    run(A);
+    if (T + 2 < chunks) load(A, T + 2);
+    run(B);
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (row[b] >= n) continue;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(w + row[b] * ldw + cb + 32 * c + 8 * q + 4 * h) =
+            make_float4(acc[b][c][4 * q], acc[b][c][4 * q + 1], acc[b][c][4 * q + 2],
+                        acc[b][c][4 * q + 3]);
+  }
+}
+
 }  // namespace hif4
 
 using namespace hif4;
@@ -398,23 +565,43 @@ hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int
   return hipGetLastError();
 }
 
+namespace {
+hipError_t launch_group(float* w, int64_t n, int64_t k, int64_t ldw, const float* u, int64_t ldu,
+                        int64_t unit, int scheme, uint8_t* codes, uint32_t* meta, float* f,
+                        int64_t ldf, hipStream_t stream) {
+  const int64_t s0 = unit * 64, units = k / 64;
+  const dim3 gg((unsigned)((16 * n + 255) / 256)), gb(256);  // 16 lanes per row
+  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
+  if (scheme == 1)
+    hipLaunchKernelGGL(higptq_group_kernel<1>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f, ldf);
+  else if (scheme == 2)
+    hipLaunchKernelGGL(higptq_group_kernel<2>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f, ldf);
+  else
+    hipLaunchKernelGGL(higptq_group_kernel<3>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
+                       unit, c32, meta, f, ldf);
+  return hipGetLastError();
+}
+
+// W[:, c0..c1) -= F[:, 0..R) U[sk.., c0..c1)
+hipError_t launch_rank_update(float* w, int64_t n, int64_t ldw, const float* u, int64_t ldu,
+                              int64_t sk, int64_t c0, int64_t c1, const float* f, int64_t ldf,
+                              int64_t R, hipStream_t stream) {
+  if (c1 <= c0) return hipSuccess;
+  const dim3 grid((unsigned)((c1 - c0) / 64), (unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(higptq_rank_update_kernel, grid, dim3(256), 0, stream, w, ldw, n, u, ldu,
+                     sk, c0, f, ldf, (int)R);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
                                    int64_t ldu, int64_t unit, int scheme, uint8_t* codes,
                                    uint32_t* meta, float* f, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t s0 = unit * 64, units = k / 64;
-  const dim3 gg((unsigned)((4 * n + 255) / 256)), gb(256);  // four lanes per row
-  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
-  if (scheme == 1)
-    hipLaunchKernelGGL(higptq_group_kernel<1>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f);
-  else if (scheme == 2)
-    hipLaunchKernelGGL(higptq_group_kernel<2>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f);
-  else
-    hipLaunchKernelGGL(higptq_group_kernel<3>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f);
-  hipError_t e = hipGetLastError();
+  const int64_t s0 = unit * 64;
+  hipError_t e = launch_group(w, n, k, ldw, u, ldu, unit, scheme, codes, meta, f, 64, stream);
   if (e != hipSuccess) return e;
   const int64_t c0 = s0 + 64;
   if (c0 >= k) return hipSuccess;
@@ -423,4 +610,25 @@ hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, 
   hipLaunchKernelGGL(higptq_update_kernel, grid, dim3(256), 0, stream, w, ldw, n, k, u, ldu, s0,
                      c0, (const float*)f);
   return hipGetLastError();
+}
+
+// One block of `units` groups from unit0: each group quantized, then the
+// block's later columns updated by that group's F; after the last group the
+// columns after the block take the whole block's F at once. F of group j sits
+// in columns 64 j .. of f (row stride 64 units).
+hipError_t hif4_launch_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
+                                    int64_t ldu, int64_t unit0, int64_t units, int scheme,
+                                    uint8_t* codes, uint32_t* meta, float* f,
+                                    hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t s = unit0 * 64, e = s + 64 * units, ldf = 64 * units;
+  for (int64_t j = 0; j < units; ++j) {
+    hipError_t st = launch_group(w, n, k, ldw, u, ldu, unit0 + j, scheme, codes, meta, f + 64 * j,
+                                 ldf, stream);
+    if (st != hipSuccess) return st;
+    st = launch_rank_update(w, n, ldw, u, ldu, s + 64 * j, s + 64 * (j + 1), e, f + 64 * j, ldf,
+                            64, stream);
+    if (st != hipSuccess) return st;
+  }
+  return launch_rank_update(w, n, ldw, u, ldu, s, e, k, f, ldf, 64 * units, stream);
 }

@@ -65,6 +65,11 @@ def lib():
         L.hif4_higptq_workspace_bytes.restype = sz
         L.hif4_higptq_unit.argtypes = [p, i64, i64, i64, p, i64, i64, ctypes.c_int, p, p, p, sz, p]
         L.hif4_higptq_unit.restype = ctypes.c_int
+        L.hif4_higptq_block_workspace_bytes.argtypes = [i64, i64]
+        L.hif4_higptq_block_workspace_bytes.restype = sz
+        L.hif4_higptq_block.argtypes = [p, i64, i64, i64, p, i64, i64, i64, ctypes.c_int, p, p, p,
+                                        sz, p]
+        L.hif4_higptq_block.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -296,13 +301,48 @@ def higptq_unit(w, u, unit, codes, meta, workspace=None, stream=None, scheme=1):
     _ok(st, "hif4_higptq_unit")
 
 
-def higptq(w, u, stream=None, scheme=1):
-    """HiGPTQ over all groups: returns (codes, meta); w is updated in place
-    (its final contents are the compensated working weights)."""
+HIGPTQ_MAX_BLOCK_UNITS = 16
+
+
+def higptq_block_workspace_bytes(n, units):
+    return int(lib().hif4_higptq_block_workspace_bytes(n, units))
+
+
+def higptq_block(w, u, unit0, units, codes, meta, workspace=None, stream=None, scheme=1):
+    """One HiGPTQ block step (blocksize 64 * units columns, groups unit0 ..
+    unit0 + units - 1, scheme 1, 2 or 3) in place on the fp32 working weights
+    w [n][k]: writes those units of codes/meta and updates the later columns
+    of w, the block's own later columns after each group and the columns after
+    the block once."""
+    _check_f32_rows(w, "w")
+    _check_f32_rows(u, "u")
     n, k = w.shape
+    if workspace is None:
+        nbytes = max(higptq_block_workspace_bytes(n, units), 1)
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=w.device)
+    st = lib().hif4_higptq_block(_ptr(w), n, k, w.stride(0), _ptr(u), u.stride(0), int(unit0),
+                                 int(units), int(scheme), _ptr(codes), _ptr(meta),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    _ok(st, "hif4_higptq_block")
+
+
+def higptq(w, u, stream=None, scheme=1, block_units=4):
+    """HiGPTQ over all groups in blocks of ``block_units`` groups (1 = one
+    group at a time through hif4_higptq_unit): returns (codes, meta); w is
+    updated in place (its final contents are the compensated working
+    weights)."""
+    n, k = w.shape
+    units = k // 64
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
-    meta = torch.empty((n, k // 64), dtype=torch.int32, device=w.device)
-    ws = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
-    for unit in range(k // 64):
-        higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream, scheme=scheme)
+    meta = torch.empty((n, units), dtype=torch.int32, device=w.device)
+    if block_units == 1:
+        ws = torch.empty((higptq_workspace_bytes(n),), dtype=torch.uint8, device=w.device)
+        for unit in range(units):
+            higptq_unit(w, u, unit, codes, meta, workspace=ws, stream=stream, scheme=scheme)
+        return codes, meta
+    ws = torch.empty((max(higptq_block_workspace_bytes(n, block_units), 1),), dtype=torch.uint8,
+                     device=w.device)
+    for unit0 in range(0, units, block_units):
+        higptq_block(w, u, unit0, min(block_units, units - unit0), codes, meta, workspace=ws,
+                     stream=stream, scheme=scheme)
     return codes, meta

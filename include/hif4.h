@@ -350,6 +350,50 @@ HIF4_EXPORT hif4_status hif4_higptq_unit(float *w, int64_t n, int64_t k, int64_t
                              uint32_t *meta, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Largest block of hif4_higptq_block, in units of 64 columns. */
+#define HIF4_HIGPTQ_MAX_BLOCK_UNITS 16
+
+/* hif4_higptq_block_workspace_bytes -- workspace of hif4_higptq_block for n
+ * rows and a block of `units` groups (0 for units outside 1..16). */
+HIF4_EXPORT size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units);
+
+/*
+ * hif4_higptq_block -- one block step of HiGPTQ with a blocksize of 64 units
+ * columns. GPTQ as the calibration article describes it (section 2.1 "GPTQ")
+ * splits the columns into blocks: inside a block the columns are quantized in
+ * order, each one's error compensated on the block's columns not yet
+ * quantized; once the block is done its whole error is carried to the
+ * columns after it in one update. Section 3.1 "HiGPTQ" requires the blocksize
+ * to be 64 or a multiple of 64, each group of 64 being one HiF4 unit. Here the
+ * groups unit0 .. unit0 + units - 1 are each taken as hif4_higptq_unit takes
+ * one group (same schemes), the block's later columns updated after each
+ * group, then W_after -= F_B U_B,after once for the block's compensation
+ * coefficients F_B.
+ * The result is that of hif4_higptq_unit called for unit0 .. unit0 + units - 1
+ * in order, up to the order of the fp32 roundings; a block carries the update
+ * of the later columns over 64 units columns at once, so a pass over W moves
+ * it 1/units as often. Call it for unit0 = 0, units, 2 units, ... (the last
+ * block may be shorter).
+ *
+ *  w, n, k, ldw, u, ldu, scheme, codes, meta: as for hif4_higptq_unit
+ *         (HIF4_ERR_SHAPE, HIF4_ERR_ARG, HIF4_ERR_ALIGN alike).
+ *  unit0, units  1 <= units <= HIF4_HIGPTQ_MAX_BLOCK_UNITS, 0 <= unit0 and
+ *         unit0 + units <= k/64 (HIF4_ERR_ARG otherwise): the block's
+ *         columns are 64 unit0 .. 64 (unit0 + units) - 1. The columns before
+ *         the block and those of its first group are not modified; each later
+ *         group's columns end holding the values that group was quantized
+ *         from (as after hif4_higptq_unit for the groups before it); the
+ *         columns after the block are updated in place.
+ *  codes, meta: units unit0 .. unit0 + units - 1 of every row written.
+ *  workspace >= hif4_higptq_block_workspace_bytes(n, units), 256-byte
+ *         aligned (HIF4_ERR_WORKSPACE / HIF4_ERR_ALIGN); on return it holds
+ *         F_B, fp32 [n][64 units] row-major (group j's F in columns 64 j ..).
+ */
+HIF4_EXPORT hif4_status hif4_higptq_block(float *w, int64_t n, int64_t k, int64_t ldw,
+                              const float *u, int64_t ldu, int64_t unit0, int64_t units,
+                              int scheme, uint8_t *codes, uint32_t *meta, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

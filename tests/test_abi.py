@@ -37,9 +37,9 @@ def test_header_declares_the_four_entry_points():
     names = declared()
     for fn in ("hif4_quantize", "hif4_dequantize", "hif4_linear_w4a4", "hif4_percentile_mask",
                "hif4_linear_xcodes_wbf16", "hif4_linear_xcodes_wbf16_noalloc",
-               "hif4_quantize_f32", "hif4_higptq_unit",
+               "hif4_quantize_f32", "hif4_higptq_unit", "hif4_higptq_block",
                "hif4_quantize_offsets",
-               "hif4_higptq_workspace_bytes",
+               "hif4_higptq_workspace_bytes", "hif4_higptq_block_workspace_bytes",
                "hif4_linear_workspace_bytes", "hif4_percentile_workspace_bytes",
                "hif4_status_string", "hif4_version"):
         assert fn in names
@@ -265,6 +265,37 @@ def test_higptq_argument_checks(L):
     assert call(ldw=130) == ALIGN
     assert call(wsp=None) == WORKSPACE
     assert call(wb=ws - 1) == WORKSPACE
+    assert call(wsp=A + 16) == ALIGN
+
+
+def test_higptq_block_argument_checks(L):
+    f = L.hif4_higptq_block
+    ws = L.hif4_higptq_block_workspace_bytes(10, 3)
+    assert ws == 7680  # 10 rows x 3 groups x 64 fp32 (a multiple of 256 bytes)
+    assert L.hif4_higptq_block_workspace_bytes(10, 0) == 0
+    assert L.hif4_higptq_block_workspace_bytes(10, 17) == 0
+    assert L.hif4_higptq_block_workspace_bytes(-1, 2) == 0
+
+    def call(w=A, n=10, k=256, ldw=256, u=A, ldu=256, unit0=1, units=3, scheme=1, c=A, m=A,
+             wsp=A, wb=None):
+        return f(w, n, k, ldw, u, ldu, unit0, units, scheme, c, m, wsp, ws if wb is None else wb,
+                 None)
+
+    assert call(k=96) == SHAPE
+    assert call(ldw=128) == SHAPE
+    assert call(ldu=1 << 22) == SHAPE
+    assert call(n=1 << 24) == SHAPE
+    assert call(units=0) == ARG
+    assert call(units=17) == ARG
+    assert call(unit0=2) == ARG  # 2 + 3 > 256 / 64
+    assert call(unit0=-1) == ARG
+    assert call(scheme=4) == ARG
+    assert call(n=0, w=None) == OK
+    assert call(u=None) == NULL
+    assert call(w=A + 4) == ALIGN
+    assert call(wsp=None) == WORKSPACE
+    assert call(wb=ws - 1) == WORKSPACE
+    assert call(units=2, wb=ws) != WORKSPACE  # a smaller block needs less
     assert call(wsp=A + 16) == ALIGN
 
 

@@ -14,6 +14,10 @@ identical codes and meta on every row whose decisions all lie farther than
 1e-5 (relative) from their boundaries in the oracle's own values, F and the
 later columns within tolerance; the rows inside that band are checked on the
 GPU's own trajectory instead (see above those tests), and counted.
+Whole passes in blocks of several groups (GPTQ's blocks, the same article,
+sections 2.1 and 3.1) are checked against the oracle's run over all groups
+on the rows whose decisions all lie outside that band, and every row on its
+own trajectory (see above those tests).
 """
 import numpy as np
 import pytest
@@ -244,11 +248,32 @@ def _check_scheme_step_oracle(before, after, codes_u, meta_u, F, U64, unit, sche
     return int(fb.size)
 
 def _check_scheme_step(before, after, codes_u, meta_u, F, U64, unit, scheme):
+    s0, r0 = 64 * unit, 64 * unit + 64
+    _scheme_group_f(before[:, s0:r0], codes_u, meta_u, U64, unit, scheme, F)
+    assert np.array_equal(after[:, :r0], before[:, :r0])
+    if r0 < before.shape[1]:
+        Us = U64[s0:r0, r0:]
+        ref = before[:, r0:].astype(np.float64) - F @ Us
+        scale = np.abs(F) @ np.abs(Us) + np.abs(before[:, r0:])
+        assert np.all(np.abs(after[:, r0:] - ref) <= 1e-5 * scale)
+
+
+def _scheme_group_f(start, codes_u, meta_u, U64, unit, scheme, F=None):
+    """Scheme 2/3 group rebuilt in fp64 from the values it started from
+    (start [n][64]) and its codes and meta: the level-1 code exactly; every
+    exponent bit and element code against the rule applied to the rebuilt
+    values, except within 1e-5 of the value's error scale from a boundary; F
+    span by span against the forward substitution of the rebuilt errors
+    (when F, the GPU's, is given: the rebuild then follows it). Returns the
+    F the rebuild followed."""
     from fractions import Fraction
 
-    n = before.shape[0]
+    n = start.shape[0]
     s0, r0 = 64 * unit, 64 * unit + 64
     span = 8 if scheme == 2 else 4
+    follow = np.zeros((n, 64)) if F is None else F
+    before = np.zeros((n, r0))
+    before[:, s0:r0] = start
     v = before[:, s0:r0].astype(np.float64).copy()
     sc = np.abs(v).copy()  # error scale of each rebuilt value
     deq = oracle.dequantize(codes_u, meta_u[:, None])
@@ -290,17 +315,15 @@ def _check_scheme_step(before, after, codes_u, meta_u, F, U64, unit, scheme):
         # scale): E = v - deq cancels, so the values' own error carries into F
         inv_norm = np.abs(np.linalg.inv(Uab)).sum(axis=0).max()
         bound = 1e-4 * np.abs(F_ref).max(axis=1) + inv_norm * tol * sc[:, t0:t0 + span].max(axis=1)
-        assert np.all(np.abs(F[:, t0:t0 + span] - F_ref).max(axis=1) <= bound)
-        # follow the GPU: update the group's later columns with its F
+        if F is None:
+            follow[:, t0:t0 + span] = F_ref
+        else:
+            assert np.all(np.abs(F[:, t0:t0 + span] - F_ref).max(axis=1) <= bound)
+        # follow the GPU's F (or the rebuilt one): update the group's later columns
         Ul = U64[s0 + t0:s0 + t0 + span, s0 + t0 + span:r0]
-        v[:, t0 + span:] -= F[:, t0:t0 + span] @ Ul
-        sc[:, t0 + span:] += np.abs(F[:, t0:t0 + span]) @ np.abs(Ul)
-    assert np.array_equal(after[:, :r0], before[:, :r0])
-    if r0 < before.shape[1]:
-        Us = U64[s0:r0, r0:]
-        ref = before[:, r0:].astype(np.float64) - F @ Us
-        scale = np.abs(F) @ np.abs(Us) + np.abs(before[:, r0:])
-        assert np.all(np.abs(after[:, r0:] - ref) <= 1e-5 * scale)
+        v[:, t0 + span:] -= follow[:, t0:t0 + span] @ Ul
+        sc[:, t0 + span:] += np.abs(follow[:, t0:t0 + span]) @ np.abs(Ul)
+    return follow
 
 
 @pytest.mark.parametrize("scheme", [2, 3])
@@ -341,3 +364,147 @@ def test_higptq_schemes_2_and_3_identity_and_layer_error(hip, scheme):
     E = W - oracle.dequantize(codes.cpu().numpy(), host_u32(meta))
     E0 = W - oracle.dequantize(c0, m0)
     assert np.trace(E @ H @ E.T) < 0.8 * np.trace(E0 @ H @ E0.T)
+
+
+# ------------------------------------------------------------ HiGPTQ in blocks
+# A block (hif4_higptq_block) runs its groups one after the other with the
+# block's later columns updated after each, and the columns after the block
+# once for the whole block: the weights a group starts from are not
+# observable between its groups. Whole passes are therefore checked against
+# the oracle's run over all groups (oracle.higptq_run, the group steps in
+# order) from the same weights: codes and meta exactly on every row whose
+# decisions on moved values -- moved inside a group or by any earlier group --
+# all lie farther than 1e-5 from their boundaries, relative to the size of
+# the sums behind them (|value| + the accumulated sum |F||U|); the final
+# working weights on those rows within 1e-5 of that size per entry. Rows
+# inside the band are counted (a decision there may go either way in fp32,
+# and the rest of the row follows it).
+
+
+def _block_pass(hip, W, U, scheme, units, pad_w=0, pad_u=0):
+    n, k = W.shape
+    w = _padded(W, pad_w) if pad_w else dev(W.astype(np.float32))
+    u = _padded(U, pad_u) if pad_u else dev(U.astype(np.float32))
+    codes = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros((n, k // 64), dtype=torch.int32, device="cuda")
+    ws = torch.empty((hip.higptq_block_workspace_bytes(n, units),), dtype=torch.uint8,
+                     device="cuda")
+    for unit0 in range(0, k // 64, units):
+        hip.higptq_block(w, u, unit0, min(units, k // 64 - unit0), codes, meta, workspace=ws,
+                         scheme=scheme)
+    torch.cuda.synchronize()
+    return w.cpu().numpy(), codes.cpu().numpy(), host_u32(meta)
+
+
+def _check_block_pass(hip, W, U, scheme, units, **pads):
+    """Returns the number of rows inside the margin band."""
+    n, k = W.shape
+    wg, cg, mg = _block_pass(hip, W, U, scheme, units, **pads)
+    U64 = U.astype(np.float32).astype(np.float64)  # the values the GPU works with
+    wo = np.array(W, dtype=np.float64, order="C")
+    co, mo = np.zeros((n, k // 2), np.uint8), np.zeros((n, k // 64), np.uint32)
+    margin, accmag = np.full(n, np.inf), np.zeros((n, k))
+    # a group's columns on the GPU end holding the values the group started
+    # from (the oracle's end holding those its sets were quantized from under
+    # schemes 2 and 3): record the oracle's at each group's start
+    start = np.empty_like(wo)
+    for unit in range(k // 64):
+        start[:, 64 * unit:64 * unit + 64] = wo[:, 64 * unit:64 * unit + 64]
+        oracle.higptq_run(wo, U64, unit, 1, co, mo, scheme, margin, accmag)
+    wo = start
+    exact = margin > MARGIN
+    assert np.array_equal(cg[exact], co[exact]), f"scheme {scheme} blocks of {units}: codes"
+    assert np.array_equal(mg[exact], mo[exact]), f"scheme {scheme} blocks of {units}: meta"
+    scale = np.abs(W.astype(np.float64)) + accmag
+    err = np.abs(wg.astype(np.float64) - wo)
+    bad = (err > 1e-5 * scale) & exact[:, None]
+    assert not bad.any(), (f"scheme {scheme} blocks of {units}: weights, worst "
+                           f"{np.max((err / np.maximum(scale, 1e-300))[exact]):.3g}")
+    return int(np.count_nonzero(~exact))
+
+
+@pytest.mark.parametrize("scheme", [1, 2, 3])
+def test_higptq_blocks_follow_the_oracle(hip, scheme, capsys):
+    """200 rows (ragged against the 16-row workgroups of the group step and
+    the 256-row workgroups of the updates), 640 columns (10 groups) in blocks
+    of 4, 4 and 2. Over a whole pass every decision after the first group
+    reads moved values (640 a row), so more rows fall inside the band than in
+    a single step; every row, those included, is checked on its own
+    trajectory below."""
+    W, _, U = _gptq_problem(200, 640, 110 + scheme)
+    inside = _check_block_pass(hip, W, U, scheme, 4)
+    with capsys.disabled():
+        print(f"\n[higptq blocks, scheme {scheme}] rows inside the margin band: {inside} of 200",
+              flush=True)
+    assert inside <= 200 // 4
+
+
+@pytest.mark.parametrize("n,k,units,scheme,pad_w,pad_u", [
+    (1, 128, 2, 1, 0, 0),      # one row, one block
+    (17, 448, 4, 3, 12, 4),    # blocks of 4 and 3, strided W and U
+    (65, 256, 3, 2, 4, 0),     # blocks of 3 and 1
+    (257, 384, 16, 1, 0, 36),  # one block of 6 (units capped by the columns left)
+    (300, 320, 1, 1, 0, 0),    # blocks of one group
+])
+def test_higptq_block_shapes(hip, n, k, units, scheme, pad_w, pad_u):
+    W, _, U = _gptq_problem(n, k, 120 + n)
+    inside = _check_block_pass(hip, W, U, scheme, units, pad_w=pad_w, pad_u=pad_u)
+    assert inside <= max(1, n // 4)
+
+
+def test_higptq_block_leaves_the_earlier_columns(hip):
+    """One block of 3 groups in the middle of W: the columns before the block
+    and those of its first group keep their values, the rest change; codes
+    and meta are written for the block's groups only, the first from the
+    weights as given."""
+    W, _, U = _gptq_problem(70, 512, 130)
+    w, u = dev(W), dev(U.astype(np.float32))
+    codes = torch.zeros((70, 256), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros((70, 8), dtype=torch.int32, device="cuda")
+    hip.higptq_block(w, u, 2, 3, codes, meta, scheme=1)
+    torch.cuda.synchronize()
+    after = w.cpu().numpy()
+    assert np.array_equal(after[:, :192], W[:, :192])
+    assert np.all(np.any(after[:, 192:256] != W[:, 192:256], axis=1))
+    assert np.all(np.any(after[:, 320:] != W[:, 320:], axis=1))
+    c, m = codes.cpu().numpy(), host_u32(meta)
+    assert not c[:, :64].any() and not c[:, 160:].any()  # units 2..4 only
+    assert not m[:, :2].any() and not m[:, 5:].any()
+    c_o, m_o = oracle.quantize_f32(W[:, 128:192])
+    assert np.array_equal(c[:, 64:96], c_o) and np.array_equal(m[:, 2], m_o[:, 0])
+
+
+@pytest.mark.parametrize("scheme,units", [(1, 2), (1, 4), (1, 16), (2, 4), (3, 4), (3, 3)])
+def test_higptq_blocks_on_their_own_trajectory(hip, scheme, units):
+    """Every row of a pass in blocks, on its own trajectory. A group's columns
+    end holding the values the group started from (the group step reads W
+    and writes only later columns), so each group can be rebuilt in fp64 from
+    the final weights: under scheme 1 its codes and meta must be exactly the
+    quantization of those values; under schemes 2 and 3 the rebuild of
+    _scheme_group_f (decisions against the rule outside the 1e-5 band, F span
+    by span). Each group's starting values must be the initial weights minus
+    the compensation of every earlier group, sum over u < v of F_u U_uv with
+    the rebuilt F_u, within 1e-5 of the size of that sum per entry."""
+    n, k = 160, 768
+    W, _, U = _gptq_problem(n, k, 131 + scheme)
+    wg, cg, mg = _block_pass(hip, W, U, scheme, units)
+    U64 = U.astype(np.float32).astype(np.float64)
+    if scheme == 1:
+        c_o, m_o = oracle.quantize_f32(wg)
+        assert np.array_equal(cg, c_o) and np.array_equal(mg, m_o)
+    W64, G = W.astype(np.float64), wg.astype(np.float64)
+    comp, size = np.zeros((n, k)), np.abs(W64).copy()
+    for unit in range(k // 64):
+        s0, r0 = 64 * unit, 64 * unit + 64
+        want = W64[:, s0:r0] - comp[:, s0:r0]
+        err = np.abs(G[:, s0:r0] - want)
+        assert np.all(err <= 1e-5 * size[:, s0:r0]), \
+            f"group {unit}: worst {np.max(err / size[:, s0:r0]):.3g}"
+        cu, mu = cg[:, 32 * unit:32 * unit + 32], mg[:, unit]
+        if scheme == 1:
+            E = G[:, s0:r0] - oracle.dequantize(cu, mu[:, None])
+            F = np.linalg.solve(U64[s0:r0, s0:r0].T, E.T).T
+        else:
+            F = _scheme_group_f(G[:, s0:r0], cu, mu, U64, unit, scheme)
+        comp[:, r0:] += F @ U64[s0:r0, r0:]
+        size[:, r0:] += np.abs(F) @ np.abs(U64[s0:r0, r0:])
