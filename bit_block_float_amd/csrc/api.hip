@@ -368,7 +368,7 @@ hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const 
 
 size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units) {
   if (n < 0 || units < 1 || units > HIF4_HIGPTQ_MAX_BLOCK_UNITS) return 0;
-  return align256((size_t)n * 64 * (size_t)units * sizeof(float));
+  return align256((size_t)((n + 63) / 64 * 64) * 64 * (size_t)units * sizeof(float));
 }
 
 hif4_status hif4_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,

@@ -117,11 +117,11 @@ __global__ __launch_bounds__(256) void quantize_f32_kernel(const float* __restri
 // F is formed right-looking, column i = 0, 1, ... in the order of the forward
 // substitution: once column i holds its final value v_i, every later column
 // takes v_j -= v_i (U_ij / U_ii), and f_i = v_i / U_ii. The workgroup stages
-// U_SS in LDS with each row scaled by its diagonal's reciprocal and zeros on
-// and below the diagonal, so the step of column i is the same four FMAs on
-// every lane (v_i broadcast over the row from its owner lane): the columns up
-// to i take -v_i * 0 and keep their values, and F is v times the reciprocals
-// once all steps are done. LDS holds row i of that matrix as lane p's four
+// -U_SS in LDS with each row scaled by its diagonal's reciprocal and zeros on
+// and below the diagonal, so the step of column i is the same FMAs on every
+// lane (v_i broadcast over the row from its owner lane, folded into the FMA):
+// the columns up to i take v_i * 0 and keep their values, and F is v times
+// the reciprocals once all steps are done. LDS holds row i of that matrix as lane p's four
 // values (columns p + 16 m) side by side.
 constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <-> 15-i in 16
 __device__ __forceinline__ float quad_maxf(float x) {
@@ -175,8 +175,8 @@ template <int kScheme>
 __global__ __launch_bounds__(256) void higptq_group_kernel(
     const float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u,
     int64_t ldu, int64_t s0, int64_t units, int64_t unit, uint32_t* __restrict__ codes32,
-    uint32_t* __restrict__ meta, float* __restrict__ f, int64_t ldf) {
-  __shared__ __align__(16) float us[64 * 64];  // row i: U_ij / U_ii for j > i, else 0
+    uint32_t* __restrict__ meta, float* __restrict__ f, int64_t fsr, int64_t fsc) {
+  __shared__ __align__(16) float us[64 * 64];  // row i: -U_ij / U_ii for j > i, else 0
   __shared__ __align__(16) float rinv[64];     // 1 / U_jj at 4 (j % 16) + j / 16
   const int p = threadIdx.x & 15;
   const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
@@ -187,19 +187,28 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) v[m] = wr[16 * m];
   }
+  // U_SS: thread t stages rows i = t / 16 + 16 it (it = 0..3), columns
+  // 4 (t % 16) .. + 3; all loads first, so that their latencies overlap
+  float4 ux[4];
+  float ud[4];
 #pragma unroll
-  for (int t = threadIdx.x; t < 64 * 16; t += 256) {
-    const int i = t >> 4, j = 4 * (t & 15);
+  for (int it = 0; it < 4; ++it) {
+    const int i = (threadIdx.x >> 4) + 16 * it, j = 4 * (threadIdx.x & 15);
     const float* ui = u + (s0 + i) * ldu + s0;
-    const float4 x = *reinterpret_cast<const float4*>(ui + j);
-    const float ri = 1.0f / ui[i];
-    const float xs[4] = {x.x, x.y, x.z, x.w};
+    ux[it] = *reinterpret_cast<const float4*>(ui + j);
+    ud[it] = ui[i];
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = (threadIdx.x >> 4) + 16 * it, j = 4 * (threadIdx.x & 15);
+    const float ri = 1.0f / ud[it];
+    const float xs[4] = {ux[it].x, ux[it].y, ux[it].z, ux[it].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jj = j + e;  // lane jj % 16, register jj / 16
-      us[64 * i + 4 * (jj & 15) + (jj >> 4)] = jj > i ? xs[e] * ri : 0.0f;
+      us[64 * i + 4 * (jj & 15) + (jj >> 4)] = jj > i ? -(xs[e] * ri) : 0.0f;
     }
-    if ((i >> 2) == (t & 15)) rinv[4 * (i & 15) + (i >> 4)] = ri;
+    if ((i >> 2) == (threadIdx.x & 15)) rinv[4 * (i & 15) + (i >> 4)] = ri;
   }
   __syncthreads();
   if (r >= n) return;  // the whole row of 16 lanes
@@ -248,15 +257,16 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
         v[m] = v[m] - (sgn ? -mag : mag);  // exact: within half a grid step
       }
     }
-    // the set's columns, right-looking: every later column updated
+    // the set's columns, right-looking: every later column updated (the
+    // registers m < i / 16 hold only columns before i and keep their values)
 #pragma unroll
     for (int i = sp * kSpan; i < sp * kSpan + kSpan; ++i) {
       const float vi = row_bcastf(v[i >> 4], i & 15);
       const float4 ur = *reinterpret_cast<const float4*>(us + 64 * i + 4 * p);
-      v[0] = fmaf(-vi, ur.x, v[0]);
-      v[1] = fmaf(-vi, ur.y, v[1]);
-      v[2] = fmaf(-vi, ur.z, v[2]);
-      v[3] = fmaf(-vi, ur.w, v[3]);
+      if (i < 16) v[0] = fmaf(vi, ur.x, v[0]);
+      if (i < 32) v[1] = fmaf(vi, ur.y, v[1]);
+      if (i < 48) v[2] = fmaf(vi, ur.z, v[2]);
+      v[3] = fmaf(vi, ur.w, v[3]);
     }
   }
   // code words: element j = p + 16 m sits in word j / 8 = 2 m + p / 8, byte
@@ -285,11 +295,11 @@ __global__ __launch_bounds__(256) void higptq_group_kernel(
   }
   if (p == 0) meta[r * units + unit] = c | (b2 << 8) | (b3 << 16);
   const float4 ri = *reinterpret_cast<const float4*>(rinv + 4 * p);
-  float* fr = f + r * ldf + p;
+  float* fr = f + r * fsr + p * fsc;
   fr[0] = v[0] * ri.x;
-  fr[16] = v[1] * ri.y;
-  fr[32] = v[2] * ri.z;
-  fr[48] = v[3] * ri.w;
+  fr[16 * fsc] = v[1] * ri.y;
+  fr[32 * fsc] = v[2] * ri.z;
+  fr[48 * fsc] = v[3] * ri.w;
 }
 
 // HiGPTQ group step, part 2: W[:, c0..k) -= F U[s0.., c0..k), a rank-64
@@ -448,105 +458,128 @@ higptq_update_kernel(float* __restrict__ w, int64_t ldw, int64_t n, int64_t k,
 }
 
 // HiGPTQ block update: W[:, c0..c1) -= F[:, 0..R) U[sk..sk+R, c0..c1) with
-// R = 64 units of F (the columns a block has quantized) on the fp32 matrix
-// cores (v_mfma_f32_32x32x2_f32). At R = 256 an element of W takes 512 flops
-// per 8 bytes moved, so the matrix cores, not HBM, set the pace: the kernel
-// keeps W in the accumulators and streams only the operands, from L2.
+// R = 64 units (the columns a block has quantized), F given transposed (F^T,
+// row i at ft + i ldt), on the fp32 matrix cores (v_mfma_f32_32x32x2_f32). At
+// R = 256 an element of W takes 512 flops per 8 bytes moved, so the matrix
+// cores, not HBM, set the pace: the kernel keeps W in the accumulators and
+// streams only the operands, from L2.
 //
 // Product taken transposed, W^T -= U^T F^T: in the output layout (lane l,
 // register r: row 8(r/4) + 4(l/32) + r%4, column l%32) a lane holds one row of
 // W and, per register quad, four consecutive columns, so the W tile moves as
-// 16-byte loads and stores straight into and out of the accumulators. The
-// contraction order is permuted: step s of lane half h takes index
-// 8(s/4) + 4h + s%4, so that a lane's -F operands for four steps are four
-// consecutive values of its F row (one 16-byte load); its U operands are the
-// same four indices' rows of one column (lanes 0-31 and 32-63 each read 128
-// contiguous bytes of a U row).
+// 16-byte loads and stores straight into and out of the accumulators. Step s
+// contracts indices 2s (lanes 0-31) and 2s + 1 (lanes 32-63): a lane's U
+// operand is U[sk + 2s + h][its column] and its -F operand F^T[2s + h][its
+// row], so each operand load of a wave reads two rows of 32 consecutive
+// floats (F transposed for this: row-major F would give a lane per row).
 //
 // Workgroup (x, y): 4 waves, wave v on rows 256 y + 64 v .. + 63, all on the
 // columns c0 + 64 x .. + 63 (c1 - c0 is a multiple of 64). Each wave: four
-// 32x32 accumulator tiles (2 row blocks x 2 column blocks). Rows past n load
-// row n - 1 and are not stored. Operands go 16 contraction indices at a time,
-// two such chunks in flight.
+// 32x32 accumulator tiles (2 row blocks x 2 column blocks). Rows of W past n
+// load row n - 1 and are not stored; F^T's rows are padded to a multiple of
+// 64, so its loads stay inside them. Operands go 16 contraction indices (8
+// steps) at a time, two such chunks in flight; addresses are a wave-uniform
+// base per chunk plus 32-bit lane offsets.
+template <int kRB>
 struct RankOps {
-  float4 fr[2][2];  // [row block][t % 2]: F[row][8t + 4h .. + 3]
-  float uc[2][8];   // [column block][4 (t % 2) + e]: U[8t + 4h + e][column]
+  float f[kRB][8];  // [row block][step]
+  float u[2][8];    // [column block][step]
 };
 
+__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+template <int kRB>  // row blocks of 32 per wave
 __global__ __launch_bounds__(256, 2) void higptq_rank_update_kernel(
     float* __restrict__ w, int64_t ldw, int64_t n, const float* __restrict__ u, int64_t ldu,
-    int64_t sk, int64_t c0, const float* __restrict__ f, int64_t ldf, int R) {
+    int64_t sk, int64_t c0, const float* __restrict__ ft, int64_t ldt, int R) {
+  constexpr int kRows = 32 * kRB;
   const int lane = threadIdx.x & 63, li = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t r0 = (int64_t)blockIdx.y * 256 + (int64_t)wave * 64;
+  const int64_t r0 = (int64_t)blockIdx.y * 4 * kRows + (int64_t)wave * kRows;
   if (r0 >= n) return;  // the whole wave lies below W
   const int64_t cb = c0 + (int64_t)blockIdx.x * 64;
-  const int64_t row[2] = {r0 + li, r0 + 32 + li};
-  const int64_t rl[2] = {row[0] < n ? row[0] : n - 1, row[1] < n ? row[1] : n - 1};
-  f32x16_t acc[2][2];  // [row block][column block]
+  // the wave's W tile: rows r0 .. r0 + kRows - 1 (past n: row n - 1), columns cb ..
+  const int last = n - r0 < kRows ? (int)(n - r0) - 1 : kRows - 1;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w + r0 * ldw + cb), (short)0, (int)((last * ldw + 64) * 4), kRsrcWord3Upd);
+  int rl[kRB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < kRB; ++b) rl[b] = 32 * b + li < last ? 32 * b + li : last;
+  f32x16_t acc[kRB][2];  // [row block][column block]
+#pragma unroll
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 x =
-            *reinterpret_cast<const float4*>(w + rl[b] * ldw + cb + 32 * c + 8 * q + 4 * h);
-        acc[b][c][4 * q] = x.x;
-        acc[b][c][4 * q + 1] = x.y;
-        acc[b][c][4 * q + 2] = x.z;
-        acc[b][c][4 * q + 3] = x.w;
+        const f32x4u_t x = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, (int)((rl[b] * ldw + 4 * h) * 4), (32 * c + 8 * q) * 4, 0);
+        acc[b][c][4 * q] = x[0];
+        acc[b][c][4 * q + 1] = x[1];
+        acc[b][c][4 * q + 2] = x[2];
+        acc[b][c][4 * q + 3] = x[3];
       }
-  const float* fp[2] = {f + rl[0] * ldf + 4 * h, f + rl[1] * ldf + 4 * h};
-  const float* up = u + (sk + 4 * h) * ldu + cb + li;
-  RankOps A, B;
-  // chunk T: indices 16T .. 16T + 15 (t = 2T, 2T + 1)
-  auto load = [&](RankOps& X, int T) {
+  // operand lane offsets (bytes): F^T[2s + h][r0 + 32b + li], U[sk + 2s + h][cb + 32c + li]
+  const int fo = (int)((h * ldt + r0 + li) * 4), fs = (int)(2 * ldt * 4);
+  const int uo = (int)((h * ldu + li) * 4), us2 = (int)(2 * ldu * 4);
+  RankOps<kRB> A, B;
+  // chunk T: steps 8T .. 8T + 7, contraction indices 16T .. 16T + 15
+  auto load = [&](RankOps<kRB>& X, int T) {
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ft + (int64_t)(16 * T) * ldt), (short)0, (int)(16 * ldt * 4), kRsrcWord3Upd);
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(u + (sk + 16 * T) * ldu + cb), (short)0, (int)(16 * ldu * 4), kRsrcWord3Upd);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        X.fr[b][tt] = *reinterpret_cast<const float4*>(fp[b] + 16 * T + 8 * tt);
+      for (int b = 0; b < kRB; ++b) X.f[b][st] = buf_ld(rf, fo + 128 * b, st * fs);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          X.uc[c][4 * tt + e] = up[(int64_t)(16 * T + 8 * tt + e) * ldu + 32 * c];
+      for (int c = 0; c < 2; ++c) X.u[c][st] = buf_ld(ru, uo + 128 * c, st * us2);
   };
-  auto run = [&](const RankOps& X) {
+  auto run = [&](const RankOps<kRB>& X) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int st = 0; st < 8; ++st) {
+      float nf[kRB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float nf0 = -X.fr[0][tt][e], nf1 = -X.fr[1][tt][e];
+      for (int b = 0; b < kRB; ++b) nf[b] = -X.f[b][st];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float uv = X.uc[c][4 * tt + e];
-          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, nf0, acc[0][c], 0, 0, 0);
-          acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(uv, nf1, acc[1][c], 0, 0, 0);
-        }
-      }
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int b = 0; b < kRB; ++b)
+          acc[b][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(X.u[c][st], nf[b], acc[b][c], 0, 0, 0);
+    }
   };
+  // the loads are unconditional so that every wait counts exactly the loads
+  // it needs across the loop (the last prefetch re-reads the last chunk); the
+  // scheduling barriers keep each chunk's loads a whole chunk of work ahead
   const int chunks = R >> 4;  // even: R is a multiple of 64
   load(A, 0);
   for (int T = 0; T < chunks; T += 2) {
     load(B, T + 1);
+    __builtin_amdgcn_sched_barrier(0);
     run(A);
-    if (T + 2 < chunks) load(A, T + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load(A, T + 2 < chunks ? T + 2 : chunks - 1);
+    __builtin_amdgcn_sched_barrier(0);
     run(B);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (row[b] >= n) continue;
+  for (int b = 0; b < kRB; ++b) {
+    if (32 * b + li > last) continue;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(w + row[b] * ldw + cb + 32 * c + 8 * q + 4 * h) =
-            make_float4(acc[b][c][4 * q], acc[b][c][4 * q + 1], acc[b][c][4 * q + 2],
-                        acc[b][c][4 * q + 3]);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4u_t x = {acc[b][c][4 * q], acc[b][c][4 * q + 1], acc[b][c][4 * q + 2],
+                            acc[b][c][4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(x, rw, (int)(((32 * b + li) * ldw + 4 * h) * 4),
+                                               (32 * c + 8 * q) * 4, 0);
+      }
   }
 }
 
@@ -568,30 +601,34 @@ hipError_t hif4_launch_quantize_f32(const float* x, int64_t rows, int64_t k, int
 namespace {
 hipError_t launch_group(float* w, int64_t n, int64_t k, int64_t ldw, const float* u, int64_t ldu,
                         int64_t unit, int scheme, uint8_t* codes, uint32_t* meta, float* f,
-                        int64_t ldf, hipStream_t stream) {
+                        int64_t fsr, int64_t fsc, hipStream_t stream) {
   const int64_t s0 = unit * 64, units = k / 64;
   const dim3 gg((unsigned)((16 * n + 255) / 256)), gb(256);  // 16 lanes per row
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
   if (scheme == 1)
     hipLaunchKernelGGL(higptq_group_kernel<1>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f, ldf);
+                       unit, c32, meta, f, fsr, fsc);
   else if (scheme == 2)
     hipLaunchKernelGGL(higptq_group_kernel<2>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f, ldf);
+                       unit, c32, meta, f, fsr, fsc);
   else
     hipLaunchKernelGGL(higptq_group_kernel<3>, gg, gb, 0, stream, w, ldw, n, u, ldu, s0, units,
-                       unit, c32, meta, f, ldf);
+                       unit, c32, meta, f, fsr, fsc);
   return hipGetLastError();
 }
 
-// W[:, c0..c1) -= F[:, 0..R) U[sk.., c0..c1)
+// W[:, c0..c1) -= F[:, 0..R) U[sk.., c0..c1), F given transposed (row stride ldt)
 hipError_t launch_rank_update(float* w, int64_t n, int64_t ldw, const float* u, int64_t ldu,
-                              int64_t sk, int64_t c0, int64_t c1, const float* f, int64_t ldf,
+                              int64_t sk, int64_t c0, int64_t c1, const float* ft, int64_t ldt,
                               int64_t R, hipStream_t stream) {
   if (c1 <= c0) return hipSuccess;
-  const dim3 grid((unsigned)((c1 - c0) / 64), (unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(higptq_rank_update_kernel, grid, dim3(256), 0, stream, w, ldw, n, u, ldu,
-                     sk, c0, f, ldf, (int)R);
+  const unsigned cols = (unsigned)((c1 - c0) / 64);
+  if (R == 64)  // the in-block updates: short, so more and shorter waves
+    hipLaunchKernelGGL(higptq_rank_update_kernel<1>, dim3(cols, (unsigned)((n + 127) / 128)),
+                       dim3(256), 0, stream, w, ldw, n, u, ldu, sk, c0, ft, ldt, (int)R);
+  else
+    hipLaunchKernelGGL(higptq_rank_update_kernel<2>, dim3(cols, (unsigned)((n + 255) / 256)),
+                       dim3(256), 0, stream, w, ldw, n, u, ldu, sk, c0, ft, ldt, (int)R);
   return hipGetLastError();
 }
 }  // namespace
@@ -601,7 +638,7 @@ hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, 
                                    uint32_t* meta, float* f, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t s0 = unit * 64;
-  hipError_t e = launch_group(w, n, k, ldw, u, ldu, unit, scheme, codes, meta, f, 64, stream);
+  hipError_t e = launch_group(w, n, k, ldw, u, ldu, unit, scheme, codes, meta, f, 64, 1, stream);
   if (e != hipSuccess) return e;
   const int64_t c0 = s0 + 64;
   if (c0 >= k) return hipSuccess;
@@ -614,21 +651,23 @@ hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, 
 
 // One block of `units` groups from unit0: each group quantized, then the
 // block's later columns updated by that group's F; after the last group the
-// columns after the block take the whole block's F at once. F of group j sits
-// in columns 64 j .. of f (row stride 64 units).
+// columns after the block take the whole block's F at once. F is kept
+// transposed: F^T [64 units][ldt], ldt = n rounded up to a multiple of 64, the
+// group j's rows at 64 j.
 hipError_t hif4_launch_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
                                     int64_t ldu, int64_t unit0, int64_t units, int scheme,
-                                    uint8_t* codes, uint32_t* meta, float* f,
+                                    uint8_t* codes, uint32_t* meta, float* ft,
                                     hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t s = unit0 * 64, e = s + 64 * units, ldf = 64 * units;
+  const int64_t s = unit0 * 64, e = s + 64 * units, ldt = (n + 63) / 64 * 64;
   for (int64_t j = 0; j < units; ++j) {
-    hipError_t st = launch_group(w, n, k, ldw, u, ldu, unit0 + j, scheme, codes, meta, f + 64 * j,
-                                 ldf, stream);
+    float* fj = ft + 64 * j * ldt;
+    hipError_t st = launch_group(w, n, k, ldw, u, ldu, unit0 + j, scheme, codes, meta, fj, 1, ldt,
+                                 stream);
     if (st != hipSuccess) return st;
-    st = launch_rank_update(w, n, ldw, u, ldu, s + 64 * j, s + 64 * (j + 1), e, f + 64 * j, ldf,
-                            64, stream);
+    st = launch_rank_update(w, n, ldw, u, ldu, s + 64 * j, s + 64 * (j + 1), e, fj, ldt, 64,
+                            stream);
     if (st != hipSuccess) return st;
   }
-  return launch_rank_update(w, n, ldw, u, ldu, s, e, k, f, ldf, 64 * units, stream);
+  return launch_rank_update(w, n, ldw, u, ldu, s, e, k, ft, ldt, 64 * units, stream);
 }

@@ -354,7 +354,8 @@ HIF4_EXPORT hif4_status hif4_higptq_unit(float *w, int64_t n, int64_t k, int64_t
 #define HIF4_HIGPTQ_MAX_BLOCK_UNITS 16
 
 /* hif4_higptq_block_workspace_bytes -- workspace of hif4_higptq_block for n
- * rows and a block of `units` groups (0 for units outside 1..16). */
+ * rows and a block of `units` groups: 256 units * ceil(n / 64) * 64 bytes
+ * (0 for units outside 1..16). */
 HIF4_EXPORT size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units);
 
 /*
@@ -387,7 +388,9 @@ HIF4_EXPORT size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units);
  *  codes, meta: units unit0 .. unit0 + units - 1 of every row written.
  *  workspace >= hif4_higptq_block_workspace_bytes(n, units), 256-byte
  *         aligned (HIF4_ERR_WORKSPACE / HIF4_ERR_ALIGN); on return it holds
- *         F_B, fp32 [n][64 units] row-major (group j's F in columns 64 j ..).
+ *         F_B transposed: fp32 [64 units][ldt], ldt = n rounded up to a
+ *         multiple of 64, row 64 j + c holding column c of group j's F for
+ *         rows 0 .. n - 1 (the padding is scratch).
  */
 HIF4_EXPORT hif4_status hif4_higptq_block(float *w, int64_t n, int64_t k, int64_t ldw,
                               const float *u, int64_t ldu, int64_t unit0, int64_t units,

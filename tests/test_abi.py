@@ -271,7 +271,8 @@ def test_higptq_argument_checks(L):
 def test_higptq_block_argument_checks(L):
     f = L.hif4_higptq_block
     ws = L.hif4_higptq_block_workspace_bytes(10, 3)
-    assert ws == 7680  # 10 rows x 3 groups x 64 fp32 (a multiple of 256 bytes)
+    assert ws == 3 * 64 * 64 * 4  # F^T: 3 groups x 64 rows of 64 (10 rows padded to 64) fp32
+    assert L.hif4_higptq_block_workspace_bytes(65, 1) == 64 * 128 * 4
     assert L.hif4_higptq_block_workspace_bytes(10, 0) == 0
     assert L.hif4_higptq_block_workspace_bytes(10, 17) == 0
     assert L.hif4_higptq_block_workspace_bytes(-1, 2) == 0
