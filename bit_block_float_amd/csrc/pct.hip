@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
           (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
 #pragma unroll
       for (int u = 0; u < kWinUnroll; ++u) {
-        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 0);
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 2);
         v[u] = *reinterpret_cast<const u32x4_t*>(&q);
       }
     };
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
         int64_t r = rb + rw + (int64_t)u * kRowStep;
         if (r > r1 - 1) r = r1 - 1;
         const auto q = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 0);
+            rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 2);
         va[u] = *reinterpret_cast<const u32x4_t*>(&q);
       }
       count(va, rb, true);
@@ -851,24 +851,28 @@ __global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
   if (threadIdx.x == 0 && fails) atomicAdd(n_failed, (uint32_t)__builtin_popcount(fails));
 }
 
-// The window path's first kernel: the sample of every S-th row and the
-// window it places, one workgroup per block of 64 channels reading all of
-// that block's sampled rows (no cross-workgroup merge: no global atomics, no
-// histogram to clear beforehand). Lanes read 16 bytes (channels 8p .. 8p+7,
-// p = lane & 7), 8 lanes per row, so a wave's load covers 8 rows. The
-// coarse histogram (key >> 7, u32) is [bin][channel] with a row stride of
-// 65 words, so the 8 rows of a wave's atomic land in distinct banks. Then
-// wave w finds, for channels 4w .. 4w+3 of the block, the coarse bin b of
-// rank floor(q (n_s - 1)) of the sample; the window starts one coarse bin
-// below it. Workgroup 0 also clears the flagged-channel count.
+// The window path's first two kernels. pct_sample_kernel: workgroup (x, y)
+// reads part y of the sampled rows (every S-th row; the parts are equal
+// contiguous runs) for the block of 64 channels x, and stores its coarse
+// histogram (key >> 7, u32) as sample partial (y, x), [channel][bin], with
+// plain stores: no atomics across workgroups and nothing to clear beforehand.
+// Lanes read 16 bytes (channels 8p .. 8p+7, p = lane & 7), 8 lanes per row, so
+// a wave's load covers one 128-byte piece of each of 8 rows. In LDS the
+// histogram is [bin][channel] with a row stride of 65 words, so the 8 rows of
+// a wave's atomic land in distinct banks. Splitting the rows keeps every CU
+// streaming (one workgroup per channel block alone ran 80 workgroups).
+// pct_place_kernel: one wave per channel sums the channel's partials and finds
+// the coarse bin b of rank floor(q (n_s - 1)) of the sample; the window starts
+// one coarse bin below it. Its workgroup 0 also clears the flagged-channel
+// count.
 constexpr int kSampCh = 64;
 constexpr int kSampStride = kSampCh + 1;
+constexpr int kSampWords = kSampCh * 256;  // one sample partial
 
-__global__ __launch_bounds__(kPctThreads) void pct_sample_window_kernel(
-    const uint16_t* __restrict__ x, int64_t rows_s, int c, int64_t ld, double q,
-    uint32_t* __restrict__ wlo, uint32_t* __restrict__ n_failed) {
+__global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
+    const uint16_t* __restrict__ x, int64_t rows_s, int c, int64_t ld, int parts,
+    uint32_t* __restrict__ samp) {
   __shared__ uint32_t hist[256 * kSampStride];
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_failed = 0u;
   for (int i = threadIdx.x; i < 256 * kSampStride; i += kPctThreads) hist[i] = 0u;
   __syncthreads();
   constexpr int kUnroll = 4, kRowStep = 8 * kPctWaves;
@@ -877,6 +881,8 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_window_kernel(
   const int rw = 8 * wave + g;  // row of the lane inside a step
   const int c0 = blockIdx.x * kSampCh;
   const int ch = c0 + 8 * p;
+  // this part's sampled rows [rbeg, rend)
+  const int64_t rbeg = rows_s * blockIdx.y / parts, rend = rows_s * (blockIdx.y + 1) / parts;
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   // lanes past the last channel read channel 0 (a valid address); their
   // columns are never read back. The row base of a block is wave-uniform;
@@ -889,14 +895,14 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_window_kernel(
         (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 0);
+      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 2);
       v[u] = *reinterpret_cast<const u32x4_t*>(&qq);
     }
   };
   auto count = [&](const u32x4_t (&v)[kUnroll], int64_t rb, bool tail) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (tail && rb + rw + (int64_t)u * kRowStep >= rows_s) continue;  // row past the end
+      if (tail && rb + rw + (int64_t)u * kRowStep >= rend) continue;  // row past the part
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t word = v[u][e >> 1];
@@ -906,51 +912,69 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_window_kernel(
     }
   };
   const int64_t blk = (int64_t)kUnroll * kRowStep;
-  int64_t rb = 0;
+  int64_t rb = rbeg;
   u32x4_t va[kUnroll], vc[kUnroll];
-  if (rb + blk <= rows_s) {
+  if (rb + blk <= rend) {
     load(va, rb);
     for (;;) {
-      const bool nxt = rb + 2 * blk <= rows_s;
+      const bool nxt = rb + 2 * blk <= rend;
       load(vc, nxt ? rb + blk : rb);
       count(va, rb, false);
       rb += blk;
       if (!nxt) break;
-      const bool nxt2 = rb + 2 * blk <= rows_s;
+      const bool nxt2 = rb + 2 * blk <= rend;
       load(va, nxt2 ? rb + blk : rb);
       count(vc, rb, false);
       rb += blk;
       if (!nxt2) break;
     }
   }
-  if (rb < rows_s) {
+  if (rb < rend) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       int64_t r = rb + rw + (int64_t)u * kRowStep;
-      if (r > rows_s - 1) r = rows_s - 1;
+      if (r > rend - 1) r = rend - 1;
       const auto qq = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 0);
+          rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 2);
       va[u] = *reinterpret_cast<const u32x4_t*>(&qq);
     }
     count(va, rb, true);
   }
   __syncthreads();
+  // [channel][bin]: consecutive threads store consecutive bins of a channel
+  uint32_t* dst = samp + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSampWords;
+  for (int i = threadIdx.x; i < kSampWords; i += kPctThreads)
+    dst[i] = hist[(i & 255) * kSampStride + (i >> 8)];
+}
+
+constexpr int kPlaceThreads = 256;
+
+__global__ __launch_bounds__(kPlaceThreads) void pct_place_kernel(
+    const uint32_t* __restrict__ samp, int parts, int c, int64_t rows_s, double q,
+    uint32_t* __restrict__ wlo, uint32_t* __restrict__ n_failed) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_failed = 0u;
+  const int lane = threadIdx.x & 63;
+  const int ch = blockIdx.x * (kPlaceThreads / 64) + (threadIdx.x >> 6);
+  if (ch >= c) return;  // the whole wave
+  const int cblocks = (c + kSampCh - 1) / kSampCh;
+  const uint32_t* src = samp + (int64_t)(ch / kSampCh) * kSampWords + (ch % kSampCh) * 256 + 4 * lane;
+  uint32_t cnt[4] = {0u, 0u, 0u, 0u};
+  for (int y = 0; y < parts; ++y) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)y * cblocks * kSampWords);
+    cnt[0] += v.x;
+    cnt[1] += v.y;
+    cnt[2] += v.z;
+    cnt[3] += v.w;
+  }
   int64_t lo, hi;
   double f;
   type7_ranks(rows_s, q, &lo, &hi, &f);
-#pragma unroll
-  for (int k = 0; k < kSampCh / kPctWaves; ++k) {
-    const int cc = wave * (kSampCh / kPctWaves) + k;  // channel within the block
-    uint32_t cnt[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cnt[i] = hist[(4 * lane + i) * kSampStride + cc];
-    uint32_t b;
-    int64_t before;
-    wave_find_rank<4>(cnt, lo, &b, &before);
-    if (lane == 0 && c0 + cc < c) wlo[c0 + cc] = (b > 0 ? b - 1 : 0u) << 7;
-  }
+  uint32_t b;
+  int64_t before;
+  wave_find_rank<4>(cnt, lo, &b, &before);
+  if (lane == 0) wlo[ch] = (b > 0 ? b - 1 : 0u) << 7;
 }
 
 }  // namespace hif4
@@ -1006,6 +1030,27 @@ int64_t window_partials(int64_t rows, int64_t c) {
   const int64_t cblocks = (c + kPctCh - 1) / kPctCh;
   return 2 * ((rows + per_wg - 1) / per_wg) * cblocks;
 }
+
+// Parts of the window path's sample: about two workgroups per CU of a
+// 256-CU device over all channel blocks, at least 256 sampled rows each, at
+// most 16 (a function of rows and c only, so the workspace is too).
+int sample_parts(int64_t rows_s, int64_t c) {
+  const int64_t cblocks = (c + kSampCh - 1) / kSampCh;
+  int64_t parts = 512 / cblocks;
+  if (parts > rows_s / 256) parts = rows_s / 256;
+  if (parts > 16) parts = 16;
+  return parts < 1 ? 1 : (int)parts;
+}
+
+// Bytes of the region that holds the window pass's partials and, before that
+// pass, the sample partials.
+size_t window_region_bytes(int64_t rows, int64_t c) {
+  if (rows < kWindowMinRows) return 0;
+  const int64_t rows_s = (rows + sample_stride(rows) - 1) / sample_stride(rows);
+  const size_t win = (size_t)window_partials(rows, c) * kPartWords * 4;
+  const size_t smp = (size_t)sample_parts(rows_s, c) * ((c + kSampCh - 1) / kSampCh) * kSampWords * 4;
+  return win > smp ? win : smp;
+}
 }  // namespace
 
 size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c) {
@@ -1015,7 +1060,7 @@ size_t hif4_percentile_ws_bytes(int64_t rows, int64_t c) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   return al((size_t)c * 256 * 4) + al((size_t)c * 128 * 4) + al((size_t)c * 4) +
          al((size_t)c * sizeof(PctSel)) + al((size_t)c * 4) +
-         al((size_t)window_partials(rows, c) * kPartWords * 4) + al(4);
+         al(window_region_bytes(rows, c)) + al(4);
 }
 
 hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, int64_t ld,
@@ -1034,7 +1079,7 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
   uint32_t* wlo = (uint32_t*)ws;
   ws += al((size_t)c * 4);
   uint32_t* part = (uint32_t*)ws;
-  ws += al((size_t)window_partials(rows, c) * kPartWords * 4);
+  ws += al(window_region_bytes(rows, c));
   uint32_t* n_exact = (uint32_t*)ws;  // channels resolved by exact passes
 
   const int ci = (int)c;
@@ -1048,9 +1093,13 @@ hipError_t hif4_launch_percentile(const uint16_t* x, int64_t rows, int64_t c, in
     const int64_t rows_s = (rows + stride_s - 1) / stride_s;
     int64_t per_w, grid_w;
     if (!pass_grid(rows, ci, kWindowResident, &per_w, &grid_w)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pct_sample_window_kernel, dim3((unsigned)((ci + kSampCh - 1) / kSampCh)),
-                       dim3(kPctThreads), 0, stream, x, rows_s, ci, ld * stride_s, q, wlo,
-                       n_exact);
+    const int parts = sample_parts(rows_s, c);
+    hipLaunchKernelGGL(pct_sample_kernel, dim3((unsigned)((ci + kSampCh - 1) / kSampCh), parts),
+                       dim3(kPctThreads), 0, stream, x, rows_s, ci, ld * stride_s, parts, part);
+    hipLaunchKernelGGL(pct_place_kernel,
+                       dim3((unsigned)((ci + kPlaceThreads / 64 - 1) / (kPlaceThreads / 64))),
+                       dim3(kPlaceThreads), 0, stream, (const uint32_t*)part, parts, ci, rows_s, q,
+                       wlo, n_exact);
     hipLaunchKernelGGL(pct_window_kernel, dim3((unsigned)grid_w), dim3(kPctThreads), 0, stream, x,
                        rows, ci, ld, per_w, (const uint32_t*)wlo, part);
     hipLaunchKernelGGL(pct_resolve_kernel,
