@@ -135,15 +135,35 @@ def linear_workspace_bytes(m, n, k, n_kept=0):
     return int(lib().hif4_linear_workspace_bytes(m, n, k, n_kept))
 
 
-def _kept_count(x_kept, w_kept):
+def _kept_count(x_kept, w_kept, m, n):
+    """n_kept from the kept-value tensors, after checking their shapes: a
+    short tensor would be read past its end by the library."""
     if w_kept is None:
+        if x_kept is not None:
+            raise ValueError("x_kept given without w_kept")
         return 0
-    if w_kept.dtype != torch.bfloat16 or not w_kept.is_contiguous():
-        raise ValueError("w_kept must be a contiguous bf16 tensor [n][n_kept]")
+    if (w_kept.dtype != torch.bfloat16 or not w_kept.is_contiguous() or w_kept.dim() != 2
+            or w_kept.shape[0] != n or not w_kept.is_cuda):
+        raise ValueError(f"w_kept must be a contiguous bf16 CUDA tensor [n={n}][n_kept]")
     if x_kept is not None and (x_kept.dtype != torch.bfloat16 or not x_kept.is_contiguous()
-                               or x_kept.shape[1] != w_kept.shape[1]):
-        raise ValueError("x_kept must be a contiguous bf16 tensor [m][n_kept]")
+                               or x_kept.dim() != 2 or x_kept.shape[0] != m
+                               or x_kept.shape[1] != w_kept.shape[1] or not x_kept.is_cuda):
+        raise ValueError(f"x_kept must be a contiguous bf16 CUDA tensor [m={m}][n_kept]")
     return w_kept.shape[1]
+
+
+def _check_mask(mask, k, n_kept):
+    """The protection mask: uint8 [k] on the GPU with exactly n_kept nonzeros
+    (the count the kept values were gathered for)."""
+    if mask is None:
+        if n_kept:
+            raise ValueError("n_kept > 0 with a bf16 x needs the mask that selects the channels")
+        return
+    if mask.dtype != torch.uint8 or mask.shape != (k,) or not mask.is_contiguous() or not mask.is_cuda:
+        raise ValueError(f"mask must be a contiguous uint8 CUDA tensor [k={k}]")
+    nz = int(torch.count_nonzero(mask).item())
+    if nz != n_kept:
+        raise ValueError(f"mask has {nz} protected channels but the kept values have {n_kept}")
 
 
 def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, mask=None, x_kept=None,
@@ -159,7 +179,11 @@ def linear_w4a4(w_codes, w_meta, x=None, x_codes=None, x_meta=None, mask=None, x
         m = x.shape[0]
     else:
         m = x_codes.shape[0]
-    n_kept = _kept_count(x_kept, w_kept)
+    n_kept = _kept_count(x_kept, w_kept, m, n)
+    if x is not None:
+        _check_mask(mask, k, n_kept)
+    elif n_kept and x_kept is None:
+        raise ValueError("X given as codes with protected channels needs x_kept")
     dev = w_codes.device
     dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
     y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=dev)
@@ -181,7 +205,9 @@ def linear_xcodes_wbf16(x_codes, x_meta, w, x_kept=None, w_kept=None, y_dtype=to
     if not w.is_contiguous():
         raise ValueError("w must be contiguous (row stride k)")
     m, n, k = x_codes.shape[0], w.shape[0], w.shape[1]
-    n_kept = _kept_count(x_kept, w_kept)
+    n_kept = _kept_count(x_kept, w_kept, m, n)
+    if n_kept and x_kept is None:
+        raise ValueError("protected channels need x_kept")
     dt = HIF4_F32 if y_dtype == torch.float32 else HIF4_BF16
     y = y if y is not None else torch.empty((m, n), dtype=y_dtype, device=w.device)
     if workspace is None and n_kept:
@@ -208,7 +234,9 @@ def linear_xcodes_wbf16_noalloc(x_codes, x_meta, w, y, x_kept=None, w_kept=None,
     m, n, k = x_codes.shape[0], w.shape[0], w.shape[1]
     if y.shape != (m, n) or not y.is_contiguous() or y.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("y must be a contiguous fp32 or bf16 tensor [m][n]")
-    n_kept = _kept_count(x_kept, w_kept)
+    n_kept = _kept_count(x_kept, w_kept, m, n)
+    if n_kept and x_kept is None:
+        raise ValueError("protected channels need x_kept")
     dt = HIF4_F32 if y.dtype == torch.float32 else HIF4_BF16
     st = lib().hif4_linear_xcodes_wbf16_noalloc(_ptr(x_codes), _ptr(x_meta), _ptr(w),
                                                 _ptr(x_kept), _ptr(w_kept), n_kept, m, n, k,

@@ -261,6 +261,42 @@ def test_linear_protected_channels(hip, m, n, k, n_kept, path):
     check_linear(y.cpu().numpy(), y_ref, s_ref)
 
 
+def test_linear_binding_rejects_inconsistent_protection(hip):
+    """The binding checks that the mask and the kept values agree before the
+    library reads them (a short mask or kept tensor would be read past its
+    end, and a mask with fewer channels than n_kept would feed uninitialized
+    workspace into the residual)."""
+    m, n, k, n_kept = 40, 24, 128, 3
+    r = np.random.default_rng(5)
+    mask = np.zeros(k, np.uint8)
+    mask[r.choice(k, n_kept, replace=False)] = 1
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=9))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=10))
+    xc, xm, xk = oracle.quantize(xb, mask)
+    wc, wm, wk = oracle.quantize(wb, mask)
+    wcd, wmd = torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda()
+    xcd, xmd = torch.from_numpy(xc).cuda(), torch.from_numpy(xm.view(np.int32)).cuda()
+    xkd, wkd = _bf16_dev(xk), _bf16_dev(wk)
+    x, md = dev_bf16(xb), torch.from_numpy(mask).cuda()
+    hip.linear_w4a4(wcd, wmd, x=x, mask=md, w_kept=wkd)  # consistent: accepted
+    bad_calls = [
+        lambda: hip.linear_w4a4(wcd, wmd, x=x, mask=md, w_kept=wkd[:, :2].contiguous()),
+        lambda: hip.linear_w4a4(wcd, wmd, x=x, mask=md[:k - 1].contiguous(), w_kept=wkd),
+        lambda: hip.linear_w4a4(wcd, wmd, x=x, mask=md.to(torch.int32), w_kept=wkd),
+        lambda: hip.linear_w4a4(wcd, wmd, x=x, w_kept=wkd),
+        lambda: hip.linear_w4a4(wcd, wmd, x=x, mask=md, w_kept=wkd[:n - 1].contiguous()),
+        lambda: hip.linear_w4a4(wcd, wmd, x_codes=xcd, x_meta=xmd, w_kept=wkd),
+        lambda: hip.linear_w4a4(wcd, wmd, x_codes=xcd, x_meta=xmd, x_kept=xkd[:m - 1].contiguous(),
+                                w_kept=wkd),
+        lambda: hip.linear_xcodes_wbf16(xcd, xmd, hip.dequantize(wcd, wmd, out_dtype=torch.bfloat16),
+                                        w_kept=wkd),
+    ]
+    for i, call in enumerate(bad_calls):
+        with pytest.raises(ValueError):
+            call()
+        print(f"[case] inconsistent protection {i} rejected", flush=True)
+
+
 def test_linear_one_hot_weight_is_exact(hip):
     """W row j = a single 7 at column t: Y[:, j] = 7 * deq(Q(X))[:, t] exactly
     (one exact product per output, no rounding)."""
