@@ -119,7 +119,7 @@ def torch_index(idx):
     return torch.from_numpy(idx).to(torch.long)
 
 
-def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2, block_units=4):
+def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2, block_units=8):
     """HiGPTQ over the whole weight (80 groups of 64 columns), each of the
     three schemes, in blocks of `block_units` groups (blocksize 64 block_units:
     the columns after a block are compensated once per block) and, for

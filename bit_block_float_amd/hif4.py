@@ -354,7 +354,7 @@ def higptq_block(w, u, unit0, units, codes, meta, workspace=None, stream=None, s
     _ok(st, "hif4_higptq_block")
 
 
-def higptq(w, u, stream=None, scheme=1, block_units=4):
+def higptq(w, u, stream=None, scheme=1, block_units=8):
     """HiGPTQ over all groups in blocks of ``block_units`` groups (1 = one
     group at a time through hif4_higptq_unit): returns (codes, meta); w is
     updated in place (its final contents are the compensated working
