@@ -623,7 +623,7 @@ hipError_t launch_rank_update(float* w, int64_t n, int64_t ldw, const float* u, 
                               int64_t R, hipStream_t stream) {
   if (c1 <= c0) return hipSuccess;
   const unsigned cols = (unsigned)((c1 - c0) / 64);
-  if (R == 64)  // the in-block updates: short, so more and shorter waves
+  if (c1 - c0 <= 512)  // narrow (in-block) updates: more and shorter waves
     hipLaunchKernelGGL(higptq_rank_update_kernel<1>, dim3(cols, (unsigned)((n + 127) / 128)),
                        dim3(256), 0, stream, w, ldw, n, u, ldu, sk, c0, ft, ldt, (int)R);
   else
@@ -649,10 +649,31 @@ hipError_t hif4_launch_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, 
   return hipGetLastError();
 }
 
-// One block of `units` groups from unit0: each group quantized, then the
-// block's later columns updated by that group's F; after the last group the
-// columns after the block take the whole block's F at once. F is kept
-// transposed: F^T [64 units][ldt], ldt = n rounded up to a multiple of 64, the
+// Groups lo .. hi - 1 of the block starting at unit0 (column s), in the
+// nested order of blocked GPTQ: the first half of the range, then the second
+// half's columns updated once with the first half's F (rank 64 (mid - lo)),
+// then the second half. Every column of the block thus takes every earlier
+// group's correction before its own group is quantized, with each in-block
+// column read and written once per level instead of once per earlier group.
+hipError_t block_range(float* w, int64_t n, int64_t k, int64_t ldw, const float* u, int64_t ldu,
+                       int64_t unit0, int64_t lo, int64_t hi, int scheme, uint8_t* codes,
+                       uint32_t* meta, float* ft, int64_t ldt, hipStream_t stream) {
+  if (hi - lo == 1)
+    return launch_group(w, n, k, ldw, u, ldu, unit0 + lo, scheme, codes, meta, ft + 64 * lo * ldt,
+                        1, ldt, stream);
+  const int64_t mid = lo + (hi - lo) / 2, s = unit0 * 64;
+  hipError_t st = block_range(w, n, k, ldw, u, ldu, unit0, lo, mid, scheme, codes, meta, ft, ldt,
+                              stream);
+  if (st != hipSuccess) return st;
+  st = launch_rank_update(w, n, ldw, u, ldu, s + 64 * lo, s + 64 * mid, s + 64 * hi,
+                          ft + 64 * lo * ldt, ldt, 64 * (mid - lo), stream);
+  if (st != hipSuccess) return st;
+  return block_range(w, n, k, ldw, u, ldu, unit0, mid, hi, scheme, codes, meta, ft, ldt, stream);
+}
+
+// One block of `units` groups from unit0 (block_range for the groups), then
+// the columns after the block take the whole block's F at once. F is kept
+// transposed: F^T [64 units][ldt], ldt = n rounded up to a multiple of 64,
 // group j's rows at 64 j.
 hipError_t hif4_launch_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw, const float* u,
                                     int64_t ldu, int64_t unit0, int64_t units, int scheme,
@@ -660,14 +681,8 @@ hipError_t hif4_launch_higptq_block(float* w, int64_t n, int64_t k, int64_t ldw,
                                     hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t s = unit0 * 64, e = s + 64 * units, ldt = (n + 63) / 64 * 64;
-  for (int64_t j = 0; j < units; ++j) {
-    float* fj = ft + 64 * j * ldt;
-    hipError_t st = launch_group(w, n, k, ldw, u, ldu, unit0 + j, scheme, codes, meta, fj, 1, ldt,
-                                 stream);
-    if (st != hipSuccess) return st;
-    st = launch_rank_update(w, n, ldw, u, ldu, s + 64 * j, s + 64 * (j + 1), e, fj, ldt, 64,
-                            stream);
-    if (st != hipSuccess) return st;
-  }
+  hipError_t st = block_range(w, n, k, ldw, u, ldu, unit0, 0, units, scheme, codes, meta, ft, ldt,
+                              stream);
+  if (st != hipSuccess) return st;
   return launch_rank_update(w, n, ldw, u, ldu, s, e, k, ft, ldt, 64 * units, stream);
 }

@@ -367,9 +367,12 @@ HIF4_EXPORT size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units);
  * columns after it in one update. Section 3.1 "HiGPTQ" requires the blocksize
  * to be 64 or a multiple of 64, each group of 64 being one HiF4 unit. Here the
  * groups unit0 .. unit0 + units - 1 are each taken as hif4_higptq_unit takes
- * one group (same schemes), the block's later columns updated after each
- * group, then W_after -= F_B U_B,after once for the block's compensation
- * coefficients F_B.
+ * one group (same schemes); inside the block the updates are nested: the
+ * first half of the groups (recursively), then the second half's columns
+ * updated once with the first half's F, then the second half (recursively);
+ * then W_after -= F_B U_B,after once for the block's compensation
+ * coefficients F_B. Every column still takes every earlier group's
+ * correction before its own group is quantized.
  * The result is that of hif4_higptq_unit called for unit0 .. unit0 + units - 1
  * in order, up to the order of the fp32 roundings; a block carries the update
  * of the later columns over 64 units columns at once, so a pass over W moves
