@@ -119,16 +119,19 @@ def torch_index(idx):
     return torch.from_numpy(idx).to(torch.long)
 
 
-def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2, block_units=8):
+def time_higptq(torch, workloads, hif4, dev, w_bf16, x_bf16, stream, reps=2, block_units=8):
     """HiGPTQ over the whole weight (80 groups of 64 columns), each of the
     three schemes, in blocks of `block_units` groups (blocksize 64 block_units:
     the columns after a block are compensated once per block) and, for
     comparison, one group per call (blocksize 64): one untimed pass, then
-    `reps` timed passes from the same start. Reported apart from the hot-path
-    step (it is a calibration pass, run once per layer)."""
-    spec = workloads.WORKLOADS["higptq"]
+    `reps` timed passes from the same start. The Hessian is the one GPTQ takes
+    from the layer's inputs, H = 2 X^T X / rows (+1% dampening), with X the
+    FFN-up activation of the step; U is the upper factor of its inverse.
+    Reported with each scheme's layer-output error tr(E H E^T), E = W - deq(Q),
+    relative to direct HiF4 quantization. Apart from the hot-path step (a
+    calibration pass, run once per layer)."""
     n, k = w_bf16.shape
-    u = workloads.higptq_factor(k, device="cuda", seed=spec["index"])
+    u, h = workloads.higptq_factor_from_x(x_bf16)
     w0 = w_bf16.float()
     w = torch.empty_like(w0)
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
@@ -171,16 +174,41 @@ def time_higptq(torch, workloads, hif4, dev, w_bf16, stream, reps=2, block_units
                 times.append(e0.elapsed_time(e1))
         return sum(times) / len(times)
 
-    out = {"workload": f"W {n}x{k} (the FFN-up weight), random inverse-Hessian factor U {k}x{k}",
+    def out_err(hh):  # tr(E H E^T) of the codes now in codes/meta
+        e = w0 - hif4.dequantize(codes, meta, out_dtype=torch.float32, stream=stream)
+        return float(((e @ hh) * e).sum())
+
+    hif4.quantize(w_bf16, codes=codes, meta=meta, stream=stream)
+    err_direct = out_err(h)
+    # The step's X has independent channels, so its H is nearly diagonal and
+    # leaves GPTQ little to compensate; the same X mixed across channels
+    # (X (I + 0.8 A / sqrt(k)), A ~ N(0, 1)) gives a Hessian with the
+    # correlations real activations have.
+    g = torch.Generator(device="cuda").manual_seed(11)
+    mix = torch.eye(k, device=dev) + 0.8 * torch.randn((k, k), generator=g, device=dev) / k ** 0.5
+    u_c, h_c = workloads.higptq_factor_from_x(x_bf16.float() @ mix)
+    del mix
+    err_direct_c = out_err(h_c)
+    out = {"workload": f"W {n}x{k} (the FFN-up weight), H = 2 X^T X / rows of the step's X "
+                       f"{x_bf16.shape[0]}x{k} (+1% dampening), U = upper factor of H^-1",
            "groups": units, "blocksize": 64 * block_units}
     for scheme in (1, 2, 3):
         ms = timed(scheme, block_units)
+        rel = out_err(h) / err_direct
+        w.copy_(w0)
+        for b0 in range(0, units, block_units):
+            hif4.higptq_block(w, u_c, b0, min(block_units, units - b0), codes, meta,
+                              workspace=wsb, stream=stream, scheme=scheme)
+        rel_c = out_err(h_c) / err_direct_c
         ms1 = timed(scheme, 1)
         log(f"HiGPTQ scheme {scheme} over W {n}x{k}: {ms:.2f} ms in blocks of {64 * block_units} "
-            f"columns, {ms1:.2f} ms one group at a time")
+            f"columns, {ms1:.2f} ms one group at a time; layer-output error {rel:.3f} x direct "
+            f"({rel_c:.3f} x with channel-correlated X)")
         # rates over the whole pass (group kernels included)
         tf = flops / (ms * 1e-3) / 1e12
-        out[f"scheme{scheme}"] = {"ms": ms, "update_TFLOP/s": tf,
+        out[f"scheme{scheme}"] = {"ms": ms, "output_error_vs_direct": rel,
+                                  "output_error_vs_direct_correlated_x": rel_c,
+                                  "update_TFLOP/s": tf,
                                   "frac_fp32_mfma": tf / FP32_MFMA_PEAK_TFLOPS,
                                   "W_GB/s": wbytesb / ms / 1e6,
                                   "ms_blocksize64": ms1,
@@ -568,7 +596,7 @@ def main():
     if not args.no_shapes:
         parts.update(time_shapes(torch, workloads, hif4, dev, stream))
     if not args.no_extras:
-        out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, stream)}
+        out["extensions"] = {"higptq": time_higptq(torch, workloads, hif4, dev, w, x, stream)}
         out["extensions"]["calibration"] = time_calibration(torch, workloads, hif4, dev, stream)
         out["extensions"]["hiautoround_quantize"] = time_autoround(torch, hif4, dev, w, stream)
     if not args.no_cpu_baseline:

@@ -20,9 +20,13 @@ Workloads (seed = workload index unless given):
   calib     16 batches of 57600x5120: Student-t(2.5) * c[ch] * d_b[ch],
             c ~ LogNormal(0,1), d_b ~ LogNormal(0,0.5); q=0.999, 52 protected;
             W 13824x5120 ~0.02 N(0,1) quantized with that mask.
-  higptq    W 13824x5120 ~0.02 N(0,1) and a random upper-triangular factor U
-            of a synthetic inverse Hessian (H^-1 = U^T U): drawn directly, since
-            any upper-triangular U with a positive diagonal is one.
+  higptq    W 13824x5120 ~0.02 N(0,1) and the upper factor U of an inverse
+            Hessian (H^-1 = U^T U): for the tests, U drawn directly
+            (higptq_factor: any upper-triangular U with a positive diagonal is
+            one); for the bench, GPTQ's H = 2 X^T X / rows (+1% dampening) of
+            the FFN-up X (higptq_factor_from_x), and of that X mixed across
+            channels by I + 0.8 A / sqrt(k), A ~ N(0,1) (the FFN-up recipe's
+            channels are independent, its H nearly diagonal).
 """
 import math
 
@@ -154,6 +158,18 @@ def bits(t: torch.Tensor):
     """uint16 numpy view of a bf16 tensor's bit patterns (host copy)."""
     import numpy as np
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def higptq_factor_from_x(x, damp=0.01):
+    """Upper factor U (fp32 [k][k]) of H^-1 = U^T U for the Hessian GPTQ takes
+    from calibration activations x [rows][k] (the layer's inputs): H =
+    2 x^T x / rows, with damp * mean(diag H) added to the diagonal (GPTQ's
+    dampening), on x's device; the inverse and factors in fp64."""
+    xf = x.float()
+    h = (xf.T @ xf).double() * (2.0 / x.shape[0])
+    h.diagonal().add_(damp * h.diagonal().mean())
+    hinv = torch.cholesky_inverse(torch.linalg.cholesky(h))
+    return torch.linalg.cholesky(hinv, upper=True).float().contiguous(), h.float()
 
 
 def higptq_factor(k, device="cpu", seed=5, spread=0.5, coupling=1.0):
