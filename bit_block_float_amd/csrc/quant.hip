@@ -157,24 +157,15 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
   return ((hi >> 7) | (hi >> 14) | (hi >> 21) | (hi >> 28)) & 0xFu;
 }
 
-// One 16-element item (two level-2 groups, words w0 and w1) of row `row`:
-// item j of the row, it = its index over all rows (code words 2it, 2it+1;
-// the unit's meta word it/4, written by the quad's first lane). Steps 1-5 of
-// the rule. kMask: `info` = the 16 mask bits of the item's channels (high
-// half) and the rank of its first masked channel among all masked channels
-// (low half), z0/z1 = the words' keep masks (0 on masked halves): masked
-// channels are quantized as +0 and do not enter the maxima, and their bf16
-// values go to kept[row][rank] once the item's codes are out (the data are
-// in registers by then, so no load wait is needed for that rare branch).
-template <bool kMask>
-__device__ __forceinline__ void quantize_item(uint4 w0, uint4 w1, uint4 z0, uint4 z1,
-                                              uint32_t info, uint32_t row, uint32_t j,
-                                              uint32_t it, uint32_t* __restrict__ codes32,
-                                              uint32_t* __restrict__ meta,
-                                              uint16_t* __restrict__ kept, int n_mask) {
+// One 16-element item (two level-2 groups, words v0 and v1, element 2i in
+// the low half of word i; protected channels already cleared to +0, so they
+// do not enter the maxima): item j of its row, it = its index over all rows
+// (code words 2it, 2it+1; the unit's meta word it/4, written by the quad's
+// first lane). Steps 1-5 of the rule.
+__device__ __forceinline__ void quantize_item(uint4 v0, uint4 v1, uint32_t j, uint32_t it,
+                                              uint32_t* __restrict__ codes32,
+                                              uint32_t* __restrict__ meta) {
   const uint32_t q = j & 3u;  // item within the unit (groups 2q, 2q+1)
-  const uint4 v0 = kMask ? make_uint4(w0.x & z0.x, w0.y & z0.y, w0.z & z0.z, w0.w & z0.w) : w0;
-  const uint4 v1 = kMask ? make_uint4(w1.x & z1.x, w1.y & z1.y, w1.z & z1.z, w1.w & z1.w) : w1;
 
   // step 1: level-3 / level-2 maxima of |x| as bf16 bit patterns (sign bits
   // dropped; monotone in |x|), then the unit maximum over the quad of lanes
@@ -204,19 +195,25 @@ __device__ __forceinline__ void quantize_item(uint4 w0, uint4 w1, uint4 z0, uint
                       (e3b1 << (17 + 2 * g1));
   const uint32_t mw = or4_u32(mb) | c;
   if (q == 0u) meta[it >> 2] = mw;
+}
 
-  if (kMask) {
-    const uint32_t m16 = info >> 16;
-    if (m16) {  // rare: only lanes whose channels include masked ones
-      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      uint32_t mm = m16;
-      while (mm) {
-        const uint32_t e = __ffs(mm) - 1;
-        const uint32_t rank = (info & 0xFFFFu) + __popc(m16 & ((1u << e) - 1u));
-        if (rank < (uint32_t)n_mask)
-          kept[(int64_t)row * n_mask + rank] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
-        mm &= mm - 1;
-      }
+// Kept values of one item of row `row`, one protected channel at a time:
+// `info` = the item's 16 mask bits (high half) and the rank of its first
+// masked channel among all masked channels (low half); the bf16 value of
+// channel e goes to kept[row][rank of e].
+__device__ __forceinline__ void keep_item_values(uint4 w0, uint4 w1, uint32_t info,
+                                                 uint32_t row, uint16_t* __restrict__ kept,
+                                                 int n_mask) {
+  const uint32_t m16 = info >> 16;
+  if (m16) {  // only lanes whose channels include masked ones
+    const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint32_t mm = m16;
+    while (mm) {
+      const uint32_t e = __ffs(mm) - 1;
+      const uint32_t rank = (info & 0xFFFFu) + __popc(m16 & ((1u << e) - 1u));
+      if (rank < (uint32_t)n_mask)
+        kept[(int64_t)row * n_mask + rank] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+      mm &= mm - 1;
     }
   }
 }
@@ -242,9 +239,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   };
   auto encode = [&](uint4 v0, uint4 v1, uint32_t it) {
     const uint32_t row = fdiv(it, item_div);
-    const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
-    quantize_item<false>(v0, v1, ones, ones, 0u, row, it - row * items_per_row, it, codes32, meta,
-                         nullptr, 0);
+    quantize_item(v0, v1, it - row * items_per_row, it, codes32, meta);
   };
   uint32_t it = blockIdx.x * blockDim.x + threadIdx.x;
   uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
@@ -265,12 +260,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 // row it visits, so the rank/mask word of its items is computed once, in
 // registers, by a workgroup prefix count over the mask before the row loop:
 // the loop itself has no table lookup. Workgroup g visits rows g, g + G, ...
+//
+// Kept values. The masked channels of a wave's items in one round hold the
+// consecutive ranks [r0, r0 + cnt), the same in every row. When cnt <= 64
+// the prologue assigns rank r0 + i to lane i and records where that value
+// sits in the wave's LDS stage (source lane * 32 + element * 2); per row the
+// lanes whose item holds masked channels write their 32 input bytes to the
+// stage, every lane reads its slot back before the item is encoded, and
+// lanes 0..cnt-1 store it after the encode, so the wave writes its kept run
+// with one contiguous store and never waits for the LDS round trip. Waves
+// with more masked channels keep the per-lane loop.
+//
+// Registers decide the occupancy of this HBM-streaming loop: with a single
+// round the items' keep masks (32 bytes per thread) live in LDS and are read
+// per item, which keeps the kernel at 8 waves per SIMD (measured on the
+// FFN-up activation, 57600 x 5120 with 52 protected channels: 171 us with
+// the per-lane loop and the masks in registers, 155-158 us this way).
 template <int kRounds>
 __global__ __launch_bounds__(1024) void quantize_masked_kernel(
     const uint16_t* __restrict__ x, int64_t ld, uint32_t rows, uint32_t items_per_row,
     const uint8_t* __restrict__ mask, uint32_t* __restrict__ codes32,
     uint32_t* __restrict__ meta, uint16_t* __restrict__ kept, int n_mask) {
+  // dynamic LDS: per wave a stage of 64 lanes x the item's 2 words, then
+  // (single round) the keep masks, 2 words per thread
+  extern __shared__ uint4 stage[];
+  constexpr bool kMasksInLds = kRounds == 1;
+  uint4* const zs = stage + (blockDim.x >> 6) * 128;
   __shared__ uint32_t part[16];
+  __shared__ uint16_t slot_src[kRounds][16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   const uint32_t B = blockDim.x;
@@ -293,8 +310,13 @@ __global__ __launch_bounds__(1024) void quantize_masked_kernel(
                                             (size_t)min(tid + r * B, items_per_row - 1u) * 16);
   uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
   load(a0, a1, blockIdx.x, 0);
+  // info: the item's 16 mask bits (high half); low half: with the stage,
+  // the stage byte offset of the lane's kept value (lanes < wcnt), else the
+  // rank of the item's first masked channel
   uint32_t info[kRounds];
-  uint4 zk0[kRounds], zk1[kRounds];  // keep masks of the item's words
+  uint4 zk0[kRounds], zk1[kRounds];  // keep masks of the item's words (several rounds)
+  uint32_t wcnt[kRounds];            // masked channels of the wave's items (wave-uniform)
+  uint32_t wrank[kRounds];           // rank of the first of them (wave-uniform)
   uint32_t run = 0;  // masked channels in the rounds before the current one
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -310,6 +332,18 @@ __global__ __launch_bounds__(1024) void quantize_masked_kernel(
       const uint32_t o = (uint32_t)__shfl_up((int)incl, d, 64);
       if (lane >= d) incl += o;
     }
+    const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    wcnt[r] = wc;
+    if (wc <= 64u) {
+      // kept slot of each masked channel = its rank within the wave
+      uint32_t mm = m16;
+      while (mm) {
+        const uint32_t e = __ffs(mm) - 1;
+        slot_src[r][wave][incl - cnt + __popc(m16 & ((1u << e) - 1u))] =
+            (uint16_t)(lane * 32 + e * 2);
+        mm &= mm - 1;
+      }
+    }
     if (lane == 63) part[wave] = incl;
     __syncthreads();
     uint32_t base = run + incl - cnt, total = 0;
@@ -318,8 +352,10 @@ __global__ __launch_bounds__(1024) void quantize_masked_kernel(
       if (w < wave) base += pw;
       total += pw;
     }
+    const uint32_t ksrc = (wc <= 64u && (uint32_t)lane < wc) ? slot_src[r][wave][lane] : 0u;
+    wrank[r] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base - (incl - cnt)));
     __syncthreads();
-    info[r] = (m16 << 16) | (base & 0xFFFFu);
+    info[r] = (m16 << 16) | (wc <= 64u ? ksrc : (base & 0xFFFFu));
     run += total;
     uint32_t z[8];
 #pragma unroll
@@ -327,17 +363,51 @@ __global__ __launch_bounds__(1024) void quantize_masked_kernel(
       const uint32_t lo = (m16 >> (2 * i)) & 1u, hi = (m16 >> (2 * i + 1)) & 1u;
       z[i] = ~((lo * 0x0000FFFFu) | (hi * 0xFFFF0000u));
     }
-    zk0[r] = make_uint4(z[0], z[1], z[2], z[3]);
-    zk1[r] = make_uint4(z[4], z[5], z[6], z[7]);
+    if (kMasksInLds) {
+      zs[2 * tid] = make_uint4(z[0], z[1], z[2], z[3]);
+      zs[2 * tid + 1] = make_uint4(z[4], z[5], z[6], z[7]);
+    } else {
+      zk0[r] = make_uint4(z[0], z[1], z[2], z[3]);
+      zk1[r] = make_uint4(z[4], z[5], z[6], z[7]);
+    }
   }
 
   // items in the order (row, round); the next item's loads go out before the
   // current one is encoded, into the register buffer that is not being read
-  auto encode = [&](uint4 v0, uint4 v1, uint32_t row, int r) {
+  uint4* const st = stage + wave * 128;
+  auto encode = [&](uint4 w0, uint4 w1, uint32_t row, int r) {
     const uint32_t j = tid + r * B;
-    if (j < items_per_row)
-      quantize_item<true>(v0, v1, zk0[r], zk1[r], info[r], row, j, row * items_per_row + j, codes32,
-                          meta, kept, n_mask);
+    uint16_t kv = 0;
+    // kept values first: the raw words die at the masking below
+    if (wcnt[r] > 64u) {
+      keep_item_values(w0, w1, info[r], row, kept, n_mask);
+    } else if (wcnt[r] != 0u) {
+      if (info[r] >> 16) {
+        st[2 * lane] = w0;
+        st[2 * lane + 1] = w1;
+      }
+      // same-wave LDS accesses complete in order: the read sees the stage
+      // writes above, and the next item's writes come after it
+      __builtin_amdgcn_wave_barrier();
+      kv = reinterpret_cast<const uint16_t*>(st)[(info[r] & 0xFFFFu) >> 1];
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (j < items_per_row) {
+      uint4 z0, z1;
+      if (kMasksInLds) {
+        z0 = zs[2 * tid];
+        z1 = zs[2 * tid + 1];
+      } else {
+        z0 = zk0[r];
+        z1 = zk1[r];
+      }
+      quantize_item(make_uint4(w0.x & z0.x, w0.y & z0.y, w0.z & z0.z, w0.w & z0.w),
+                    make_uint4(w1.x & z1.x, w1.y & z1.y, w1.z & z1.z, w1.w & z1.w), j,
+                    row * items_per_row + j, codes32, meta);
+    }
+    const uint32_t rank = wrank[r] + lane;
+    if (wcnt[r] <= 64u && (uint32_t)lane < wcnt[r] && rank < (uint32_t)n_mask)
+      kept[(int64_t)row * n_mask + rank] = kv;
   };
   // (row, round) after (row, r)
   auto next = [&](uint32_t& row, int& r) {
@@ -439,6 +509,8 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
       const int rounds = (int)((gpr + 1023) / 1024);
       const uint32_t per = (gpr + rounds - 1) / rounds;
       const dim3 block((per + 63) / 64 * 64);
+      // kept-value stage, and the keep masks with a single round
+      const size_t lds = (size_t)block.x * 32 * (rounds == 1 ? 2 : 1);
       // at least ~4 rows per workgroup (the mask prologue is paid per
       // workgroup), at most 48 workgroups per CU
       const int64_t want = std::min<int64_t>(256 * 48, (nr + 3) / 4);
@@ -447,19 +519,23 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
       const uint32_t nrow = (uint32_t)nr;
       switch (rounds) {
         case 1:
-          hipLaunchKernelGGL(quantize_masked_kernel<1>, grid, block, 0, stream, xs, ld, nrow, gpr,
+          hipLaunchKernelGGL(quantize_masked_kernel<1>, grid, block, lds, stream, xs, ld, nrow,
+                             gpr,
                              mask, cs, ms, ks, (int)n_mask);
           break;
         case 2:
-          hipLaunchKernelGGL(quantize_masked_kernel<2>, grid, block, 0, stream, xs, ld, nrow, gpr,
+          hipLaunchKernelGGL(quantize_masked_kernel<2>, grid, block, lds, stream, xs, ld, nrow,
+                             gpr,
                              mask, cs, ms, ks, (int)n_mask);
           break;
         case 3:
-          hipLaunchKernelGGL(quantize_masked_kernel<3>, grid, block, 0, stream, xs, ld, nrow, gpr,
+          hipLaunchKernelGGL(quantize_masked_kernel<3>, grid, block, lds, stream, xs, ld, nrow,
+                             gpr,
                              mask, cs, ms, ks, (int)n_mask);
           break;
         default:
-          hipLaunchKernelGGL(quantize_masked_kernel<4>, grid, block, 0, stream, xs, ld, nrow, gpr,
+          hipLaunchKernelGGL(quantize_masked_kernel<4>, grid, block, lds, stream, xs, ld, nrow,
+                             gpr,
                              mask, cs, ms, ks, (int)n_mask);
           break;
       }

@@ -103,15 +103,32 @@ def test_quantize_with_mask_and_kept(hip):
         assert_same_quant(hip, bits, mask)
 
 
-@pytest.mark.parametrize("rows,k,n", [(3, 13824, 52), (5, 16448, 300), (2, 40960, 9),
-                                      (2, 65536, 655), (4, 1024, 1024)])
+@pytest.mark.parametrize("rows,k,n", [(3, 13824, 52), (2, 16384, 100), (5, 16448, 300),
+                                      (2, 40960, 9), (2, 65536, 655), (4, 1024, 1024)])
 def test_quantize_with_mask_wide_rows(hip, rows, k, n):
     """Masked rows of 1 to 4 rounds of the row-mapped masked kernel, with idle
-    lanes in the last wave (k / 16 not a multiple of 64), and a fully masked row."""
+    lanes in the last wave (k / 16 not a multiple of 64), the widest
+    single-round row (1024 items: the largest LDS stage), and a fully masked
+    row."""
     bits = uc.random_bits(rows * k // 64, seed=k + n).reshape(rows, k)
     r = np.random.default_rng(k)
     mask = np.zeros(k, np.uint8)
     mask[r.choice(k, size=n, replace=False)] = 1
+    assert_same_quant(hip, bits, mask)
+
+
+@pytest.mark.parametrize("dense", [63, 64, 65, 200])
+def test_quantize_with_mask_dense_and_sparse_waves(hip, dense):
+    """A wave whose items hold `dense` masked channels (the first 1024
+    channels: one wave's items) beside waves with a few: the kept values of
+    waves with at most 64 go through the wave's LDS stage, the others one
+    lane at a time, and the ranks run on across both."""
+    k = 5120
+    bits = uc.random_bits(9 * k // 64, seed=dense).reshape(9, k)
+    r = np.random.default_rng(dense)
+    mask = np.zeros(k, np.uint8)
+    mask[r.choice(1024, size=dense, replace=False)] = 1
+    mask[1024 + r.choice(k - 1024, size=40, replace=False)] = 1
     assert_same_quant(hip, bits, mask)
 
 
