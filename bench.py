@@ -430,6 +430,23 @@ def ceilings(torch, dev, stream):
                         "what": "v_mfma_f32_32x32x16_bf16 back to back from registers, 12,150 "
                                 "workgroups x 4 waves x 5184 MFMAs (the FFN-up launch's count)"}
     log(f"MFMA-only bf16: {tf:.0f} TFLOP/s")
+    del sink
+    # reference point: the vendor bf16 GEMM (torch.mm, hipBLASLt) at the FFN-up shape on plain
+    # bf16 operands (no HiF4 decode, no protected-channel residual)
+    m, n, k = 57600, 13824, 5120
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    x = torch.randn((m, k), device=dev, dtype=torch.bfloat16, generator=g)
+    w = torch.randn((n, k), device=dev, dtype=torch.bfloat16, generator=g)
+    vendor = {"shape": f"{m}x{n}x{k}",
+              "what": "torch.mm(X, W^T) on plain bf16 operands (hipBLASLt), same M, N, K as "
+                      "the W4A4 kernel's FFN-up launch"}
+    for name, kw in (("bf16_out", {}), ("fp32_out", {"out_dtype": torch.float32})):
+        ms_v, _ = rate(lambda: torch.mm(x, w.t(), **kw), 0.0, reps=5)
+        tf_v = 2.0 * m * n * k / (ms_v * 1e-3) / 1e12
+        vendor[name] = {"ms": ms_v, "TFLOP/s": tf_v}
+        log(f"vendor bf16 GEMM ({name}): {ms_v:.3f} ms, {tf_v:.0f} TFLOP/s")
+    out["vendor_gemm_bf16_ffn_up"] = vendor
     return out
 
 
