@@ -478,8 +478,12 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t* __restr
 // Blocks for a grid-stride launch over `threads` work items, at most `cap`.
 // Far more blocks than fit at once (2048 of 256 threads on 256 CUs): as
 // blocks retire, new ones land on whichever CUs are ahead, which balances
-// CUs and XCDs that stream at different rates (measured on the FFN-up
-// activation: 2048 blocks 175 us, 16384 blocks 143 us, 32768 blocks 139 us).
+// CUs and XCDs that stream at different rates. Measured for the unmasked
+// quantize (median of 20 calls, two runs on one box), FFN-up activation
+// 57600 x 5120 / FFN-down activation 57600 x 13824: 8192 blocks 158 / 451 us,
+// 32768 blocks 145 / 407 us, 131072 blocks 134-137 / 381-391 us, one item per
+// thread (72000 / 194400 blocks) 135-136 / 377-388 us; the quantize takes a
+// cap of 1024 blocks per CU, which leaves these shapes uncapped.
 static unsigned grid_for(uint64_t threads, uint64_t cap = 256ull * 128) {
   const uint64_t blocks = (threads + 255) / 256;
   return (unsigned)(blocks < cap ? (blocks ? blocks : 1) : cap);
@@ -540,8 +544,8 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
           break;
       }
     } else {
-      hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total)), dim3(256), 0, stream, xs, ld,
-                         gpr, fd, total, cs, ms);
+      hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total, 256ull * 1024)), dim3(256), 0,
+                         stream, xs, ld, gpr, fd, total, cs, ms);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
