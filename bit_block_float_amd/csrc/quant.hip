@@ -515,9 +515,12 @@ hipError_t hif4_launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int6
       const dim3 block((per + 63) / 64 * 64);
       // kept-value stage, and the keep masks with a single round
       const size_t lds = (size_t)block.x * 32 * (rounds == 1 ? 2 : 1);
-      // at least ~4 rows per workgroup (the mask prologue is paid per
-      // workgroup), at most 48 workgroups per CU
-      const int64_t want = std::min<int64_t>(256 * 48, (nr + 3) / 4);
+      // at least ~6 rows per workgroup (the mask prologue is paid per
+      // workgroup), at most 48 workgroups per CU. Measured on the FFN-up
+      // activation (57600 x 5120, 52 protected channels; two runs on one
+      // box): 1 row 235-242 us, 4 rows 157-162 us, 6 rows 153 us, 8 rows
+      // 153-154 us, 12 rows 157-159 us, 24 rows 168 us
+      const int64_t want = std::min<int64_t>(256 * 48, (nr + 5) / 6);
       const dim3 grid((unsigned)std::max<int64_t>(1, want));
       uint16_t* ks = kept ? kept + r0 * n_mask : nullptr;
       const uint32_t nrow = (uint32_t)nr;
