@@ -102,7 +102,9 @@ static size_t ws_resid(int64_t rows, int64_t nk) {
   return align256((size_t)rows * (size_t)resid_cols(nk) * 2);
 }
 size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t n_kept) {
+  // 0 for sizes no linear entry point accepts (so the sums below never wrap)
   if (m < 0 || n < 0 || k < 0 || n_kept < 0) return 0;
+  if (m >= (1ll << 31) || n >= (1ll << 31) || k >= (1ll << 31) || n_kept > 65536) return 0;
   return ws_x_codes(m, k) + ws_x_meta(m, k) + ws_w_deq(n, k) + ws_x_kept(m, n_kept) +
          ws_resid(m, n_kept) + ws_resid(n, n_kept);
 }
@@ -291,7 +293,8 @@ hif4_status hif4_linear_xcodes_wbf16_noalloc(const uint8_t* x_codes, const uint3
 }
 
 size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c) {
-  if (c < 0 || rows < 0) return 0;
+  // 0 beyond the entry point's limits (rows below 2^32, at most 65536 channels)
+  if (c < 0 || rows < 0 || rows > 0xFFFFFFFFll || c > 65536) return 0;
   return hif4_percentile_ws_bytes(rows, c);
 }
 
@@ -341,7 +344,7 @@ hif4_status hif4_quantize_offsets(const void* x, int64_t rows, int64_t k, int64_
 }
 
 size_t hif4_higptq_workspace_bytes(int64_t n) {
-  if (n < 0) return 0;
+  if (n < 0 || n >= (int64_t(1) << 24)) return 0;  // the entry point's row limit
   return align256((size_t)n * 64 * sizeof(float));
 }
 
@@ -367,7 +370,8 @@ hif4_status hif4_higptq_unit(float* w, int64_t n, int64_t k, int64_t ldw, const 
 }
 
 size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units) {
-  if (n < 0 || units < 1 || units > HIF4_HIGPTQ_MAX_BLOCK_UNITS) return 0;
+  if (n < 0 || n >= (int64_t(1) << 24) || units < 1 || units > HIF4_HIGPTQ_MAX_BLOCK_UNITS)
+    return 0;
   return align256((size_t)((n + 63) / 64 * 64) * 64 * (size_t)units * sizeof(float));
 }
 

@@ -125,7 +125,8 @@ HIF4_EXPORT hif4_status hif4_dequantize(const uint8_t *codes, const uint32_t *me
  * points need for an (m x k) activation, an (n x k) weight and n_kept
  * protected channels: hif4_linear_w4a4 needs (m, n, k, n_kept),
  * hif4_linear_xcodes_wbf16 needs (m, n, 0, n_kept) (0 when n_kept == 0).
- * Returns 0 for negative sizes.
+ * Returns 0 for sizes no linear entry point accepts: negative, m, n or k of
+ * 2^31 or more, or n_kept above 65536.
  */
 HIF4_EXPORT size_t hif4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t n_kept);
 
@@ -223,6 +224,8 @@ HIF4_EXPORT hif4_status hif4_linear_xcodes_wbf16_noalloc(const uint8_t *x_codes,
 /*
  * hif4_percentile_workspace_bytes -- workspace bytes for hif4_percentile_mask
  * over rows x c values (depends on rows from 8192 rows on; no device needed).
+ * Returns 0 beyond the entry point's limits: negative sizes, rows of 2^32 or
+ * more, c above 65536.
  */
 HIF4_EXPORT size_t hif4_percentile_workspace_bytes(int64_t rows, int64_t c);
 
@@ -307,7 +310,8 @@ HIF4_EXPORT hif4_status hif4_quantize_offsets(const void *x, int64_t rows, int64
                                   const float *koff, const float *moff, uint8_t *codes,
                                   uint32_t *meta, hipStream_t stream);
 
-/* hif4_higptq_workspace_bytes -- workspace of hif4_higptq_unit for n rows. */
+/* hif4_higptq_workspace_bytes -- workspace of hif4_higptq_unit for n rows
+ * (0 for n < 0 or n >= 2^24, which the entry point refuses). */
 HIF4_EXPORT size_t hif4_higptq_workspace_bytes(int64_t n);
 
 /*
@@ -355,7 +359,7 @@ HIF4_EXPORT hif4_status hif4_higptq_unit(float *w, int64_t n, int64_t k, int64_t
 
 /* hif4_higptq_block_workspace_bytes -- workspace of hif4_higptq_block for n
  * rows and a block of `units` groups: 256 units * ceil(n / 64) * 64 bytes
- * (0 for units outside 1..16). */
+ * (0 for units outside 1..16, n < 0 or n >= 2^24). */
 HIF4_EXPORT size_t hif4_higptq_block_workspace_bytes(int64_t n, int64_t units);
 
 /*
