@@ -274,8 +274,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 // Registers decide the occupancy of this HBM-streaming loop: with a single
 // round the items' keep masks (32 bytes per thread) live in LDS and are read
 // per item, which keeps the kernel at 8 waves per SIMD (measured on the
-// FFN-up activation, 57600 x 5120 with 52 protected channels: 171 us with
-// the per-lane loop and the masks in registers, 155-158 us this way).
+// FFN-up activation, 57600 x 5120 with 52 protected channels, at 4 rows per
+// workgroup: 171 us with the per-lane loop and the masks in registers,
+// 155-158 us this way).
 template <int kRounds>
 __global__ __launch_bounds__(1024) void quantize_masked_kernel(
     const uint16_t* __restrict__ x, int64_t ld, uint32_t rows, uint32_t items_per_row,
