@@ -60,6 +60,24 @@ __device__ __forceinline__ float inv_mant_lo(uint32_t m) {
   return __uint_as_float(select4(m, 0x00000000u, 0xB34CCCCDu, 0xB3AAAAABu, 0xB3DB6DB7u));
 }
 
+// Fast unsigned division by a runtime-invariant divisor, valid for n < 2^31
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994: q = (mulhi(n, m) + n) >> s).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 // DPP lane moves within a row of 16 lanes (gfx9 encodings).
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]

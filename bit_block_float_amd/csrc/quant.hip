@@ -23,24 +23,6 @@
 
 namespace hif4 {
 
-// Fast unsigned division by a runtime-invariant divisor, valid for n < 2^31
-// (Granlund & Montgomery, "Division by invariant integers using
-// multiplication", 1994: q = (mulhi(n, m) + n) >> s).
-struct FastDiv {
-  uint32_t d, m, s;
-};
-
-static FastDiv make_fastdiv(uint32_t d) {
-  uint32_t s = 0;
-  while ((1ull << s) < d) ++s;
-  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
-  return FastDiv{d, (uint32_t)m, s};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  return (__umulhi(n, f.m) + n) >> f.s;
-}
-
 // Max over the 4 lanes of an aligned quad (DPP quad_perm), and OR.
 __device__ __forceinline__ uint32_t max4_u32(uint32_t v) {
   v = max(v, dpp<kDppQuadXor1>(v));
