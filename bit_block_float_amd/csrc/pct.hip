@@ -870,7 +870,8 @@ __global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
 // count.
 constexpr int kSampCh = 64;
 constexpr int kSampStride = kSampCh + 1;
-constexpr int kSampWords = kSampCh * 256;  // one sample partial
+constexpr int kSampWords = kSampCh * 256;       // bins of one sample partial
+constexpr int kSampPartWords = kSampWords / 2;  // its words (u16 counts)
 
 __global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
     const uint16_t* __restrict__ x, int64_t rows_s, int c, int64_t ld, int parts,
@@ -949,9 +950,13 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
   }
   __syncthreads();
   // [channel][bin]: consecutive threads store consecutive bins of a channel
-  uint32_t* dst = samp + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSampWords;
-  for (int i = threadIdx.x; i < kSampWords; i += kPctThreads)
-    dst[i] = hist[(i & 255) * kSampStride + (i >> 8)];
+  // as u16 pairs (a part holds at most ~8192 sampled rows, so no count
+  // reaches 2^16): word w of a channel holds bins 2w (low) and 2w + 1 (high)
+  uint32_t* dst = samp + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kSampPartWords;
+  for (int i = threadIdx.x; i < kSampPartWords; i += kPctThreads) {
+    const int ch = i >> 7, w = i & 127;
+    dst[i] = hist[(2 * w) * kSampStride + ch] | (hist[(2 * w + 1) * kSampStride + ch] << 16);
+  }
 }
 
 constexpr int kPlaceThreads = 256;
@@ -964,14 +969,15 @@ __global__ __launch_bounds__(kPlaceThreads) void pct_place_kernel(
   const int ch = blockIdx.x * (kPlaceThreads / 64) + (threadIdx.x >> 6);
   if (ch >= c) return;  // the whole wave
   const int cblocks = (c + kSampCh - 1) / kSampCh;
-  const uint32_t* src = samp + (int64_t)(ch / kSampCh) * kSampWords + (ch % kSampCh) * 256 + 4 * lane;
+  const uint32_t* src =
+      samp + (int64_t)(ch / kSampCh) * kSampPartWords + (ch % kSampCh) * 128 + 2 * lane;
   uint32_t cnt[4] = {0u, 0u, 0u, 0u};
   for (int y = 0; y < parts; ++y) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)y * cblocks * kSampWords);
-    cnt[0] += v.x;
-    cnt[1] += v.y;
-    cnt[2] += v.z;
-    cnt[3] += v.w;
+    const uint2 v = *reinterpret_cast<const uint2*>(src + (int64_t)y * cblocks * kSampPartWords);
+    cnt[0] += v.x & 0xFFFFu;
+    cnt[1] += v.x >> 16;
+    cnt[2] += v.y & 0xFFFFu;
+    cnt[3] += v.y >> 16;
   }
   int64_t lo, hi;
   double f;
