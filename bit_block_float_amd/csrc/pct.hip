@@ -857,8 +857,9 @@ __global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
 // The window path's first two kernels. pct_sample_kernel: workgroup (x, y)
 // reads part y of the sampled rows (every S-th row; the parts are equal
 // contiguous runs) for the block of 64 channels x, and stores its coarse
-// histogram (key >> 7, u32) as sample partial (y, x), [channel][bin], with
-// plain stores: no atomics across workgroups and nothing to clear beforehand.
+// histogram (key >> 7; u32 in LDS, u16 pairs in the partial) as sample
+// partial (y, x), [channel][bin], with plain stores: no atomics across
+// workgroups and nothing to clear beforehand.
 // Lanes read 16 bytes (channels 8p .. 8p+7, p = lane & 7), 8 lanes per row, so
 // a wave's load covers one 128-byte piece of each of 8 rows. In LDS the
 // histogram is [bin][channel] with a row stride of 65 words, so the 8 rows of
