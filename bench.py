@@ -412,6 +412,26 @@ def ceilings(torch, dev, stream):
                     "what": "grid-stride read of 2 GiB, 16-byte non-temporal loads, four in "
                             "flight per lane (libhif4_probe.so)"}
     out["hbm_read"] = best
+    lib.hif4_probe_read4_write1.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]
+    lib.hif4_probe_read4_write1.restype = ctypes.c_int
+    best = None
+    for blocks in (4096, 16384, 65536, nbytes // 64 // 256):
+        def rw():
+            st = lib.hif4_probe_read4_write1(ctypes.c_void_p(a.data_ptr()), nbytes,
+                                             ctypes.c_void_p(b.data_ptr()), blocks,
+                                             ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"hif4_probe_read4_write1: status {st}")
+        ms, gbs = rate(rw, nbytes + nbytes // 4)
+        log(f"HBM read 4 : write 1 (probe, {blocks} workgroups): {gbs:.0f} GB/s")
+        if best is None or gbs > best["GB/s"]:
+            best = {"bytes": nbytes + nbytes // 4, "ms": ms, "GB/s": gbs,
+                    "frac_hbm": gbs / HBM_PEAK_GBS, "workgroups": blocks,
+                    "what": "2 GiB read + 0.5 GiB written, four 16-byte non-temporal loads (one "
+                            "from each quarter of the source) and one store per lane (the "
+                            "quantizer's mix; libhif4_probe.so)"}
+    out["hbm_read4_write1"] = best
     del a, b
     blocks, iters = 12150, 324  # the FFN-up launch: 12,150 tiles x 4 waves x 5184 MFMAs
     sink = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)

@@ -2,12 +2,14 @@
 // against; not part of the method and not in libhif4.so (built as
 // libhif4_probe.so, declared in include/hif4_probe.h).
 //
-// Two probes. The bf16 matrix-core ceiling under a full-chip load: every wave issues
-// back-to-back v_mfma_f32_32x32x16_bf16 on 16 independent accumulator blocks
-// (the W4A4 kernel's 128 x 128 wave tile, one wave per SIMD, four waves per
-// workgroup), with register operands only -- no memory traffic, no LDS, no
-// other VALU work in the loop. Its rate is what the contraction could reach
-// at the clock the chip holds under that load.
+// Probes: HBM streaming rates (copy, read only, and the quantizer's 4 : 1
+// read : write mix) and the bf16 matrix-core ceiling under a full-chip load.
+// For the latter every wave issues back-to-back v_mfma_f32_32x32x16_bf16 on
+// 16 independent accumulator blocks (the W4A4 kernel's 128 x 128 wave tile,
+// one wave per SIMD, four waves per workgroup), with register operands only
+// -- no memory traffic, no LDS, no other VALU work in the loop. Its rate is
+// what the contraction could reach at the clock the chip holds under that
+// load.
 #include <hip/hip_runtime.h>
 
 #include "../../include/hif4_probe.h"
@@ -85,7 +87,33 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restri
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Streaming ceiling with the quantizer's traffic mix: per lane four 16-byte
+// loads and one 16-byte store (4 bytes read for each one written; the
+// quantizer reads 2 bytes per element and writes 0.5625), grid-stride. The
+// source is read as four contiguous quarters, so that every load
+// instruction covers 1 KiB of consecutive words, as the store does.
+__global__ __launch_bounds__(256) void read4_write1_probe_kernel(const u32x4_t* __restrict__ src,
+                                                                 u32x4_t* __restrict__ dst,
+                                                                 size_t n_out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += stride) {
+    const u32x4_t a = __builtin_nontemporal_load(src + i);
+    const u32x4_t b = __builtin_nontemporal_load(src + n_out + i);
+    const u32x4_t c = __builtin_nontemporal_load(src + 2 * n_out + i);
+    const u32x4_t d = __builtin_nontemporal_load(src + 3 * n_out + i);
+    __builtin_nontemporal_store(a ^ b ^ c ^ d, dst + i);
+  }
+}
+
 }  // namespace
+
+extern "C" int hif4_probe_read4_write1(const void* src, size_t src_bytes, void* dst, int blocks,
+                                       hipStream_t stream) {
+  if (!src || !dst || src_bytes % 64 != 0 || blocks <= 0) return 1;
+  hipLaunchKernelGGL(read4_write1_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const u32x4_t*)src, (u32x4_t*)dst, src_bytes / 64);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
 
 extern "C" int hif4_probe_read(const void* src, size_t bytes, void* out, int blocks,
                                hipStream_t stream) {

@@ -44,6 +44,20 @@ __attribute__((visibility("default"))) int hif4_probe_copy(const void *src, void
 __attribute__((visibility("default"))) int hif4_probe_read(const void *src, size_t bytes, void *out,
                                                             int blocks, hipStream_t stream);
 
+/*
+ * hif4_probe_read4_write1 -- the achievable HBM rate for the quantizer's
+ * traffic mix: reads `src_bytes` (a multiple of 64) of src and writes
+ * src_bytes / 4 to dst (device buffers, not overlapping): lane i loads word
+ * i of each quarter of src (16-byte non-temporal loads) and stores their XOR
+ * to word i of dst, with a grid-stride kernel of `blocks` workgroups of 256
+ * threads.
+ * Returns 0, 1 for a bad argument, 7 if the launch failed.
+ */
+__attribute__((visibility("default"))) int hif4_probe_read4_write1(const void *src,
+                                                                    size_t src_bytes, void *dst,
+                                                                    int blocks,
+                                                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
