@@ -55,6 +55,24 @@ def test_library_exports_exactly_the_declared_symbols(L):
         assert hasattr(L, s)
 
 
+def test_probe_library_exports_exactly_its_header():
+    """libhif4_probe.so (the measurement probes bench.py --ceilings runs)
+    exports exactly the functions include/hif4_probe.h declares."""
+    probe = os.path.join(ROOT, "bit_block_float_amd", "libhif4_probe.so")
+    if not os.path.exists(probe):
+        from bit_block_float_amd import build
+        build.build_probe()
+    text = open(os.path.join(ROOT, "include", "hif4_probe.h"), encoding="utf-8").read()
+    want = set(re.findall(r'visibility\("default"\)\)\s+int\s+(hif4_probe_\w+)\s*\(', text))
+    assert want >= {"hif4_probe_mfma_bf16", "hif4_probe_copy", "hif4_probe_read",
+                    "hif4_probe_read4_write1"}
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True,
+                         check=True).stdout
+    got = {line.split()[-1] for line in out.splitlines()
+           if " T " in line and line.split()[-1].startswith("hif4_")}
+    assert got == want
+
+
 def test_version_and_status_strings(L):
     assert L.hif4_version() == 1
     for s in range(10):
