@@ -63,7 +63,7 @@ def test_probe_library_exports_exactly_its_header():
         from bit_block_float_amd import build
         build.build_probe()
     text = open(os.path.join(ROOT, "include", "hif4_probe.h"), encoding="utf-8").read()
-    want = set(re.findall(r'visibility\("default"\)\)\s+int\s+(hif4_probe_\w+)\s*\(', text))
+    want = set(re.findall(r'visibility\("default"\)\)\)\s+int\s+(hif4_probe_\w+)\s*\(', text))
     assert want >= {"hif4_probe_mfma_bf16", "hif4_probe_copy", "hif4_probe_read",
                     "hif4_probe_read4_write1"}
     out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True,
