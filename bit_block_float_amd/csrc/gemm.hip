@@ -12,15 +12,15 @@
 // inside the MFMA. The per-unit level-1 scales are therefore already inside
 // the operands: no per-unit rescale is needed in the K loop.
 //
-// Tiling: 256x256 output tile per workgroup (4 waves, 2x2, each 128x128 =
-// 4x4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane in
-// AGPRs), one workgroup per CU. Two schedules share this design: steps of
-// one HiF4 unit (64 K values, one barrier per step) when K is a multiple of
-// 256 (gemm_w4a4_u64_kernel), else steps of half a unit
-// (gemm_w4a4_kernel); both issue the MFMAs of an output block in the same
-// K order, so they give the same bits. Operands reach LDS by direct-to-LDS buffer
-// DMA (buffer_load ... lds): no VGPR staging, the K offset rides in an SGPR,
-// rows past M / N read as zero through the buffer range check.
+// Tiling: 256x256 output tile per workgroup, 4 waves, v_mfma_f32_32x32x16_bf16,
+// 256 fp32 accumulators per lane in AGPRs, one workgroup per CU. Two kernels:
+// gemm_w4a4_rd_kernel (K a multiple of 256, 16-byte meta rows: every
+// workload here) steps one HiF4 unit (64 K values) per barrier, with the
+// waves splitting the tile by rows and each lane decoding its A fragments
+// straight into registers; gemm_w4a4_kernel (any other K) steps half a unit
+// with a 2x2 wave split and the activation decoded once into an LDS tile.
+// Operands reach LDS by direct-to-LDS buffer DMA (buffer_load ... lds): no
+// VGPR staging, rows past M / N read as zero through the buffer range check.
 //
 // LDS rows of bf16 operands are 64 B (32 K values) = 4 chunks of 16 B; chunk
 // c of row r sits in slot c ^ ((r >> 2) & 3). gfx950's LDS serves a 16-byte
@@ -134,9 +134,9 @@ __device__ __forceinline__ uint2 decode_quad(uint32_t nib, uint4 t) {
                     __builtin_amdgcn_perm(hib, lob, 0x07030602u));
 }
 
-// This 32-wide schedule serves the shapes the unit-step kernel below does
-// not take (K not a multiple of 256, or meta rows not 16-byte aligned): a
-// unit quad of meta is four 4-byte loads per row, one per unit.
+// This 32-wide schedule serves the shapes the register-decoded kernel below
+// does not take (K not a multiple of 256, or meta rows not 16-byte aligned):
+// a unit quad of meta is four 4-byte loads per row, one per unit.
 //
 // kResid: protected channels ([TA-method]: kept in high precision). Xr [M][KR]
 // and Wr [N][KR] hold their bf16 values, zero-padded to KR (a multiple of
@@ -582,51 +582,106 @@ void gemm_w4a4_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restric
   }
 }
 
-// ---------------------------------------------------------------------------
-// The same contraction in steps of one HiF4 unit (64 K values): four 16-wide
-// MFMA K-chunks per step and ONE barrier per step (half the barriers and
-// waits of the 32-wide schedule). Needs K % 256 == 0 and 16-byte meta rows.
-//
-// LDS map (bytes):
-//   [0, 64K)       B ring: 2 stages x 256 rows x 128 B, chunk c (16 B) of row
-//                  r in slot c ^ ((r >> 1) & 7)
-//   [64K, 128K)    decoded A: 2 buffers x 256 rows x 128 B (same swizzle)
-//   [128K, 152K)   A code ring: 3 slots x 256 rows x 32 B, chunk c of row r in
-//                  slot c ^ ((r >> 3) & 1)
-//   [152K, 156K)   A meta: 1 slot, 256 rows x 16 B (4 units)
-//   [156K, +256)   decode table
-// Step u: loops L0..L2 run the MFMAs of chunks 0..2 of stage u while unit
-// u+1 is decoded into the other buffer; then s_waitcnt vmcnt(0) +
-// lgkmcnt(0) + barrier; L3 runs chunk 3 while the chunk-0 fragments of
-// stage u+1 load, B stage u+2 and the codes of unit u+3 go out (and, every
-// fourth step, the next meta quad), and unit u+2 is read and prepared.
-// Ring reuse after the barrier of step u: B slot u&1 and decoded buffer u&1
-// (stage / unit u, last read before the barrier), code slot u%3 (unit u,
-// read in step u-2), the meta slot (its quad's last unit was read in this
-// step's L3 before the next quad is issued, behind an lgkmcnt(0)).
+// bf16 operand rows of one HiF4 unit (64 K values) in LDS
 constexpr int kRowBytes2 = 128;
 constexpr int kTileBytes2 = 256 * kRowBytes2;              // 32 KiB
-constexpr int kL2B = 0;
-constexpr int kL2X = 2 * kTileBytes2;                      // 65536
-constexpr int kL2C = 4 * kTileBytes2;                      // 131072
-constexpr int kCodeSlot2 = 256 * 32;                       // 8192
-constexpr int kL2M = kL2C + 3 * kCodeSlot2;                // 155648
-constexpr int kL2T = kL2M + 256 * 16;                      // 159744
-constexpr int kLds2Bytes = kL2T + 16 * 16;                 // 160000
+
+// ---------------------------------------------------------------------------
+// The unit-step contraction with the activation decoded straight into the
+// MFMA's operand registers (K % 256 == 0, 16-byte meta rows).
+//
+// The four waves split the 256x256 tile by rows: wave w owns rows
+// 64w..64w+63 and all 256 columns (2 x 8 blocks of 32x32, the same 256 fp32
+// accumulators per lane). No wave then needs another wave's A rows, so each
+// lane decodes its own A fragments from HiF4 into the registers the MFMA
+// reads: the decoded tile is neither written to nor read back from LDS, and
+// the decode is not tied to the step barrier. B fragments are read from LDS
+// as before (8 per K-chunk per wave instead of 4 A + 4 B).
+//
+// K order: in unit u, lane half h (lanes 32h..32h+31) supplies K values
+// 64u + 32h + 8s .. +7 of MFMA K-chunk s, for both operands. Every
+// assignment of K values to chunks gives the same sum up to the order of the
+// fp32 roundings; this one makes a lane's codes for the four chunks of a
+// unit one 16-byte run of its row (code word 4h + s = level-2 group 4h + s).
+//
+// Table addressing: for a row and unit the lane precomputes, per quad it
+// decodes, the byte offset 64m + 16(p + E) of its table entry (E = e2 + e3
+// of the quad); these 8 offsets (each <= 240) sit in the bytes of two words,
+// so a quad's entry address is one byte extract. The table lives at LDS
+// address 0 for that reason.
+//
+// LDS map (bytes):
+//   [0, 256)          decode table, entry (m, s) at 64m + 16s
+//   [256, +64K)       B ring: 2 stages x 256 rows x 128 B, chunk c of row r in
+//                     slot c ^ ((r >> 1) & 7)
+//   [65792, +64K)     code ring: 2 groups of 4 units x 256 rows x 128 B, chunk
+//                     c (= 2 x unit-in-group + half) of row r in slot
+//                     c ^ ((r >> 1) & 7)
+//   [131328, +8K)     meta ring: 2 slots x 256 rows x 16 B (4 units each)
+// Codes, meta and the table entries a lane reads are its own wave's rows,
+// fetched by its own wave: those reads need the wave's own vmcnt only.
+// Codes are fetched four units (one 128-byte line) per row, 8 rows per DMA
+// instruction: the cost of a DMA instruction grows with the cache lines it
+// touches, and one unit per row (32 rows of 32 B per instruction) made the
+// code fetch cost as much as the eight times larger B fetch.
+//
+// Step u (one unit, 64 MFMAs per wave, one barrier):
+//   L0  chunk 0 of unit u; B chunk-1 fragments; decode A(u) chunk 3;
+//       table entries for A(u+1) chunk 0 (decode halves in the even MFMA
+//       slots, table reads in the odd ones, so that at most ~6 VALU ops sit
+//       between two MFMAs)
+//   L1  chunk 1; B chunk 2; decode A(u+1) chunk 0; entries for chunk 1
+//   L2  chunk 2; B chunk 3; decode A(u+1) chunk 1; entries for chunk 2
+//   s_waitcnt vmcnt(0 or 1) + lgkmcnt(0) + barrier
+//   L3  chunk 3; B chunk-0 fragments of stage u+1; decode A(u+1) chunk 2;
+//       entries for chunk 3; codes + meta of unit u+2 read and prepared;
+//       DMA: B stage u+2, a quarter of code group (u+6)/4 (parts
+//       2((u+2)%4), +1 of 8), (u % 4 == 2) meta quad (u+6)/4
+// A chunk s of unit u+1 overwrites chunk s of unit u once the MFMAs that
+// read it have issued, so one set of A registers serves (32 VGPRs).
+// Ring reuse: B slot u&1 held stage u (last read in L2 of step u, before the
+// barrier); code group g = (u+6)/4 goes to slot g&1, which held group g-2,
+// whose last unit 4g-5 was read in step 4g-7 (the group's parts go out in
+// steps 4g-6 .. 4g-3, and unit 4g is first read in step 4g-2); meta slot
+// q&1 held quad q-2, whose last unit was read in step 4q-7.
+// vmcnt: at the barrier of step u, B stage u+1 and the codes of unit u+2
+// (all issued by step u-1) must be in; only a meta quad issued in step u-1
+// (u % 4 == 3, issued last) may still be in flight: vmcnt(1), else vmcnt(0).
+// In the last steps the B DMA of stages past K reads clamped data into slots
+// no one reads; with protected channels the two such DMAs of the last two
+// steps fetch the first 64 residual columns of Wr and Xr into slots 0 and 1.
+constexpr int kRdT = 0;
+constexpr int kRdB = 256;
+constexpr int kRdC = kRdB + 2 * kTileBytes2;       // 65792
+constexpr int kRdCodeGroup = 256 * 128;            // 4 units x 256 rows
+constexpr int kRdM = kRdC + 2 * kRdCodeGroup;      // 131328
+constexpr int kRdBytes = kRdM + 2 * 256 * 16;      // 139520
+
+// bits 0..3 of x -> the low bit of bytes 0..3 (the partial products of the
+// multiply land on disjoint bits, so nothing carries)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  return ((x & 15u) * 0x204081u) & 0x01010101u;
+}
+// bit 0 of x -> bytes 0 and 1, bit 1 -> bytes 2 and 3
+__device__ __forceinline__ uint32_t spread2x2(uint32_t x) {
+  return ((x & 3u) * 0x808101u) & 0x01010101u;
+}
+
+__device__ __forceinline__ u32x4_t lds_v4(const char* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
 
 template <bool kResid>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
-                          const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
-                          const uint16_t* __restrict__ B, int M, int N, int K,
-                          void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLds2Bytes];
+void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
+                         const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
+                         const uint16_t* __restrict__ B, int M, int N, int K,
+                         void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[kRdBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave-uniform: the DMA destinations (M0) then come from scalar arithmetic
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
 
   const int ntiles = tiles_m * tiles_n;
   int t = blockIdx.x;
@@ -644,7 +699,7 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // decode table: entry (m, s = E + p) at 16 (4m + s)
+  // decode table: entry (m, s = E + p) at 64m + 16s
   if (tid < 16) {
     const int m = tid >> 2, sx = tid & 3;
     const float d = ldexpf(1.0f + 0.25f * (float)m, sx - 33);
@@ -662,7 +717,7 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
       }
     }
     const u32x4_t v = {lo0, lo1, hi0, hi1};
-    *reinterpret_cast<u32x4_t*>(lds + kL2T + 16 * tid) = v;
+    *reinterpret_cast<u32x4_t*>(lds + kRdT + 16 * tid) = v;
   }
 
   const __amdgpu_buffer_rsrc_t rsAc =
@@ -679,307 +734,355 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
     const uint32_t r = (uint32_t)(wave * 64 + 8 * i + (lane >> 3));
     voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 8u)) * 2u;
   }
-  // codes: wave w rows 64w.., 2 x 1 KiB (32 rows each); lane l -> row 32i + (l >> 1),
-  // slot l & 1 holding chunk (l & 1) ^ ((row >> 3) & 1) of the row's unit
+  // codes: a group of 4 units of wave w's rows 64w.. is 8 x 1 KiB (8 rows of
+  // 128 B each); part p: lane l -> row 8p + (l >> 3), slot l & 7 holding chunk
+  // (l & 7) ^ ((row >> 1) & 7). The swizzle depends on p only through p & 1.
   uint32_t voffC[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t r = (uint32_t)(wave * 64 + 32 * i + (lane >> 1));
-    voffC[i] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (((uint32_t)(lane & 1) ^ ((r >> 3) & 1u)) * 16u);
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t r = (uint32_t)(wave * 64 + 8 * e + (lane >> 3));
+    voffC[e] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 16u);
   }
   const uint32_t KU = (uint32_t)(K / 64);
   const uint32_t voffM = (uint32_t)(m0 + wave * 64 + lane) * KU * 4u;
   const int KUi = K / 64;
 
   auto dma_b = [&](int st, int i) {  // part i of B stage min(st, KU-1) into slot st & 1
-    char* dst = lds + kL2B + (st & 1) * kTileBytes2 + wave * 64 * kRowBytes2 + i * 1024;
+    char* dst = lds + kRdB + (st & 1) * kTileBytes2 + wave * 64 * kRowBytes2 + i * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)dst, 16, voffB[i],
                                              min(st, KUi - 1) * kRowBytes2, 0, 0);
   };
-  auto dma_codes = [&](int un, int i) {  // part i of unit un's codes into slot un % 3
-    char* dst = lds + kL2C + (un % 3) * kCodeSlot2 + wave * 2048 + i * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAc, (lds_void_t*)dst, 16,
-                                             voffC[i] + (uint32_t)un * 32u, 0, 0, 0);
+  // part p of code group g (units 4g..4g+3) into slot g & 1; the whole offset
+  // rides in the range-checked vector offset (rows past M and bytes past the
+  // end read zeros)
+  auto dma_codes = [&](int g, int p) {
+    char* dst = lds + kRdC + (g & 1) * kRdCodeGroup + wave * 8192 + p * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsAc, (lds_void_t*)dst, 16,
+        voffC[p & 1] + (uint32_t)(p & ~1) * 8u * (uint32_t)(K / 2) + (uint32_t)g * 128u, 0, 0, 0);
   };
-  auto dma_meta = [&](int q) {  // units 4q..4q+3, 16 B per row
-    char* dst = lds + kL2M + wave * 1024;
+  auto dma_meta = [&](int q) {  // units 4q..4q+3, 16 B per row, into slot q & 1
+    char* dst = lds + kRdM + (q & 1) * 4096 + wave * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)dst, 16,
                                              voffM + (uint32_t)q * 16u, 0, 0, 0);
   };
-  // residual chunk c: Wr columns 64c.. into B slot 0, Xr columns 64c.. into
-  // decoded buffer 0, both with the stage swizzle; rows past M / N read zeros
-  auto dma_resid = [&](int c, bool is_x, int i) {
+  // residual chunk c: Wr (is_x false) or Xr columns 64c.. into B slot `slot`,
+  // with the stage swizzle; rows past M / N read zeros
+  auto dma_resid = [&](int c, bool is_x, int i, int slot) {
     const uint32_t r = (uint32_t)(wave * 64 + 8 * i + (lane >> 3));
     const uint32_t row = (uint32_t)((is_x ? m0 : n0)) + r;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(is_x ? (const void*)Xr : (const void*)Wr), (short)0, (is_x ? M : N) * KR * 2,
         kRsrcWord3);
-    char* dst = lds + (is_x ? kL2X : kL2B) + wave * 64 * kRowBytes2 + i * 1024;
+    char* dst = lds + kRdB + slot * kTileBytes2 + wave * 64 * kRowBytes2 + i * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (lds_void_t*)dst, 16,
         row * (uint32_t)(KR * 2) + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 16u),
         c * 128, 0, 0);
   };
 
-  // ---- decode state: thread tid decodes row tid of unit un
-  const int csw = (tid >> 3) & 1;  // code chunk swizzle of this row
-  const int xsw = (tid >> 1) & 7;  // decoded-row chunk swizzle of this row
-  uint32_t dmw = 0;
-  uint4 dca = make_uint4(0, 0, 0, 0), dcb = make_uint4(0, 0, 0, 0);  // code words 0-3, 4-7
-  uint4 t8[8];
-  const char* dbase = lds;
-  uint32_t dd = 0, dd0 = 0;
-  uint2 dq0 = make_uint2(0, 0);
-  auto dec_in = [&](int un) {
-    dmw = *reinterpret_cast<const uint32_t*>(lds + kL2M + tid * 16 + (un & 3) * 4);
-    const char* cs = lds + kL2C + (un % 3) * kCodeSlot2 + tid * 32;
-    // no masking of units past K: K % 256 == 0 leaves no padding steps, and
-    // the only such units (decoded in the last two steps) are never read by
-    // an MFMA; using the words only at their consumers keeps this read off
-    // the critical path
-    dca = lds_u32x4(cs + ((0 ^ csw) * 16));
-    dcb = lds_u32x4(cs + ((1 ^ csw) * 16));
+  // ---- per-lane constants: row 64*wave + 32*rb + r32 of the tile, K half hh
+  const uint32_t r32 = (uint32_t)(lane & 31), hh = (uint32_t)(lane >> 5);
+  const uint32_t fsw = (r32 >> 1) & 7u;
+  // fragment address of K-chunk s for lane row r32 (slot and column block
+  // in the DS offset field)
+  uint32_t fbo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    fbo[s] = (uint32_t)kRdB + r32 * kRowBytes2 + (((4u * hh + (uint32_t)s) ^ fsw) << 4);
+  // code run of unit j (0..3) of a group for lane row r32, half hh
+  uint32_t cb4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    cb4[j] = (uint32_t)kRdC + ((uint32_t)wave * 64u + r32) * 128u +
+             (((2u * (uint32_t)j + hh) ^ fsw) << 4);
+  const uint32_t mbase = (uint32_t)kRdM + ((uint32_t)wave * 64u + r32) * 16u;
+  const uint32_t sh2 = 8u + 4u * hh, sh3 = 16u + 8u * hh;
+
+  auto fragB = [&](int slot, int s, int cb) -> bf16x8_t {
+    const uint32_t a = fbo[s] + (uint32_t)((slot & 1) * kTileBytes2 + cb * 32 * kRowBytes2);
+    return *reinterpret_cast<const bf16x8_t*>(lds + a);
   };
-  auto dec_unit = [&]() {
-    const uint32_t c = dmw & 255u;
-    const uint32_t a = c >> 3, p = (c >> 2) & 1u, m = c & 3u;
-    dbase = lds + kL2T + (m * 4u + p) * 16u;
-    dd = __builtin_amdgcn_perm(a, a, 0u);
-    dd0 = dd & 0xFFFFFF00u;
-  };
-  // table entry of quad q (0..15) into t8[q & 7]
-  auto dec_tab = [&](int q) {
-    const int g = q >> 1;
-    const uint32_t E = ((dmw >> (8 + g)) & 1u) + ((dmw >> (16 + q)) & 1u);
-    t8[q & 7] = lds_u32x4(dbase + 16 * E);
-  };
-  uint32_t qlo = 0, qhi = 0, qnib = 0;
-  auto dec_quad_a = [&](int q) {
-    const uint32_t words[8] = {dca.x, dca.y, dca.z, dca.w, dcb.x, dcb.y, dcb.z, dcb.w};
-    qnib = words[q >> 1] >> (4 * (q & 1));
-    uint4 tq = t8[q & 7];
-    tq.z += dd0;
-    tq.w += dd;
-    const uint32_t sel = qnib & 0x07070707u;
-    qlo = __builtin_amdgcn_perm(tq.y, tq.x, sel);
-    qhi = __builtin_amdgcn_perm(tq.w, tq.z, sel);
-  };
-  auto dec_quad_b = [&](int un, int q) {  // the second quad of a pair writes chunk q >> 1
-    const uint32_t hib = qhi | ((qnib << 4) & 0x80808080u);
-    const uint2 v = make_uint2(__builtin_amdgcn_perm(hib, qlo, 0x05010400u),
-                               __builtin_amdgcn_perm(hib, qlo, 0x07030602u));
-    if ((q & 1) == 0) {
-      dq0 = v;
-    } else {
-      char* dst = lds + kL2X + (un & 1) * kTileBytes2 + tid * kRowBytes2;
-      const u32x4_t w = {dq0.x, dq0.y, v.x, v.y};
-      *reinterpret_cast<u32x4_t*>(dst + (((q >> 1) ^ xsw) * 16)) = w;
+
+  // ---- decode state, two sets (unit parity): meta word, code run, per-quad
+  // table offsets, exponent add for the high plane
+  uint32_t mw[2][2];
+  u32x4_t cw[2][2];
+  uint32_t ew[2][2][2], dd[2][2], dd0[2][2];
+  u32x4_t tq[8];
+  u32x4_t fa[2][4];
+  uint32_t qlo = 0, qhi = 0;
+
+  // unit un's meta and codes into set S; j = un & 3 (a compile-time constant)
+  auto dec_in = [&](int un, int S, int j) {
+    const uint32_t msl = (uint32_t)((un >> 2) & 1) * 4096u + (uint32_t)j * 4u;
+    const uint32_t csl = cb4[j] + (uint32_t)((un >> 2) & 1) * (uint32_t)kRdCodeGroup;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      mw[S][rb] = *reinterpret_cast<const uint32_t*>(lds + mbase + msl + rb * 512);
+      cw[S][rb] = lds_v4(lds + csl + rb * 4096);
     }
   };
+  auto dec_unit0 = [&](int S, int rb) {  // offsets of quads 0..3
+    const uint32_t w = mw[S][rb];
+    const uint32_t base = ((w & 3u) << 6) | ((w & 4u) << 2);  // 64m + 16p
+    const uint32_t base4 = __builtin_amdgcn_perm(base, base, 0u);  // in all four bytes
+    const uint32_t e2 = w >> sh2, e3 = w >> sh3;
+    ew[S][rb][0] = ((spread2x2(e2) + spread4(e3)) << 4) + base4;
+    ew[S][rb][1] = base4;
+  };
+  auto dec_unit1 = [&](int S, int rb) {  // offsets of quads 4..7, exponent add
+    const uint32_t w = mw[S][rb];
+    const uint32_t e2 = w >> sh2, e3 = w >> sh3;
+    ew[S][rb][1] += (spread2x2(e2 >> 2) + spread4(e3 >> 4)) << 4;
+    const uint32_t a = (w & 255u) >> 3;
+    dd[S][rb] = __builtin_amdgcn_perm(a, a, 0u);
+    dd0[S][rb] = dd[S][rb] & 0xFFFFFF00u;
+  };
+  // table entry of quad j (0..7) of row block rb, set S, into tq[slot]
+  auto tab = [&](int S, int rb, int j, int slot) {
+    const uint32_t off = (ew[S][rb][j >> 2] >> (8 * (j & 3))) & 255u;
+    tq[slot] = lds_v4(lds + kRdT + off);
+  };
+  // quad j (even: low nibbles of code word j/2, odd: high nibbles), two halves
+  auto dq_a = [&](int S, int rb, int j, int slot) {
+    const uint32_t word = cw[S][rb][j >> 1];
+    const uint32_t sel = ((j & 1) ? (word >> 4) : word) & 0x07070707u;
+    const u32x4_t tv = tq[slot];
+    qlo = __builtin_amdgcn_perm(tv.y, tv.x, sel);
+    qhi = __builtin_amdgcn_perm(tv.w + dd[S][rb], tv.z + dd0[S][rb], sel);
+  };
+  auto dq_b = [&](int S, int rb, int j) {
+    const uint32_t word = cw[S][rb][j >> 1];
+    const uint32_t hib = qhi | (((j & 1) ? word : (word << 4)) & 0x80808080u);
+    const uint32_t v0 = __builtin_amdgcn_perm(hib, qlo, 0x05010400u);
+    const uint32_t v1 = __builtin_amdgcn_perm(hib, qlo, 0x07030602u);
+    const int s = j >> 1;
+    if (j & 1) {
+      fa[rb][s].z = v0;
+      fa[rb][s].w = v1;
+    } else {
+      fa[rb][s].x = v0;
+      fa[rb][s].y = v1;
+    }
+  };
+  // half i (0..7) of the decode of chunk s of set S: quad (rb, j) =
+  // (i >> 2, 2s + ((i >> 1) & 1)), first or second half; entries in tq[tb..tb+3]
+  auto dec_half = [&](int S, int s, int tb, int i) {
+    const int rb = i >> 2, jj = (i >> 1) & 1;
+    if ((i & 1) == 0) dq_a(S, rb, 2 * s + jj, tb + rb * 2 + jj);
+    else dq_b(S, rb, 2 * s + jj);
+  };
+  // table entry i (0..3) for chunk s of set S into tq[tb + i]
+  auto tab_chunk = [&](int S, int s, int tb, int i) {
+    const int rb = i >> 1, jj = i & 1;
+    tab(S, rb, 2 * s + jj, tb + i);
+  };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) fa[rb][s] = u32x4_t{0u, 0u, 0u, 0u};
 
-  const int frow = lane & 31;
-  const int fsw = (frow >> 1) & 7;
-  const int fhalf = lane >> 5;
-  // fragment f of K-chunk s (0..3) of stage/unit st: f < 4 -> A rows wm*128 + 32f,
-  // else B rows wn*128 + 32(f-4); slot parity st & 1
-  auto frag = [&](int st, int s, int f) {
-    const char* p = f < 4
-        ? lds + kL2X + (st & 1) * kTileBytes2 + (wm * 128 + f * 32 + frow) * kRowBytes2
-        : lds + kL2B + (st & 1) * kTileBytes2 + (wn * 128 + (f - 4) * 32 + frow) * kRowBytes2;
-    return *reinterpret_cast<const bf16x8_t*>(p + (((2 * s + fhalf) ^ fsw) * 16));
+  bf16x8_t fb0[8], fb1[8];
+  auto mfma = [&](int c, int s, const bf16x8_t* fb) {
+    const int rb = c >> 3, cb = c & 7;
+    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8_t, fa[rb][s]), fb[cb], acc[rb][cb], 0, 0, 0);
   };
-  bf16x8_t f0[8], f1[8];
 
-  // ---- prologue: B stages 0, 1; codes of units 0..2; meta quad 0; unit 0
-  // decoded; unit 1 read and its first table entries in flight; chunk-0
-  // fragments of stage 0.
+  // ---- prologue: meta quads 0 and 1, code group 0, B stages 0 and 1, and
+  // the parts 0..3 of code group 1 that steps -2 and -1 would have issued
+  // (parts 4..7 follow in steps 0 and 1)
+  dma_meta(0);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) dma_codes(0, p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma_b(0, i);
+  dma_meta(1);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma_b(1, i);
 #pragma unroll
-  for (int un = 0; un < 3; ++un) {
-    dma_codes(un, 0);
-    dma_codes(un, 1);
-  }
-  dma_meta(0);
-  wait_vmcnt0();
-  __syncthreads();  // table + every wave's loads visible
-  dec_in(0);
-  dec_unit();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dec_tab(8 * h + q);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      dec_quad_a(8 * h + q);
-      dec_quad_b(0, 8 * h + q);
-    }
-  }
-  dec_in(1);
-  dec_unit();
-  dec_tab(0);
-  dec_tab(1);
-  dec_tab(2);
+  for (int p = 0; p < 4; ++p) dma_codes(1, p);
+  // meta quad 0, code group 0 and B 0 in (13 loads issued after them)
+  asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __syncthreads();  // unit 0 decoded by every wave
+  stage_barrier();  // table and every wave's B stage 0 visible
+  dec_in(0, 0, 0);
+  dec_in(1, 1, 1);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) f0[f] = frag(0, 0, f);
+  for (int S = 0; S < 2; ++S)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      dec_unit0(S, rb);
+      dec_unit1(S, rb);
+    }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tab_chunk(0, s, (s & 1) * 4, i);
+    if (s < 3) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dec_half(0, s, (s & 1) * 4, i);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) fb0[c] = fragB(0, 0, c);
 
-  auto step = [&](int u, auto phase) {
+  auto step = [&](int u, auto phase, auto tail) {
     constexpr int kPh = decltype(phase)::value;  // u mod 4
-    // L0: chunk 0 (f0); chunk-1 fragments -> f1; table entries of quads 3..7
-    // of unit u+1; quads 0..5 of unit u+1
+    constexpr bool kTail = decltype(tail)::value;  // the last four steps, residual ahead
+    constexpr int Sc = kPh & 1, Sn = Sc ^ 1;     // sets of units u (and u+2), u+1
+    // L0: chunk 0; B chunk 1 -> fb1; decode A(u) chunk 3 (tq 4..7); entries
+    // of A(u+1) chunk 0 -> tq 0..3
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8) f1[c] = frag(kPh, 1, c);
-      if (c < 5) dec_tab(3 + c);
-      if (c >= 2 && c < 14) {
-        if (((c - 2) & 1) == 0) dec_quad_a((c - 2) >> 1);
-        else dec_quad_b(u + 1, (c - 2) >> 1);
-      }
-      const int i = c >> 2, j = c & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+      if (c < 8) fb1[c] = fragB(kPh, 1, c);
+      if ((c & 1) == 0) dec_half(Sc, 3, 4, c >> 1);
+      if ((c & 1) && c < 8) tab_chunk(Sn, 0, 0, c >> 1);
+      mfma(c, 0, fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // L1: chunk 1 (f1); chunk-2 fragments -> f0; quads 6, 7; table entries of
-    // quads 8..15 (into the slots quads 0..7 no longer need)
+    // L1: chunk 1; B chunk 2 -> fb0; decode A(u+1) chunk 0; entries of chunk 1
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8) f0[c] = frag(kPh, 2, c);
-      if (c < 4) {
-        if ((c & 1) == 0) dec_quad_a(6 + (c >> 1));
-        else dec_quad_b(u + 1, 6 + (c >> 1));
-      }
-      if (c >= 4 && c < 12) dec_tab(8 + (c - 4));
-      const int i = c >> 2, j = c & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+      if (c < 8) fb0[c] = fragB(kPh, 2, c);
+      if ((c & 1) == 0) dec_half(Sn, 0, 0, c >> 1);
+      if ((c & 1) && c < 8) tab_chunk(Sn, 1, 4, c >> 1);
+      mfma(c, 1, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // L2: chunk 2 (f0); chunk-3 fragments -> f1; quads 8..15
+    // L2: chunk 2; B chunk 3 -> fb1; decode A(u+1) chunk 1; entries of chunk 2
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8) f1[c] = frag(kPh, 3, c);
-      if ((c & 1) == 0) dec_quad_a(8 + (c >> 1));
-      else dec_quad_b(u + 1, 8 + (c >> 1));
-      const int i = c >> 2, j = c & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+      if (c < 8) fb1[c] = fragB(kPh, 3, c);
+      if ((c & 1) == 0) dec_half(Sn, 1, 4, c >> 1);
+      if ((c & 1) && c < 8) tab_chunk(Sn, 2, 0, c >> 1);
+      mfma(c, 2, fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (kPh == 3) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // L3: chunk 3 (f1); chunk-0 fragments of stage u+1 -> f0; B stage u+2;
-    // codes of unit u+3; unit u+2 read; every fourth step the next meta quad
+    // L3: chunk 3; B chunk 0 of stage u+1 -> fb0; decode A(u+1) chunk 2;
+    // entries of chunk 3; unit u+2 read and prepared; DMA codes u+3, meta,
+    // B stage u+4 (or the first residual columns)
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      if (c < 8) {
-        f0[c] = frag(kPh + 1, 0, c);
-        dma_b(u + 2, c);
+      if (c == 0) dec_in(u + 2, Sc, (kPh + 2) & 3);
+      if (c < 8) fb0[c] = fragB((kPh + 1) & 3, 0, c);
+      if ((c & 1) == 0) dec_half(Sn, 2, 0, c >> 1);
+      if ((c & 1) && c < 8) tab_chunk(Sn, 3, 4, c >> 1);
+      if (c == 9) dec_unit0(Sc, 0);
+      if (c == 11) dec_unit0(Sc, 1);
+      if (c == 13) dec_unit1(Sc, 0);
+      if (c == 15) dec_unit1(Sc, 1);
+      if (c >= 2 && c < 10) {
+        if constexpr (kResid && kTail && kPh == 2) dma_resid(0, false, c - 2, 0);
+        else if constexpr (kResid && kTail && kPh == 3) dma_resid(0, true, c - 2, 1);
+        else dma_b(u + 2, c - 2);
       }
-      if (c == 0) dec_in(u + 2);
-      if (c == 8) dma_codes(u + 3, 0);
-      if (c == 9) dma_codes(u + 3, 1);
-      if constexpr (kPh == 1) {  // u + 3 = 4q: the quad holding units u+3.. (u+2 was its predecessor's last)
-        if (c == 11) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          dma_meta((u + 3) >> 2);
-        }
+      if (c == 10) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3));
+      if (c == 11) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3) + 1);
+      if constexpr (kPh == 2) {
+        if (c == 12) dma_meta((u + 6) >> 2);
       }
-      if (c == 4) dec_unit();
-      if (c >= 13) dec_tab(c - 13);
-      const int i = c >> 2, j = c & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+      mfma(c, 3, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const int KUp = (KUi + 3) & ~3;
-  for (int u = 0; u < KUp; u += 4) {
-    step(u + 0, std::integral_constant<int, 0>{});
-    step(u + 1, std::integral_constant<int, 1>{});
-    step(u + 2, std::integral_constant<int, 2>{});
-    step(u + 3, std::integral_constant<int, 3>{});
+  // with protected channels the last four steps are a copy whose last two
+  // B DMAs (stages past K) fetch residual chunk 0 instead
+  const int KUmain = kResid ? KUi - 4 : KUi;
+  for (int u = 0; u < KUmain; u += 4) {
+    step(u + 0, std::integral_constant<int, 0>{}, std::false_type{});
+    step(u + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    step(u + 2, std::integral_constant<int, 2>{}, std::false_type{});
+    step(u + 3, std::integral_constant<int, 3>{}, std::false_type{});
+  }
+  if constexpr (kResid) {
+    const int u = KUi - 4;
+    step(u + 0, std::integral_constant<int, 0>{}, std::true_type{});
+    step(u + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    step(u + 2, std::integral_constant<int, 2>{}, std::true_type{});
+    step(u + 3, std::integral_constant<int, 3>{}, std::true_type{});
   }
   wait_vmcnt0();  // no LDS-DMA may outlive the workgroup (or overlap the residual's)
 
   if constexpr (kResid) {
-    // Y += Xr Wr^T, 64 columns per chunk: Wr in B slot 0, Xr in decoded buffer 0
+    // Y += Xr Wr^T, 64 columns per chunk: Wr in B slot 0, Xr in B slot 1
+    // (chunk 0 was fetched by the last steps of the loop)
     const int chunks = KR / 64;
     for (int c = 0; c < chunks; ++c) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      stage_barrier();  // every wave is done with the previous contents
+      if (c > 0) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();  // every wave is done with the previous contents
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dma_resid(c, false, i);
-        dma_resid(c, true, i);
+        for (int i = 0; i < 8; ++i) {
+          dma_resid(c, false, i, 0);
+          dma_resid(c, true, i, 1);
+        }
+        wait_vmcnt0();
       }
-      wait_vmcnt0();
       stage_barrier();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8_t fr[8];
+        bf16x8_t fr[8], xa[2];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) fr[f] = frag(0, s, f);
+        for (int cb = 0; cb < 8; ++cb) fr[cb] = fragB(0, s, cb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int rb = 0; rb < 2; ++rb)
+          xa[rb] = *reinterpret_cast<const bf16x8_t*>(
+              lds + fbo[s] + kTileBytes2 + (wave * 64 + rb * 32) * kRowBytes2);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], fr[4 + j], acc[i][j], 0, 0, 0);
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[rb], fr[cb], acc[rb][cb], 0, 0, 0);
       }
     }
   }
 
-  // Epilogue. In the 32x32 MFMA output a lane holds one column and, per
-  // group g of 4 accumulator registers, 4 consecutive rows. A 4x4 transpose
-  // across each aligned quad of lanes (two DPP exchange steps) gives every
-  // lane 4 consecutive columns of one row instead, stored as one 16-byte
-  // (fp32) or 8-byte (bf16) write: a quarter of the store instructions of
-  // element-wise stores, each row segment written whole. Rows are
-  // 16-byte aligned when ldy % 4 == 0 (and Y is); otherwise, and for a
-  // column group that crosses N, the values go out one by one.
+  // Epilogue: as in the kernels above (4x4 lane-quad transpose, one 16- or
+  // 8-byte store per lane and group), for the row blocks rb of this wave and
+  // all eight column blocks.
   const int col_in = lane & 31, row_in = (lane >> 5) * 4, qt = lane & 3;
   const bool q_odd = (qt & 1) != 0, q_hi = (qt & 2) != 0;
   const bool vec_ok = (ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int colq = n0 + wn * 128 + j * 32 + (col_in & ~3);  // the quad's first column
+    for (int cb = 0; cb < 8; ++cb) {
+      const int colq = n0 + cb * 32 + (col_in & ~3);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        // step 1 (lanes t, t^1): c[t][k] = a[t^1][k^1] where bit 0 of k and t differ
+        const float v0 = acc[rb][cb][4 * g], v1 = acc[rb][cb][4 * g + 1];
+        const float v2 = acc[rb][cb][4 * g + 2], v3 = acc[rb][cb][4 * g + 3];
         const float x0 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v1)));
         const float x1 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v0)));
         const float x2 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v3)));
         const float x3 = __uint_as_float(dpp<kDppQuadXor1>(__float_as_uint(v2)));
         const float c0 = q_odd ? x0 : v0, c1 = q_odd ? v1 : x1;
         const float c2 = q_odd ? x2 : v2, c3 = q_odd ? v3 : x3;
-        // step 2 (lanes t, t^2): d[t][k] = c[t^2][k^2] where bit 1 of k and t differ
         const float y0 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c2)));
         const float y1 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c3)));
         const float y2 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c0)));
         const float y3 = __uint_as_float(dpp<kDppQuadXor2>(__float_as_uint(c1)));
         const float d0 = q_hi ? y0 : c0, d1 = q_hi ? y1 : c1;
         const float d2 = q_hi ? c2 : y2, d3 = q_hi ? c3 : y3;
-        // lane t of the quad: row (group row + t), columns colq .. colq + 3
-        const int row = m0 + wm * 128 + i * 32 + 8 * g + row_in + qt;
+        const int row = m0 + wave * 64 + rb * 32 + 8 * g + row_in + qt;
         if (row >= M || colq >= N) continue;
         const size_t off = (size_t)row * ldy + colq;
         if (vec_ok && colq + 4 <= N) {
-          // non-temporal: Y is written once and read by no one in this
-          // kernel, so it should not push the operand tiles out of L2/MALL
           if (y_bf16) {
             const uint32_t lo = f32_to_bf16_rne(d0) | (f32_to_bf16_rne(d1) << 16);
             const uint32_t hi = f32_to_bf16_rne(d2) | (f32_to_bf16_rne(d3) << 16);
@@ -1004,7 +1107,6 @@ void gemm_w4a4_u64_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __res
     }
   }
 }
-
 
 // Protected-channel values for the residual: kept [rows][nk] (dense, any
 // nk) -> out [rows][kr] zero-padded, kr a multiple of 64, so that the
@@ -1098,14 +1200,14 @@ hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
       const uint16_t* xs = kr ? xr + m0 * kr : nullptr;
       const uint16_t* ws = kr ? wr + n0 * kr : nullptr;
       const bool meta16 = (k / 64) % 4 == 0 && ((uintptr_t)am & 15) == 0;
-      // K % 256 == 0 with 16-byte meta rows: the unit-step schedule; other
+      // K % 256 == 0 with 16-byte meta rows: the register-decoded unit-step kernel; other
       // shapes take the 32-wide schedule
       if (meta16 && kr)
-        hipLaunchKernelGGL((gemm_w4a4_u64_kernel<true>), grid, dim3(256), 0, stream, xs, ws,
+        hipLaunchKernelGGL((gemm_w4a4_rd_kernel<true>), grid, dim3(256), 0, stream, xs, ws,
                            (int)kr, ac, am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16,
                            tiles_m, tiles_n);
       else if (meta16)
-        hipLaunchKernelGGL((gemm_w4a4_u64_kernel<false>), grid, dim3(256), 0, stream, xs, ws, 0, ac,
+        hipLaunchKernelGGL((gemm_w4a4_rd_kernel<false>), grid, dim3(256), 0, stream, xs, ws, 0, ac,
                            am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16, tiles_m, tiles_n);
       else if (kr)
         launch_w4a4<true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
