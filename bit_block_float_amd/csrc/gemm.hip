@@ -617,35 +617,40 @@ constexpr int kTileBytes2 = 256 * kRowBytes2;              // 32 KiB
 //   [65792, +64K)     code ring: 2 groups of 4 units x 256 rows x 128 B, chunk
 //                     c (= 2 x unit-in-group + half) of row r in slot
 //                     c ^ ((r >> 1) & 7)
-//   [131328, +8K)     meta ring: 2 slots x 256 rows x 16 B (4 units each)
+//   [131328, +16K)    meta ring: 2 groups of 8 units x 256 rows x 32 B, half c
+//                     (units 4c..4c+3) of row r in slot c ^ ((r >> 3) & 1)
 // Codes, meta and the table entries a lane reads are its own wave's rows,
 // fetched by its own wave: those reads need the wave's own vmcnt only.
 // Codes are fetched four units (one 128-byte line) per row, 8 rows per DMA
 // instruction: the cost of a DMA instruction grows with the cache lines it
 // touches, and one unit per row (32 rows of 32 B per instruction) made the
-// code fetch cost as much as the eight times larger B fetch.
+// code fetch cost as much as the eight times larger B fetch. Meta words
+// likewise come 8 units (32 B) per row, 32 rows per instruction.
 //
 // Step u (one unit, 64 MFMAs per wave, one barrier):
 //   L0  chunk 0 of unit u; B chunk-1 fragments; decode A(u) chunk 3;
 //       table entries for A(u+1) chunk 0 (decode halves in the even MFMA
-//       slots, table reads in the odd ones, so that at most ~6 VALU ops sit
-//       between two MFMAs)
+//       slots, table reads and the per-unit preparation pieces in the odd
+//       ones, so that at most ~6 VALU ops sit between two MFMAs: more than
+//       that leaves the matrix core idle)
 //   L1  chunk 1; B chunk 2; decode A(u+1) chunk 0; entries for chunk 1
 //   L2  chunk 2; B chunk 3; decode A(u+1) chunk 1; entries for chunk 2
 //   s_waitcnt vmcnt(0 or 1) + lgkmcnt(0) + barrier
 //   L3  chunk 3; B chunk-0 fragments of stage u+1; decode A(u+1) chunk 2;
 //       entries for chunk 3; codes + meta of unit u+2 read and prepared;
 //       DMA: B stage u+2, a quarter of code group (u+6)/4 (parts
-//       2((u+2)%4), +1 of 8), (u % 4 == 2) meta quad (u+6)/4
+//       2((u+2)%4), +1 of 8), (u % 4 == 2) half ((u+10)/4 % 2) of meta
+//       group (u+10)/8
 // A chunk s of unit u+1 overwrites chunk s of unit u once the MFMAs that
 // read it have issued, so one set of A registers serves (32 VGPRs).
 // Ring reuse: B slot u&1 held stage u (last read in L2 of step u, before the
 // barrier); code group g = (u+6)/4 goes to slot g&1, which held group g-2,
 // whose last unit 4g-5 was read in step 4g-7 (the group's parts go out in
-// steps 4g-6 .. 4g-3, and unit 4g is first read in step 4g-2); meta slot
-// q&1 held quad q-2, whose last unit was read in step 4q-7.
+// steps 4g-6 .. 4g-3, and unit 4g is first read in step 4g-2); meta group
+// G goes out in steps 8G-10 and 8G-6 to slot G&1, which held group G-2,
+// whose last unit 8G-9 was read in step 8G-11 (unit 8G is read in 8G-2).
 // vmcnt: at the barrier of step u, B stage u+1 and the codes of unit u+2
-// (all issued by step u-1) must be in; only a meta quad issued in step u-1
+// (all issued by step u-1) must be in; only a meta part issued in step u-1
 // (u % 4 == 3, issued last) may still be in flight: vmcnt(1), else vmcnt(0).
 // In the last steps the B DMA of stages past K reads clamped data into slots
 // no one reads; with protected channels the two such DMAs of the last two
@@ -655,7 +660,8 @@ constexpr int kRdB = 256;
 constexpr int kRdC = kRdB + 2 * kTileBytes2;       // 65792
 constexpr int kRdCodeGroup = 256 * 128;            // 4 units x 256 rows
 constexpr int kRdM = kRdC + 2 * kRdCodeGroup;      // 131328
-constexpr int kRdBytes = kRdM + 2 * 256 * 16;      // 139520
+constexpr int kRdMetaGroup = 256 * 32;             // 8 units x 256 rows
+constexpr int kRdBytes = kRdM + 2 * kRdMetaGroup;  // 147712
 
 // bits 0..3 of x -> the low bit of bytes 0..3 (the partial products of the
 // multiply land on disjoint bits, so nothing carries)
@@ -744,7 +750,10 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     voffC[e] = (uint32_t)(m0 + r) * (uint32_t)(K / 2) + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 16u);
   }
   const uint32_t KU = (uint32_t)(K / 64);
-  const uint32_t voffM = (uint32_t)(m0 + wave * 64 + lane) * KU * 4u;
+  // meta: half p of a group of 8 units: lane l -> row 32p + (l >> 1) of
+  // wave w's rows, slot l & 1 holding half (l & 1) ^ ((row >> 3) & 1)
+  const uint32_t voffM = (uint32_t)(m0 + wave * 64 + (lane >> 1)) * KU * 4u +
+                         (((uint32_t)(lane & 1) ^ ((uint32_t)(lane >> 4) & 1u)) * 16u);
   const int KUi = K / 64;
 
   auto dma_b = [&](int st, int i) {  // part i of B stage min(st, KU-1) into slot st & 1
@@ -761,10 +770,11 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
         rsAc, (lds_void_t*)dst, 16,
         voffC[p & 1] + (uint32_t)(p & ~1) * 8u * (uint32_t)(K / 2) + (uint32_t)g * 128u, 0, 0, 0);
   };
-  auto dma_meta = [&](int q) {  // units 4q..4q+3, 16 B per row, into slot q & 1
-    char* dst = lds + kRdM + (q & 1) * 4096 + wave * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsAm, (lds_void_t*)dst, 16,
-                                             voffM + (uint32_t)q * 16u, 0, 0, 0);
+  // part p (rows 32p..) of meta group G (units 8G..8G+7) into slot G & 1
+  auto dma_meta = [&](int G, int p) {
+    char* dst = lds + kRdM + (G & 1) * kRdMetaGroup + wave * 2048 + p * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsAm, (lds_void_t*)dst, 16, voffM + (uint32_t)p * 32u * KU * 4u + (uint32_t)G * 32u, 0, 0, 0);
   };
   // residual chunk c: Wr (is_x false) or Xr columns 64c.. into B slot `slot`,
   // with the stage swizzle; rows past M / N read zeros
@@ -796,7 +806,10 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   for (int j = 0; j < 4; ++j)
     cb4[j] = (uint32_t)kRdC + ((uint32_t)wave * 64u + r32) * 128u +
              (((2u * (uint32_t)j + hh) ^ fsw) << 4);
-  const uint32_t mbase = (uint32_t)kRdM + ((uint32_t)wave * 64u + r32) * 16u;
+  // meta word of lane row r32: half c of the row's group at slot c ^ msw
+  const uint32_t msw = (r32 >> 3) & 1u;
+  const uint32_t mb0 = (uint32_t)kRdM + ((uint32_t)wave * 64u + r32) * 32u + (msw << 4);
+  const uint32_t mb1 = (uint32_t)kRdM + ((uint32_t)wave * 64u + r32) * 32u + ((msw ^ 1u) << 4);
   const uint32_t sh2 = 8u + 4u * hh, sh3 = 16u + 8u * hh;
 
   auto fragB = [&](int slot, int s, int cb) -> bf16x8_t {
@@ -815,29 +828,36 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
 
   // unit un's meta and codes into set S; j = un & 3 (a compile-time constant)
   auto dec_in = [&](int un, int S, int j) {
-    const uint32_t msl = (uint32_t)((un >> 2) & 1) * 4096u + (uint32_t)j * 4u;
+    const uint32_t msl = (((un >> 2) & 1) ? mb1 : mb0) + (uint32_t)((un >> 3) & 1) * (uint32_t)kRdMetaGroup;
     const uint32_t csl = cb4[j] + (uint32_t)((un >> 2) & 1) * (uint32_t)kRdCodeGroup;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      mw[S][rb] = *reinterpret_cast<const uint32_t*>(lds + mbase + msl + rb * 512);
+      mw[S][rb] = *reinterpret_cast<const uint32_t*>(lds + msl + j * 4 + rb * 1024);
       cw[S][rb] = lds_v4(lds + csl + rb * 4096);
     }
   };
-  auto dec_unit0 = [&](int S, int rb) {  // offsets of quads 0..3
+  // Per row and unit, in six pieces of 3..6 VALU ops (each has an MFMA slot
+  // of its own): piece 0 puts 64m + 16p in every byte of both offset words;
+  // pieces 1..4 add 16 e2 and 16 e3 of quads 0..3 and 4..7; piece 5 makes the
+  // exponent add of the high plane (a in every byte, and without byte 0).
+  auto prep = [&](int S, int rb, int piece) {
     const uint32_t w = mw[S][rb];
-    const uint32_t base = ((w & 3u) << 6) | ((w & 4u) << 2);  // 64m + 16p
-    const uint32_t base4 = __builtin_amdgcn_perm(base, base, 0u);  // in all four bytes
-    const uint32_t e2 = w >> sh2, e3 = w >> sh3;
-    ew[S][rb][0] = ((spread2x2(e2) + spread4(e3)) << 4) + base4;
-    ew[S][rb][1] = base4;
-  };
-  auto dec_unit1 = [&](int S, int rb) {  // offsets of quads 4..7, exponent add
-    const uint32_t w = mw[S][rb];
-    const uint32_t e2 = w >> sh2, e3 = w >> sh3;
-    ew[S][rb][1] += (spread2x2(e2 >> 2) + spread4(e3 >> 4)) << 4;
-    const uint32_t a = (w & 255u) >> 3;
-    dd[S][rb] = __builtin_amdgcn_perm(a, a, 0u);
-    dd0[S][rb] = dd[S][rb] & 0xFFFFFF00u;
+    if (piece == 0) {
+      const uint32_t base = ((w & 3u) << 6) | ((w & 4u) << 2);
+      ew[S][rb][0] = ew[S][rb][1] = __builtin_amdgcn_perm(base, base, 0u);
+    } else if (piece == 1) {
+      ew[S][rb][0] += spread2x2(w >> sh2) << 4;
+    } else if (piece == 2) {
+      ew[S][rb][0] += spread4(w >> sh3) << 4;
+    } else if (piece == 3) {
+      ew[S][rb][1] += spread2x2(w >> (sh2 + 2u)) << 4;
+    } else if (piece == 4) {
+      ew[S][rb][1] += spread4(w >> (sh3 + 4u)) << 4;
+    } else {
+      const uint32_t a = (w & 255u) >> 3;
+      dd[S][rb] = __builtin_amdgcn_perm(a, a, 0u);
+      dd0[S][rb] = dd[S][rb] & 0xFFFFFF00u;
+    }
   };
   // table entry of quad j (0..7) of row block rb, set S, into tq[slot]
   auto tab = [&](int S, int rb, int j, int slot) {
@@ -898,20 +918,21 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
         __builtin_bit_cast(bf16x8_t, fa[rb][s]), fb[cb], acc[rb][cb], 0, 0, 0);
   };
 
-  // ---- prologue: meta quads 0 and 1, code group 0, B stages 0 and 1, and
-  // the parts 0..3 of code group 1 that steps -2 and -1 would have issued
-  // (parts 4..7 follow in steps 0 and 1)
-  dma_meta(0);
+  // ---- prologue: meta group 0, code group 0, B stages 0 and 1, the first
+  // half of meta group 1 (step -2's) and the parts 0..3 of code group 1 that
+  // steps -2 and -1 would have issued (parts 4..7 follow in steps 0 and 1)
+  dma_meta(0, 0);
+  dma_meta(0, 1);
 #pragma unroll
   for (int p = 0; p < 8; ++p) dma_codes(0, p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma_b(0, i);
-  dma_meta(1);
+  dma_meta(1, 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dma_b(1, i);
 #pragma unroll
   for (int p = 0; p < 4; ++p) dma_codes(1, p);
-  // meta quad 0, code group 0 and B 0 in (13 loads issued after them)
+  // meta group 0, code group 0 and B 0 in (13 loads issued after them)
   asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   stage_barrier();  // table and every wave's B stage 0 visible
@@ -921,8 +942,13 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   for (int S = 0; S < 2; ++S)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      dec_unit0(S, rb);
-      dec_unit1(S, rb);
+      if (S == 0) {
+#pragma unroll
+        for (int piece = 0; piece < 6; ++piece) prep(S, rb, piece);
+      } else {  // set 1 gets the pieces step -1 would have made (0, 1)
+        prep(S, rb, 0);
+        prep(S, rb, 1);
+      }
     }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -946,7 +972,9 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     for (int c = 0; c < 16; ++c) {
       if (c < 8) fb1[c] = fragB(kPh, 1, c);
       if ((c & 1) == 0) dec_half(Sc, 3, 4, c >> 1);
-      if ((c & 1) && c < 8) tab_chunk(Sn, 0, 0, c >> 1);
+      if (c == 1 || c == 3) prep(Sn, c >> 1, 2);
+      if (c >= 5 && c <= 11 && (c & 1)) tab_chunk(Sn, 0, 0, (c - 5) >> 1);
+      if (c == 13 || c == 15) prep(Sn, (c - 13) >> 1, 5);
       mfma(c, 0, fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -956,6 +984,8 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       if (c < 8) fb0[c] = fragB(kPh, 2, c);
       if ((c & 1) == 0) dec_half(Sn, 0, 0, c >> 1);
       if ((c & 1) && c < 8) tab_chunk(Sn, 1, 4, c >> 1);
+      if (c == 9 || c == 11) prep(Sn, (c - 9) >> 1, 3);
+      if (c == 13 || c == 15) prep(Sn, (c - 13) >> 1, 4);
       mfma(c, 1, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -982,10 +1012,8 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       if (c < 8) fb0[c] = fragB((kPh + 1) & 3, 0, c);
       if ((c & 1) == 0) dec_half(Sn, 2, 0, c >> 1);
       if ((c & 1) && c < 8) tab_chunk(Sn, 3, 4, c >> 1);
-      if (c == 9) dec_unit0(Sc, 0);
-      if (c == 11) dec_unit0(Sc, 1);
-      if (c == 13) dec_unit1(Sc, 0);
-      if (c == 15) dec_unit1(Sc, 1);
+      if (c == 9 || c == 11) prep(Sc, (c - 9) >> 1, 0);
+      if (c == 13 || c == 15) prep(Sc, (c - 13) >> 1, 1);
       if (c >= 2 && c < 10) {
         if constexpr (kResid && kTail && kPh == 2) dma_resid(0, false, c - 2, 0);
         else if constexpr (kResid && kTail && kPh == 3) dma_resid(0, true, c - 2, 1);
@@ -994,7 +1022,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       if (c == 10) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3));
       if (c == 11) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3) + 1);
       if constexpr (kPh == 2) {
-        if (c == 12) dma_meta((u + 6) >> 2);
+        if (c == 12) dma_meta((u + 10) >> 3, ((u + 10) >> 2) & 1);
       }
       mfma(c, 3, fb1);
       __builtin_amdgcn_sched_barrier(0);
