@@ -604,20 +604,24 @@ constexpr int kTileBytes2 = 256 * kRowBytes2;              // 32 KiB
 // fp32 roundings; this one makes a lane's codes for the four chunks of a
 // unit one 16-byte run of its row (code word 4h + s = level-2 group 4h + s).
 //
-// Table addressing: for a row and unit the lane precomputes, per quad it
-// decodes, the byte offset 64m + 16(p + E) of its table entry (E = e2 + e3
-// of the quad); these 8 offsets (each <= 240) sit in the bytes of two words,
-// so a quad's entry address is one byte extract. The table lives at LDS
-// address 0 for that reason.
+// Decode table: 512 entries, one per (a, m, s = p + E), the high plane
+// already multiplied by 2^(2a), so a quad decodes without the two adds of
+// the exponent (a = e >> 1, e = 2a + p the level-1 exponent). Entry
+// (a, m, s) sits at 256a + 16((4m + s + a) & 15): rotating each a-block by a
+// spreads the entries 16 rows of different a read together over bank
+// groups. For a row and unit the lane precomputes, per quad it decodes, the
+// byte 16((4m + p + E + a) & 15) (E = e2 + e3 of the quad); these 8 bytes sit
+// in two words, and a quad's entry address is one v_perm of a byte of them
+// and a. The table lives at LDS address 0 for that reason.
 //
 // LDS map (bytes):
-//   [0, 256)          decode table, entry (m, s) at 64m + 16s
-//   [256, +64K)       B ring: 2 stages x 256 rows x 128 B, chunk c of row r in
+//   [0, 8K)           decode table, entry (a, m, s) at 256a + 16((4m + s + a) & 15)
+//   [8192, +64K)      B ring: 2 stages x 256 rows x 128 B, chunk c of row r in
 //                     slot c ^ ((r >> 1) & 7)
-//   [65792, +64K)     code ring: 2 groups of 4 units x 256 rows x 128 B, chunk
+//   [73728, +64K)     code ring: 2 groups of 4 units x 256 rows x 128 B, chunk
 //                     c (= 2 x unit-in-group + half) of row r in slot
 //                     c ^ ((r >> 1) & 7)
-//   [131328, +16K)    meta ring: 2 groups of 8 units x 256 rows x 32 B, half c
+//   [139264, +16K)    meta ring: 2 groups of 8 units x 256 rows x 32 B, half c
 //                     (units 4c..4c+3) of row r in slot c ^ ((r >> 3) & 1)
 // Codes, meta and the table entries a lane reads are its own wave's rows,
 // fetched by its own wave: those reads need the wave's own vmcnt only.
@@ -656,12 +660,12 @@ constexpr int kTileBytes2 = 256 * kRowBytes2;              // 32 KiB
 // no one reads; with protected channels the two such DMAs of the last two
 // steps fetch the first 64 residual columns of Wr and Xr into slots 0 and 1.
 constexpr int kRdT = 0;
-constexpr int kRdB = 256;
-constexpr int kRdC = kRdB + 2 * kTileBytes2;       // 65792
+constexpr int kRdB = 8192;
+constexpr int kRdC = kRdB + 2 * kTileBytes2;       // 73728
 constexpr int kRdCodeGroup = 256 * 128;            // 4 units x 256 rows
-constexpr int kRdM = kRdC + 2 * kRdCodeGroup;      // 131328
+constexpr int kRdM = kRdC + 2 * kRdCodeGroup;      // 139264
 constexpr int kRdMetaGroup = 256 * 32;             // 8 units x 256 rows
-constexpr int kRdBytes = kRdM + 2 * kRdMetaGroup;  // 147712
+constexpr int kRdBytes = kRdM + 2 * kRdMetaGroup;  // 155648
 
 // bits 0..3 of x -> the low bit of bytes 0..3 (the partial products of the
 // multiply land on disjoint bits, so nothing carries)
@@ -705,15 +709,19 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // decode table: entry (m, s = E + p) at 64m + 16s
-  if (tid < 16) {
-    const int m = tid >> 2, sx = tid & 3;
+  // decode table: entry (a, m, s = E + p) at 256a + 16((4m + s + a) & 15), its high
+  // plane already multiplied by 2^(2a) (a added to every non-zero high byte);
+  // rotating each a-block by a spreads rows of different a over bank groups
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 2 * tid + h;  // a = e >> 4, 4m + s = e & 15
+    const int a = e >> 4, m = (e >> 2) & 3, sx = e & 3;
     const float d = ldexpf(1.0f + 0.25f * (float)m, sx - 33);
     uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
 #pragma unroll
     for (int k = 1; k < 8; ++k) {
       const uint32_t bits = __float_as_uint((float)k * d) >> 16;
-      const uint32_t lb = bits & 0xFFu, hb = bits >> 8;
+      const uint32_t lb = bits & 0xFFu, hb = (bits >> 8) + (uint32_t)a;
       if (k < 4) {
         lo0 |= lb << (8 * k);
         hi0 |= hb << (8 * k);
@@ -723,7 +731,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       }
     }
     const u32x4_t v = {lo0, lo1, hi0, hi1};
-    *reinterpret_cast<u32x4_t*>(lds + kRdT + 16 * tid) = v;
+    *reinterpret_cast<u32x4_t*>(lds + kRdT + 256 * a + 16 * (((e & 15) + a) & 15)) = v;
   }
 
   const __amdgpu_buffer_rsrc_t rsAc =
@@ -821,7 +829,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   // table offsets, exponent add for the high plane
   uint32_t mw[2][2];
   u32x4_t cw[2][2];
-  uint32_t ew[2][2][2], dd[2][2], dd0[2][2];
+  uint32_t ew[2][2][2], dd[2][2];  // per set and row: entry offsets of the 8 quads, a
   u32x4_t tq[8];
   u32x4_t fa[2][4];
   uint32_t qlo = 0, qhi = 0;
@@ -836,32 +844,31 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       cw[S][rb] = lds_v4(lds + csl + rb * 4096);
     }
   };
-  // Per row and unit, in six pieces of 3..6 VALU ops (each has an MFMA slot
-  // of its own): piece 0 puts 64m + 16p in every byte of both offset words;
-  // pieces 1..4 add 16 e2 and 16 e3 of quads 0..3 and 4..7; piece 5 makes the
-  // exponent add of the high plane (a in every byte, and without byte 0).
+  // Per row and unit, in five pieces of 3..6 VALU ops (each has an MFMA slot
+  // of its own): piece 0 puts 4m + p + a in every byte of both offset words
+  // and keeps a (dd); pieces 1..4 add e2 and e3 of quads 0..3 and 4..7, and
+  // pieces 2 and 4 turn each byte into 16 ((4m + p + E + a) & 15).
   auto prep = [&](int S, int rb, int piece) {
     const uint32_t w = mw[S][rb];
-    if (piece == 0) {
-      const uint32_t base = ((w & 3u) << 6) | ((w & 4u) << 2);
+    if (piece == 0) {  // 4m + p + a in every byte of both offset words, a apart
+      const uint32_t c = w & 255u;
+      const uint32_t base = ((c & 3u) << 2) + ((c >> 2) & 1u) + (c >> 3);
       ew[S][rb][0] = ew[S][rb][1] = __builtin_amdgcn_perm(base, base, 0u);
+      dd[S][rb] = c >> 3;
     } else if (piece == 1) {
-      ew[S][rb][0] += spread2x2(w >> sh2) << 4;
+      ew[S][rb][0] += spread2x2(w >> sh2);
     } else if (piece == 2) {
-      ew[S][rb][0] += spread4(w >> sh3) << 4;
+      ew[S][rb][0] = ((ew[S][rb][0] + spread4(w >> sh3)) & 0x0F0F0F0Fu) << 4;
     } else if (piece == 3) {
-      ew[S][rb][1] += spread2x2(w >> (sh2 + 2u)) << 4;
+      ew[S][rb][1] += spread2x2(w >> (sh2 + 2u));
     } else if (piece == 4) {
-      ew[S][rb][1] += spread4(w >> (sh3 + 4u)) << 4;
-    } else {
-      const uint32_t a = (w & 255u) >> 3;
-      dd[S][rb] = __builtin_amdgcn_perm(a, a, 0u);
-      dd0[S][rb] = dd[S][rb] & 0xFFFFFF00u;
+      ew[S][rb][1] = ((ew[S][rb][1] + spread4(w >> (sh3 + 4u))) & 0x0F0F0F0Fu) << 4;
     }
   };
   // table entry of quad j (0..7) of row block rb, set S, into tq[slot]
+  // entry address 256a + (byte j&3 of the offset word): one v_perm
   auto tab = [&](int S, int rb, int j, int slot) {
-    const uint32_t off = (ew[S][rb][j >> 2] >> (8 * (j & 3))) & 255u;
+    const uint32_t off = __builtin_amdgcn_perm(dd[S][rb], ew[S][rb][j >> 2], 0x0C0C0400u | (uint32_t)(j & 3));
     tq[slot] = lds_v4(lds + kRdT + off);
   };
   // quad j (even: low nibbles of code word j/2, odd: high nibbles), two halves
@@ -870,7 +877,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     const uint32_t sel = ((j & 1) ? (word >> 4) : word) & 0x07070707u;
     const u32x4_t tv = tq[slot];
     qlo = __builtin_amdgcn_perm(tv.y, tv.x, sel);
-    qhi = __builtin_amdgcn_perm(tv.w + dd[S][rb], tv.z + dd0[S][rb], sel);
+    qhi = __builtin_amdgcn_perm(tv.w, tv.z, sel);
   };
   auto dq_b = [&](int S, int rb, int j) {
     const uint32_t word = cw[S][rb][j >> 1];
@@ -944,7 +951,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     for (int rb = 0; rb < 2; ++rb) {
       if (S == 0) {
 #pragma unroll
-        for (int piece = 0; piece < 6; ++piece) prep(S, rb, piece);
+        for (int piece = 0; piece < 5; ++piece) prep(S, rb, piece);
       } else {  // set 1 gets the pieces step -1 would have made (0, 1)
         prep(S, rb, 0);
         prep(S, rb, 1);
@@ -974,7 +981,6 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       if ((c & 1) == 0) dec_half(Sc, 3, 4, c >> 1);
       if (c == 1 || c == 3) prep(Sn, c >> 1, 2);
       if (c >= 5 && c <= 11 && (c & 1)) tab_chunk(Sn, 0, 0, (c - 5) >> 1);
-      if (c == 13 || c == 15) prep(Sn, (c - 13) >> 1, 5);
       mfma(c, 0, fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
