@@ -198,6 +198,42 @@ def test_linear_ragged_shapes(hip, m, n, k, via_codes):
     run_linear_case(hip, xb, wb, via_codes=via_codes)
 
 
+@pytest.mark.parametrize("m,n,k,n_kept", [(1, 1, 256, 0), (300, 260, 256, 0), (300, 260, 256, 5),
+                                          (257, 130, 512, 0), (257, 130, 512, 70),
+                                          (520, 300, 1280, 0), (64, 520, 2304, 129)])
+def test_linear_unit_step_kernel_edges(hip, m, n, k, n_kept):
+    """The unit-step contraction (K % 256 == 0) at its loop-structure edges:
+    K = 256 (one block of four unit steps; with protected channels only the
+    copy of the last four steps that fetches the residual), K = 512 (the first
+    full 8-unit meta group), K = 1280 and 2304 (20 and 36 units: code groups
+    and meta groups that end mid-group), one-output and ragged tiles, and 1 to
+    3 residual chunks. Against the oracle, through the decoded-weight entry
+    point (the bench's) and the codes entry point."""
+    print(f"[case] unit-step {m}x{n}x{k} n_kept={n_kept}", flush=True)
+    r = np.random.default_rng(m * 7 + n + k + n_kept)
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + k, outlier_channels=2))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=n + k))
+    if n_kept:
+        mask = np.zeros(k, np.uint8)
+        mask[r.choice(k, n_kept, replace=False)] = 1
+        xc, xm, xk = oracle.quantize(xb, mask)
+        wc, wm, wk = oracle.quantize(wb, mask)
+        y_ref, s_ref = oracle.linear_protected(xc, xm, xk, wc, wm, wk)
+        xkd, wkd = _bf16_dev(xk), _bf16_dev(wk)
+    else:
+        xc, xm, _ = oracle.quantize(xb)
+        wc, wm, _ = oracle.quantize(wb)
+        y_ref, s_ref = oracle.linear(xc, xm, wc, wm)
+        xkd = wkd = None
+    xcd, xmd = torch.from_numpy(xc).cuda(), torch.from_numpy(xm.view(np.int32)).cuda()
+    wcd, wmd = torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda()
+    w_deq = hip.dequantize(wcd, wmd, out_dtype=torch.bfloat16)
+    y1 = hip.linear_xcodes_wbf16(xcd, xmd, w_deq, x_kept=xkd, w_kept=wkd)
+    check_linear(y1.cpu().numpy(), y_ref, s_ref)
+    y2 = hip.linear_w4a4(wcd, wmd, x_codes=xcd, x_meta=xmd, x_kept=xkd, w_kept=wkd)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 def random_units(rows, k, seed):
     """Arbitrary well-formed HiF4 units: every level-1 code, every micro-exponent
     pattern, every nibble (both signs, both zeros)."""
