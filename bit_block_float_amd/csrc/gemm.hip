@@ -681,12 +681,19 @@ __device__ __forceinline__ u32x4_t lds_v4(const char* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-template <bool kResid>
+// kNB: 32-column blocks per wave. 8 is the 256x256 tile; 4 is a 256x128 half
+// tile, launched (two per tile) only for the tiles of a last partial round of
+// workgroups, tile_base being the first of them in the tile order below: a
+// half tile decodes as much as a whole one but does half the MFMAs, DMA and
+// fragment reads, so the last round ends sooner than with whole tiles.
+template <bool kResid, int kNB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __restrict__ Wr, int KR,
                          const uint8_t* __restrict__ Ac, const uint32_t* __restrict__ Am,
                          const uint16_t* __restrict__ B, int M, int N, int K,
-                         void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m, int tiles_n) {
+                         void* __restrict__ Y, int64_t ldy, int y_bf16, int tiles_m, int tiles_n,
+                         int tile_base) {
+  static_assert(kNB == 8 || kNB == 4, "whole or half tiles");
   __shared__ __attribute__((aligned(1024))) char lds[kRdBytes];
 
   const int tid = threadIdx.x;
@@ -694,7 +701,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int ntiles = tiles_m * tiles_n;
-  int t = blockIdx.x;
+  int t = kNB == 8 ? (int)blockIdx.x : tile_base + (int)(blockIdx.x >> 1);
   {
     const int per_xcd = ntiles / 8;
     if (t < per_xcd * 8) t = (t & 7) * per_xcd + (t >> 3);
@@ -707,7 +714,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     t = (first_m + in % gsize) * tiles_n + in / gsize;
   }
   const int tm = t / tiles_n, tn = t - (t / tiles_n) * tiles_n;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * kBM, n0 = tn * kBN + (kNB == 8 ? 0 : (int)(blockIdx.x & 1) * 128);
 
   // decode table: entry (a, m, s = E + p) at 256a + 16((4m + s + a) & 15), its high
   // plane already multiplied by 2^(2a) (a added to every non-zero high byte);
@@ -740,12 +747,12 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       __builtin_amdgcn_make_buffer_rsrc((void*)Am, (short)0, M * (K / 64) * 4, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, N * K * 2, kRsrcWord3);
-  // B: wave w rows 64w.. of the stage, 8 x 1 KiB (8 rows each); lane l ->
+  // B: wave w rows 8 kNB w.. of the stage, kNB x 1 KiB (8 rows each); lane l ->
   // row 8i + (l >> 3), LDS slot l & 7 holding global chunk (l & 7) ^ ((row >> 1) & 7)
-  uint32_t voffB[8];
+  uint32_t voffB[8];  // (arrays sized by kNB break the host-side instantiation)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t r = (uint32_t)(wave * 64 + 8 * i + (lane >> 3));
+  for (int i = 0; i < kNB; ++i) {
+    const uint32_t r = (uint32_t)(wave * 8 * kNB + 8 * i + (lane >> 3));
     voffB[i] = ((uint32_t)(n0 + r) * (uint32_t)K + (((uint32_t)(lane & 7) ^ ((r >> 1) & 7u)) * 8u)) * 2u;
   }
   // codes: a group of 4 units of wave w's rows 64w.. is 8 x 1 KiB (8 rows of
@@ -765,7 +772,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
   const int KUi = K / 64;
 
   auto dma_b = [&](int st, int i) {  // part i of B stage min(st, KU-1) into slot st & 1
-    char* dst = lds + kRdB + (st & 1) * kTileBytes2 + wave * 64 * kRowBytes2 + i * 1024;
+    char* dst = lds + kRdB + (st & 1) * kTileBytes2 + wave * 8 * kNB * kRowBytes2 + i * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t*)dst, 16, voffB[i],
                                              min(st, KUi - 1) * kRowBytes2, 0, 0);
   };
@@ -906,11 +913,11 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     tab(S, rb, 2 * s + jj, tb + i);
   };
 
-  f32x16_t acc[2][8];
+  f32x16_t acc[2][8];  // the first kNB blocks used
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 #pragma unroll
@@ -920,7 +927,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
 
   bf16x8_t fb0[8], fb1[8];
   auto mfma = [&](int c, int s, const bf16x8_t* fb) {
-    const int rb = c >> 3, cb = c & 7;
+    const int rb = c / kNB, cb = c % kNB;
     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         __builtin_bit_cast(bf16x8_t, fa[rb][s]), fb[cb], acc[rb][cb], 0, 0, 0);
   };
@@ -933,14 +940,15 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
 #pragma unroll
   for (int p = 0; p < 8; ++p) dma_codes(0, p);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma_b(0, i);
+  for (int i = 0; i < kNB; ++i) dma_b(0, i);
   dma_meta(1, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma_b(1, i);
+  for (int i = 0; i < kNB; ++i) dma_b(1, i);
 #pragma unroll
   for (int p = 0; p < 4; ++p) dma_codes(1, p);
-  // meta group 0, code group 0 and B 0 in (13 loads issued after them)
-  asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+  // meta group 0, code group 0 and B 0 in (5 + kNB loads issued after them)
+  if constexpr (kNB == 8) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   stage_barrier();  // table and every wave's B stage 0 visible
   dec_in(0, 0, 0);
@@ -967,12 +975,13 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
     }
   }
 #pragma unroll
-  for (int c = 0; c < 8; ++c) fb0[c] = fragB(0, 0, c);
+  for (int c = 0; c < kNB; ++c) fb0[c] = fragB(0, 0, c);
 
   auto step = [&](int u, auto phase, auto tail) {
     constexpr int kPh = decltype(phase)::value;  // u mod 4
     constexpr bool kTail = decltype(tail)::value;  // the last four steps, residual ahead
     constexpr int Sc = kPh & 1, Sn = Sc ^ 1;     // sets of units u (and u+2), u+1
+    if constexpr (kNB == 8) {
     // L0: chunk 0; B chunk 1 -> fb1; decode A(u) chunk 3 (tq 4..7); entries
     // of A(u+1) chunk 0 -> tq 0..3
 #pragma unroll
@@ -1033,6 +1042,60 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       mfma(c, 3, fb1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    } else {
+    // Half tile: 8 MFMAs per K-chunk, one slot each, the same work per step
+    // otherwise (the decode of 8 halves per chunk fills every slot).
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < 4) fb1[c] = fragB(kPh, 1, c);
+      dec_half(Sc, 3, 4, c);
+      if (c < 2) prep(Sn, c, 2);
+      if (c >= 4) tab_chunk(Sn, 0, 0, c - 4);
+      mfma(c, 0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < 4) fb0[c] = fragB(kPh, 2, c);
+      dec_half(Sn, 0, 0, c);
+      if (c < 2) prep(Sn, c, 3);
+      else if (c < 4) prep(Sn, c - 2, 4);
+      if (c >= 4) tab_chunk(Sn, 1, 4, c - 4);
+      mfma(c, 1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < 4) fb1[c] = fragB(kPh, 3, c);
+      dec_half(Sn, 1, 4, c);
+      if (c >= 4) tab_chunk(Sn, 2, 0, c - 4);
+      mfma(c, 2, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kPh == 3) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c == 0) dec_in(u + 2, Sc, (kPh + 2) & 3);
+      if (c < 4) fb0[c] = fragB((kPh + 1) & 3, 0, c);
+      dec_half(Sn, 2, 0, c);
+      if (c >= 4) tab_chunk(Sn, 3, 4, c - 4);
+      if (c == 4 || c == 5) prep(Sc, c - 4, 0);
+      if (c == 6 || c == 7) prep(Sc, c - 6, 1);
+      if constexpr (kResid && kTail && (kPh == 2 || kPh == 3)) dma_resid(0, kPh == 3, c, kPh - 2);
+      else if (c < 4) dma_b(u + 2, c);
+      if (c == 4) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3));
+      if (c == 5) dma_codes((u + 6) >> 2, 2 * ((kPh + 2) & 3) + 1);
+      if constexpr (kPh == 2) {
+        if (c == 7) dma_meta((u + 10) >> 3, ((u + 10) >> 2) & 1);
+      }
+      mfma(c, 3, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    }
   };
   // with protected channels the last four steps are a copy whose last two
   // B DMAs (stages past K) fetch residual chunk 0 instead
@@ -1072,7 +1135,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
       for (int s = 0; s < 4; ++s) {
         bf16x8_t fr[8], xa[2];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) fr[cb] = fragB(0, s, cb);
+        for (int cb = 0; cb < kNB; ++cb) fr[cb] = fragB(0, s, cb);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           xa[rb] = *reinterpret_cast<const bf16x8_t*>(
@@ -1080,7 +1143,7 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb)
+          for (int cb = 0; cb < kNB; ++cb)
             acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[rb], fr[cb], acc[rb][cb], 0, 0, 0);
       }
     }
@@ -1088,14 +1151,14 @@ void gemm_w4a4_rd_kernel(const uint16_t* __restrict__ Xr, const uint16_t* __rest
 
   // Epilogue: as in the kernels above (4x4 lane-quad transpose, one 16- or
   // 8-byte store per lane and group), for the row blocks rb of this wave and
-  // all eight column blocks.
+  // its kNB column blocks.
   const int col_in = lane & 31, row_in = (lane >> 5) * 4, qt = lane & 3;
   const bool q_odd = (qt & 1) != 0, q_hi = (qt & 2) != 0;
   const bool vec_ok = (ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
+    for (int cb = 0; cb < kNB; ++cb) {
       const int colq = n0 + cb * 32 + (col_in & ~3);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -1212,6 +1275,42 @@ static void launch_w4a4(dim3 grid, hipStream_t stream, const uint16_t* xr, const
                      ac, am, b, mc, nc, k, ys, ldy, y_bf16, tiles_m, tiles_n);
 }
 
+// The register-decoded kernel over tiles_m x tiles_n tiles. When at most two
+// whole rounds of tiles (one workgroup per CU) leave a last partial round of
+// at most half the CUs, those tiles go to a second launch as half tiles, two
+// workgroups each, which end that round sooner; the split follows the
+// kernel's own tile order, so the two launches cover every tile exactly once.
+// After more rounds the CUs finish at times spread widely enough that the
+// leftover tiles of a single launch, started by the first CUs to free up,
+// end sooner than a second launch could start (measured: 8192 x 5120 x 5120,
+// 640 tiles, 0.377 -> 0.359 ms split; FFN-up, 12,150 tiles, 6.10 -> 6.17 ms).
+template <bool kResid>
+static void launch_rd(int tiles_m, int tiles_n, hipStream_t stream, const uint16_t* xr,
+                      const uint16_t* wr, int kr, const uint8_t* ac, const uint32_t* am,
+                      const uint16_t* b, int mc, int nc, int k, void* ys, int64_t ldy, int y_bf16) {
+  static int cu_count[64];  // per device, queried once (0: not yet, or unknown)
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    cus = cu_count[dev];
+    if (cus == 0 &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cu_count[dev] = cus;
+  }
+  if (cus < 0) cus = 0;
+  const int ntiles = tiles_m * tiles_n;
+  const int tail = cus > 0 ? ntiles % cus : 0;
+  const bool split = tail != 0 && 2 * tail <= cus && ntiles - tail <= 2 * cus;
+  const int whole = split ? ntiles - tail : ntiles;
+  if (whole > 0)
+    hipLaunchKernelGGL((gemm_w4a4_rd_kernel<kResid, 8>), dim3((unsigned)whole), dim3(256), 0,
+                       stream, xr, wr, kr, ac, am, b, mc, nc, k, ys, ldy, y_bf16, tiles_m, tiles_n,
+                       0);
+  if (split)
+    hipLaunchKernelGGL((gemm_w4a4_rd_kernel<kResid, 4>), dim3((unsigned)(2 * tail)), dim3(256), 0,
+                       stream, xr, wr, kr, ac, am, b, mc, nc, k, ys, ldy, y_bf16, tiles_m, tiles_n,
+                       whole);
+}
+
 hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
                                  const uint16_t* b, int64_t m, int64_t n, int64_t k, void* y,
                                  int y_bf16, const uint16_t* xr, const uint16_t* wr, int64_t kr,
@@ -1237,12 +1336,11 @@ hipError_t hif4_launch_gemm_w4a4(const uint8_t* a_codes, const uint32_t* a_meta,
       // K % 256 == 0 with 16-byte meta rows: the register-decoded unit-step kernel; other
       // shapes take the 32-wide schedule
       if (meta16 && kr)
-        hipLaunchKernelGGL((gemm_w4a4_rd_kernel<true>), grid, dim3(256), 0, stream, xs, ws,
-                           (int)kr, ac, am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16,
-                           tiles_m, tiles_n);
+        launch_rd<true>(tiles_m, tiles_n, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
+                        (int)k, ys, (int64_t)n, y_bf16);
       else if (meta16)
-        hipLaunchKernelGGL((gemm_w4a4_rd_kernel<false>), grid, dim3(256), 0, stream, xs, ws, 0, ac,
-                           am, bs, (int)mc, (int)nc, (int)k, ys, (int64_t)n, y_bf16, tiles_m, tiles_n);
+        launch_rd<false>(tiles_m, tiles_n, stream, xs, ws, 0, ac, am, bs, (int)mc, (int)nc, (int)k,
+                         ys, (int64_t)n, y_bf16);
       else if (kr)
         launch_w4a4<true>(grid, stream, xs, ws, (int)kr, ac, am, bs, (int)mc, (int)nc,
                                  (int)k, ys, n, y_bf16, tiles_m, tiles_n);

@@ -234,6 +234,38 @@ def test_linear_unit_step_kernel_edges(hip, m, n, k, n_kept):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("m,n,k,n_kept", [(2304, 4096, 512, 0), (2304, 4096, 512, 70),
+                                          (4608, 4096, 256, 0), (4608, 4096, 256, 5)])
+def test_linear_whole_and_half_tiles(hip, m, n, k, n_kept):
+    """Enough 256x256 tiles for the whole-tile kernel: 144 tiles (more than half
+    of the MI355X's 256 CUs: whole tiles only) and 288 (one round of whole tiles,
+    then the last 32 as 64 half tiles). Two rows of every tile row are checked
+    against the oracle over all columns, so every tile and half tile is."""
+    print(f"[case] tiles {m}x{n}x{k} n_kept={n_kept}", flush=True)
+    r = np.random.default_rng(m + n + k + n_kept)
+    xb = workloads.bits(workloads.heavy_tailed_x(m, k, seed=m + k + 1, outlier_channels=2))
+    wb = workloads.bits(workloads.normal_bf16(n, k, 0.02, seed=n + k + 1))
+    rows = np.sort(np.concatenate([np.arange(0, m, 256) + 17, np.arange(0, m, 256) + 230]))
+    rows = rows[rows < m]
+    if n_kept:
+        mask = np.zeros(k, np.uint8)
+        mask[r.choice(k, n_kept, replace=False)] = 1
+        xc, xm, xk = oracle.quantize(xb, mask)
+        wc, wm, wk = oracle.quantize(wb, mask)
+        y_ref, s_ref = oracle.linear_protected(xc[rows], xm[rows], xk[rows], wc, wm, wk)
+        xkd, wkd = _bf16_dev(xk), _bf16_dev(wk)
+    else:
+        xc, xm, _ = oracle.quantize(xb)
+        wc, wm, _ = oracle.quantize(wb)
+        y_ref, s_ref = oracle.linear(xc[rows], xm[rows], wc, wm)
+        xkd = wkd = None
+    xcd, xmd = torch.from_numpy(xc).cuda(), torch.from_numpy(xm.view(np.int32)).cuda()
+    wcd, wmd = torch.from_numpy(wc).cuda(), torch.from_numpy(wm.view(np.int32)).cuda()
+    w_deq = hip.dequantize(wcd, wmd, out_dtype=torch.bfloat16)
+    y = hip.linear_xcodes_wbf16(xcd, xmd, w_deq, x_kept=xkd, w_kept=wkd)
+    check_linear(y[torch.from_numpy(rows).cuda()].cpu().numpy(), y_ref, s_ref)
+
+
 def random_units(rows, k, seed):
     """Arbitrary well-formed HiF4 units: every level-1 code, every micro-exponent
     pattern, every nibble (both signs, both zeros)."""
