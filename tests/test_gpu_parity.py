@@ -235,6 +235,7 @@ def test_linear_unit_step_kernel_edges(hip, m, n, k, n_kept):
 
 
 @pytest.mark.parametrize("m,n,k,n_kept", [(2304, 4096, 512, 0), (2304, 4096, 512, 70),
+                                          (2304, 4093, 256, 3),   # odd N: element-wise stores
                                           (4608, 4096, 256, 0), (4608, 4096, 256, 5)])
 def test_linear_whole_and_half_tiles(hip, m, n, k, n_kept):
     """Enough 256x256 tiles for the whole-tile kernel: 144 tiles (more than half
