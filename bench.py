@@ -46,13 +46,24 @@ def log(msg):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping numbers (a virtualised host may report only a family name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo", encoding="utf-8"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = (t.strip() for t in line.split(":", 1))
+                if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                    fields[key] = val
+            elif fields:
+                break  # first processor's block only
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = "/".join(fields.get(k, "?") for k in ("cpu family", "model", "stepping"))
+    return f"{name} (family/model/stepping {ids}, {os.cpu_count()} logical CPUs visible)"
 
 
 def cpu_baseline(x, w, mask_np, rows_sample):
