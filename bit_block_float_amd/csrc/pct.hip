@@ -777,39 +777,41 @@ __global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
     const int64_t n_slabs = (rows + per_wg - 1) / per_wg;
     uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int64_t nbelow = 0;
-    // The channel's partials, kBatch slabs at a time with every load issued
-    // before any is summed (a slab's second partial is read only when a
-    // slice boundary -- a multiple of per_wg -- falls strictly inside its
-    // unit; otherwise it is never written and its words are masked off).
-    // Batches of 4 keep the kernel at 72 VGPRs, 7 waves per SIMD, so its one
-    // wave per channel fits the chip in one round at 5120 channels (batches
-    // of 8: 128 VGPRs, 12.9 instead of 11.3 us at FFN-up).
-    constexpr int kBatch = 4;
-    for (int64_t sb = 0; sb < n_slabs; sb += kBatch) {
-      uint4 w[2 * kBatch];
-      uint32_t bl[2 * kBatch];
-      bool use[2 * kBatch];
+    // The channel's partials. A unit of a whole slab starts at a multiple of
+    // per_wg and is per_wg rows long: it is one slice, one segment, and only
+    // its first partial is written. Only the last slab's units (shorter than
+    // per_wg) can straddle a slice boundary; then the unit's second partial
+    // holds the rest. So the partials are p = 0 .. n_slabs - 1 (first
+    // partial of slab p), plus, when the channel block's last unit straddles,
+    // p = n_slabs (that unit's second partial): one wave-uniform test, no
+    // division per partial.
+    bool last_two = false;
+    if (n_slabs > full_slabs) {
+      const int64_t rn = rows - full_slabs * per_wg;
+      const int64_t s0 = full_slabs * cblocks * per_wg + cb * rn;
+      last_two = s0 / per_wg != (s0 + rn - 1) / per_wg;
+    }
+    const int64_t n_part = n_slabs + (last_two ? 1 : 0);
+    // kBatch partials at a time, every load issued before any is summed;
+    // indexes past the end read the last partial again, not summed. Batches
+    // of 8 keep the kernel within 72 VGPRs (7 waves per SIMD: its one wave per
+    // channel fits the chip in one round at 5120 channels).
+    constexpr int kBatch = 8;
+    for (int64_t pb = 0; pb < n_part; pb += kBatch) {
+      uint4 w[kBatch];
+      uint32_t bl[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const int64_t slab = min(sb + i, n_slabs - 1);
-        const int64_t rn = slab < full_slabs ? per_wg : rows - full_slabs * per_wg;
-        const int64_t s0 = slab * cblocks * per_wg + cb * rn;
-        const bool two = s0 / per_wg != (s0 + rn - 1) / per_wg;
-        const int64_t unit = slab * cblocks + cb;
-        use[2 * i] = sb + i < n_slabs;
-        use[2 * i + 1] = use[2 * i] && two;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          // an unused second partial reads the first one again (a valid address)
-          const uint32_t* src = part + (2 * unit + (use[2 * i + 1] ? k : 0)) * kPartWords +
-                                (int64_t)col * kPartStride;
-          w[2 * i + k] = reinterpret_cast<const uint4*>(src)[lane];
-          bl[2 * i + k] = src[kWin / 2];
-        }
+        const int64_t p = min(pb + i, n_part - 1);
+        const int64_t slab = p < n_slabs ? p : n_slabs - 1;
+        const uint32_t* src = part + (2 * (slab * cblocks + cb) + (p < n_slabs ? 0 : 1)) * kPartWords +
+                              (int64_t)col * kPartStride;
+        w[i] = reinterpret_cast<const uint4*>(src)[lane];
+        bl[i] = src[kWin / 2];
       }
 #pragma unroll
-      for (int i = 0; i < 2 * kBatch; ++i) {
-        if (!use[i]) continue;
+      for (int i = 0; i < kBatch; ++i) {
+        if (pb + i >= n_part) continue;
         cnt[0] += w[i].x & 0xFFFFu;
         cnt[1] += w[i].x >> 16;
         cnt[2] += w[i].y & 0xFFFFu;
