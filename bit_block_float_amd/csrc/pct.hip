@@ -389,7 +389,12 @@ __global__ __launch_bounds__(256) void pct_final_kernel(const uint32_t* __restri
 // sample that misled) is computed exactly from its column in the same final
 // kernel (pct_resolve_kernel), which also builds the mask.
 constexpr int kWin = 512;          // keys in the window
-constexpr int kPartStride = 260;   // u32 per column of a partial: 256 packed words, below, pad
+// u32 per column of a partial: 256 packed words, below, pad to a whole number
+// of 128-byte lines (so that the flush below writes whole lines)
+constexpr int kPartStride = 288;
+// LDS words per histogram row ([bin/2][column]): one pad word, so that the
+// flush's lanes that read 8 consecutive quads of one column hit 8 banks
+constexpr int kHistStride = kPctCh + 1;
 constexpr int64_t kPartWords = (int64_t)kPctCh * kPartStride;  // one partial (a segment's counts)
 
 // The window pass. A key below the window only adds to its lane's register
@@ -415,9 +420,9 @@ constexpr int64_t kPartWords = (int64_t)kPctCh * kPartStride;  // one partial (a
 __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int c, int64_t ld, int64_t per_wg,
     const uint32_t* __restrict__ wlo, uint32_t* __restrict__ part) {
-  __shared__ uint32_t hist[(kWin / 2) * kPctCh];  // [bin/2][column]
+  __shared__ uint32_t hist[(kWin / 2) * kHistStride];  // [bin/2][column]
   __shared__ uint32_t below[kPctCh];
-  for (int i = threadIdx.x; i < (kWin / 2) * kPctCh; i += kPctThreads) hist[i] = 0u;
+  for (int i = threadIdx.x; i < (kWin / 2) * kHistStride; i += kPctThreads) hist[i] = 0u;
   for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) below[i] = 0u;
   __syncthreads();
 
@@ -468,7 +473,8 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
           // bit set) exactly for keys below the window
           const uint32_t d = key - wv[e];
           nb[e] += d >> 31;
-          if (d < (uint32_t)kWin) atomicAdd(&hist[(d >> 1) * kPctCh + col[e]], 1u << (16 * (d & 1u)));
+          if (d < (uint32_t)kWin)
+            atomicAdd(&hist[(d >> 1) * kHistStride + col[e]], 1u << (16 * (d & 1u)));
         }
       }
     };
@@ -516,17 +522,21 @@ __global__ __launch_bounds__(kPctThreads) void pct_window_kernel(
     const int64_t slab = r0 / per_wg;
     const int64_t unit = slab * cblocks + c0 / kPctCh;
     uint32_t* dst = part + (2 * unit + (r0 == slab * per_wg ? 0 : 1)) * kPartWords;
+    // Item i = (column, quad: words 4 quad .. 4 quad + 3). The 8 lanes of an
+    // aligned group take 8 consecutive quads of one column, so each group
+    // stores one whole 128-byte line of the partial (64 lanes: 8 columns).
     for (int i = threadIdx.x; i < (kWin / 8) * kPctCh; i += kPctThreads) {
-      const int col = i % kPctCh, quad = i / kPctCh;  // words 4 quad .. 4 quad + 3
+      const int grp = i >> 6, l = i & 63;
+      const int quad = (grp & 7) * 8 + (l & 7), col = (grp >> 3) * 8 + (l >> 3);
       uint4 w;
-      w.x = hist[(4 * quad + 0) * kPctCh + col];
-      w.y = hist[(4 * quad + 1) * kPctCh + col];
-      w.z = hist[(4 * quad + 2) * kPctCh + col];
-      w.w = hist[(4 * quad + 3) * kPctCh + col];
-      hist[(4 * quad + 0) * kPctCh + col] = 0u;
-      hist[(4 * quad + 1) * kPctCh + col] = 0u;
-      hist[(4 * quad + 2) * kPctCh + col] = 0u;
-      hist[(4 * quad + 3) * kPctCh + col] = 0u;
+      w.x = hist[(4 * quad + 0) * kHistStride + col];
+      w.y = hist[(4 * quad + 1) * kHistStride + col];
+      w.z = hist[(4 * quad + 2) * kHistStride + col];
+      w.w = hist[(4 * quad + 3) * kHistStride + col];
+      hist[(4 * quad + 0) * kHistStride + col] = 0u;
+      hist[(4 * quad + 1) * kHistStride + col] = 0u;
+      hist[(4 * quad + 2) * kHistStride + col] = 0u;
+      hist[(4 * quad + 3) * kHistStride + col] = 0u;
       *reinterpret_cast<uint4*>(dst + col * kPartStride + 4 * quad) = w;
     }
     for (int i = threadIdx.x; i < kPctCh; i += kPctThreads) {

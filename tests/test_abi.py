@@ -215,12 +215,14 @@ def test_percentile_argument_checks(L):
 
 def test_percentile_workspace_grows_with_rows(L):
     """Long columns (>= 8192 rows) add the one-pass path's per-segment
-    partials: 2 per (slab, 128-channel block), 128 x 260 u32 each. For
+    partials: 2 per (slab, 128-channel block), 128 x 288 u32 each (per
+    channel 256 packed bin words, the below count and padding to whole
+    128-byte lines). For
     57,600 x 5120 the slabs are 9000 rows (57,600 x 40 blocks over 256
     workgroups): 7 slabs x 40 blocks x 2 = 560 partials."""
     w = L.hif4_percentile_workspace_bytes
     assert w(8191, 5120) == w(100, 5120)
-    assert w(57600, 5120) - w(100, 5120) == 560 * 128 * 260 * 4
+    assert w(57600, 5120) - w(100, 5120) == 560 * 128 * 288 * 4
 
 
 def test_quantize_f32_argument_checks(L):
