@@ -892,9 +892,14 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
   __shared__ uint32_t hist[256 * kSampStride];
   for (int i = threadIdx.x; i < 256 * kSampStride; i += kPctThreads) hist[i] = 0u;
   __syncthreads();
-  // 8 loads in flight per lane (74 VGPRs): at FFN-up a part's 1200 sampled
-  // rows take two blocks (28.7 us against 30.0 us with 4)
-  constexpr int kUnroll = 8, kRowStep = 8 * kPctWaves;
+  // Single-buffered blocks of kUnroll steps (8 rows per wave per step,
+  // 128 rows per step): all of a block's loads go out at once and are counted
+  // as they arrive. 11 steps (1408 rows) cover a part at 5120 channels (1200
+  // rows at FFN-up, at most 1366) in one block, and the kernel stays within
+  // 64 VGPRs, so two workgroups share a CU and its grid (480 workgroups at
+  // 5120 channels) runs in one round. Double-buffered blocks of 8 needed 80
+  // VGPRs: one workgroup per CU, about two rounds.
+  constexpr int kUnroll = 11, kHalf = 6, kRowStep = 8 * kPctWaves;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 3, p = lane & 7;
   const int rw = 8 * wave + g;  // row of the lane inside a step
@@ -903,25 +908,34 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
   // this part's sampled rows [rbeg, rend)
   const int64_t rbeg = rows_s * blockIdx.y / parts, rend = rows_s * (blockIdx.y + 1) / parts;
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  // lanes past the last channel read channel 0 (a valid address); their
-  // columns are never read back. The row base of a block is wave-uniform;
-  // the lane's row and channel ride in its 32-bit offset (ld <= 2^20 here:
-  // below 2^31 over the 512 rows of a block of loads).
+  // Lanes past the last channel read channel 0 (a valid address); their
+  // columns are never read back. Offsets are 32-bit from a wave-uniform row
+  // base: steps 0..kHalf-1 of a block from its first row, the others from
+  // row kHalf * kRowStep, so that an offset spans at most kHalf * 128 rows of
+  // ld <= 2^20 elements (below 2^31 bytes). Each base's buffer range ends
+  // with the part's last row: loads of rows past it return zeros (and are
+  // not counted); a base at or past the end gets an empty range.
   const uint32_t vb = (uint32_t)((rw * ld + (ch < c ? ch : 0)) * 2);
-  const int sstep = (int)(kRowStep * ld * 2);
-  auto load = [&](u32x4_t (&v)[kUnroll], int64_t rb) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
+  const uint32_t sstep = (uint32_t)(kRowStep * ld * 2);
+  const int64_t blk = (int64_t)kUnroll * kRowStep;
+  for (int64_t rb = rbeg; rb < rend; rb += blk) {
+    u32x4_t v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, u * sstep, 2);
-      v[u] = *reinterpret_cast<const u32x4_t*>(&qq);
+    for (int h = 0; h < 2; ++h) {
+      const int64_t hb = rb + (int64_t)h * kHalf * kRowStep;
+      const int64_t nrec = hb < rend ? min((rend - hb) * ld * 2, (int64_t)0x7FFFFFFF) : 0;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(x + min(hb, rend - 1) * ld), (short)0, (int)nrec, kRsrcWord3Pct);
+#pragma unroll
+      for (int u = h * kHalf; u < (h == 0 ? kHalf : kUnroll); ++u) {
+        const auto qq =
+            __builtin_amdgcn_raw_buffer_load_b128(rs, (int)vb, (int)((u - h * kHalf) * sstep), 2);
+        v[u] = *reinterpret_cast<const u32x4_t*>(&qq);
+      }
     }
-  };
-  auto count = [&](const u32x4_t (&v)[kUnroll], int64_t rb, bool tail) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (tail && rb + rw + (int64_t)u * kRowStep >= rend) continue;  // row past the part
+      if (rb + rw + (int64_t)u * kRowStep >= rend) continue;  // row past the part
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t word = v[u][e >> 1];
@@ -929,37 +943,6 @@ __global__ __launch_bounds__(kPctThreads) void pct_sample_kernel(
         atomicAdd(&hist[bin * kSampStride + 8 * p + e], 1u);
       }
     }
-  };
-  const int64_t blk = (int64_t)kUnroll * kRowStep;
-  int64_t rb = rbeg;
-  u32x4_t va[kUnroll], vc[kUnroll];
-  if (rb + blk <= rend) {
-    load(va, rb);
-    for (;;) {
-      const bool nxt = rb + 2 * blk <= rend;
-      load(vc, nxt ? rb + blk : rb);
-      count(va, rb, false);
-      rb += blk;
-      if (!nxt) break;
-      const bool nxt2 = rb + 2 * blk <= rend;
-      load(va, nxt2 ? rb + blk : rb);
-      count(vc, rb, false);
-      rb += blk;
-      if (!nxt2) break;
-    }
-  }
-  if (rb < rend) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(x + rb * ld), (short)0, 0x7FFFFFFF, kRsrcWord3Pct);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int64_t r = rb + rw + (int64_t)u * kRowStep;
-      if (r > rend - 1) r = rend - 1;
-      const auto qq = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, (int)(((r - rb) * ld + (ch < c ? ch : 0)) * 2), 0, 2);
-      va[u] = *reinterpret_cast<const u32x4_t*>(&qq);
-    }
-    count(va, rb, true);
   }
   __syncthreads();
   // [channel][bin]: consecutive threads store consecutive bins of a channel
