@@ -508,6 +508,20 @@ def test_percentile_sampled_window_misled_falls_back(hip):
         assert run_pct_case(hip, bits, q, 9) >= 20  # at least the 20 zero columns fall back
 
 
+def test_percentile_sample_pass_in_several_blocks(hip):
+    """A wide activation: 16,448 channels, i.e. 257 blocks of 64, so one
+    sample part per block. With 11,400 rows (1,425 sampled, every 8th) that
+    part is longer than the 1,408 rows one single-buffered block of the sample
+    pass reads. The pass takes two blocks, the second one 17 rows long, and
+    every statistic still matches."""
+    r = np.random.default_rng(71)
+    rows, c = 11400, 16448
+    scale = np.exp(r.standard_normal(c)).astype(np.float32)
+    x = r.standard_normal((rows, c), dtype=np.float32) * scale
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # bf16 by truncation
+    assert run_pct_case(hip, bits, 0.999, 40) == 0
+
+
 def test_percentile_ties_across_many_channels(hip):
     """Most channels share one statistic: the protected ties are the lowest
     channel indices, counted across every thread of the mask kernel."""
