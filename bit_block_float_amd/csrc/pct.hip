@@ -804,8 +804,8 @@ __global__ __launch_bounds__(kResolveThreads) void pct_resolve_kernel(
     const int64_t n_part = n_slabs + (last_two ? 1 : 0);
     // kBatch partials at a time, every load issued before any is summed;
     // indexes past the end read the last partial again, not summed. Batches
-    // of 8 keep the kernel within 72 VGPRs (7 waves per SIMD: its one wave per
-    // channel fits the chip in one round at 5120 channels).
+    // of 8 keep the kernel at 78 VGPRs (6 waves per SIMD: its one wave per
+    // channel, 5 per SIMD at 5120 channels, fits the chip in one round).
     constexpr int kBatch = 8;
     for (int64_t pb = 0; pb < n_part; pb += kBatch) {
       uint4 w[kBatch];
